@@ -1,0 +1,181 @@
+"""CPU fp64 oracle for the tensor-parallel MLP shard forward.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product path never imports this
+package, and this package imports nothing from the product path.
+
+The arithmetic is in ``tp_mlp_oracle.c`` (plain fp64 loops in the order of the
+definition, OpenMP over output rows).  This wrapper only widens inputs exactly
+to float64 and marshals pointers.  Input arrays may be float64, float32, or
+uint16 holding bfloat16 bit patterns; bf16 widening puts the 16 bits in the
+top half of a float32, which is exact.
+
+Definition (cited passages in the C file's header):
+  W_i = W[:, i*Fk:(i+1)*Fk], b_i = b[i*Fk:(i+1)*Fk], V_i = V[i*Fk:(i+1)*Fk, :]
+  Y_i = GeLU(X W_i + b_i),  GeLU(x) = x/2 (1 + erf(x/sqrt 2))
+  Z_i = Y_i V_i,  Z = sum_i Z_i  (shard order).
+
+Every function here is pinned by tests/test_oracle_pins.py (brute force in
+exact rational arithmetic with 50-digit erf, the column-split and row-split
+identities, GeLU closed forms, special cases that reduce to library routines,
+row independence and exact scaling).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tp_mlp_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build_oracle(force: bool = False) -> str:
+    """Compile liboracle.so with gcc and OpenMP."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build_oracle()
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.oracle_gelu.argtypes = [ctypes.c_double]
+        lib.oracle_gelu.restype = ctypes.c_double
+        lib.oracle_gelu_array.argtypes = [vp, i64, vp]
+        lib.oracle_col_preact.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        lib.oracle_col_gelu.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        lib.oracle_row_partial.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
+        lib.oracle_shard_reduce.argtypes = [vp, ci, i64, vp]
+        lib.oracle_forward_rows.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp, i64, vp]
+        lib.oracle_max_threads.restype = ci
+        for f in (lib.oracle_gelu_array, lib.oracle_col_preact, lib.oracle_col_gelu,
+                  lib.oracle_row_partial, lib.oracle_shard_reduce, lib.oracle_forward_rows):
+            f.restype = None
+        _lib = lib
+    return _lib
+
+
+def widen(a) -> np.ndarray:
+    """Exact float64 copy of a float64/float32 array or of bf16 bits in uint16."""
+    a = np.asarray(a)
+    if a.dtype == np.float64:
+        return np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a.astype(np.float64)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    raise TypeError("oracle inputs must be float64, float32 or uint16 (bf16 bits), got %s" % a.dtype)
+
+
+def _p(a):
+    return a.ctypes.data if a is not None else None
+
+
+def max_threads() -> int:
+    return int(_L().oracle_max_threads())
+
+
+def gelu_scalar(x: float) -> float:
+    return float(_L().oracle_gelu(float(x)))
+
+
+def gelu(x) -> np.ndarray:
+    x = widen(x)
+    y = np.empty_like(x)
+    _L().oracle_gelu_array(_p(x), x.size, _p(y))
+    return y
+
+
+def _check_shard(F: int, k: int, i: int):
+    if k < 1 or F % k:
+        raise ValueError("k must be >= 1 and divide F")
+    if not 0 <= i < k:
+        raise ValueError("shard index out of range")
+
+
+def col_preact(X, W, b, k: int, i: int) -> np.ndarray:
+    """A_i = X W_i + b_i, float64 [M, F/k].  b may be None."""
+    X, W = widen(X), widen(W)
+    b = widen(b) if b is not None else None
+    M, H = X.shape
+    F = W.shape[1]
+    assert W.shape[0] == H
+    _check_shard(F, k, i)
+    A = np.empty((M, F // k))
+    _L().oracle_col_preact(_p(X), _p(W), _p(b), M, H, F, k, i, _p(A))
+    return A
+
+
+def col_gelu(X, W, b, k: int, i: int) -> np.ndarray:
+    """Y_i = GeLU(X W_i + b_i), float64 [M, F/k]."""
+    X, W = widen(X), widen(W)
+    b = widen(b) if b is not None else None
+    M, H = X.shape
+    F = W.shape[1]
+    assert W.shape[0] == H
+    _check_shard(F, k, i)
+    Y = np.empty((M, F // k))
+    _L().oracle_col_gelu(_p(X), _p(W), _p(b), M, H, F, k, i, _p(Y))
+    return Y
+
+
+def row_partial(Yi, V, k: int, i: int) -> np.ndarray:
+    """Z_i = Y_i V_i with V the full [F, H] matrix, float64 [M, H]."""
+    Yi, V = widen(Yi), widen(V)
+    F, H = V.shape
+    _check_shard(F, k, i)
+    M, Fk = Yi.shape
+    assert Fk == F // k
+    Z = np.empty((M, H))
+    _L().oracle_row_partial(_p(Yi), _p(V), M, F, H, k, i, _p(Z))
+    return Z
+
+
+def shard_reduce(parts) -> np.ndarray:
+    """Z = parts[0] + ... + parts[k-1] (float64, left to right)."""
+    ws = [np.ascontiguousarray(widen(p)).reshape(-1) for p in parts]
+    n = ws[0].size
+    assert all(w.size == n for w in ws)
+    ptrs = (ctypes.c_void_p * len(ws))(*[w.ctypes.data for w in ws])
+    Z = np.empty(n)
+    _L().oracle_shard_reduce(ptrs, len(ws), n, _p(Z))
+    return Z.reshape(np.asarray(parts[0]).shape)
+
+
+def forward_rows(X, W, b, V, k: int, rows=None) -> np.ndarray:
+    """Z[rows, :] of the whole forward, float64 [len(rows), H] (all rows if None)."""
+    X, W, V = widen(X), widen(W), widen(V)
+    b = widen(b) if b is not None else None
+    M, H = X.shape
+    F = W.shape[1]
+    assert W.shape[0] == H and V.shape == (F, H)
+    _check_shard(F, k, 0)
+    if rows is None:
+        r = None
+        nrows = M
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        if r.size and (r.min() < 0 or r.max() >= M):
+            raise IndexError("row index out of range")
+        nrows = r.size
+    Z = np.empty((nrows, H))
+    if nrows:
+        _L().oracle_forward_rows(_p(X), _p(W), _p(b), _p(V), H, F, k, _p(r), nrows, _p(Z))
+    return Z
+
+
+def forward(X, W, b, V, k: int) -> np.ndarray:
+    """Z = sum_i GeLU(X W_i + b_i) V_i, float64 [M, H]."""
+    return forward_rows(X, W, b, V, k, None)

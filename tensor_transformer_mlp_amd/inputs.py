@@ -1,0 +1,206 @@
+"""Seeded synthetic inputs for the tensor-parallel MLP shard forward.
+
+This module draws numbers and lays them out; it holds none of the MLP's
+arithmetic.  The GPU path and the CPU oracle are both fed from it, so they see
+bit-identical inputs.  Draws come from ``csrc/synth_inputs.c`` (counter-based
+Philox4x64-10 plus Box-Muller, OpenMP), built with gcc into ``libtpsynth.so``.
+
+Workloads (the shapes of the MLP block on the pages: the first linear layer
+W is (H, 4H) and the second V is (4H, H), "大模型分布式并行策略详解：TP、DP、PP、CP、EP
+核心原理与实战" §4.1; weights laid out ``[in, out]`` and X as ``[batch, seq,
+hidden]`` as in the ColumnParallelLinear / RowParallelLinear classes of
+"AI大模型分布式训练：张量并行与流水线并行深度实践" §2.1-2.2):
+
+=============  ===========  =====  =====  ==  =====  =====  =======
+name           B x S = M    H      F      k   F/k    dtype  std
+=============  ===========  =====  =====  ==  =====  =====  =======
+tiny           1x8 = 8      64     256    2   128    f32    0.02
+gpt2_small     8x1024       768    3072   4   768    bf16   0.02
+llama7b        4x2048       4096   16384  8   2048   bf16   0.02
+gpt3_175b      1x2048       12288  49152  8   6144   bf16   0.006
+long_seq       1x32768      8192   32768  8   4096   bf16   0.01
+=============  ===========  =====  =====  ==  =====  =====  =======
+
+X ~ N(0, 1); W, b, V ~ N(0, std) (the second parameter is the standard
+deviation).  Streams: X = 0, W = 1, b = 2, V = 3 under base seed 42.  The full
+W, b and V are drawn first and shards are slices of them, so the same weights
+serve every shard count k.  bf16 workloads store the float32 draw rounded to
+nearest-even bfloat16 (as raw uint16 bit patterns on the host).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "csrc", "synth_inputs.c")
+_LIB_PATH = os.path.join(_HERE, "libtpsynth.so")
+
+STREAM_X, STREAM_W, STREAM_B, STREAM_V = 0, 1, 2, 3
+BASE_SEED = 42
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    S: int
+    H: int
+    F: int
+    k: int
+    dtype: str  # "f32" or "bf16"
+    std: float
+
+    @property
+    def M(self) -> int:
+        return self.B * self.S
+
+    @property
+    def Fk(self) -> int:
+        return self.F // self.k
+
+    @property
+    def flop(self) -> int:
+        """Two GEMMs of 2*M*H*(F/k) per shard, k shards: 4*M*H*F."""
+        return 4 * self.M * self.H * self.F
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "S": self.S, "M": self.M, "H": self.H,
+                "F": self.F, "k": self.k, "Fk": self.Fk, "dtype": self.dtype,
+                "init_std": self.std}
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny", 1, 8, 64, 256, 2, "f32", 0.02),
+        Workload("gpt2_small", 8, 1024, 768, 3072, 4, "bf16", 0.02),
+        Workload("llama7b", 4, 2048, 4096, 16384, 8, "bf16", 0.02),
+        Workload("gpt3_175b", 1, 2048, 12288, 49152, 8, "bf16", 0.006),
+        Workload("long_seq", 1, 32768, 8192, 32768, 8, "bf16", 0.01),
+    ]
+}
+
+
+def build_synth(force: bool = False) -> str:
+    """Compile libtpsynth.so with gcc (host code only)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _synth():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build_synth()
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, u64, dbl, vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_double, ctypes.c_void_p
+        lib.synth_philox4x64.argtypes = [vp, vp, ctypes.c_int, vp]
+        lib.synth_normal_f64.argtypes = [u64, u64, i64, i64, vp]
+        lib.synth_normal_f32.argtypes = [u64, u64, i64, i64, dbl, vp]
+        lib.synth_normal_bf16.argtypes = [u64, u64, i64, i64, dbl, vp]
+        lib.synth_round_bf16.argtypes = [vp, i64, vp]
+        for f in (lib.synth_philox4x64, lib.synth_normal_f64, lib.synth_normal_f32,
+                  lib.synth_normal_bf16, lib.synth_round_bf16):
+            f.restype = None
+        _lib = lib
+    return _lib
+
+
+def philox4x64(ctr, key, rounds: int = 10) -> np.ndarray:
+    c = np.ascontiguousarray(ctr, dtype=np.uint64)
+    kk = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.zeros(4, dtype=np.uint64)
+    _synth().synth_philox4x64(c.ctypes.data, kk.ctypes.data, rounds, out.ctypes.data)
+    return out
+
+
+def normal_f64(stream: int, n: int, first: int = 0, seed: int = BASE_SEED) -> np.ndarray:
+    out = np.empty(n, dtype=np.float64)
+    if n:
+        _synth().synth_normal_f64(seed, stream, first, n, out.ctypes.data)
+    return out
+
+
+def draw(stream: int, shape, std: float, dtype: str, seed: int = BASE_SEED, first: int = 0) -> np.ndarray:
+    """N(0, std) of ``shape``: float32 array, or uint16 bf16 bit patterns."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    if dtype == "f32":
+        out = np.empty(shape, dtype=np.float32)
+        if n:
+            _synth().synth_normal_f32(seed, stream, first, n, float(std), out.ctypes.data)
+    elif dtype == "bf16":
+        out = np.empty(shape, dtype=np.uint16)
+        if n:
+            _synth().synth_normal_bf16(seed, stream, first, n, float(std), out.ctypes.data)
+    else:
+        raise ValueError("dtype must be 'f32' or 'bf16', got %r" % (dtype,))
+    return out
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """float32 array -> bf16 bit patterns (round to nearest, ties to even)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    if a.size:
+        _synth().synth_round_bf16(a.ctypes.data, a.size, out.ctypes.data)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def make_inputs(w: Workload, seed: int = BASE_SEED, M: int | None = None) -> dict:
+    """Full X[M,H], W[H,F], b[F], V[F,H] for a workload (host numpy arrays).
+
+    ``M`` overrides the row count (rows are a prefix of the same X stream).
+    """
+    M = w.M if M is None else M
+    return {
+        "X": draw(STREAM_X, (M, w.H), 1.0, w.dtype, seed),
+        "W": draw(STREAM_W, (w.H, w.F), w.std, w.dtype, seed),
+        "b": draw(STREAM_B, (w.F,), w.std, w.dtype, seed),
+        "V": draw(STREAM_V, (w.F, w.H), w.std, w.dtype, seed),
+    }
+
+
+def make_custom(M: int, H: int, F: int, dtype: str, std: float = 0.02, x_std: float = 1.0,
+                seed: int = BASE_SEED) -> dict:
+    """Inputs of an arbitrary shape from the same four streams."""
+    return {
+        "X": draw(STREAM_X, (M, H), x_std, dtype, seed),
+        "W": draw(STREAM_W, (H, F), std, dtype, seed),
+        "b": draw(STREAM_B, (F,), std, dtype, seed),
+        "V": draw(STREAM_V, (F, H), std, dtype, seed),
+    }
+
+
+def shard_slices(W: np.ndarray, b: np.ndarray, V: np.ndarray, k: int):
+    """Contiguous per-shard copies: W_i = W[:, i*Fk:(i+1)*Fk], b_i, V_i = V[i*Fk:(i+1)*Fk, :].
+
+    Shard i owns the i-th block of columns of W (entries of b, rows of V), in
+    index order, as in the column split W = [W_1, W_2] and the row split of V on
+    "千亿参数模型如何拆分到多张GPU上训练" (张量并行 section).  This is data
+    placement only (what each GPU of a TP group would hold).
+    """
+    F = W.shape[1]
+    if F % k:
+        raise ValueError("k must divide F")
+    Fk = F // k
+    Ws = [np.ascontiguousarray(W[:, i * Fk:(i + 1) * Fk]) for i in range(k)]
+    bs = [np.ascontiguousarray(b[i * Fk:(i + 1) * Fk]) for i in range(k)]
+    Vs = [np.ascontiguousarray(V[i * Fk:(i + 1) * Fk, :]) for i in range(k)]
+    return Ws, bs, Vs
