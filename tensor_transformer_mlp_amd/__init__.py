@@ -1,0 +1,214 @@
+"""MI355X (gfx950) tensor-parallel MLP shard forward.
+
+Python binding of libtpmlp.so (C ABI in include/tp_mlp.h).  The functions have
+the C names and only marshal arguments: PyTorch supplies device memory and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is not built, or a tensor is not
+on the GPU, the call raises.
+
+    Y_i = GeLU(X W_i + b_i)      tp_mlp_col_gelu
+    Z_i = Y_i V_i                tp_mlp_row_partial
+    Z   = sum_i Z_i              tp_shard_reduce
+    all of the above, k shards   tp_mlp_shard_forward
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "TP_F32", "TP_BF16", "TP_ACCUMULATE", "TP_FUSED_ACCUM", "TP_MAX_SHARDS", "TpMlpError",
+    "lib", "tp_status_string", "tp_mlp_version", "tp_mlp_col_gelu", "tp_mlp_row_partial",
+    "tp_shard_reduce", "tp_mlp_workspace_bytes", "tp_mlp_shard_forward",
+]
+
+TP_F32 = 0
+TP_BF16 = 1
+TP_ACCUMULATE = 1
+TP_FUSED_ACCUM = 1
+TP_MAX_SHARDS = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtpmlp.so")
+_lib = None
+
+
+class TpMlpError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (status %d)" % (where, tp_status_string(code), code))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtpmlp.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libtpmlp.so is not built (run `python -m tensor_transformer_mlp_amd.build`"
+                               " or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, ci, cu, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+        L.tp_status_string.argtypes = [ci]
+        L.tp_status_string.restype = ctypes.c_char_p
+        L.tp_mlp_version.argtypes = []
+        L.tp_mlp_version.restype = ci
+        L.tp_mlp_col_gelu.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
+        L.tp_mlp_col_gelu.restype = ci
+        L.tp_mlp_row_partial.argtypes = [vp, vp, vp, i64, i64, i64, ci, cu, vp]
+        L.tp_mlp_row_partial.restype = ci
+        L.tp_shard_reduce.argtypes = [vp, ci, vp, i64, vp]
+        L.tp_shard_reduce.restype = ci
+        L.tp_mlp_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, cu]
+        L.tp_mlp_workspace_bytes.restype = sz
+        L.tp_mlp_shard_forward.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, vp, cu, vp]
+        L.tp_mlp_shard_forward.restype = ci
+        _lib = L
+    return _lib
+
+
+def tp_status_string(code: int) -> str:
+    return lib().tp_status_string(int(code)).decode()
+
+
+def tp_mlp_version() -> int:
+    return int(lib().tp_mlp_version())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    if t.dtype == torch.float32:
+        return TP_F32
+    raise TypeError("tensors must be torch.bfloat16 or torch.float32, got %s" % (t.dtype,))
+
+
+def _dev(t, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (the library has no CPU path)" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise TpMlpError(code, where)
+
+
+def tp_mlp_col_gelu(X, W_i, b_i=None, Y_i=None, stream=None):
+    """Y_i = GeLU(X W_i + b_i); X [..., H], W_i [H, Fk], b_i [Fk] or None."""
+    torch = _torch()
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = W_i.shape[-1]
+    dt = _dtype_code(X)
+    if W_i.dtype != X.dtype or (b_i is not None and b_i.dtype != X.dtype):
+        raise TypeError("X, W_i and b_i must share one dtype")
+    if tuple(W_i.shape) != (H, Fk) or (b_i is not None and tuple(b_i.shape) != (Fk,)):
+        raise ValueError("shape mismatch: X %s, W_i %s, b_i %s" % (tuple(X.shape), tuple(W_i.shape),
+                                                                  None if b_i is None else tuple(b_i.shape)))
+    if Y_i is None:
+        Y_i = torch.empty(*X.shape[:-1], Fk, dtype=X.dtype, device=X.device)
+    elif Y_i.dtype != X.dtype or Y_i.numel() != M * Fk:
+        raise ValueError("Y_i must be %s with %d elements" % (X.dtype, M * Fk))
+    _check(lib().tp_mlp_col_gelu(_dev(X, "X"), _dev(W_i, "W_i"), _dev(b_i, "b_i"), _dev(Y_i, "Y_i"),
+                                 M, H, Fk, dt, _stream(stream)), "tp_mlp_col_gelu")
+    return Y_i
+
+
+def tp_mlp_row_partial(Y_i, V_i, Z_i=None, accumulate: bool = False, stream=None):
+    """Z_i = Y_i V_i (float32), or Z_i += Y_i V_i with accumulate=True."""
+    torch = _torch()
+    Fk = Y_i.shape[-1]
+    M = Y_i.numel() // Fk if Fk else 0
+    H = V_i.shape[-1]
+    dt = _dtype_code(Y_i)
+    if V_i.dtype != Y_i.dtype:
+        raise TypeError("Y_i and V_i must share one dtype")
+    if tuple(V_i.shape) != (Fk, H):
+        raise ValueError("shape mismatch: Y_i %s, V_i %s" % (tuple(Y_i.shape), tuple(V_i.shape)))
+    if Z_i is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing Z_i")
+        Z_i = torch.empty(*Y_i.shape[:-1], H, dtype=torch.float32, device=Y_i.device)
+    elif Z_i.dtype != torch.float32 or Z_i.numel() != M * H:
+        raise ValueError("Z_i must be float32 with %d elements" % (M * H))
+    _check(lib().tp_mlp_row_partial(_dev(Y_i, "Y_i"), _dev(V_i, "V_i"), _dev(Z_i, "Z_i"), M, Fk, H,
+                                    dt, TP_ACCUMULATE if accumulate else 0, _stream(stream)),
+           "tp_mlp_row_partial")
+    return Z_i
+
+
+def tp_shard_reduce(parts, Z=None, stream=None):
+    """Z = parts[0] + parts[1] + ... (float32, left to right).  Z may be parts[0]."""
+    torch = _torch()
+    k = len(parts)
+    if k < 1:
+        raise ValueError("need at least one partial")
+    n = parts[0].numel()
+    for p in parts:
+        if p.dtype != torch.float32 or p.numel() != n:
+            raise ValueError("partials must be float32 tensors of one size")
+    if Z is None:
+        Z = torch.empty_like(parts[0])
+    elif Z.dtype != torch.float32 or Z.numel() != n:
+        raise ValueError("Z must be float32 with %d elements" % n)
+    ptrs = (ctypes.c_void_p * k)(*[_dev(p, "parts[%d]" % i) for i, p in enumerate(parts)])
+    _check(lib().tp_shard_reduce(ptrs, k, _dev(Z, "Z"), n, _stream(stream)), "tp_shard_reduce")
+    return Z
+
+
+def tp_mlp_workspace_bytes(k: int, M: int, H: int, Fk: int, dtype: int, flags: int = 0) -> int:
+    return int(lib().tp_mlp_workspace_bytes(k, M, H, Fk, dtype, flags))
+
+
+def tp_mlp_shard_forward(X, W, b, V, Z=None, workspace=None, fused: bool = False, stream=None):
+    """Z = sum_i GeLU(X W[i] + b[i]) V[i] over the k shards in the lists W, b, V.
+
+    ``b`` may be None (no bias).  ``workspace`` is a uint8 GPU tensor of at
+    least tp_mlp_workspace_bytes(...) bytes; it is allocated if None.
+    """
+    torch = _torch()
+    k = len(W)
+    if k < 1 or len(V) != k or (b is not None and len(b) != k):
+        raise ValueError("W, V (and b) must hold the same number k >= 1 of shards")
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = W[0].shape[-1]
+    dt = _dtype_code(X)
+    for i in range(k):
+        if tuple(W[i].shape) != (H, Fk) or tuple(V[i].shape) != (Fk, H) or \
+                (b is not None and tuple(b[i].shape) != (Fk,)):
+            raise ValueError("shard %d has the wrong shape" % i)
+        if W[i].dtype != X.dtype or V[i].dtype != X.dtype or (b is not None and b[i].dtype != X.dtype):
+            raise TypeError("shard %d has the wrong dtype" % i)
+    flags = TP_FUSED_ACCUM if fused else 0
+    need = tp_mlp_workspace_bytes(k, M, H, Fk, dt, flags)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    if Z is None:
+        Z = torch.empty(*X.shape[:-1], H, dtype=torch.float32, device=X.device)
+    elif Z.dtype != torch.float32 or Z.numel() != M * H:
+        raise ValueError("Z must be float32 with %d elements" % (M * H))
+    Wp = (ctypes.c_void_p * k)(*[_dev(w, "W[%d]" % i) for i, w in enumerate(W)])
+    Vp = (ctypes.c_void_p * k)(*[_dev(v, "V[%d]" % i) for i, v in enumerate(V)])
+    bp = None if b is None else (ctypes.c_void_p * k)(*[_dev(x, "b[%d]" % i) for i, x in enumerate(b)])
+    _check(lib().tp_mlp_shard_forward(_dev(X, "X"), Wp, bp, Vp, k, M, H, Fk, dt,
+                                      _dev(workspace, "workspace"), workspace.numel(), _dev(Z, "Z"),
+                                      flags, _stream(stream)), "tp_mlp_shard_forward")
+    return Z

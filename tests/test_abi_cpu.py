@@ -1,0 +1,195 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library must load and export every function include/tp_mlp.h declares, and
+every argument error must be reported before any HIP call (so these calls are
+safe without a device: fake, aligned, non-NULL pointers are never touched).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_mlp.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import tensor_transformer_mlp_amd as tpm
+    from tensor_transformer_mlp_amd import build
+    build.build_lib(force=False)
+    return tpm.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^(?:int|size_t|const char\s*\*)\s*(tp_\w+)\s*\(", text, re.M))
+
+
+def _header_constants():
+    text = open(HEADER).read()
+    out = {}
+    for name, val in re.findall(r"^#define\s+(TP_\w+)\s+\(?(-?\d+)u?\)?", text, re.M):
+        out[name] = int(val)
+    return out
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert names == {"tp_mlp_col_gelu", "tp_mlp_row_partial", "tp_shard_reduce",
+                     "tp_mlp_workspace_bytes", "tp_mlp_shard_forward", "tp_status_string",
+                     "tp_mlp_version"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_python_constants_match_header():
+    import tensor_transformer_mlp_amd as tpm
+    c = _header_constants()
+    for n in ("TP_F32", "TP_BF16", "TP_ACCUMULATE", "TP_FUSED_ACCUM", "TP_MAX_SHARDS"):
+        assert getattr(tpm, n) == c[n], n
+
+
+def test_status_strings(L):
+    import tensor_transformer_mlp_amd as tpm
+    c = _header_constants()
+    seen = set()
+    for n, v in c.items():
+        if n.startswith("TP_ERR_") or n == "TP_OK":
+            s = tpm.tp_status_string(v)
+            assert s and s != "unknown status"
+            seen.add(s)
+    assert tpm.tp_status_string(12345) == "unknown status"
+    assert len(seen) == 9
+    assert tpm.tp_mlp_version() >= 100
+
+
+P = 0x10000  # fake aligned device addresses; never dereferenced by a rejected call
+
+
+def _p(i):
+    return ctypes.c_void_p(P * (i + 1))
+
+
+def test_col_gelu_errors(L):
+    c = _header_constants()
+    f = L.tp_mlp_col_gelu
+    ok_args = lambda: [_p(0), _p(1), _p(2), _p(3), 16, 64, 128, 1, None]
+    a = ok_args(); a[7] = 7
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    for idx, val in [(5, 60), (5, 0), (6, 12), (6, 0), (4, -1), (5, -8)]:
+        a = ok_args(); a[idx] = val
+        assert f(*a) == c["TP_ERR_SHAPE"], (idx, val)
+    for idx in (0, 1, 3):
+        a = ok_args(); a[idx] = None
+        assert f(*a) == c["TP_ERR_NULL"], idx
+    for idx in (0, 1, 2, 3):
+        a = ok_args(); a[idx] = ctypes.c_void_p(P * (idx + 1) + 8)
+        assert f(*a) == c["TP_ERR_ALIGN"], idx
+    a = ok_args(); a[3] = _p(0)  # Y overlaps X
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    # M == 0 is a valid no-op, even with NULL pointers
+    a = ok_args(); a[4] = 0; a[0] = None; a[3] = None
+    assert f(*a) == c["TP_OK"]
+
+
+def test_row_partial_errors(L):
+    c = _header_constants()
+    f = L.tp_mlp_row_partial
+    ok_args = lambda: [_p(0), _p(1), _p(2), 16, 128, 64, 1, 0, None]
+    a = ok_args(); a[7] = 2
+    assert f(*a) == c["TP_ERR_FLAGS"]
+    a = ok_args(); a[6] = -1
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    a = ok_args(); a[4] = 100
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = ok_args(); a[2] = None
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = ok_args(); a[2] = ctypes.c_void_p(P * 3 + 4)
+    assert f(*a) == c["TP_ERR_ALIGN"]
+    a = ok_args(); a[2] = ctypes.c_void_p(P * 2 + 16)  # Z inside V
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = ok_args(); a[3] = 0
+    assert f(*a) == c["TP_OK"]
+
+
+def test_shard_reduce_errors(L):
+    c = _header_constants()
+    f = L.tp_shard_reduce
+    parts = (ctypes.c_void_p * 4)(P, 2 * P, 3 * P, 4 * P)
+    assert f(parts, 0, _p(9), 64, None) == c["TP_ERR_SHAPE"]
+    assert f(parts, 65, _p(9), 64, None) == c["TP_ERR_SHAPE"]
+    assert f(parts, 4, _p(9), -1, None) == c["TP_ERR_SHAPE"]
+    assert f(parts, 4, None, 64, None) == c["TP_ERR_NULL"]
+    assert f(None, 4, _p(9), 64, None) == c["TP_ERR_NULL"]
+    bad = (ctypes.c_void_p * 4)(P, None, 3 * P, 4 * P)
+    assert f(bad, 4, _p(9), 64, None) == c["TP_ERR_NULL"]
+    bad = (ctypes.c_void_p * 4)(P, 2 * P + 4, 3 * P, 4 * P)
+    assert f(bad, 4, _p(9), 64, None) == c["TP_ERR_ALIGN"]
+    # Z may be parts[0] but no other partial
+    assert f(parts, 4, ctypes.c_void_p(2 * P), 64, None) == c["TP_ERR_ALIAS"]
+    assert f(parts, 4, ctypes.c_void_p(2 * P + 16), 64, None) == c["TP_ERR_ALIAS"]
+    assert f(parts, 4, _p(9), 0, None) == c["TP_OK"]
+
+
+def test_workspace_bytes(L):
+    f = L.tp_mlp_workspace_bytes
+    # Y buffer (M*Fk*elt rounded to 256) + (k-1) fp32 partials of M*H
+    assert f(4, 8192, 768, 768, 1, 0) == 8192 * 768 * 2 + 3 * 8192 * 768 * 4
+    assert f(4, 8192, 768, 768, 1, 1) == 8192 * 768 * 2
+    assert f(2, 8, 64, 128, 0, 0) == 8 * 128 * 4 + 8 * 64 * 4
+    assert f(1, 3, 8, 8, 1, 0) == 256
+    assert f(2, 3, 8, 8, 1, 0) == 256 + 256
+    assert f(0, 8, 64, 128, 0, 0) == 0
+    assert f(2, 8, 60, 128, 0, 0) == 0
+    assert f(2, 8, 64, 128, 5, 0) == 0
+    assert f(2, 8, 64, 128, 0, 4) == 0
+    assert f(2, 0, 64, 128, 0, 0) == 0
+    big = f(8, 32768, 8192, 4096, 1, 0)
+    assert big == 32768 * 4096 * 2 + 7 * 32768 * 8192 * 4
+
+
+def test_shard_forward_errors(L):
+    c = _header_constants()
+    f = L.tp_mlp_shard_forward
+    k = 2
+    W = (ctypes.c_void_p * k)(10 * P, 11 * P)
+    V = (ctypes.c_void_p * k)(12 * P, 13 * P)
+    b = (ctypes.c_void_p * k)(14 * P, 15 * P)
+    need = L.tp_mlp_workspace_bytes(k, 8, 64, 128, 1, 0)
+    ws = ctypes.c_void_p(1 << 40)
+    Z = ctypes.c_void_p(1 << 41)
+    X = ctypes.c_void_p(1 << 42)
+    base = lambda: [X, W, b, V, k, 8, 64, 128, 1, ws, need, Z, 0, None]
+    a = base(); a[12] = 2
+    assert f(*a) == c["TP_ERR_FLAGS"]
+    a = base(); a[4] = 0
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[4] = 65
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[10] = need - 1
+    assert f(*a) == c["TP_ERR_WORKSPACE"]
+    a = base(); a[9] = None
+    assert f(*a) == c["TP_ERR_WORKSPACE"]
+    a = base(); a[1] = (ctypes.c_void_p * k)(10 * P, None)
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = base(); a[2] = (ctypes.c_void_p * k)(14 * P, None)
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = base(); a[3] = (ctypes.c_void_p * k)(12 * P + 2, 13 * P)
+    assert f(*a) == c["TP_ERR_ALIGN"]
+    a = base(); a[11] = ctypes.c_void_p((1 << 40) + 256)  # Z inside the workspace
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[8] = 3
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    a = base(); a[5] = 0
+    assert f(*a) == c["TP_OK"]
+
+
+def test_binding_rejects_cpu_tensors(L):
+    import torch
+    import tensor_transformer_mlp_amd as tpm
+    X = torch.zeros(4, 64)
+    W = torch.zeros(64, 128)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tpm.tp_mlp_col_gelu(X, W, None, Y_i=torch.zeros(4, 128))
