@@ -46,6 +46,8 @@ COL_CASES = [
     (257, 520, 392, "bf16"), (300, 64, 8, "bf16"), (64, 8, 64, "bf16"),
     (1, 64, 128, "f32"), (8, 64, 128, "f32"), (65, 200, 136, "f32"), (257, 72, 264, "f32"),
     (130, 8, 8, "f32"),
+    # interior shapes (whole 256x256 / 256x128 tiles, K % 128 == 0): direct-to-LDS kernel
+    (256, 128, 256, "bf16"), (512, 384, 512, "bf16"), (768, 256, 384, "bf16"),
 ]
 
 
@@ -77,6 +79,7 @@ def test_col_gelu_parity(tpm, orc, M, H, Fk, dtype):
 ROW_CASES = [
     (1, 128, 64, "bf16"), (9, 136, 200, "bf16"), (129, 264, 72, "bf16"), (257, 392, 520, "bf16"),
     (300, 8, 64, "bf16"), (8, 128, 64, "f32"), (65, 136, 200, "f32"), (257, 264, 72, "f32"),
+    (256, 128, 256, "bf16"), (512, 512, 384, "bf16"), (768, 384, 256, "bf16"),
 ]
 
 
@@ -149,6 +152,7 @@ FWD_CASES = [
     (8, 64, 256, 2, "f32"), (1, 64, 256, 2, "f32"), (33, 72, 288, 3, "f32"), (16, 64, 256, 1, "f32"),
     (8, 64, 256, 2, "bf16"), (1, 64, 256, 4, "bf16"), (131, 136, 544, 4, "bf16"), (64, 64, 512, 16, "bf16"),
     (40, 64, 512, 64, "bf16"), (257, 200, 800, 1, "bf16"), (300, 96, 384, 8, "bf16"),
+    (512, 256, 1024, 4, "bf16"), (256, 384, 1536, 3, "bf16"),
 ]
 
 
