@@ -1,0 +1,117 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (tp_mlp_shard_forward, both variants), against the CPU fp64
+oracle.
+
+The oracle recomputes sampled output rows one by one (rows of the MLP are
+independent: a pinned invariant of the oracle), so even the 175B-shaped layer
+is checked element by element on those rows.  Every kernel is checked on its
+own too: the column step Y_i (shards 0 and k-1) against the oracle, the row
+step Z_i from the GPU's own Y_i, and the shard reduce against an fp64 sum of
+the GPU partials.  Properties checked on the whole output: finite, literal
+and fused variants bit-identical, bitwise run-to-run determinism.
+"""
+import numpy as np
+import pytest
+
+from _helpers import (assert_within, col_bound, f64, forward_bound, from_dev, rel_fro,
+                      row_bound, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+WORKLOADS = ["tiny", "gpt2_small", "llama7b", "gpt3_175b", "long_seq"]
+
+
+def _rows(M, n_random=10, seed=7):
+    if M <= 64:
+        return np.arange(M)
+    base = {0, 1, 255, 256, M // 2, M - 1}
+    rng = np.random.default_rng(seed)
+    base.update(int(x) for x in rng.integers(0, M, size=n_random))
+    return np.array(sorted(base))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_workload_parity(name):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle
+    import tensor_transformer_mlp_amd as tpm
+    from tensor_transformer_mlp_amd import inputs
+
+    w = inputs.WORKLOADS[name]
+    tol = 1e-2 if w.dtype == "bf16" else 1e-5
+    say("workload %s: M=%d H=%d F=%d k=%d %s" % (name, w.M, w.H, w.F, w.k, w.dtype))
+    inp = inputs.make_inputs(w)
+    X, W, b, V = inp["X"], inp["W"], inp["b"], inp["V"]
+    Fk = w.Fk
+    dev = torch.device("cuda")
+    Xd = to_dev(X)
+    Wd, bd, Vd = to_dev(W), to_dev(b), to_dev(V)
+    Ws = [Wd[:, i * Fk:(i + 1) * Fk].contiguous() for i in range(w.k)]
+    bs = [bd[i * Fk:(i + 1) * Fk].contiguous() for i in range(w.k)]
+    Vs = [Vd[i * Fk:(i + 1) * Fk, :].contiguous() for i in range(w.k)]
+    del Wd, bd, Vd
+
+    say("  %s: forward literal x2, fused" % name)
+    Z1 = tpm.tp_mlp_shard_forward(Xd, Ws, bs, Vs, fused=False)
+    Z2 = tpm.tp_mlp_shard_forward(Xd, Ws, bs, Vs, fused=False)
+    Zf = tpm.tp_mlp_shard_forward(Xd, Ws, bs, Vs, fused=True)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Z1).all())
+    assert torch.equal(Z1, Z2), "run-to-run results differ"
+    assert torch.equal(Z1, Zf), "literal and fused variants differ"
+
+    rows = _rows(w.M)
+    rows_t = torch.from_numpy(rows).to(dev)
+    Xr = X[rows]
+    X64r = f64(Xr)
+    W64, b64, V64 = oracle.widen(W), oracle.widen(b), oracle.widen(V)
+
+    # Per-kernel: column step of shards 0 and k-1, row step from the GPU's Y_i.
+    parts_rows = []
+    for i in sorted({0, w.k - 1}):
+        say("  %s: col_gelu / row_partial shard %d" % (name, i))
+        Y = tpm.tp_mlp_col_gelu(Xd, Ws[i], bs[i])
+        Zi = tpm.tp_mlp_row_partial(Y, Vs[i])
+        torch.cuda.synchronize()
+        Yg = from_dev(Y.index_select(0, rows_t))
+        A = oracle.col_preact(X64r, W64, b64, w.k, i)
+        Yr = oracle.col_gelu(X64r, W64, b64, w.k, i)
+        bound = col_bound(X64r, W64[:, i * Fk:(i + 1) * Fk], b64[i * Fk:(i + 1) * Fk], A, Yr, w.dtype)
+        assert_within(f64(Yg), Yr, bound, "%s Y_%d" % (name, i))
+        assert rel_fro(f64(Yg), Yr) <= tol
+        Zig = from_dev(Zi.index_select(0, rows_t)).astype(np.float64)
+        Zir = oracle.row_partial(Yg, V64, w.k, i)
+        assert_within(Zig, Zir, row_bound(f64(Yg), V64[i * Fk:(i + 1) * Fk]), "%s Z_%d" % (name, i))
+        del Y, Zi
+
+    # Shard reduce: the literal Z equals the fp32 left-to-right sum of the GPU
+    # partials, within the fp32 rounding of k - 1 additions of the fp64 sum.
+    say("  %s: shard partials and reduce" % name)
+    Yb = torch.empty(w.M, Fk, dtype=Xd.dtype, device=dev)
+    for i in range(w.k):
+        tpm.tp_mlp_col_gelu(Xd, Ws[i], bs[i], Y_i=Yb)
+        P = tpm.tp_mlp_row_partial(Yb, Vs[i])
+        parts_rows.append(from_dev(P.index_select(0, rows_t)))
+        del P
+    torch.cuda.synchronize()
+    red = oracle.shard_reduce(parts_rows)
+    absum = oracle.shard_reduce([np.abs(p) for p in parts_rows])
+    Z1r = from_dev(Z1.index_select(0, rows_t)).astype(np.float64)
+    assert_within(Z1r, red, w.k * 2.0 ** -24 * absum + 1e-30, "%s reduce" % name)
+
+    # End to end against the oracle, on the sampled rows.
+    say("  %s: oracle forward on %d rows" % (name, rows.size))
+    Zr = oracle.forward_rows(X64r, W64, b64, V64, w.k)
+    A = np.concatenate([oracle.col_preact(X64r, W64, b64, w.k, i) for i in range(w.k)], axis=1)
+    Yall = np.concatenate([oracle.col_gelu(X64r, W64, b64, w.k, i) for i in range(w.k)], axis=1)
+    tolY = np.concatenate([col_bound(X64r, W64[:, i * Fk:(i + 1) * Fk], b64[i * Fk:(i + 1) * Fk],
+                                     A[:, i * Fk:(i + 1) * Fk], Yall[:, i * Fk:(i + 1) * Fk], w.dtype)
+                           for i in range(w.k)], axis=1)
+    bound = forward_bound(tolY, Yall, V64, w.k)
+    assert_within(Z1r, Zr, bound, "%s Z" % name)
+    err = rel_fro(Z1r, Zr)
+    say("  %s: rel_fro on sampled rows = %.3e (bar %.0e)" % (name, err, tol))
+    assert err <= tol
