@@ -42,6 +42,9 @@ def parse():
                     help="target CPU time of the oracle sample (0 disables the CPU leg)")
     ap.add_argument("--kernel-steps", type=int, default=None,
                     help="steps of the per-kernel timing pass (default: --steps)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain float32 copy kernel (y = x * 1) over MIB MiB, 5 times: "
+                         "the known-size reference for the HBM byte counters")
     return ap.parse_args()
 
 
@@ -75,6 +78,17 @@ def main():
     import torch
     import tensor_transformer_mlp_amd as tpm
     from tensor_transformer_mlp_amd import inputs
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
+                          "launches": 5}), flush=True)
+        return
 
     tpm.lib()  # raises if the HIP library is not built: there is no fallback
     w = inputs.WORKLOADS[args.workload]
@@ -127,49 +141,60 @@ def main():
     if not bool(torch.isfinite(Z).all()):
         raise RuntimeError("non-finite output")
 
-    # Per-kernel pass: the same kernels through the per-step entry points, with
-    # a HIP event pair around every launch on the stream they run on.
+    # Per-kernel pass: the kernels of one step through the per-kernel entry
+    # points, in the same launch configuration; each kind's launches of the
+    # step run back to back between one HIP event pair on the stream they are
+    # launched on, and a spin kernel queued first keeps the GPU busy while the
+    # host enqueues, so no host gap falls inside a pair.
     stream = torch.cuda.current_stream()
     ks = args.kernel_steps or args.steps
     Y = torch.empty(w.M, Fk, dtype=tdt, device=dev)
-    parts = [Z] + [torch.empty(w.M, w.H, dtype=torch.float32, device=dev) for _ in range(w.k - 1)]
-    durs = {"col_gelu": [], "row_partial": [], "shard_reduce": []}
-    if fused:
-        durs["row_partial_accum"] = []
+    parts = [torch.empty(w.M, w.H, dtype=torch.float32, device=dev) for _ in range(w.k)]
+    kinds = ["col_gelu", "row_partial"] + (["row_partial_accum"] if fused and w.k > 1 else []) + \
+        (["shard_reduce"] if not fused and w.k > 1 else [])
+    durs = {kd: [] for kd in kinds}
+    nlaunch = {"col_gelu": w.k, "row_partial": 1 if fused else w.k, "row_partial_accum": w.k - 1,
+               "shard_reduce": 1}
 
-    def timed(kind, fn, rec):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        fn()
-        b.record(stream)
-        rec.append((kind, a, b))
+    def launch(kind):
+        if kind == "col_gelu":
+            for i in range(w.k):
+                tpm.tp_mlp_col_gelu(X, Ws[i], bs[i], Y_i=Y)
+        elif kind == "row_partial":
+            for i in range(nlaunch["row_partial"]):
+                tpm.tp_mlp_row_partial(Y, Vs[i], Z_i=Z if fused else parts[i])
+        elif kind == "row_partial_accum":
+            for i in range(1, w.k):
+                tpm.tp_mlp_row_partial(Y, Vs[i], Z_i=Z, accumulate=True)
+        else:
+            tpm.tp_shard_reduce(parts, Z=Z)
 
+    spin = getattr(torch.cuda, "_sleep", None)
     for it in range(args.warmup + ks):
+        if spin is not None:
+            spin(3_000_000)
         rec = []
-        for i in range(w.k):
-            timed("col_gelu", lambda: tpm.tp_mlp_col_gelu(X, Ws[i], bs[i], Y_i=Y), rec)
-            if fused:
-                kind = "row_partial" if i == 0 else "row_partial_accum"
-                timed(kind, lambda: tpm.tp_mlp_row_partial(Y, Vs[i], Z_i=Z, accumulate=i > 0), rec)
-            else:
-                timed("row_partial", lambda: tpm.tp_mlp_row_partial(Y, Vs[i], Z_i=parts[i]), rec)
-        if not fused and w.k > 1:
-            timed("shard_reduce", lambda: tpm.tp_shard_reduce(parts, Z=Z), rec)
+        for kind in kinds:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch(kind)
+            b.record(stream)
+            rec.append((kind, a, b))
         torch.cuda.synchronize()
         if it >= args.warmup:
             for kind, a, b in rec:
-                durs[kind].append(a.elapsed_time(b))
+                durs[kind].append(a.elapsed_time(b) / nlaunch[kind])
     kern = {}
     for kind, d in durs.items():
         if not d:
             continue
         avg = float(np.mean(d))
-        per_step = avg * len(d) / ks
-        kern[kind] = {"launches_per_step": len(d) // ks, "avg_ms": avg, "ms_per_step": per_step,
+        per_step = avg * nlaunch[kind]
+        kern[kind] = {"launches_per_step": nlaunch[kind], "avg_ms": avg, "ms_per_step": per_step,
                       "flop": kernel_flops(kind, w), "bytes": kernel_bytes(kind, w, elt)}
         log("  %-18s %2d/step  avg %.4f ms  (%.4f ms/step)  %.1f TFLOP/s  %.0f GB/s" % (
-            kind, len(d) // ks, avg, per_step, kernel_flops(kind, w) / avg / 1e9,
+            kind, nlaunch[kind], avg, per_step, kernel_flops(kind, w) / avg / 1e9,
             kernel_bytes(kind, w, elt) / avg / 1e6))
     dom = max(kern, key=lambda k_: kern[k_]["ms_per_step"])
     d = kern[dom]
@@ -183,7 +208,7 @@ def main():
         roof = {"bound": "hbm", "achieved": d["bytes"] / (d["avg_ms"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name, args.variant, dom)
     roof["kernel"] = dom
     roof["avg_ms"] = d["avg_ms"]
 
@@ -205,8 +230,30 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def measured_traffic(workload, variant, kind):
+    """HBM bytes per launch of `kind` from the committed counter summary
+    (profiles/traffic.json), or None if that summary does not cover this
+    kernel or was taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "tensor_transformer_mlp_amd", "csrc", "tp_mlp_kernels.hip")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    e = rec.get("entries", {}).get("%s/%s/%s" % (workload, variant, kind))
+    if not e:
+        return None
+    return e["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(w, inp, target_s):
-    """The fp64 oracle, as it stands, on a bounded row sample of the same workload."""
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    the first rows of the batch (all k shards, full W and V), or, when the whole
+    batch takes less than the target time, whole-batch passes repeated up to it."""
     import numpy as np
     import oracle
 
@@ -218,14 +265,19 @@ def cpu_baseline(w, inp, target_s):
     oracle.forward_rows(X64, W64, b64, V64, w.k, np.arange(probe))
     tp = time.perf_counter() - t
     rows = int(min(w.M, max(probe, probe * target_s / max(tp, 1e-6))))
-    t = time.perf_counter()
-    oracle.forward_rows(X64, W64, b64, V64, w.k, np.arange(rows))
-    dt = time.perf_counter() - t
-    flop = 4 * rows * w.H * w.F
+    passes, dt = 0, 0.0
+    while passes == 0 or (rows == w.M and dt < target_s and passes < 100):
+        t = time.perf_counter()
+        oracle.forward_rows(X64, W64, b64, V64, w.k, np.arange(rows))
+        dt += time.perf_counter() - t
+        passes += 1
+    flop = 4 * rows * w.H * w.F * passes
     val = flop / dt / 1e12
-    log("cpu oracle: %d rows in %.2f s with %d threads: %.4f TFLOP/s" % (rows, dt, oracle.max_threads(), val))
+    what = ("%d full passes over all %d rows" % (passes, w.M)) if rows == w.M else \
+        ("rows 0..%d of %d" % (rows - 1, w.M))
+    log("cpu oracle: %s in %.2f s with %d threads: %.4f TFLOP/s" % (what, dt, oracle.max_threads(), val))
     return {"value": val, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": "rows 0..%d of %d (all %d shards, full W and V), fp64, %.1f s" % (rows - 1, w.M, w.k, dt)}
+            "sample": "%s (all %d shards, full W and V), fp64, %.1f s" % (what, w.k, dt)}
 
 
 if __name__ == "__main__":
