@@ -24,7 +24,7 @@ DEPS = SOURCES + [os.path.join(CSRC, "tp_mlp_kernels.h"), os.path.join(INCLUDE, 
 
 
 def hipcc_cmd(out: str, extra=()) -> list:
-    return [HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+    return [HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", CSRC, *extra, "-o", out, *SOURCES]
 

@@ -466,10 +466,33 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swzA4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int swzB(int k) { return 4 * (k & 3); }
 
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff,
-                                          uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rs, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, (int)soff, 0, 0);
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// gfx9 raw buffer descriptor (stride 0, num_records = bytes) as four SGPRs.
+__device__ __forceinline__ i32x4_t buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4_t{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's data lands
+// at LDS byte address `lds + 16 l` (lds is wave-uniform); out-of-range lanes
+// write zeros.  Written as inline assembly so that the compiler does not track
+// the LDS write itself: its conservative alias tracking of in-flight LDS DMA
+// would otherwise insert vmcnt(0) waits before fragment reads of other stage
+// buffers.  Completion is waited for explicitly (vmcnt) before the barrier
+// that publishes a stage; the "memory" clobber keeps LDS accesses in order
+// around it.  M0 is set here for the instruction; no compiler-generated code
+// in the kernels that use this relies on M0.
+__device__ __forceinline__ void lds_dma16(i32x4_t desc, char* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(desc), "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory", "m0");
 }
 
 __device__ __forceinline__ bf16x8_t ds_read_tr_pair(const char* p0, const char* p1) {
@@ -482,12 +505,13 @@ __device__ __forceinline__ bf16x8_t ds_read_tr_pair(const char* p0, const char* 
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int NBUF, int EPI>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const uint16_t* __restrict__ bias, void* __restrict__ C, int M, int N, int K, int tiles_m,
     int tiles_n) {
-  constexpr int BK = 32, NBUF = 4;
+  constexpr int BK = 32;
+  constexpr int D = NBUF - 1;  // prefetch distance in K steps
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -499,7 +523,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA split");
   static_assert(BN % 128 == 0 && BN <= 512, "B swizzle needs 16-chunk groups");
-  static_assert(2 * L <= 15, "vmcnt immediate");
+  static_assert(NBUF >= 3 && NBUF <= 6, "stage count");
+  static_assert((D - 1) * L <= 63, "vmcnt immediate");
+  static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
 
   // One array per stage: distinct LDS objects get distinct alias scopes, so
   // the compiler can tell that fragment reads of one stage do not depend on
@@ -507,13 +533,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[STAGE];
-  __shared__ __attribute__((aligned(1024))) char st3[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[NBUF > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st4[NBUF > 4 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st5[NBUF > 5 ? STAGE : 16];
   auto stage = [&](auto bset) -> char* {
     constexpr int b = decltype(bset)::value;
     if constexpr (b == 0) return st0;
     else if constexpr (b == 1) return st1;
     else if constexpr (b == 2) return st2;
-    else return st3;
+    else if constexpr (b == 3) return st3;
+    else if constexpr (b == 4) return st4;
+    else return st5;
   };
 
   int tm, tn;
@@ -524,10 +554,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(
   const int wm = wave / WN, wn = wave % WN;
   const int m0 = tm * BM;
   const int n0 = tn * BN;
-  const int nk = K / BK;  // a multiple of 4 (checked by the launcher)
+  const int nk = K / BK;
 
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(B, (uint32_t)K * (uint32_t)N * 2u);
+  const i32x4_t rsA = buffer_desc(A, (uint32_t)M * (uint32_t)K * 2u);
+  const i32x4_t rsB = buffer_desc(B, (uint32_t)K * (uint32_t)N * 2u);
 
   // Global byte offsets (loop-invariant) of the chunk each lane fetches for
   // its wave's DMA instructions; K advances through the scalar offset.
@@ -606,17 +636,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(
   using I1 = std::integral_constant<int, 1>;
   constexpr int kMfma = FM * FN;
   constexpr int kReads = FM + 2 * FN;
-  // vmcnt(2L), expcnt(7), lgkmcnt(0): this wave's loads of the next stage and
-  // all of its LDS reads are complete.
-  constexpr int kWaitNext = ((2 * L) & 15) | (((2 * L) >> 4) << 14) | (7 << 4);
+  // vmcnt((D - 1) L), expcnt(7), lgkmcnt(0): this wave's loads of the next
+  // stage (all but the D - 1 younger stages) and all its LDS reads are done.
+  constexpr int kWaitN = (D - 1) * L;
+  constexpr int kWaitNext = (kWaitN & 15) | ((kWaitN >> 4) << 14) | (7 << 4);
   constexpr int kWaitFirst = kWaitNext;
 
   using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  using B2 = std::integral_constant<int, 2>;
-  issue_stage(B0{}, 0);
-  issue_stage(B1{}, 1);
-  issue_stage(B2{}, 2);
+  [&]<int... b>(std::integer_sequence<int, b...>) {
+    (issue_stage(std::integral_constant<int, b>{}, b), ...);
+  }(std::make_integer_sequence<int, D>{});
   __builtin_amdgcn_s_waitcnt(kWaitFirst);
   asm volatile("s_barrier" ::: "memory");
   read_frags(I0{}, B0{}, 0);
@@ -625,11 +654,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(
   // names its buffer at compile time).
   auto kstep = [&](auto cset, int kt) {
     constexpr int c = decltype(cset)::value;
-    using Refill = std::integral_constant<int, (c + 3) & 3>;
-    using Next = std::integral_constant<int, (c + 1) & 3>;
-    // k16 step 0: refill the buffer freed by stage kt - 1, read step 1's
-    // fragments, MFMAs of step 0.
-    issue_stage(Refill{}, kt + 3);
+    using Refill = std::integral_constant<int, (c + D) % NBUF>;
+    using Next = std::integral_constant<int, (c + 1) % NBUF>;
+    // k16 step 0: refill the buffer freed by stage kt - 1 with stage kt + D,
+    // read step 1's fragments, MFMAs of step 0.
+    issue_stage(Refill{}, kt + D);
     read_frags(I1{}, cset, 1);
     mfmas(I0{});
 #pragma unroll
@@ -652,12 +681,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  for (int kt = 0; kt < nk; kt += 4) {
-    kstep(B0{}, kt);
-    kstep(B1{}, kt + 1);
-    kstep(B2{}, kt + 2);
-    kstep(std::integral_constant<int, 3>{}, kt + 3);
+  // The loop body walks the NBUF buffers in order; an early exit handles a
+  // step count that is not a multiple of NBUF (uniform across the workgroup).
+  for (int kt = 0; kt < nk; kt += NBUF) {
+    bool more = true;
+    [&]<int... b>(std::integer_sequence<int, b...>) {
+      ((more = more && (kt + b < nk), more ? (kstep(std::integral_constant<int, b>{}, kt + b), 0) : 0), ...);
+    }(std::make_integer_sequence<int, NBUF>{});
   }
+  // The last D stages' loads (out of range, writing zeros) must have landed
+  // before this workgroup's LDS can be handed to another.
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
 
   const int hcol = 4 * (lane >> 5);
 #pragma unroll
@@ -789,26 +823,51 @@ struct PartPtrs {
   const float* p[64];
 };
 
-template <int KC>
+// U 16-byte vectors per thread per iteration, all 1 + (k - 1) loads of them
+// issued before the adds, so that each thread keeps U * k loads in flight.
+template <int KC, int U>
 __global__ __launch_bounds__(256) void shard_reduce_kernel(PartPtrs parts, int k,
                                                            float* __restrict__ Z, int64_t n) {
   const int kk = KC > 0 ? KC : k;
   const int64_t n4 = n >> 2;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n4; v += stride) {
-    f32x4_t s = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(parts.p[0]) + v);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * U;
+  for (int64_t v0 = ((int64_t)blockIdx.x * blockDim.x) * U + threadIdx.x; v0 < n4; v0 += stride) {
+    f32x4_t s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + (int64_t)u * blockDim.x;
+      s[u] = v < n4 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(parts.p[0]) + v)
+                    : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     if constexpr (KC > 0) {
-      f32x4_t t[KC > 1 ? KC - 1 : 1];
+      f32x4_t t[KC > 1 ? KC - 1 : 1][U];
 #pragma unroll
       for (int i = 1; i < KC; ++i)
-        t[i - 1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(parts.p[i]) + v);
 #pragma unroll
-      for (int i = 1; i < KC; ++i) s = s + t[i - 1];
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + (int64_t)u * blockDim.x;
+          t[i - 1][u] = v < n4 ? __builtin_nontemporal_load(
+                                     reinterpret_cast<const f32x4_t*>(parts.p[i]) + v)
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int i = 1; i < KC; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) s[u] = s[u] + t[i - 1][u];
     } else {
       for (int i = 1; i < kk; ++i)
-        s = s + __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(parts.p[i]) + v);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + (int64_t)u * blockDim.x;
+          if (v < n4)
+            s[u] = s[u] + __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(parts.p[i]) + v);
+        }
     }
-    __builtin_nontemporal_store(s, reinterpret_cast<f32x4_t*>(Z) + v);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + (int64_t)u * blockDim.x;
+      if (v < n4) __builtin_nontemporal_store(s[u], reinterpret_cast<f32x4_t*>(Z) + v);
+    }
   }
   // scalar tail (n not a multiple of 4)
   if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
@@ -816,6 +875,35 @@ __global__ __launch_bounds__(256) void shard_reduce_kernel(PartPtrs parts, int k
     float s = parts.p[0][e];
     for (int i = 1; i < kk; ++i) s = s + parts.p[i][e];
     Z[e] = s;
+  }
+}
+
+template <int U>
+hipError_t launch_reduce_u(const PartPtrs& pp, int k, float* Z, int64_t n, int64_t max_blocks,
+                           hipStream_t s) {
+  const int64_t n4 = n >> 2;
+  int64_t blocks = (n4 + 256 * U - 1) / (256 * U);
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks), block(256);
+  switch (k) {
+    case 1: hipLaunchKernelGGL((shard_reduce_kernel<1, U>), grid, block, 0, s, pp, k, Z, n); break;
+    case 2: hipLaunchKernelGGL((shard_reduce_kernel<2, U>), grid, block, 0, s, pp, k, Z, n); break;
+    case 4: hipLaunchKernelGGL((shard_reduce_kernel<4, U>), grid, block, 0, s, pp, k, Z, n); break;
+    case 8: hipLaunchKernelGGL((shard_reduce_kernel<8, U>), grid, block, 0, s, pp, k, Z, n); break;
+    default: hipLaunchKernelGGL((shard_reduce_kernel<0, U>), grid, block, 0, s, pp, k, Z, n); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_reduce_cfg(const float* const* parts, int k, float* Z, int64_t n, int unroll,
+                                   int64_t max_blocks, hipStream_t s) {
+  PartPtrs pp;
+  for (int i = 0; i < 64; ++i) pp.p[i] = i < k ? parts[i] : nullptr;
+  switch (unroll) {
+    case 1: return launch_reduce_u<1>(pp, k, Z, n, max_blocks, s);
+    case 2: return launch_reduce_u<2>(pp, k, Z, n, max_blocks, s);
+    default: return launch_reduce_u<4>(pp, k, Z, n, max_blocks, s);
   }
 }
 
@@ -854,10 +942,10 @@ hipError_t launch_bf16_cfg(const uint16_t* A, const uint16_t* B, const uint16_t*
   return hipSuccess;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NBUF>
 hipError_t launch_bf16_dma(const uint16_t* A, const uint16_t* B, const uint16_t* bias, void* C,
                            int64_t M, int64_t N, int64_t K, Epilogue epi, hipStream_t s) {
-  // Interior shapes only (M % BM, N % BN, K % 128 all zero: checked by the
+  // Interior shapes only (M % BM, N % BN, K % 32 all zero: checked by the
   // caller); 32-bit buffer offsets.
   const int64_t rows_per_launch = ((int64_t(1) << 31) / (K * 2)) / BM * BM;
   const size_t c_elt = epi == kEpiBiasGelu ? 2 : 4;
@@ -870,15 +958,15 @@ hipError_t launch_bf16_dma(const uint16_t* A, const uint16_t* B, const uint16_t*
     const dim3 grid(tiles_m * tiles_n), block(WM * WN * 64);
     switch (epi) {
       case kEpiBiasGelu:
-        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, kEpiBiasGelu>), grid, block, 0,
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, NBUF, kEpiBiasGelu>), grid, block, 0,
                            s, Ac, B, bias, Cc, (int)Mc, (int)N, (int)K, tiles_m, tiles_n);
         break;
       case kEpiStoreF32:
-        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, kEpiStoreF32>), grid, block, 0,
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, NBUF, kEpiStoreF32>), grid, block, 0,
                            s, Ac, B, bias, Cc, (int)Mc, (int)N, (int)K, tiles_m, tiles_n);
         break;
       default:
-        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, kEpiAccumF32>), grid, block, 0,
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, NBUF, kEpiAccumF32>), grid, block, 0,
                            s, Ac, B, bias, Cc, (int)Mc, (int)N, (int)K, tiles_m, tiles_n);
         break;
     }
@@ -888,39 +976,80 @@ hipError_t launch_bf16_dma(const uint16_t* A, const uint16_t* B, const uint16_t*
   return hipSuccess;
 }
 
-// Workgroup tile shapes of the bf16 GEMM, all with 4 waves (2 x 2, or 4 x 1 for 256x96).
-enum Bf16Tile : int { kT256x256 = 0, kT256x192, kT256x128, kT256x96, kT128x128, kD256x256, kD256x128, kNumBf16Tiles };
+// The bf16 GEMM configurations: workgroup tile, wave grid, LDS stages, kernel
+// variant (direct-to-LDS for interior shapes, register-staged otherwise) and
+// a relative per-tile efficiency used by the tile picker.
+typedef hipError_t (*Bf16Launch)(const uint16_t*, const uint16_t*, const uint16_t*, void*, int64_t,
+                                 int64_t, int64_t, Epilogue, hipStream_t);
+struct Bf16Tile {
+  int bm, bn;
+  bool dma;
+  int wgs_per_cu;  // workgroups that fit on one CU (LDS and registers)
+  double eff;
+  Bf16Launch launch;
+};
+const Bf16Tile kBf16Tiles[] = {
+    {256, 256, false, 1, 1.0, launch_bf16_cfg<256, 256, 2, 2>},
+    {256, 192, false, 1, 0.97, launch_bf16_cfg<256, 192, 2, 2>},
+    {256, 128, false, 1, 0.88, launch_bf16_cfg<256, 128, 2, 2>},
+    {256, 96, false, 1, 0.8, launch_bf16_cfg<256, 96, 4, 1>},
+    {128, 128, false, 2, 0.7, launch_bf16_cfg<128, 128, 2, 2>},
+    {256, 256, true, 1, 1.4, launch_bf16_dma<256, 256, 2, 4, 4>},
+    {256, 256, true, 1, 1.4, launch_bf16_dma<256, 256, 2, 4, 5>},
+    {256, 128, true, 1, 1.2, launch_bf16_dma<256, 128, 4, 2, 4>},
+    {256, 128, true, 2, 1.2, launch_bf16_dma<256, 128, 4, 2, 3>},
+    {256, 128, true, 1, 1.2, launch_bf16_dma<256, 128, 2, 4, 4>},
+    {128, 256, true, 1, 1.2, launch_bf16_dma<128, 256, 2, 4, 4>},
+    {128, 256, true, 2, 1.2, launch_bf16_dma<128, 256, 2, 4, 3>},
+    {128, 128, true, 2, 1.0, launch_bf16_dma<128, 128, 2, 2, 4>},
+    {128, 128, true, 2, 1.0, launch_bf16_dma<128, 128, 2, 4, 4>},
+    {256, 256, true, 1, 1.4, launch_bf16_dma<256, 256, 2, 2, 4>},
+    {256, 256, true, 1, 1.4, launch_bf16_dma<256, 256, 2, 2, 5>},
+    {256, 128, true, 1, 1.2, launch_bf16_dma<256, 128, 2, 2, 4>},
+    {256, 128, true, 1, 1.2, launch_bf16_dma<256, 128, 2, 2, 6>},
+};
+constexpr int kNumBf16Tiles = sizeof(kBf16Tiles) / sizeof(kBf16Tiles[0]);
+
+bool tile_fits(const Bf16Tile& t, int64_t M, int64_t N, int64_t K) {
+  return !t.dma || (M % t.bm == 0 && N % t.bn == 0 && K % 32 == 0);
+}
 
 hipError_t launch_bf16_tile(int tile, const uint16_t* A, const uint16_t* B, const uint16_t* bias,
                             void* C, int64_t M, int64_t N, int64_t K, Epilogue epi,
                             hipStream_t s) {
-  switch (tile) {
-    case kT256x256: return launch_bf16_cfg<256, 256, 2, 2>(A, B, bias, C, M, N, K, epi, s);
-    case kT256x192: return launch_bf16_cfg<256, 192, 2, 2>(A, B, bias, C, M, N, K, epi, s);
-    case kT256x128: return launch_bf16_cfg<256, 128, 2, 2>(A, B, bias, C, M, N, K, epi, s);
-    case kT256x96: return launch_bf16_cfg<256, 96, 4, 1>(A, B, bias, C, M, N, K, epi, s);
-    case kD256x256: return launch_bf16_dma<256, 256, 2, 4>(A, B, bias, C, M, N, K, epi, s);
-    case kD256x128: return launch_bf16_dma<256, 128, 4, 2>(A, B, bias, C, M, N, K, epi, s);
-    default: return launch_bf16_cfg<128, 128, 2, 2>(A, B, bias, C, M, N, K, epi, s);
-  }
+  if (tile < 0 || tile >= kNumBf16Tiles || !tile_fits(kBf16Tiles[tile], M, N, K))
+    return hipErrorInvalidValue;
+  return kBf16Tiles[tile].launch(A, B, bias, C, M, N, K, epi, s);
 }
 
-// Pick the tile with the least estimated time: rounds of 256 resident
-// workgroups (one per CU) times the per-tile time, with the per-tile
-// efficiency of each kernel variant.  The direct-to-LDS tiles need interior
-// shapes (M, N multiples of the tile, K a multiple of 128).
+// Tile choice.  Interior shapes use the direct-to-LDS kernel; measured on the
+// per-shard GEMMs of the five workloads (MI355X, random bf16 data):
+//   * 256x256 (8 waves, 4 stages) when it fills at least two rounds of the 256
+//     CUs, or 192..255 tiles (a 0.75 round still beats the smaller tiles);
+//   * otherwise 128x256 with 3 stages (two workgroups per CU);
+//   * otherwise 128x128 (two workgroups per CU).
+// Ragged shapes use the register-staged kernel with the tile of least
+// estimated time (rounds of resident workgroups x tile work / efficiency).
+constexpr int kTileD256 = 5, kTileD128x256 = 11, kTileD128x128 = 13;
+
 int pick_bf16_tile(int64_t M, int64_t N, int64_t K) {
-  static const int bm[kNumBf16Tiles] = {256, 256, 256, 256, 128, 256, 256};
-  static const int bn[kNumBf16Tiles] = {256, 192, 128, 96, 128, 256, 128};
-  static const double eff[kNumBf16Tiles] = {1.0, 0.97, 0.88, 0.8, 0.7, 1.4, 1.2};
-  int best = kT128x128;
+  if (K % 32 == 0) {
+    if (M % 256 == 0 && N % 256 == 0) {
+      const int64_t t = (M / 256) * (N / 256);
+      if (t >= 512 || (t >= 192 && t < 256)) return kTileD256;
+    }
+    if (M % 128 == 0 && N % 256 == 0) return kTileD128x256;
+    if (M % 128 == 0 && N % 128 == 0) return kTileD128x128;
+  }
+  int best = 4;  // register-staged 128x128: fits every shape
   double best_t = 1e300;
   for (int t = 0; t < kNumBf16Tiles; ++t) {
-    const bool dma = t == kD256x256 || t == kD256x128;
-    if (dma && (M % bm[t] || N % bn[t] || K % 128)) continue;
-    const int64_t tiles = ((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]);
-    const int64_t rounds = (tiles + 255) / 256;
-    const double time = double(rounds) * bm[t] * bn[t] / eff[t];
+    const Bf16Tile& c = kBf16Tiles[t];
+    if (c.dma) continue;
+    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const int64_t slots = 256 * c.wgs_per_cu;
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    const double time = double(rounds) * c.bm * c.bn * c.wgs_per_cu / c.eff;
     if (time < best_t * 0.999) {
       best_t = time;
       best = t;
@@ -960,31 +1089,7 @@ hipError_t launch_gemm_f32(const float* A, const float* B, const float* bias, vo
 
 hipError_t launch_shard_reduce(const float* const* parts, int k, float* Z, int64_t n,
                                hipStream_t s) {
-  PartPtrs pp;
-  for (int i = 0; i < 64; ++i) pp.p[i] = i < k ? parts[i] : nullptr;
-  const int64_t n4 = n >> 2;
-  int64_t blocks = (n4 + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) blocks = 1;
-  const dim3 grid((unsigned)blocks), block(256);
-  switch (k) {
-    case 1:
-      hipLaunchKernelGGL(shard_reduce_kernel<1>, grid, block, 0, s, pp, k, Z, n);
-      break;
-    case 2:
-      hipLaunchKernelGGL(shard_reduce_kernel<2>, grid, block, 0, s, pp, k, Z, n);
-      break;
-    case 4:
-      hipLaunchKernelGGL(shard_reduce_kernel<4>, grid, block, 0, s, pp, k, Z, n);
-      break;
-    case 8:
-      hipLaunchKernelGGL(shard_reduce_kernel<8>, grid, block, 0, s, pp, k, Z, n);
-      break;
-    default:
-      hipLaunchKernelGGL(shard_reduce_kernel<0>, grid, block, 0, s, pp, k, Z, n);
-      break;
-  }
-  return hipGetLastError();
+  return launch_shard_reduce_cfg(parts, k, Z, n, 4, 65536, s);
 }
 
 }  // namespace tpmlp
