@@ -1,4 +1,4 @@
-"""CPU fp64 oracle for the tensor-parallel MLP shard forward.
+"""CPU fp64 oracle for the tensor-parallel MLP shard forward and backward.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only callers.  The product path never imports this
@@ -14,11 +14,18 @@ Definition (cited passages in the C file's header):
   W_i = W[:, i*Fk:(i+1)*Fk], b_i = b[i*Fk:(i+1)*Fk], V_i = V[i*Fk:(i+1)*Fk, :]
   Y_i = GeLU(X W_i + b_i),  GeLU(x) = x/2 (1 + erf(x/sqrt 2))
   Z_i = Y_i V_i,  Z = sum_i Z_i  (shard order).
+Backward for dZ = dL/dZ (chain rule through the same steps):
+  G_i = GeLU'(A_i) = Phi(A_i) + A_i phi(A_i),  dA_i = (dZ V_i^T) * G_i,
+  dV_i = Y_i^T dZ,  dW_i = X^T dA_i,  db_i = colsum(dA_i),
+  dX = sum_i dA_i W_i^T.
 
-Every function here is pinned by tests/test_oracle_pins.py (brute force in
-exact rational arithmetic with 50-digit erf, the column-split and row-split
-identities, GeLU closed forms, special cases that reduce to library routines,
-row independence and exact scaling).
+Every forward function here is pinned by tests/test_oracle_pins.py (brute
+force in exact rational arithmetic with 50-digit erf, the column-split and
+row-split identities, GeLU closed forms, special cases that reduce to library
+routines, row independence and exact scaling); every backward function by
+tests/test_oracle_backward_pins.py (50-digit numerical differentiation of the
+exact forward, float64 autograd of an independent implementation, GeLU' closed
+forms, the ones-column identity between db and dW, k-invariance, linearity).
 """
 from __future__ import annotations
 
@@ -60,8 +67,21 @@ def _L():
         lib.oracle_shard_reduce.argtypes = [vp, ci, i64, vp]
         lib.oracle_forward_rows.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp, i64, vp]
         lib.oracle_max_threads.restype = ci
+        lib.oracle_gelu_grad.argtypes = [ctypes.c_double]
+        lib.oracle_gelu_grad.restype = ctypes.c_double
+        lib.oracle_gelu_grad_array.argtypes = [vp, i64, vp]
+        lib.oracle_col_gelu_grad.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        lib.oracle_act_grad.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        lib.oracle_row_weight_grad.argtypes = [vp, vp, i64, i64, i64, vp]
+        lib.oracle_col_weight_grad.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+        lib.oracle_input_grad_partial.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
+        lib.oracle_backward_rows.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, vp, i64, vp]
+        lib.oracle_backward_cols.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp]
         for f in (lib.oracle_gelu_array, lib.oracle_col_preact, lib.oracle_col_gelu,
-                  lib.oracle_row_partial, lib.oracle_shard_reduce, lib.oracle_forward_rows):
+                  lib.oracle_row_partial, lib.oracle_shard_reduce, lib.oracle_forward_rows,
+                  lib.oracle_gelu_grad_array, lib.oracle_col_gelu_grad, lib.oracle_act_grad,
+                  lib.oracle_row_weight_grad, lib.oracle_col_weight_grad,
+                  lib.oracle_input_grad_partial, lib.oracle_backward_rows, lib.oracle_backward_cols):
             f.restype = None
         _lib = lib
     return _lib
@@ -179,3 +199,142 @@ def forward_rows(X, W, b, V, k: int, rows=None) -> np.ndarray:
 def forward(X, W, b, V, k: int) -> np.ndarray:
     """Z = sum_i GeLU(X W_i + b_i) V_i, float64 [M, H]."""
     return forward_rows(X, W, b, V, k, None)
+
+
+# ---------------------------------------------------------------------------
+# Backward.
+
+def gelu_grad_scalar(x: float) -> float:
+    return float(_L().oracle_gelu_grad(float(x)))
+
+
+def gelu_grad(x) -> np.ndarray:
+    """GeLU'(x) = Phi(x) + x phi(x), float64."""
+    x = widen(x)
+    g = np.empty_like(x)
+    _L().oracle_gelu_grad_array(_p(x), x.size, _p(g))
+    return g
+
+
+def col_gelu_grad(X, W, b, k: int, i: int) -> np.ndarray:
+    """G_i = GeLU'(X W_i + b_i), float64 [M, F/k]."""
+    X, W = widen(X), widen(W)
+    b = widen(b) if b is not None else None
+    M, H = X.shape
+    F = W.shape[1]
+    assert W.shape[0] == H
+    _check_shard(F, k, i)
+    G = np.empty((M, F // k))
+    _L().oracle_col_gelu_grad(_p(X), _p(W), _p(b), M, H, F, k, i, _p(G))
+    return G
+
+
+def act_grad(dZ, V, Gi, k: int, i: int) -> np.ndarray:
+    """dA_i = (dZ V_i^T) * G_i with V the full [F, H] matrix, float64 [M, F/k]."""
+    dZ, V, Gi = widen(dZ), widen(V), widen(Gi)
+    F, H = V.shape
+    _check_shard(F, k, i)
+    M = dZ.shape[0]
+    assert dZ.shape == (M, H) and Gi.shape == (M, F // k)
+    dA = np.empty((M, F // k))
+    _L().oracle_act_grad(_p(dZ), _p(V), _p(Gi), M, F, H, k, i, _p(dA))
+    return dA
+
+
+def row_weight_grad(Yi, dZ) -> np.ndarray:
+    """dV_i = Y_i^T dZ, float64 [Fk, H]."""
+    Yi, dZ = widen(Yi), widen(dZ)
+    M, Fk = Yi.shape
+    H = dZ.shape[1]
+    assert dZ.shape[0] == M
+    dV = np.empty((Fk, H))
+    _L().oracle_row_weight_grad(_p(Yi), _p(dZ), M, Fk, H, _p(dV))
+    return dV
+
+
+def col_weight_grad(X, dAi):
+    """(dW_i, db_i) = (X^T dA_i, colsum dA_i), float64 [H, Fk] and [Fk]."""
+    X, dAi = widen(X), widen(dAi)
+    M, H = X.shape
+    Fk = dAi.shape[1]
+    assert dAi.shape[0] == M
+    dW = np.empty((H, Fk))
+    db = np.empty(Fk)
+    _L().oracle_col_weight_grad(_p(X), _p(dAi), M, H, Fk, _p(dW), _p(db))
+    return dW, db
+
+
+def input_grad_partial(dAi, W, k: int, i: int) -> np.ndarray:
+    """dX_i = dA_i W_i^T with W the full [H, F] matrix, float64 [M, H]."""
+    dAi, W = widen(dAi), widen(W)
+    H, F = W.shape
+    _check_shard(F, k, i)
+    M = dAi.shape[0]
+    assert dAi.shape == (M, F // k)
+    dX = np.empty((M, H))
+    _L().oracle_input_grad_partial(_p(dAi), _p(W), M, H, F, k, i, _p(dX))
+    return dX
+
+
+def backward_rows(X, W, b, V, dZ, k: int, rows=None) -> np.ndarray:
+    """dX[rows, :] of the whole backward, float64 (all rows if None)."""
+    X, W, V, dZ = widen(X), widen(W), widen(V), widen(dZ)
+    b = widen(b) if b is not None else None
+    M, H = X.shape
+    F = W.shape[1]
+    assert W.shape[0] == H and V.shape == (F, H) and dZ.shape == (M, H)
+    _check_shard(F, k, 0)
+    if rows is None:
+        r, nrows = None, M
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        if r.size and (r.min() < 0 or r.max() >= M):
+            raise IndexError("row index out of range")
+        nrows = r.size
+    dX = np.empty((nrows, H))
+    if nrows:
+        _L().oracle_backward_rows(_p(X), _p(W), _p(b), _p(V), _p(dZ), H, F, k, _p(r), nrows, _p(dX))
+    return dX
+
+
+def backward_cols(X, W, b, V, dZ, cols):
+    """Parameter gradients of columns `cols` of the full F: (dW[:, cols].T,
+    db[cols], dV[cols, :]), float64 [n, H], [n], [n, H]."""
+    X, W, V, dZ = widen(X), widen(W), widen(V), widen(dZ)
+    b = widen(b) if b is not None else None
+    M, H = X.shape
+    F = W.shape[1]
+    assert W.shape[0] == H and V.shape == (F, H) and dZ.shape == (M, H)
+    c = np.ascontiguousarray(cols, dtype=np.int64)
+    if c.size and (c.min() < 0 or c.max() >= F):
+        raise IndexError("column index out of range")
+    n = c.size
+    dWc, dbc, dVc = np.empty((n, H)), np.empty(n), np.empty((n, H))
+    if n:
+        _L().oracle_backward_cols(_p(X), _p(W), _p(b), _p(V), _p(dZ), M, H, F, _p(c), n, _p(dWc),
+                                  _p(dbc), _p(dVc))
+    return dWc, dbc, dVc
+
+
+def backward(X, W, b, V, dZ, k: int):
+    """The whole backward by shards, in the order of the steps:
+    returns (dX [M, H], dW [H, F], db [F], dV [F, H]), float64."""
+    X, W, V, dZ = widen(X), widen(W), widen(V), widen(dZ)
+    b = widen(b) if b is not None else None
+    M, H = X.shape
+    F = W.shape[1]
+    _check_shard(F, k, 0)
+    Fk = F // k
+    dW, db, dV = np.empty((H, F)), np.empty(F), np.empty((F, H))
+    parts = []
+    for i in range(k):
+        Yi = col_gelu(X, W, b, k, i)
+        Gi = col_gelu_grad(X, W, b, k, i)
+        dAi = act_grad(dZ, V, Gi, k, i)
+        dV[i * Fk:(i + 1) * Fk] = row_weight_grad(Yi, dZ)
+        dWi, dbi = col_weight_grad(X, dAi)
+        dW[:, i * Fk:(i + 1) * Fk] = dWi
+        db[i * Fk:(i + 1) * Fk] = dbi
+        parts.append(input_grad_partial(dAi, W, k, i))
+    dX = shard_reduce(parts)
+    return dX, dW, db, dV

@@ -1,5 +1,6 @@
 /*
- * CPU fp64 oracle for the tensor-parallel (Megatron-style) MLP shard forward.
+ * CPU fp64 oracle for the tensor-parallel (Megatron-style) MLP shard forward
+ * and its backward pass.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
@@ -24,6 +25,20 @@
  *      third page above);
  *   5. Z = Z_0 + Z_1 + ... + Z_{k-1}, the all-reduce SUM (§2.2 ibid.; the
  *      identity Z = Y V = Y_1 V_1 + Y_2 V_2, 方案二).
+ *
+ * The backward (the gradients of the same block for a loss L, given dZ =
+ * dL/dZ; the backward exchange mirrors the forward one:
+ * "大模型分布式训练四维并行：DDP、ZeRO、张量、流水线与上下文" §4.3, and forward and
+ * backward each take one all-reduce per MLP: "AI大模型分布式训练：张量并行与流水线
+ * 并行深度实践" §2.4), by the chain rule through steps 5 .. 2:
+ *   6. every shard receives the same dZ (the forward SUM is linear, so
+ *      dL/dZ_i = dZ);
+ *   7. dY_i = dZ V_i^T and dV_i = Y_i^T dZ  (step 4);
+ *   8. dA_i = dY_i * GeLU'(A_i) element-wise, with
+ *      GeLU'(x) = Phi(x) + x phi(x), phi(x) = exp(-x^2/2) / sqrt(2 pi)  (step 3);
+ *   9. dW_i = X^T dA_i, db_i[j] = sum_m dA_i[m, j], dX_i = dA_i W_i^T  (step 2);
+ *  10. dX = dX_0 + ... + dX_{k-1}: X feeds every shard, so its gradient is the
+ *      sum over shards (the backward all-reduce).
  *
  * All arrays are row-major doubles; the Python wrapper widens bf16/f32 inputs
  * to double exactly before calling.  Sums run in index order.  Parallelism is
@@ -131,6 +146,181 @@ void oracle_forward_rows(const double* X, const double* W, const double* b, cons
     }
     free(y);
     free(zi);
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Backward.                                                               */
+
+/* GeLU'(x) = Phi(x) + x phi(x) (step 8), Phi as in oracle_gelu. */
+double oracle_gelu_grad(double x) {
+  const double inv_sqrt_2pi = 0.39894228040143267793994605993438;
+  return 0.5 * erfc(-x / sqrt(2.0)) + x * exp(-0.5 * x * x) * inv_sqrt_2pi;
+}
+
+void oracle_gelu_grad_array(const double* x, int64_t n, double* g) {
+  for (int64_t i = 0; i < n; ++i) g[i] = oracle_gelu_grad(x[i]);
+}
+
+/* G_i[M,Fk] = GeLU'(X W_i + b_i) of shard i (steps 2 and 8). */
+void oracle_col_gelu_grad(const double* X, const double* W, const double* b, int64_t M, int64_t H,
+                          int64_t F, int k, int i, double* G) {
+  const int64_t Fk = F / k;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < M; ++m) {
+    double* g = G + m * Fk;
+    preact_row(X, W, b, m, H, F, Fk, i, g);
+    for (int64_t j = 0; j < Fk; ++j) g[j] = oracle_gelu_grad(g[j]);
+  }
+}
+
+/* One row of steps 7-8: da[j] = g[j] * sum_n dz[n] V[i*Fk + j, n]. */
+static void act_grad_row(const double* dz, const double* V, const double* g, int64_t H, int64_t Fk,
+                         int64_t i, double* da) {
+  for (int64_t j = 0; j < Fk; ++j) {
+    const double* v = V + (i * Fk + j) * H;
+    double s = 0.0;
+    for (int64_t n = 0; n < H; ++n) s += dz[n] * v[n];
+    da[j] = s * g[j];
+  }
+}
+
+/* dA_i[M,Fk] = (dZ V_i^T) * G_i (steps 7-8); V is the full [F,H] matrix. */
+void oracle_act_grad(const double* dZ, const double* V, const double* Gi, int64_t M, int64_t F,
+                     int64_t H, int k, int i, double* dAi) {
+  const int64_t Fk = F / k;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < M; ++m) act_grad_row(dZ + m * H, V, Gi + m * Fk, H, Fk, i, dAi + m * Fk);
+}
+
+/* dV_i[Fk,H]: dV_i[j,n] = sum_m Y_i[m,j] dZ[m,n] (step 7). */
+void oracle_row_weight_grad(const double* Yi, const double* dZ, int64_t M, int64_t Fk, int64_t H,
+                            double* dVi) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t j = 0; j < Fk; ++j) {
+    double* out = dVi + j * H;
+    for (int64_t n = 0; n < H; ++n) out[n] = 0.0;
+    for (int64_t m = 0; m < M; ++m) {
+      const double y = Yi[m * Fk + j];
+      const double* dz = dZ + m * H;
+      for (int64_t n = 0; n < H; ++n) out[n] += y * dz[n];
+    }
+  }
+}
+
+/* dW_i[H,Fk]: dW_i[h,j] = sum_m X[m,h] dA_i[m,j], and db_i[j] = sum_m dA_i[m,j]
+   (step 9).  db_i may be NULL. */
+void oracle_col_weight_grad(const double* X, const double* dAi, int64_t M, int64_t H, int64_t Fk,
+                            double* dWi, double* dbi) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t h = 0; h < H; ++h) {
+    double* out = dWi + h * Fk;
+    for (int64_t j = 0; j < Fk; ++j) out[j] = 0.0;
+    for (int64_t m = 0; m < M; ++m) {
+      const double x = X[m * H + h];
+      const double* da = dAi + m * Fk;
+      for (int64_t j = 0; j < Fk; ++j) out[j] += x * da[j];
+    }
+  }
+  if (dbi) {
+    for (int64_t j = 0; j < Fk; ++j) dbi[j] = 0.0;
+    for (int64_t m = 0; m < M; ++m)
+      for (int64_t j = 0; j < Fk; ++j) dbi[j] += dAi[m * Fk + j];
+  }
+}
+
+/* One row of step 9's input gradient: dx[h] = sum_j da[j] W[h, i*Fk + j]. */
+static void input_grad_row(const double* da, const double* W, int64_t H, int64_t F, int64_t Fk,
+                           int64_t i, double* dx) {
+  for (int64_t h = 0; h < H; ++h) {
+    const double* w = W + h * F + i * Fk;
+    double s = 0.0;
+    for (int64_t j = 0; j < Fk; ++j) s += da[j] * w[j];
+    dx[h] = s;
+  }
+}
+
+/* dX_i[M,H] = dA_i W_i^T (step 9); W is the full [H,F] matrix. */
+void oracle_input_grad_partial(const double* dAi, const double* W, int64_t M, int64_t H, int64_t F,
+                               int k, int i, double* dXi) {
+  const int64_t Fk = F / k;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < M; ++m) input_grad_row(dAi + m * Fk, W, H, F, Fk, i, dXi + m * H);
+}
+
+/* Whole backward for selected rows of dX (steps 6-10 for each row, which
+   only needs that row of X and dZ): dX[r,:] = sum_i dA_i[m,:] W_i^T with
+   m = rows[r] (rows == NULL: 0..nrows-1).  b may be NULL. */
+void oracle_backward_rows(const double* X, const double* W, const double* b, const double* V,
+                          const double* dZ, int64_t H, int64_t F, int k, const int64_t* rows,
+                          int64_t nrows, double* dX) {
+  const int64_t Fk = F / k;
+#pragma omp parallel
+  {
+    double* g = (double*)malloc(sizeof(double) * (size_t)Fk);
+    double* da = (double*)malloc(sizeof(double) * (size_t)Fk);
+    double* dxi = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+      const int64_t m = rows ? rows[r] : r;
+      double* dx = dX + r * H;
+      for (int64_t h = 0; h < H; ++h) dx[h] = 0.0;
+      for (int i = 0; i < k; ++i) {
+        preact_row(X, W, b, m, H, F, Fk, i, g);                        /* step 2 */
+        for (int64_t j = 0; j < Fk; ++j) g[j] = oracle_gelu_grad(g[j]); /* step 8 */
+        act_grad_row(dZ + m * H, V, g, H, Fk, i, da);                   /* steps 7-8 */
+        input_grad_row(da, W, H, F, Fk, i, dxi);                        /* step 9 */
+        for (int64_t h = 0; h < H; ++h) dx[h] += dxi[h];                /* step 10 */
+      }
+    }
+    free(g);
+    free(da);
+    free(dxi);
+  }
+}
+
+/* Parameter gradients for selected columns c of the full F (shard c / Fk):
+   dWc[r,:] = dW[:, c] (H values), dbc[r] = db[c], dVc[r,:] = dV[c, :], with
+   c = cols[r].  Column c of A = X W + b, and so of Y, G and dA, depends on
+   column c of W, entry c of b and row c of V only. */
+void oracle_backward_cols(const double* X, const double* W, const double* b, const double* V,
+                          const double* dZ, int64_t M, int64_t H, int64_t F, const int64_t* cols,
+                          int64_t ncols, double* dWc, double* dbc, double* dVc) {
+#pragma omp parallel
+  {
+    double* y = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+    double* da = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < ncols; ++r) {
+      const int64_t c = cols[r];
+      const double* v = V + c * H;
+      for (int64_t m = 0; m < M; ++m) {
+        double a = 0.0;                                                  /* step 2 */
+        for (int64_t h = 0; h < H; ++h) a += X[m * H + h] * W[h * F + c];
+        if (b) a += b[c];
+        double s = 0.0;                                                  /* step 7 */
+        for (int64_t n = 0; n < H; ++n) s += dZ[m * H + n] * v[n];
+        y[m] = oracle_gelu(a);                                           /* step 3 */
+        da[m] = s * oracle_gelu_grad(a);                                 /* step 8 */
+      }
+      double* dw = dWc + r * H;                                          /* step 9 */
+      for (int64_t h = 0; h < H; ++h) {
+        double s = 0.0;
+        for (int64_t m = 0; m < M; ++m) s += X[m * H + h] * da[m];
+        dw[h] = s;
+      }
+      double sb = 0.0;
+      for (int64_t m = 0; m < M; ++m) sb += da[m];
+      dbc[r] = sb;
+      double* dv = dVc + r * H;                                          /* step 7 */
+      for (int64_t n = 0; n < H; ++n) {
+        double s = 0.0;
+        for (int64_t m = 0; m < M; ++m) s += y[m] * dZ[m * H + n];
+        dv[n] = s;
+      }
+    }
+    free(y);
+    free(da);
   }
 }
 
