@@ -1,7 +1,7 @@
 /*
- * tp_mlp.h — C ABI of libtpmlp.so: the forward pass of one Megatron-style
- * tensor-parallel MLP block, every shard of it on one AMD Instinct MI355X
- * (gfx950).
+ * tp_mlp.h — C ABI of libtpmlp.so: the forward and backward passes of one
+ * Megatron-style tensor-parallel MLP block, every shard of it on one AMD
+ * Instinct MI355X (gfx950).
  *
  * The block (the first linear layer split by columns, the second by rows, one
  * all-reduce per MLP; "千亿参数模型如何拆分到多张GPU上训练", 张量并行 section,
@@ -31,10 +31,32 @@
  * result is rounded to nearest-even bfloat16.  TP_F32: everything float32.
  * Z_i and Z are float32 in both cases.
  *
- * Constraints.  H and Fk are multiples of 8 and at least 8; M >= 0 (M == 0 is
- * a no-op that returns TP_OK); 1 <= k <= TP_MAX_SHARDS; M, H, Fk < 2^31 and
- * each matrix holds fewer than 2^40 elements; every pointer is 16-byte
- * aligned.  Outputs must not overlap inputs unless stated.
+ * Constraints.  H and Fk are multiples of 8, at least 8 and at most 2^22
+ * (the kernels address the rows of a tile with 32-bit offsets); M >= 0 (for
+ * the forward entry points M == 0 is a no-op that returns TP_OK);
+ * 1 <= k <= TP_MAX_SHARDS; M < 2^31 and each matrix holds fewer than 2^40
+ * elements; every pointer is 16-byte aligned.  Outputs must not overlap
+ * inputs or each other unless stated.
+ *
+ * Backward.  The entry points after tp_mlp_shard_forward compute the
+ * gradients of the same block for a loss L, given dZ = dL/dZ.  In the
+ * tensor-parallel block the forward all-reduce becomes an identity in the
+ * backward pass and the (identity) broadcast of X becomes an all-reduce of
+ * the input gradient, so every shard sees the same dZ, computes its own
+ * parameter gradients and a partial dX_i, and the partials are summed
+ * ("大模型分布式训练四维并行：DDP、ZeRO、张量、流水线与上下文" §4.3: the backward
+ * exchange mirrors the forward one; "AI大模型分布式训练：张量并行与流水线并行深度实践"
+ * §2.4: forward and backward each take one all-reduce per MLP):
+ *
+ *     A_i  = X W_i + b_i,  G_i = GeLU'(A_i) = Phi(A_i) + A_i phi(A_i)
+ *     dA_i = (dZ V_i^T) * G_i             (element-wise product)
+ *     dV_i = Y_i^T dZ,  dW_i = X^T dA_i,  db_i = sum over rows of dA_i
+ *     dX_i = dA_i W_i^T,  dX = dX_0 + ... + dX_{k-1}
+ *
+ * with phi the standard normal density.  dZ [M, H] has the input dtype;
+ * G_i and dA_i [M, Fk] have the input dtype; dV_i [Fk, H], dW_i [H, Fk],
+ * db_i [Fk], dX_i and dX [M, H] are float32.  In TP_BF16 the products
+ * accumulate in float32 and G_i, dA_i are rounded to bfloat16 once.
  *
  * Ownership.  The caller owns every buffer (device memory unless stated).  The
  * library never allocates, frees or synchronises; it keeps no state between
@@ -74,8 +96,9 @@ extern "C" {
 #define TP_MAX_SHARDS 64
 
 /* Flags. */
-#define TP_ACCUMULATE 1u  /* tp_mlp_row_partial: Z_i += Y_i V_i instead of Z_i = Y_i V_i */
-#define TP_FUSED_ACCUM 1u /* tp_mlp_shard_forward: fold the shard sum into the row GEMMs */
+#define TP_ACCUMULATE 1u  /* tp_mlp_row_partial, tp_mlp_grad_input_partial: add into the output */
+#define TP_FUSED_ACCUM 1u /* tp_mlp_shard_forward / _backward: fold the shard sum into the GEMMs */
+#define TP_GRAD_ACCUMULATE 2u /* weight-gradient entry points: add into dW, db, dV */
 
 /*
  * Column-parallel linear + bias + GeLU of one shard (ColumnParallelLinear
@@ -144,6 +167,116 @@ int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const*
                          const void* const* V, int k, int64_t M, int64_t H, int64_t Fk,
                          int dtype, void* workspace, size_t workspace_bytes, float* Z,
                          unsigned flags, void* stream);
+
+/*
+ * Training-mode column step: tp_mlp_col_gelu that also keeps the derivative
+ * of the activation for the backward pass (the closed form of GeLU' above):
+ *
+ *   Y_i[m, j] = GeLU(A_i[m, j]),  G_i[m, j] = GeLU'(A_i[m, j]),
+ *   A_i = X W_i + b_i
+ *
+ * Same arguments as tp_mlp_col_gelu plus G_i [M, Fk] of type `dtype`, which
+ * must not overlap any other argument.
+ */
+int tp_mlp_col_gelu_save(const void* X, const void* W_i, const void* b_i, void* Y_i, void* G_i,
+                         int64_t M, int64_t H, int64_t Fk, int dtype, void* stream);
+
+/*
+ * Gradient at the pre-activation of shard i (the backward of the row-parallel
+ * linear through the activation):
+ *
+ *   dA_i[m, j] = G_i[m, j] * sum_n dZ[m, n] V_i[j, n]
+ *
+ * dZ [M, H], V_i [Fk, H], G_i and dA_i [M, Fk], all of type `dtype`.  dA_i may
+ * be G_i itself (in place); otherwise it must not overlap any input.
+ */
+int tp_mlp_grad_act(const void* dZ, const void* V_i, const void* G_i, void* dA_i, int64_t M,
+                    int64_t H, int64_t Fk, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace that tp_mlp_grad_row_weight and
+ * tp_mlp_grad_col_weight need for these sizes (room for the partial products
+ * of a K-split of the M rows and for the column-sum partials of db_i).
+ * Returns 0 for invalid arguments.
+ */
+size_t tp_mlp_grad_weight_workspace_bytes(int64_t M, int64_t H, int64_t Fk, int dtype);
+
+/*
+ * Weight gradient of the row-parallel linear of shard i:
+ *
+ *   dV_i[j, n] = sum_m Y_i[m, j] dZ[m, n]               (flags = 0)
+ *   dV_i[j, n] = dV_i[j, n] + sum_m Y_i[m, j] dZ[m, n]  (TP_GRAD_ACCUMULATE)
+ *
+ * Y_i [M, Fk], dZ [M, H] of type `dtype`; dV_i [Fk, H] float32.  M == 0 gives
+ * zeros (or leaves dV_i unchanged with TP_GRAD_ACCUMULATE); Y_i and dZ may
+ * then be NULL.  `workspace`:
+ * device memory of tp_mlp_grad_weight_workspace_bytes(M, H, Fk, dtype) bytes
+ * (may be NULL when that is 0).  Sums over m are formed in float32 in a fixed
+ * order, so the result is deterministic.
+ */
+int tp_mlp_grad_row_weight(const void* Y_i, const void* dZ, float* dV_i, int64_t M, int64_t Fk,
+                           int64_t H, int dtype, void* workspace, size_t workspace_bytes,
+                           unsigned flags, void* stream);
+
+/*
+ * Weight and bias gradients of the column-parallel linear of shard i:
+ *
+ *   dW_i[h, j] = sum_m X[m, h] dA_i[m, j],   db_i[j] = sum_m dA_i[m, j]
+ *
+ * X [M, H], dA_i [M, Fk] of type `dtype`; dW_i [H, Fk] and db_i [Fk] float32
+ * (db_i may be NULL: no bias gradient).  TP_GRAD_ACCUMULATE adds into dW_i
+ * and db_i.  Workspace, M == 0 and determinism as for tp_mlp_grad_row_weight.
+ */
+int tp_mlp_grad_col_weight(const void* X, const void* dA_i, float* dW_i, float* db_i, int64_t M,
+                           int64_t H, int64_t Fk, int dtype, void* workspace,
+                           size_t workspace_bytes, unsigned flags, void* stream);
+
+/*
+ * Partial input gradient of shard i, the term the backward all-reduce sums:
+ *
+ *   dX_i[m, h] = sum_j dA_i[m, j] W_i[h, j]          (flags = 0)
+ *   dX_i[m, h] = dX_i[m, h] + sum_j ...             (TP_ACCUMULATE)
+ *
+ * dA_i [M, Fk], W_i [H, Fk] of type `dtype`; dX_i [M, H] float32.
+ */
+int tp_mlp_grad_input_partial(const void* dA_i, const void* W_i, float* dX_i, int64_t M,
+                              int64_t Fk, int64_t H, int dtype, unsigned flags, void* stream);
+
+/*
+ * Bytes of device workspace tp_mlp_shard_backward needs: Y_i and G_i / dA_i
+ * [M, Fk] (reused by every shard), the weight-gradient workspace, and k - 1
+ * float32 partials [M, H] unless TP_FUSED_ACCUM is set.  Returns 0 for
+ * invalid arguments.
+ */
+size_t tp_mlp_backward_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dtype,
+                                       unsigned flags);
+
+/*
+ * The whole block backward over k shards, back to back on `stream`; Y_i and
+ * G_i are recomputed from X (activation recomputation), so nothing from the
+ * forward call needs to be kept:
+ *
+ *   for i in 0..k-1:
+ *     Y, G = GeLU(A_i), GeLU'(A_i)          tp_mlp_col_gelu_save
+ *     dA   = (dZ V[i]^T) * G               tp_mlp_grad_act (in place over G)
+ *     dV[i] = Y^T dZ                        tp_mlp_grad_row_weight
+ *     dW[i] = X^T dA,  db[i] = colsum(dA)   tp_mlp_grad_col_weight
+ *     P_i  = dA W[i]^T                      tp_mlp_grad_input_partial
+ *   dX = P_0 + P_1 + ... + P_{k-1}          tp_shard_reduce
+ *
+ * W, b, V, dW, db and dV are HOST arrays of k device pointers (b == NULL: no
+ * bias; db == NULL: no bias gradient; otherwise every entry is non-NULL).
+ * flags: TP_FUSED_ACCUM folds the sum of the P_i into the dX GEMMs (same
+ * additions in the same order as the literal sum, bit-identical dX);
+ * TP_GRAD_ACCUMULATE adds into dW, db and dV.  M == 0 leaves dX empty and
+ * gives zero (or unchanged) parameter gradients; X, dZ and dX may then be
+ * NULL.
+ */
+int tp_mlp_shard_backward(const void* X, const void* const* W, const void* const* b,
+                          const void* const* V, const void* dZ, int k, int64_t M, int64_t H,
+                          int64_t Fk, int dtype, void* workspace, size_t workspace_bytes,
+                          float* dX, float* const* dW, float* const* db, float* const* dV,
+                          unsigned flags, void* stream);
 
 /* Static text for a status code. */
 const char* tp_status_string(int status);

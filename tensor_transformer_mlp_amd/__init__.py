@@ -1,4 +1,4 @@
-"""MI355X (gfx950) tensor-parallel MLP shard forward.
+"""MI355X (gfx950) tensor-parallel MLP shard forward and backward.
 
 Python binding of libtpmlp.so (C ABI in include/tp_mlp.h).  The functions have
 the C names and only marshal arguments: PyTorch supplies device memory and the
@@ -10,6 +10,15 @@ on the GPU, the call raises.
     Z_i = Y_i V_i                tp_mlp_row_partial
     Z   = sum_i Z_i              tp_shard_reduce
     all of the above, k shards   tp_mlp_shard_forward
+
+Backward (dZ = dL/dZ):
+
+    Y_i, G_i = GeLU(A_i), GeLU'(A_i)   tp_mlp_col_gelu_save
+    dA_i = (dZ V_i^T) * G_i            tp_mlp_grad_act
+    dV_i = Y_i^T dZ                    tp_mlp_grad_row_weight
+    dW_i = X^T dA_i, db_i = colsum     tp_mlp_grad_col_weight
+    dX_i = dA_i W_i^T                  tp_mlp_grad_input_partial
+    all of the above, k shards, + dX   tp_mlp_shard_backward
 """
 from __future__ import annotations
 
@@ -19,13 +28,17 @@ import os
 __all__ = [
     "TP_F32", "TP_BF16", "TP_ACCUMULATE", "TP_FUSED_ACCUM", "TP_MAX_SHARDS", "TpMlpError",
     "lib", "tp_status_string", "tp_mlp_version", "tp_mlp_col_gelu", "tp_mlp_row_partial",
-    "tp_shard_reduce", "tp_mlp_workspace_bytes", "tp_mlp_shard_forward",
+    "tp_shard_reduce", "tp_mlp_workspace_bytes", "tp_mlp_shard_forward", "TP_GRAD_ACCUMULATE",
+    "tp_mlp_col_gelu_save", "tp_mlp_grad_act", "tp_mlp_grad_weight_workspace_bytes",
+    "tp_mlp_grad_row_weight", "tp_mlp_grad_col_weight", "tp_mlp_grad_input_partial",
+    "tp_mlp_backward_workspace_bytes", "tp_mlp_shard_backward",
 ]
 
 TP_F32 = 0
 TP_BF16 = 1
 TP_ACCUMULATE = 1
 TP_FUSED_ACCUM = 1
+TP_GRAD_ACCUMULATE = 2
 TP_MAX_SHARDS = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +75,23 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_workspace_bytes.restype = sz
         L.tp_mlp_shard_forward.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, vp, cu, vp]
         L.tp_mlp_shard_forward.restype = ci
+        L.tp_mlp_col_gelu_save.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
+        L.tp_mlp_col_gelu_save.restype = ci
+        L.tp_mlp_grad_act.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
+        L.tp_mlp_grad_act.restype = ci
+        L.tp_mlp_grad_weight_workspace_bytes.argtypes = [i64, i64, i64, ci]
+        L.tp_mlp_grad_weight_workspace_bytes.restype = sz
+        L.tp_mlp_grad_row_weight.argtypes = [vp, vp, vp, i64, i64, i64, ci, vp, sz, cu, vp]
+        L.tp_mlp_grad_row_weight.restype = ci
+        L.tp_mlp_grad_col_weight.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, sz, cu, vp]
+        L.tp_mlp_grad_col_weight.restype = ci
+        L.tp_mlp_grad_input_partial.argtypes = [vp, vp, vp, i64, i64, i64, ci, cu, vp]
+        L.tp_mlp_grad_input_partial.restype = ci
+        L.tp_mlp_backward_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, cu]
+        L.tp_mlp_backward_workspace_bytes.restype = sz
+        L.tp_mlp_shard_backward.argtypes = [vp, vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, vp, vp,
+                                            vp, vp, cu, vp]
+        L.tp_mlp_shard_backward.restype = ci
         _lib = L
     return _lib
 
@@ -212,3 +242,182 @@ def tp_mlp_shard_forward(X, W, b, V, Z=None, workspace=None, fused: bool = False
                                       _dev(workspace, "workspace"), workspace.numel(), _dev(Z, "Z"),
                                       flags, _stream(stream)), "tp_mlp_shard_forward")
     return Z
+
+
+def _same_dtype(where, ref, *ts):
+    for t in ts:
+        if t is not None and t.dtype != ref.dtype:
+            raise TypeError("%s: every operand must be %s" % (where, ref.dtype))
+
+
+def _out(t, shape, dtype, device, name):
+    torch = _torch()
+    n = 1
+    for d in shape:
+        n *= d
+    if t is None:
+        return torch.empty(*shape, dtype=dtype, device=device)
+    if t.dtype != dtype or t.numel() != n:
+        raise ValueError("%s must be %s with %d elements" % (name, dtype, n))
+    return t
+
+
+def _workspace(t, need, device):
+    torch = _torch()
+    if t is None:
+        t = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return t
+
+
+def tp_mlp_col_gelu_save(X, W_i, b_i=None, Y_i=None, G_i=None, stream=None):
+    """Y_i = GeLU(A_i), G_i = GeLU'(A_i) with A_i = X W_i + b_i.  Returns (Y_i, G_i)."""
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = W_i.shape[-1]
+    dt = _dtype_code(X)
+    _same_dtype("tp_mlp_col_gelu_save", X, W_i, b_i)
+    if tuple(W_i.shape) != (H, Fk) or (b_i is not None and tuple(b_i.shape) != (Fk,)):
+        raise ValueError("shape mismatch: X %s, W_i %s" % (tuple(X.shape), tuple(W_i.shape)))
+    Y_i = _out(Y_i, (M, Fk), X.dtype, X.device, "Y_i")
+    G_i = _out(G_i, (M, Fk), X.dtype, X.device, "G_i")
+    _check(lib().tp_mlp_col_gelu_save(_dev(X, "X"), _dev(W_i, "W_i"), _dev(b_i, "b_i"), _dev(Y_i, "Y_i"),
+                                      _dev(G_i, "G_i"), M, H, Fk, dt, _stream(stream)),
+           "tp_mlp_col_gelu_save")
+    return Y_i, G_i
+
+
+def tp_mlp_grad_act(dZ, V_i, G_i, dA_i=None, stream=None):
+    """dA_i = (dZ V_i^T) * G_i; dA_i may be G_i (in place)."""
+    H = dZ.shape[-1]
+    M = dZ.numel() // H if H else 0
+    Fk = V_i.shape[0]
+    dt = _dtype_code(dZ)
+    _same_dtype("tp_mlp_grad_act", dZ, V_i, G_i, dA_i)
+    if tuple(V_i.shape) != (Fk, H) or G_i.numel() != M * Fk:
+        raise ValueError("shape mismatch: dZ %s, V_i %s, G_i %s" % (tuple(dZ.shape), tuple(V_i.shape),
+                                                                   tuple(G_i.shape)))
+    dA_i = _out(dA_i, (M, Fk), dZ.dtype, dZ.device, "dA_i")
+    _check(lib().tp_mlp_grad_act(_dev(dZ, "dZ"), _dev(V_i, "V_i"), _dev(G_i, "G_i"), _dev(dA_i, "dA_i"),
+                                 M, H, Fk, dt, _stream(stream)), "tp_mlp_grad_act")
+    return dA_i
+
+
+def tp_mlp_grad_weight_workspace_bytes(M: int, H: int, Fk: int, dtype: int) -> int:
+    return int(lib().tp_mlp_grad_weight_workspace_bytes(M, H, Fk, dtype))
+
+
+def tp_mlp_grad_row_weight(Y_i, dZ, dV_i=None, workspace=None, accumulate: bool = False, stream=None):
+    """dV_i = Y_i^T dZ (float32), or dV_i += ... with accumulate=True."""
+    torch = _torch()
+    Fk = Y_i.shape[-1]
+    M = Y_i.numel() // Fk if Fk else 0
+    H = dZ.shape[-1]
+    dt = _dtype_code(Y_i)
+    _same_dtype("tp_mlp_grad_row_weight", Y_i, dZ)
+    if dZ.numel() != M * H:
+        raise ValueError("shape mismatch: Y_i %s, dZ %s" % (tuple(Y_i.shape), tuple(dZ.shape)))
+    if dV_i is None and accumulate:
+        raise ValueError("accumulate=True needs an existing dV_i")
+    dV_i = _out(dV_i, (Fk, H), torch.float32, Y_i.device, "dV_i")
+    need = tp_mlp_grad_weight_workspace_bytes(M, H, Fk, dt)
+    workspace = _workspace(workspace, need, Y_i.device)
+    _check(lib().tp_mlp_grad_row_weight(_dev(Y_i, "Y_i"), _dev(dZ, "dZ"), _dev(dV_i, "dV_i"), M, Fk, H, dt,
+                                        _dev(workspace, "workspace"), workspace.numel(),
+                                        TP_GRAD_ACCUMULATE if accumulate else 0, _stream(stream)),
+           "tp_mlp_grad_row_weight")
+    return dV_i
+
+
+def tp_mlp_grad_col_weight(X, dA_i, dW_i=None, db_i=None, want_db: bool = True, workspace=None,
+                           accumulate: bool = False, stream=None):
+    """dW_i = X^T dA_i and db_i = sum over rows of dA_i (float32).  Returns (dW_i, db_i)."""
+    torch = _torch()
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = dA_i.shape[-1]
+    dt = _dtype_code(X)
+    _same_dtype("tp_mlp_grad_col_weight", X, dA_i)
+    if dA_i.numel() != M * Fk:
+        raise ValueError("shape mismatch: X %s, dA_i %s" % (tuple(X.shape), tuple(dA_i.shape)))
+    if accumulate and (dW_i is None or (want_db and db_i is None)):
+        raise ValueError("accumulate=True needs existing dW_i (and db_i)")
+    dW_i = _out(dW_i, (H, Fk), torch.float32, X.device, "dW_i")
+    if want_db:
+        db_i = _out(db_i, (Fk,), torch.float32, X.device, "db_i")
+    need = tp_mlp_grad_weight_workspace_bytes(M, H, Fk, dt)
+    workspace = _workspace(workspace, need, X.device)
+    _check(lib().tp_mlp_grad_col_weight(_dev(X, "X"), _dev(dA_i, "dA_i"), _dev(dW_i, "dW_i"),
+                                        _dev(db_i, "db_i") if want_db else None, M, H, Fk, dt,
+                                        _dev(workspace, "workspace"), workspace.numel(),
+                                        TP_GRAD_ACCUMULATE if accumulate else 0, _stream(stream)),
+           "tp_mlp_grad_col_weight")
+    return dW_i, (db_i if want_db else None)
+
+
+def tp_mlp_grad_input_partial(dA_i, W_i, dX_i=None, accumulate: bool = False, stream=None):
+    """dX_i = dA_i W_i^T (float32), or dX_i += ... with accumulate=True."""
+    torch = _torch()
+    Fk = dA_i.shape[-1]
+    M = dA_i.numel() // Fk if Fk else 0
+    H = W_i.shape[0]
+    dt = _dtype_code(dA_i)
+    _same_dtype("tp_mlp_grad_input_partial", dA_i, W_i)
+    if tuple(W_i.shape) != (H, Fk):
+        raise ValueError("shape mismatch: dA_i %s, W_i %s" % (tuple(dA_i.shape), tuple(W_i.shape)))
+    if dX_i is None and accumulate:
+        raise ValueError("accumulate=True needs an existing dX_i")
+    dX_i = _out(dX_i, (M, H), torch.float32, dA_i.device, "dX_i")
+    _check(lib().tp_mlp_grad_input_partial(_dev(dA_i, "dA_i"), _dev(W_i, "W_i"), _dev(dX_i, "dX_i"), M, Fk,
+                                           H, dt, TP_ACCUMULATE if accumulate else 0, _stream(stream)),
+           "tp_mlp_grad_input_partial")
+    return dX_i
+
+
+def tp_mlp_backward_workspace_bytes(k: int, M: int, H: int, Fk: int, dtype: int, flags: int = 0) -> int:
+    return int(lib().tp_mlp_backward_workspace_bytes(k, M, H, Fk, dtype, flags))
+
+
+def tp_mlp_shard_backward(X, W, b, V, dZ, dX=None, dW=None, db=None, dV=None, want_db: bool = True,
+                          workspace=None, fused: bool = False, accumulate: bool = False, stream=None):
+    """Gradients of Z = sum_i GeLU(X W[i] + b[i]) V[i] for dZ = dL/dZ.
+
+    Returns (dX, dW, db, dV): dX [M, H] and per-shard lists dW[i] [H, Fk],
+    db[i] [Fk] (None when b is None or want_db is False) and dV[i] [Fk, H], all
+    float32.  ``fused`` folds the dX shard sum into the GEMMs; ``accumulate``
+    adds into the given dW, db, dV.
+    """
+    torch = _torch()
+    k = len(W)
+    if k < 1 or len(V) != k or (b is not None and len(b) != k):
+        raise ValueError("W, V (and b) must hold the same number k >= 1 of shards")
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = W[0].shape[-1]
+    dt = _dtype_code(X)
+    _same_dtype("tp_mlp_shard_backward", X, dZ, *W, *V, *(b or []))
+    if dZ.numel() != M * H:
+        raise ValueError("dZ must have %d elements" % (M * H))
+    for i in range(k):
+        if tuple(W[i].shape) != (H, Fk) or tuple(V[i].shape) != (Fk, H) or \
+                (b is not None and tuple(b[i].shape) != (Fk,)):
+            raise ValueError("shard %d has the wrong shape" % i)
+    want_db = want_db and b is not None
+    if accumulate and (dW is None or dV is None or (want_db and db is None)):
+        raise ValueError("accumulate=True needs existing dW, dV (and db)")
+    dX = _out(dX, (M, H), torch.float32, X.device, "dX")
+    dW = [_out(None if dW is None else dW[i], (H, Fk), torch.float32, X.device, "dW[%d]" % i) for i in range(k)]
+    dV = [_out(None if dV is None else dV[i], (Fk, H), torch.float32, X.device, "dV[%d]" % i) for i in range(k)]
+    if want_db:
+        db = [_out(None if db is None else db[i], (Fk,), torch.float32, X.device, "db[%d]" % i) for i in range(k)]
+    else:
+        db = None
+    flags = (TP_FUSED_ACCUM if fused else 0) | (TP_GRAD_ACCUMULATE if accumulate else 0)
+    need = tp_mlp_backward_workspace_bytes(k, M, H, Fk, dt, flags)
+    workspace = _workspace(workspace, need, X.device)
+    arr = lambda ts, name: (ctypes.c_void_p * k)(*[_dev(t, "%s[%d]" % (name, i)) for i, t in enumerate(ts)])
+    _check(lib().tp_mlp_shard_backward(_dev(X, "X"), arr(W, "W"), None if b is None else arr(b, "b"), arr(V, "V"),
+                                       _dev(dZ, "dZ"), k, M, H, Fk, dt, _dev(workspace, "workspace"),
+                                       workspace.numel(), _dev(dX, "dX"), arr(dW, "dW"),
+                                       None if db is None else arr(db, "db"), arr(dV, "dV"), flags,
+                                       _stream(stream)), "tp_mlp_shard_backward")
+    return dX, dW, db, dV

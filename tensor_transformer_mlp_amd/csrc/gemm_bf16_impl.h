@@ -1,0 +1,473 @@
+// bf16 GEMM for gfx950: C[M,N] = epilogue(A B), bf16 operands on the
+// v_mfma_f32_32x32x16_bf16 matrix cores, float32 accumulate, for the three
+// operand layouts the MLP shard's forward and backward use (kNN, kNT, kTN).
+//
+// Workgroup tile BM x BN, WM x WN waves, each wave a (BM/WM) x (BN/WN) block
+// of 32x32 MFMA tiles.  K advances 32 per stage through NBUF LDS stages with a
+// prefetch distance of NBUF - 1.  Global data goes straight into LDS with
+// `buffer_load_dwordx4 ... lds` (lane l of a wave instruction fills bytes
+// 16 l .. 16 l + 15 of a 1 KB LDS block, so the LDS swizzle is applied by
+// choosing which global 16-byte chunk each lane fetches): no staging
+// registers and no LDS store instructions.
+//
+// Each operand tile is stored in LDS in its global orientation:
+//   K-major operand (A in kNN/kNT, B in kNT): [R rows][32 k], 64-byte rows;
+//     chunk c (8 k-values) of row r at position c ^ swzK(r).  An MFMA
+//     fragment (8 consecutive k of one row) is one 16-byte LDS read.
+//   MN-major operand (B in kNN/kTN, A in kTN): [32 k][R], 2R-byte rows;
+//     chunk c (8 row/column indices) of k-row k at position c ^ swzMN(k).  A
+//     fragment is two ds_read_b64_tr_b16 transpose reads.
+// Both swizzles make the DMA writes and the fragment reads free of LDS bank
+// conflicts.
+//
+// Edges.  Every 16-byte chunk of global memory is either wholly inside or
+// wholly outside the matrix (contiguous dimensions are multiples of 8).  A
+// lane whose chunk lies outside (rows past M or N, k past K) is given an
+// out-of-range buffer offset and the DMA writes zeros, so partial tiles need
+// no branches in the K loop; the epilogue skips stores outside C.
+//
+// MFMA operand order: the B-fragment goes in the instruction's A slot and the
+// A-fragment in its B slot, so the instruction computes the transposed tile
+// and each lane ends up owning runs of 4 consecutive output columns of one
+// row (16-byte fp32 / 8-byte bf16 stores).
+//
+// One barrier per stage, placed before the MFMAs of the stage's second k16
+// step, so the next stage's first fragment reads overlap those MFMAs.  The
+// barrier is a bare s_barrier after an explicit wait for this wave's loads
+// of the next stage only (a full workgroup fence would also wait for the
+// loads of the stages still in flight).
+#pragma once
+
+#include <type_traits>
+#include <utility>
+
+#include "device_common.h"
+#include "tp_mlp_kernels.h"
+
+namespace tpmlp {
+
+struct GemmParams {
+  const uint16_t* A;
+  const uint16_t* B;
+  const uint16_t* bias;
+  void* C;
+  void* aux;
+  const char* a_end;  // one past the last byte of A / B (bounds the buffer descriptors)
+  const char* b_end;
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  int tiles_m, tiles_n;
+};
+
+// Workgroup tile configurations (index = tile id used by the picker).
+struct TileCfg {
+  int bm, bn, wm, wn, nbuf;
+};
+constexpr TileCfg kTiles[] = {
+    {256, 256, 2, 4, 4},  // 0
+    {256, 256, 2, 4, 5},  // 1
+    {256, 256, 2, 2, 4},  // 2
+    {256, 128, 4, 2, 4},  // 3
+    {256, 128, 4, 2, 3},  // 4
+    {128, 256, 2, 4, 4},  // 5
+    {128, 256, 2, 4, 3},  // 6
+    {128, 128, 2, 2, 4},  // 7
+    {128, 128, 2, 4, 4},  // 8
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+// Epilogues each layout is instantiated with.
+constexpr bool layout_has_epi(int layout, int epi) {
+  return layout == kNN ? (epi == kEpiBiasGelu || epi == kEpiBiasGeluSave || epi == kEpiStoreF32 ||
+                          epi == kEpiAccumF32)
+       : layout == kNT ? (epi == kEpiMulAux || epi == kEpiStoreF32 || epi == kEpiAccumF32)
+                       : (epi == kEpiStoreF32 || epi == kEpiAccumF32);
+}
+
+// LDS chunk swizzles (see the file comment).  K-major rows are 64 bytes
+// (four chunks); a 16-byte LDS access is served per 16 lanes over 64 banks,
+// i.e. sixteen 16-byte slots, and swzK spreads the 16 consecutive rows of a
+// fragment read over the four chunk positions of four row pairs.  MN-major
+// rows hold >= 16 chunks; swzMN rotates by 4 chunks per k-row so that the
+// four k-rows of a transpose read fall in distinct bank groups.
+__device__ __forceinline__ int swzK(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swzMN(int k) { return 4 * (k & 3); }
+
+// One operand's tile: R rows of the operand (rows of A, or columns of B) by
+// 32 k per stage, loaded by NW waves.
+template <int R, bool KMAJ, int NW>
+struct OperandTile {
+  static constexpr int kBytes = R * 64;  // R x 32 x 2 bytes
+  static constexpr int kPerWave = kBytes / 1024 / NW;
+  static constexpr int kRow = KMAJ ? 64 : 2 * R;  // LDS row bytes
+  static constexpr int kRowsPerBlock = 1024 / kRow;
+  static constexpr int kLanesPerRow = kRow / 16;
+  static_assert(kBytes % (1024 * NW) == 0, "DMA split");
+  static_assert(KMAJ || (R % 128 == 0 && R <= 512), "MN-major tiles need 16-chunk row groups");
+
+  uint64_t base;     // global address of (tile row 0, k = 0)
+  uint64_t end;      // one past the operand's last byte
+  uint64_t kstride;  // bytes per unit of k
+  uint32_t src[kPerWave];  // byte offset of the lane's chunk from (tile row 0, stage k 0)
+  int kidx[kPerWave];      // first k (within a stage) of the lane's chunk
+
+  // r0: first row (K-major) or column (MN-major) of the tile; rtot: the
+  // operand's extent in that dimension; ld: leading dimension in elements.
+  __device__ __forceinline__ void init(const uint16_t* ptr, const char* ptr_end, int64_t ld, int r0,
+                                       int rtot, int wave, int lane) {
+    end = reinterpret_cast<uint64_t>(ptr_end);
+    if constexpr (KMAJ) {
+      base = reinterpret_cast<uint64_t>(ptr + (int64_t)r0 * ld);
+      kstride = 2;
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int row = (wave * kPerWave + i) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swzK(row);
+        src[i] = r0 + row < rtot ? (uint32_t)row * (uint32_t)ld * 2u + (uint32_t)c * 16u : kOob;
+        kidx[i] = c * 8;
+      }
+    } else {
+      base = reinterpret_cast<uint64_t>(ptr + r0);
+      kstride = (uint64_t)ld * 2u;
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int row = (wave * kPerWave + i) * kRowsPerBlock + lane / kLanesPerRow;
+        const int c = (lane % kLanesPerRow) ^ swzMN(row);
+        src[i] = r0 + c * 8 < rtot ? (uint32_t)row * (uint32_t)ld * 2u + (uint32_t)c * 16u : kOob;
+        kidx[i] = row;
+      }
+    }
+  }
+
+  // Loads of stage k0 .. k0 + 31 into `lds`; kleft = K - k0 (<= 0: nothing
+  // valid, every lane writes zeros and no memory is read).
+  __device__ __forceinline__ void issue(char* lds, int wave, int k0, int kleft) const {
+    const bool live = kleft > 0;
+    const uint64_t addr = base + (live ? (uint64_t)k0 * kstride : 0);
+    const uint64_t rem = end > addr ? end - addr : 0;
+    const uint32_t rec = live ? (uint32_t)(rem < 0x7FFFFFF0ull ? rem : 0x7FFFFFF0ull) : 0u;
+    const i32x4_t desc = buffer_desc(reinterpret_cast<const void*>(addr), rec);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      lds_dma16(desc, lds + (wave * kPerWave + i) * 1024, kidx[i] < kleft ? src[i] : kOob);
+  }
+};
+
+// Fragment reads of one operand for a wave whose F fragments start at tile
+// row `wbase` (K-major: F row blocks of 32; MN-major: F column blocks of 32).
+template <int R, bool KMAJ, int F>
+struct OperandFrags {
+  static constexpr int kRow = KMAJ ? 64 : 2 * R;
+  static constexpr int kReads = KMAJ ? F : 2 * F;  // LDS read instructions per k16 step
+  int off[KMAJ ? 2 : F];
+
+  __device__ __forceinline__ void init(int wbase, int lane) {
+    if constexpr (KMAJ) {
+      const int row = wbase + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) off[ks] = row * 64 + ((2 * ks + (lane >> 5)) ^ swzK(row)) * 16;
+    } else {
+      const int g = lane >> 4, t = lane & 15;
+      const int krow = 8 * (g >> 1) + (t >> 2);  // + 16 ks, + 4 for the second read
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const int col = wbase + 32 * f + 16 * (g & 1) + 4 * (t & 3);
+        off[f] = krow * kRow + (((col >> 3) ^ swzMN(krow)) * 16) + ((col >> 2) & 1) * 8;
+      }
+    }
+  }
+
+  // swzK(r + 32 f) == swzK(r) and swzMN(k + 4) == swzMN(k + 16) == swzMN(k).
+  __device__ __forceinline__ void read(const char* S, int ks, bf16x8_t (&dst)[F]) const {
+    if constexpr (KMAJ) {
+#pragma unroll
+      for (int f = 0; f < F; ++f) dst[f] = *reinterpret_cast<const bf16x8_t*>(S + off[ks] + f * 2048);
+    } else {
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const char* p = S + off[f] + ks * 16 * kRow;
+        dst[f] = ds_read_tr_pair(p, p + 4 * kRow);
+      }
+    }
+  }
+};
+
+template <int EPI, int LAYOUT, int BM, int BN, int WM, int WN, int NBUF>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
+  constexpr bool AK = LAYOUT != kTN;  // A K-major
+  constexpr bool BK = LAYOUT == kNT;  // B K-major
+  constexpr int D = NBUF - 1;         // prefetch distance in K steps of 32
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  using TA = OperandTile<BM, AK, NW>;
+  using TB = OperandTile<BN, BK, NW>;
+  using RA = OperandFrags<BM, AK, FM>;
+  using RB = OperandFrags<BN, BK, FN>;
+  constexpr int A_BYTES = TA::kBytes, STAGE = TA::kBytes + TB::kBytes;
+  constexpr int L = TA::kPerWave + TB::kPerWave;  // DMA instructions per wave per stage
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(NBUF >= 3 && NBUF <= 6, "stage count");
+  static_assert((D - 1) * L <= 63, "vmcnt immediate");
+  static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
+
+  // One array per stage: distinct LDS objects get distinct alias scopes, so
+  // the compiler can tell that fragment reads of one stage do not depend on
+  // the DMA writes in flight into the others (and inserts no vmcnt wait).
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[NBUF > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st4[NBUF > 4 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st5[NBUF > 5 ? STAGE : 16];
+  auto stage = [&](auto bset) -> char* {
+    constexpr int b = decltype(bset)::value;
+    if constexpr (b == 0) return st0;
+    else if constexpr (b == 1) return st1;
+    else if constexpr (b == 2) return st2;
+    else if constexpr (b == 3) return st3;
+    else if constexpr (b == 4) return st4;
+    else return st5;
+  };
+
+  int tm, tn;
+  tile_coords<8>(p.tiles_m, p.tiles_n, tm, tn);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+  const int K = p.K;
+  const int nk = (K + 31) / 32;
+
+  TA ta;
+  TB tb;
+  ta.init(p.A, p.a_end, p.lda, m0, p.M, wave, lane);
+  tb.init(p.B, p.b_end, p.ldb, n0, p.N, wave, lane);
+  auto issue_stage = [&](auto bset, int kt) {
+    char* S = stage(bset);
+    const int k0 = kt * 32;
+    ta.issue(S, wave, k0, K - k0);
+    tb.issue(S + A_BYTES, wave, k0, K - k0);
+  };
+
+  RA ra;
+  RB rb;
+  ra.init(wm * WTM, lane);
+  rb.init(wn * WTN, lane);
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  bf16x8_t fa[2][FM], fb[2][FN];
+  auto read_frags = [&](auto fset, auto bset, int ks) {
+    constexpr int f = decltype(fset)::value;
+    const char* S = stage(bset);
+    ra.read(S, ks, fa[f]);
+    rb.read(S + A_BYTES, ks, fb[f]);
+  };
+  auto mfmas = [&](auto fset) {
+    constexpr int f = decltype(fset)::value;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  constexpr int kMfma = FM * FN;
+  constexpr int kReads = RA::kReads + RB::kReads;
+  // vmcnt((D - 1) L), expcnt(7), lgkmcnt(0): this wave's loads of the next
+  // stage (all but the D - 1 younger stages) and all its LDS reads are done.
+  constexpr int kWaitN = (D - 1) * L;
+  constexpr int kWaitNext = (kWaitN & 15) | ((kWaitN >> 4) << 14) | (7 << 4);
+
+  [&]<int... b>(std::integer_sequence<int, b...>) {
+    (issue_stage(std::integral_constant<int, b>{}, b), ...);
+  }(std::make_integer_sequence<int, D>{});
+  __builtin_amdgcn_s_waitcnt(kWaitNext);
+  asm volatile("s_barrier" ::: "memory");
+  read_frags(I0{}, I0{}, 0);
+
+  // One K step of 32 on stage buffer c (static, so that every LDS access
+  // names its buffer at compile time).
+  auto kstep = [&](auto cset, int kt) {
+    constexpr int c = decltype(cset)::value;
+    using Refill = std::integral_constant<int, (c + D) % NBUF>;
+    using Next = std::integral_constant<int, (c + 1) % NBUF>;
+    // k16 step 0: refill the buffer freed by stage kt - 1 with stage kt + D,
+    // read step 1's fragments, MFMAs of step 0.
+    issue_stage(Refill{}, kt + D);
+    read_frags(I1{}, cset, 1);
+    mfmas(I0{});
+#pragma unroll
+    for (int m = 0; m < kMfma; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (m < L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // k16 step 1: once stage kt + 1 has landed for every wave, read its step
+    // 0 fragments while the MFMAs of step 1 run.
+    __builtin_amdgcn_s_waitcnt(kWaitNext);
+    asm volatile("s_barrier" ::: "memory");
+    read_frags(I0{}, Next{}, 0);
+    mfmas(I1{});
+#pragma unroll
+    for (int m = 0; m < kMfma; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The loop body walks the NBUF buffers in order; an early exit handles a
+  // step count that is not a multiple of NBUF (uniform across the workgroup).
+  for (int kt = 0; kt < nk; kt += NBUF) {
+    bool more = true;
+    [&]<int... b>(std::integer_sequence<int, b...>) {
+      ((more = more && (kt + b < nk), more ? (kstep(std::integral_constant<int, b>{}, kt + b), 0) : 0),
+       ...);
+    }(std::make_integer_sequence<int, NBUF>{});
+  }
+  // The last stages' loads (out of range, writing zeros) must have landed
+  // before this workgroup's LDS can be handed to another.
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+
+  // Epilogue.  Per 32-row block i, every global load the epilogue needs (the
+  // multiplier or the old value of C) is issued before any store, so the
+  // loads overlap; each element is read and written by the same lane only,
+  // so this order is also correct when C is aux.  The bias is loaded once.
+  const int l32 = lane & 31;
+  const int hcol = 4 * (lane >> 5);
+  const int M = p.M, N = p.N;
+  const int64_t ldc = p.ldc;
+  constexpr bool kBias = EPI == kEpiBiasGelu || EPI == kEpiBiasGeluSave;
+  f32x4_t bias4[FN][4];
+  if constexpr (kBias) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
+        u32x2_t bb = u32x2_t{0u, 0u};
+        if (p.bias && n < N) bb = *reinterpret_cast<const u32x2_t*>(p.bias + n);
+        bias4[j][gq] = f32x4_t{bf16_bits_to_f32(bb[0] & 0xFFFFu), bf16_bits_to_f32(bb[0] >> 16),
+                               bf16_bits_to_f32(bb[1] & 0xFFFFu), bf16_bits_to_f32(bb[1] >> 16)};
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + l32;
+    const bool mrow = m < M;
+    const int64_t row = (int64_t)m * ldc;
+    u32x2_t aux2[FN][4];
+    f32x4_t old4[FN][4];
+    if constexpr (EPI == kEpiMulAux || EPI == kEpiAccumF32) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
+          if constexpr (EPI == kEpiMulAux) {
+            aux2[j][gq] = u32x2_t{0u, 0u};
+            if (mrow && n < N)
+              aux2[j][gq] = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(p.aux) + row + n);
+          } else {
+            old4[j][gq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (mrow && n < N)
+              old4[j][gq] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.C) + row + n);
+          }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
+        if (!mrow || n >= N) continue;
+        const int64_t idx = row + n;
+        f32x4_t v = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                            acc[i][j][4 * gq + 3]};
+        if constexpr (kBias) {
+          v += bias4[j][gq];
+          if constexpr (EPI == kEpiBiasGelu) {
+            u32x2_t o;
+            o[0] = f32_to_bf16_bits(gelu_f32(v[0])) | (f32_to_bf16_bits(gelu_f32(v[1])) << 16);
+            o[1] = f32_to_bf16_bits(gelu_f32(v[2])) | (f32_to_bf16_bits(gelu_f32(v[3])) << 16);
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.C) + idx) = o;
+          } else {
+            float y[4], g[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gelu_and_grad_f32(v[e], y[e], g[e]);
+            u32x2_t oy, og;
+            oy[0] = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+            oy[1] = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
+            og[0] = f32_to_bf16_bits(g[0]) | (f32_to_bf16_bits(g[1]) << 16);
+            og[1] = f32_to_bf16_bits(g[2]) | (f32_to_bf16_bits(g[3]) << 16);
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.C) + idx) = oy;
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.aux) + idx) = og;
+          }
+        } else if constexpr (EPI == kEpiMulAux) {
+          const u32x2_t gg = aux2[j][gq];
+          u32x2_t o;
+          o[0] = f32_to_bf16_bits(v[0] * bf16_bits_to_f32(gg[0] & 0xFFFFu)) |
+                 (f32_to_bf16_bits(v[1] * bf16_bits_to_f32(gg[0] >> 16)) << 16);
+          o[1] = f32_to_bf16_bits(v[2] * bf16_bits_to_f32(gg[1] & 0xFFFFu)) |
+                 (f32_to_bf16_bits(v[3] * bf16_bits_to_f32(gg[1] >> 16)) << 16);
+          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.C) + idx) = o;
+        } else if constexpr (EPI == kEpiStoreF32) {
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.C) + idx) = v;
+        } else {
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.C) + idx) = old4[j][gq] + v;
+        }
+      }
+    }
+  }
+}
+
+// Launch one tile configuration of one layout (p.tiles_m / p.tiles_n set).
+template <int LAYOUT, int T>
+hipError_t launch_bf16_tile(const GemmParams& p, Epilogue epi, hipStream_t s) {
+  constexpr TileCfg c = kTiles[T];
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n), block(c.wm * c.wn * 64);
+  bool done = false;
+  [&]<int... e>(std::integer_sequence<int, e...>) {
+    (([&] {
+       if constexpr (layout_has_epi(LAYOUT, e)) {
+         if (epi == e) {
+           hipLaunchKernelGGL((gemm_bf16_kernel<e, LAYOUT, c.bm, c.bn, c.wm, c.wn, c.nbuf>), grid,
+                              block, 0, s, p);
+           done = true;
+         }
+       }
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, 5>{});
+  return done ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+template <int LAYOUT>
+hipError_t launch_bf16_layout_tile(int tile, const GemmParams& p, Epilogue epi, hipStream_t s) {
+  hipError_t r = hipErrorInvalidValue;
+  [&]<int... t>(std::integer_sequence<int, t...>) {
+    ((tile == t ? (r = launch_bf16_tile<LAYOUT, t>(p, epi, s), 0) : 0), ...);
+  }(std::make_integer_sequence<int, kNumTiles>{});
+  return r;
+}
+
+// Per-layout entry points (one translation unit each), and the launcher that
+// splits a large problem into launches of at most kMaxTilesPerLaunch tiles.
+hipError_t launch_bf16_nn(int tile, const GemmParams& p, Epilogue epi, hipStream_t s);
+hipError_t launch_bf16_nt(int tile, const GemmParams& p, Epilogue epi, hipStream_t s);
+hipError_t launch_bf16_tn(int tile, const GemmParams& p, Epilogue epi, hipStream_t s);
+hipError_t launch_gemm_bf16_tile(int tile, const GemmArgs& g, hipStream_t s);
+int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K);
+
+}  // namespace tpmlp

@@ -1,0 +1,10 @@
+// bf16 GEMM instantiations for the kNT operand layout (see gemm_bf16_impl.h).
+#include "gemm_bf16_impl.h"
+
+namespace tpmlp {
+
+hipError_t launch_bf16_nt(int tile, const GemmParams& p, Epilogue epi, hipStream_t s) {
+  return launch_bf16_layout_tile<kNT>(tile, p, epi, s);
+}
+
+}  // namespace tpmlp

@@ -1,0 +1,200 @@
+// Streaming reductions for gfx950: the sum of the k shard partials (the
+// one-device stand-in for the all-reduce) and a deterministic column sum.
+#include "device_common.h"
+#include "tp_mlp_kernels.h"
+
+namespace tpmlp {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Shard reduce: Z = ((P_0 + P_1) + P_2) + ... in float32, 16-byte vectors,
+// grid-stride.  KC > 0 fixes k at compile time so that all k loads of a
+// vector are in flight together; KC == 0 reads k at run time.
+// ---------------------------------------------------------------------------
+struct PartPtrs {
+  const float* p[64];
+};
+
+// U 16-byte vectors per thread per iteration, all 1 + (k - 1) loads of them
+// issued before the adds, so that each thread keeps U * k loads in flight.
+template <int KC, int U>
+__global__ __launch_bounds__(256) void shard_reduce_kernel(PartPtrs parts, int k,
+                                                           float* __restrict__ Z, int64_t n) {
+  const int kk = KC > 0 ? KC : k;
+  const int64_t n4 = n >> 2;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * U;
+  for (int64_t v0 = ((int64_t)blockIdx.x * blockDim.x) * U + threadIdx.x; v0 < n4; v0 += stride) {
+    f32x4_t s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + (int64_t)u * blockDim.x;
+      s[u] = v < n4 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(parts.p[0]) + v)
+                    : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (KC > 0) {
+      f32x4_t t[KC > 1 ? KC - 1 : 1][U];
+#pragma unroll
+      for (int i = 1; i < KC; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + (int64_t)u * blockDim.x;
+          t[i - 1][u] = v < n4 ? __builtin_nontemporal_load(
+                                     reinterpret_cast<const f32x4_t*>(parts.p[i]) + v)
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int i = 1; i < KC; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) s[u] = s[u] + t[i - 1][u];
+    } else {
+      for (int i = 1; i < kk; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + (int64_t)u * blockDim.x;
+          if (v < n4)
+            s[u] = s[u] + __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(parts.p[i]) + v);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + (int64_t)u * blockDim.x;
+      if (v < n4) __builtin_nontemporal_store(s[u], reinterpret_cast<f32x4_t*>(Z) + v);
+    }
+  }
+  // scalar tail (n not a multiple of 4)
+  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+    const int64_t e = (n4 << 2) + threadIdx.x;
+    float s = parts.p[0][e];
+    for (int i = 1; i < kk; ++i) s = s + parts.p[i][e];
+    Z[e] = s;
+  }
+}
+
+template <int U>
+hipError_t launch_reduce_u(const PartPtrs& pp, int k, float* Z, int64_t n, int64_t max_blocks,
+                           hipStream_t s) {
+  const int64_t n4 = n >> 2;
+  int64_t blocks = (n4 + 256 * U - 1) / (256 * U);
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks), block(256);
+  switch (k) {
+    case 1: hipLaunchKernelGGL((shard_reduce_kernel<1, U>), grid, block, 0, s, pp, k, Z, n); break;
+    case 2: hipLaunchKernelGGL((shard_reduce_kernel<2, U>), grid, block, 0, s, pp, k, Z, n); break;
+    case 4: hipLaunchKernelGGL((shard_reduce_kernel<4, U>), grid, block, 0, s, pp, k, Z, n); break;
+    case 8: hipLaunchKernelGGL((shard_reduce_kernel<8, U>), grid, block, 0, s, pp, k, Z, n); break;
+    default: hipLaunchKernelGGL((shard_reduce_kernel<0, U>), grid, block, 0, s, pp, k, Z, n); break;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Column sum out[n] (+)= sum_m A[m, n], two passes:
+//   1. workgroup (cb, rb) sums rows [rb R, rb R + R) of columns
+//      [256 cb, 256 cb + 256): 32 column groups of 8 x 8 row lanes, each lane
+//      a running float32 sum over every 8th row, then the 8 row lanes are
+//      added in order through LDS; the result is partials[rb][n];
+//   2. out[n] = (out[n] +) partials[0][n] + partials[1][n] + ... in order.
+// The row-block count depends only on (M, N), so the result is reproducible.
+// ---------------------------------------------------------------------------
+constexpr int kColsPerBlock = 256;
+
+int64_t colsum_row_blocks(int64_t M, int64_t N) {
+  if (M <= 0) return 0;
+  const int64_t cb = (N + kColsPerBlock - 1) / kColsPerBlock;
+  int64_t rb = (2048 + cb - 1) / cb;        // aim for ~2048 workgroups
+  const int64_t max_rb = (M + 63) / 64;      // at least 64 rows per workgroup
+  if (rb > max_rb) rb = max_rb;
+  if (rb > 4096) rb = 4096;
+  return rb < 1 ? 1 : rb;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const void* __restrict__ A, int64_t M,
+                                                             int64_t N, int64_t rows_per_block,
+                                                             float* __restrict__ partials) {
+  __shared__ float red[8][kColsPerBlock + 4];
+  const int cg = threadIdx.x & 31, rl = threadIdx.x >> 5;
+  const int64_t n = (int64_t)blockIdx.x * kColsPerBlock + cg * 8;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+  int64_t r1 = r0 + rows_per_block;
+  if (r1 > M) r1 = M;
+  float s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = 0.f;
+  if (n < N) {
+    for (int64_t r = r0 + rl; r < r1; r += 8) {
+      if constexpr (BF16) {
+        const u32x4_t v =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(A) + r * N + n));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[2 * e] += bf16_bits_to_f32(v[e] & 0xFFFFu);
+          s[2 * e + 1] += bf16_bits_to_f32(v[e] >> 16);
+        }
+      } else {
+        const f32x4_t* q = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(A) + r * N + n);
+        const f32x4_t a = __builtin_nontemporal_load(q), b = __builtin_nontemporal_load(q + 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[e] += a[e];
+          s[4 + e] += b[e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rl][cg * 8 + e] = s[e];
+  __syncthreads();
+  const int c = threadIdx.x;  // one column of the block per thread
+  const int64_t nc = (int64_t)blockIdx.x * kColsPerBlock + c;
+  if (nc < N) {
+    float t = red[0][c];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) t += red[i][c];
+    partials[(int64_t)blockIdx.y * N + nc] = t;
+  }
+}
+
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ partials,
+                                                           int64_t rb, int64_t N,
+                                                           float* __restrict__ out, int accumulate) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float t = accumulate ? out[n] : 0.f;
+  for (int64_t i = 0; i < rb; ++i) t += partials[i * N + n];
+  out[n] = t;
+}
+
+}  // namespace
+
+hipError_t launch_shard_reduce(const float* const* parts, int k, float* Z, int64_t n,
+                               hipStream_t s) {
+  PartPtrs pp;
+  for (int i = 0; i < 64; ++i) pp.p[i] = i < k ? parts[i] : nullptr;
+  return launch_reduce_u<4>(pp, k, Z, n, 65536, s);
+}
+
+int64_t colsum_partials_floats(int64_t M, int64_t N) { return colsum_row_blocks(M, N) * N; }
+
+hipError_t launch_colsum(const void* A, bool bf16, int64_t M, int64_t N, float* out,
+                         bool accumulate, float* partials, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int64_t rb = colsum_row_blocks(M, N);
+  if (rb > 0) {
+    const int64_t rows = (M + rb - 1) / rb;
+    const dim3 grid((unsigned)((N + kColsPerBlock - 1) / kColsPerBlock), (unsigned)rb), block(256);
+    if (bf16)
+      hipLaunchKernelGGL(colsum_partial_kernel<true>, grid, block, 0, s, A, M, N, rows, partials);
+    else
+      hipLaunchKernelGGL(colsum_partial_kernel<false>, grid, block, 0, s, A, M, N, rows, partials);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
+                     partials, rb, N, out, accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace tpmlp

@@ -1,5 +1,5 @@
 // C ABI of libtpmlp.so (declared in include/tp_mlp.h): argument checks, the
-// shard loop and the workspace layout.  Every check runs on the host before
+// shard loops and the workspace layouts.  Every check runs on the host before
 // the first HIP call, so a rejected call launches nothing.
 #include "tp_mlp.h"
 
@@ -10,7 +10,10 @@
 
 namespace {
 
+using tpmlp::GemmArgs;
+
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxLd = int64_t(1) << 22;  // H, Fk: 32-bit row offsets inside a tile
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 constexpr size_t kWsAlign = 256;
 
@@ -23,8 +26,8 @@ size_t elt_size(int dtype) { return dtype == TP_BF16 ? 2 : 4; }
 // Shape rules shared by every entry point.  M may be 0.
 int check_dims(int64_t M, int64_t H, int64_t Fk) {
   if (M < 0 || M > kMaxDim) return TP_ERR_SHAPE;
-  if (H < 8 || H > kMaxDim || H % 8) return TP_ERR_SHAPE;
-  if (Fk < 8 || Fk > kMaxDim || Fk % 8) return TP_ERR_SHAPE;
+  if (H < 8 || H > kMaxLd || H % 8) return TP_ERR_SHAPE;
+  if (Fk < 8 || Fk > kMaxLd || Fk % 8) return TP_ERR_SHAPE;
   if (M > 0 && (M > kMaxElems / H || M > kMaxElems / Fk)) return TP_ERR_SHAPE;
   if (H > kMaxElems / Fk) return TP_ERR_SHAPE;
   return TP_OK;
@@ -38,31 +41,122 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
-
-int col_gelu_checked(const void* X, const void* W_i, const void* b_i, void* Y_i, int64_t M,
-                     int64_t H, int64_t Fk, int dtype, hipStream_t s) {
-  if (dtype == TP_BF16)
-    return hip_status(tpmlp::launch_gemm_bf16(static_cast<const uint16_t*>(X),
-                                              static_cast<const uint16_t*>(W_i),
-                                              static_cast<const uint16_t*>(b_i), Y_i, M, Fk, H,
-                                              tpmlp::kEpiBiasGelu, s));
-  return hip_status(tpmlp::launch_gemm_f32(static_cast<const float*>(X),
-                                           static_cast<const float*>(W_i),
-                                           static_cast<const float*>(b_i), Y_i, M, Fk, H,
-                                           tpmlp::kEpiBiasGelu, s));
+// A set of byte ranges: outputs may overlap neither an input nor each other.
+struct Region {
+  const void* p;
+  size_t n;
+};
+struct Regions {
+  static constexpr int kMax = 4 * TP_MAX_SHARDS + 8;
+  Region r[kMax];
+  int n = 0;
+  void add(const void* p, size_t bytes) {
+    if (p && bytes && n < kMax) r[n++] = Region{p, bytes};
+  }
+};
+bool any_overlap(const Regions& outs, const Regions& ins) {
+  for (int i = 0; i < outs.n; ++i) {
+    for (int j = 0; j < ins.n; ++j)
+      if (overlap(outs.r[i].p, outs.r[i].n, ins.r[j].p, ins.r[j].n)) return true;
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs.r[i].p, outs.r[i].n, outs.r[j].p, outs.r[j].n)) return true;
+  }
+  return false;
 }
 
-int row_partial_checked(const void* Y_i, const void* V_i, float* Z_i, int64_t M, int64_t Fk,
-                        int64_t H, int dtype, bool accumulate, hipStream_t s) {
-  const tpmlp::Epilogue epi = accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32;
-  if (dtype == TP_BF16)
-    return hip_status(tpmlp::launch_gemm_bf16(static_cast<const uint16_t*>(Y_i),
-                                              static_cast<const uint16_t*>(V_i), nullptr, Z_i, M,
-                                              H, Fk, epi, s));
-  return hip_status(tpmlp::launch_gemm_f32(static_cast<const float*>(Y_i),
-                                           static_cast<const float*>(V_i), nullptr, Z_i, M, H, Fk,
-                                           epi, s));
+int hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
+
+hipError_t gemm(const GemmArgs& g, int dtype, hipStream_t s) {
+  return dtype == TP_BF16 ? tpmlp::launch_gemm_bf16(g, s) : tpmlp::launch_gemm_f32(g, s);
+}
+
+GemmArgs args(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
+              int64_t ldb, tpmlp::Layout layout, tpmlp::Epilogue epi) {
+  GemmArgs g;
+  g.A = A;
+  g.B = B;
+  g.bias = nullptr;
+  g.C = C;
+  g.aux = nullptr;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = N;
+  g.layout = layout;
+  g.epi = epi;
+  return g;
+}
+
+// The steps, after validation.
+// Y_i (and G_i) = act(X W_i + b_i): [M, H] x [H, Fk], both row-major.
+int col_step(const void* X, const void* W_i, const void* b_i, void* Y_i, void* G_i, int64_t M,
+             int64_t H, int64_t Fk, int dtype, hipStream_t s) {
+  GemmArgs g = args(X, W_i, Y_i, M, Fk, H, H, Fk, tpmlp::kNN,
+                    G_i ? tpmlp::kEpiBiasGeluSave : tpmlp::kEpiBiasGelu);
+  g.bias = b_i;
+  g.aux = G_i;
+  return hip_status(gemm(g, dtype, s));
+}
+
+// Z_i (+)= Y_i V_i: [M, Fk] x [Fk, H].
+int row_step(const void* Y_i, const void* V_i, float* Z_i, int64_t M, int64_t Fk, int64_t H,
+             int dtype, bool accumulate, hipStream_t s) {
+  return hip_status(gemm(args(Y_i, V_i, Z_i, M, H, Fk, Fk, H, tpmlp::kNN,
+                              accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32),
+                         dtype, s));
+}
+
+// dA_i = (dZ V_i^T) * G_i: [M, H] x ([Fk, H] read as its transpose).
+int act_grad_step(const void* dZ, const void* V_i, const void* G_i, void* dA_i, int64_t M,
+                  int64_t H, int64_t Fk, int dtype, hipStream_t s) {
+  GemmArgs g = args(dZ, V_i, dA_i, M, Fk, H, H, H, tpmlp::kNT, tpmlp::kEpiMulAux);
+  g.aux = const_cast<void*>(G_i);
+  return hip_status(gemm(g, dtype, s));
+}
+
+// Weight-gradient workspace: the larger K-split of the two weight GEMMs and
+// the column-sum partials, side by side.
+size_t split_bytes(int64_t M, int64_t H, int64_t Fk, int dtype) {
+  const bool bf16 = dtype == TP_BF16;
+  const size_t a = tpmlp::gemm_split_workspace_bytes(bf16, Fk, H, M);
+  const size_t b = tpmlp::gemm_split_workspace_bytes(bf16, H, Fk, M);
+  return a > b ? a : b;
+}
+size_t colsum_bytes(int64_t M, int64_t Fk) {
+  return round_up(size_t(tpmlp::colsum_partials_floats(M, Fk)) * 4, kWsAlign);
+}
+size_t grad_weight_ws(int64_t M, int64_t H, int64_t Fk, int dtype) {
+  return round_up(split_bytes(M, H, Fk, dtype), kWsAlign) + colsum_bytes(M, Fk);
+}
+
+// dV_i (+)= Y_i^T dZ: ([M, Fk] read as its transpose) x [M, H], K = M.
+int row_weight_step(const void* Y_i, const void* dZ, float* dV_i, int64_t M, int64_t Fk, int64_t H,
+                    int dtype, void* ws, bool accumulate, hipStream_t s) {
+  const GemmArgs g = args(Y_i, dZ, dV_i, Fk, H, M, Fk, H, tpmlp::kTN,
+                          accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32);
+  return hip_status(tpmlp::launch_gemm_split(g, dtype == TP_BF16, ws, s));
+}
+
+// dW_i (+)= X^T dA_i and db_i (+)= colsum(dA_i).
+int col_weight_step(const void* X, const void* dA_i, float* dW_i, float* db_i, int64_t M,
+                    int64_t H, int64_t Fk, int dtype, void* ws, bool accumulate, hipStream_t s) {
+  const GemmArgs g = args(X, dA_i, dW_i, H, Fk, M, H, Fk, tpmlp::kTN,
+                          accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32);
+  int st = hip_status(tpmlp::launch_gemm_split(g, dtype == TP_BF16, ws, s));
+  if (st || !db_i) return st;
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                             round_up(split_bytes(M, H, Fk, dtype), kWsAlign));
+  return hip_status(tpmlp::launch_colsum(dA_i, dtype == TP_BF16, M, Fk, db_i, accumulate, partials, s));
+}
+
+// dX_i (+)= dA_i W_i^T: [M, Fk] x ([H, Fk] read as its transpose).
+int input_grad_step(const void* dA_i, const void* W_i, float* dX_i, int64_t M, int64_t Fk,
+                    int64_t H, int dtype, bool accumulate, hipStream_t s) {
+  return hip_status(gemm(args(dA_i, W_i, dX_i, M, H, Fk, Fk, Fk, tpmlp::kNT,
+                              accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32),
+                         dtype, s));
 }
 
 }  // namespace
@@ -73,18 +167,19 @@ const char* tp_status_string(int status) {
   switch (status) {
     case TP_OK: return "ok";
     case TP_ERR_NULL: return "a required pointer is NULL";
-    case TP_ERR_SHAPE: return "a size is out of range (H and F/k must be multiples of 8, >= 8)";
+    case TP_ERR_SHAPE:
+      return "a size is out of range (H and F/k must be multiples of 8, 8 <= H, F/k <= 2^22)";
     case TP_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case TP_ERR_DTYPE: return "unknown dtype (expected TP_F32 or TP_BF16)";
     case TP_ERR_WORKSPACE: return "workspace is missing or too small";
     case TP_ERR_HIP: return "a HIP launch failed";
     case TP_ERR_FLAGS: return "unknown flag bits";
-    case TP_ERR_ALIAS: return "an output overlaps an input";
+    case TP_ERR_ALIAS: return "an output overlaps an input or another output";
     default: return "unknown status";
   }
 }
 
-int tp_mlp_version(void) { return 100; }
+int tp_mlp_version(void) { return 110; }
 
 int tp_mlp_col_gelu(const void* X, const void* W_i, const void* b_i, void* Y_i, int64_t M,
                     int64_t H, int64_t Fk, int dtype, void* stream) {
@@ -96,12 +191,34 @@ int tp_mlp_col_gelu(const void* X, const void* W_i, const void* b_i, void* Y_i, 
   if (!aligned16(X) || !aligned16(W_i) || !aligned16(Y_i) || (b_i && !aligned16(b_i)))
     return TP_ERR_ALIGN;
   const size_t e = elt_size(dtype);
-  const size_t ny = size_t(M) * size_t(Fk) * e;
-  if (overlap(Y_i, ny, X, size_t(M) * size_t(H) * e) ||
-      overlap(Y_i, ny, W_i, size_t(H) * size_t(Fk) * e) ||
-      (b_i && overlap(Y_i, ny, b_i, size_t(Fk) * e)))
-    return TP_ERR_ALIAS;
-  return col_gelu_checked(X, W_i, b_i, Y_i, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+  Regions in, out;
+  in.add(X, size_t(M) * size_t(H) * e);
+  in.add(W_i, size_t(H) * size_t(Fk) * e);
+  in.add(b_i, size_t(Fk) * e);
+  out.add(Y_i, size_t(M) * size_t(Fk) * e);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return col_step(X, W_i, b_i, Y_i, nullptr, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+}
+
+int tp_mlp_col_gelu_save(const void* X, const void* W_i, const void* b_i, void* Y_i, void* G_i,
+                         int64_t M, int64_t H, int64_t Fk, int dtype, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (M == 0) return TP_OK;
+  if (!X || !W_i || !Y_i || !G_i) return TP_ERR_NULL;
+  if (!aligned16(X) || !aligned16(W_i) || !aligned16(Y_i) || !aligned16(G_i) ||
+      (b_i && !aligned16(b_i)))
+    return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  Regions in, out;
+  in.add(X, size_t(M) * size_t(H) * e);
+  in.add(W_i, size_t(H) * size_t(Fk) * e);
+  in.add(b_i, size_t(Fk) * e);
+  out.add(Y_i, size_t(M) * size_t(Fk) * e);
+  out.add(G_i, size_t(M) * size_t(Fk) * e);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return col_step(X, W_i, b_i, Y_i, G_i, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
 }
 
 int tp_mlp_row_partial(const void* Y_i, const void* V_i, float* Z_i, int64_t M, int64_t Fk,
@@ -114,12 +231,13 @@ int tp_mlp_row_partial(const void* Y_i, const void* V_i, float* Z_i, int64_t M, 
   if (!Y_i || !V_i || !Z_i) return TP_ERR_NULL;
   if (!aligned16(Y_i) || !aligned16(V_i) || !aligned16(Z_i)) return TP_ERR_ALIGN;
   const size_t e = elt_size(dtype);
-  const size_t nz = size_t(M) * size_t(H) * 4;
-  if (overlap(Z_i, nz, Y_i, size_t(M) * size_t(Fk) * e) ||
-      overlap(Z_i, nz, V_i, size_t(Fk) * size_t(H) * e))
-    return TP_ERR_ALIAS;
-  return row_partial_checked(Y_i, V_i, Z_i, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
-                             static_cast<hipStream_t>(stream));
+  Regions in, out;
+  in.add(Y_i, size_t(M) * size_t(Fk) * e);
+  in.add(V_i, size_t(Fk) * size_t(H) * e);
+  out.add(Z_i, size_t(M) * size_t(H) * 4);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return row_step(Y_i, V_i, Z_i, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
+                  static_cast<hipStream_t>(stream));
 }
 
 int tp_shard_reduce(const float* const* Z_parts, int k, float* Z, int64_t n, void* stream) {
@@ -170,16 +288,16 @@ int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const*
   if (!aligned16(workspace)) return TP_ERR_ALIGN;
   const size_t e = elt_size(dtype);
   const size_t nz = size_t(M) * size_t(H) * 4;
-  if (overlap(Z, nz, X, size_t(M) * size_t(H) * e) || overlap(Z, nz, workspace, need))
-    return TP_ERR_ALIAS;
-  if (overlap(workspace, need, X, size_t(M) * size_t(H) * e)) return TP_ERR_ALIAS;
+  Regions in, out;
+  in.add(X, size_t(M) * size_t(H) * e);
   for (int i = 0; i < k; ++i) {
-    const size_t nw = size_t(H) * size_t(Fk) * e;
-    if (overlap(Z, nz, W[i], nw) || overlap(Z, nz, V[i], nw) ||
-        overlap(workspace, need, W[i], nw) || overlap(workspace, need, V[i], nw) ||
-        (b && (overlap(Z, nz, b[i], size_t(Fk) * e) || overlap(workspace, need, b[i], size_t(Fk) * e))))
-      return TP_ERR_ALIAS;
+    in.add(W[i], size_t(H) * size_t(Fk) * e);
+    in.add(V[i], size_t(Fk) * size_t(H) * e);
+    if (b) in.add(b[i], size_t(Fk) * e);
   }
+  out.add(Z, nz);
+  out.add(workspace, need);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fused = (flags & TP_FUSED_ACCUM) != 0;
@@ -191,7 +309,7 @@ int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const*
 
   for (int i = 0; i < k; ++i) {
     // Column-parallel linear + bias + GeLU of shard i into the shared Y buffer.
-    if ((st = col_gelu_checked(X, W[i], b ? b[i] : nullptr, Y, M, H, Fk, dtype, s))) return st;
+    if ((st = col_step(X, W[i], b ? b[i] : nullptr, Y, nullptr, M, H, Fk, dtype, s))) return st;
     // Row-parallel partial of shard i.
     float* P;
     bool accumulate = false;
@@ -204,10 +322,185 @@ int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const*
       P = reinterpret_cast<float*>(ws + y_bytes + size_t(i - 1) * part_bytes);
     }
     parts[i] = P;
-    if ((st = row_partial_checked(Y, V[i], P, M, Fk, H, dtype, accumulate, s))) return st;
+    if ((st = row_step(Y, V[i], P, M, Fk, H, dtype, accumulate, s))) return st;
   }
-  if (!fused && k > 1)
-    return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
+  if (!fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
+  return TP_OK;
+}
+
+int tp_mlp_grad_act(const void* dZ, const void* V_i, const void* G_i, void* dA_i, int64_t M,
+                    int64_t H, int64_t Fk, int dtype, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (M == 0) return TP_OK;
+  if (!dZ || !V_i || !G_i || !dA_i) return TP_ERR_NULL;
+  if (!aligned16(dZ) || !aligned16(V_i) || !aligned16(G_i) || !aligned16(dA_i)) return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  Regions in, out;
+  in.add(dZ, size_t(M) * size_t(H) * e);
+  in.add(V_i, size_t(Fk) * size_t(H) * e);
+  if (dA_i != G_i) in.add(G_i, size_t(M) * size_t(Fk) * e);
+  out.add(dA_i, size_t(M) * size_t(Fk) * e);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return act_grad_step(dZ, V_i, G_i, dA_i, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+}
+
+size_t tp_mlp_grad_weight_workspace_bytes(int64_t M, int64_t H, int64_t Fk, int dtype) {
+  if (check_dtype(dtype) || check_dims(M, H, Fk)) return 0;
+  return grad_weight_ws(M, H, Fk, dtype);
+}
+
+int tp_mlp_grad_row_weight(const void* Y_i, const void* dZ, float* dV_i, int64_t M, int64_t Fk,
+                           int64_t H, int dtype, void* workspace, size_t workspace_bytes,
+                           unsigned flags, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (flags & ~TP_GRAD_ACCUMULATE) return TP_ERR_FLAGS;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (!dV_i || (M > 0 && (!Y_i || !dZ))) return TP_ERR_NULL;
+  if (!aligned16(Y_i) || !aligned16(dZ) || !aligned16(dV_i)) return TP_ERR_ALIGN;
+  const size_t need = grad_weight_ws(M, H, Fk, dtype);
+  if (need && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  Regions in, out;
+  in.add(Y_i, size_t(M) * size_t(Fk) * e);
+  in.add(dZ, size_t(M) * size_t(H) * e);
+  out.add(dV_i, size_t(Fk) * size_t(H) * 4);
+  out.add(workspace, need);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return row_weight_step(Y_i, dZ, dV_i, M, Fk, H, dtype, workspace,
+                         (flags & TP_GRAD_ACCUMULATE) != 0, static_cast<hipStream_t>(stream));
+}
+
+int tp_mlp_grad_col_weight(const void* X, const void* dA_i, float* dW_i, float* db_i, int64_t M,
+                           int64_t H, int64_t Fk, int dtype, void* workspace,
+                           size_t workspace_bytes, unsigned flags, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (flags & ~TP_GRAD_ACCUMULATE) return TP_ERR_FLAGS;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (!dW_i || (M > 0 && (!X || !dA_i))) return TP_ERR_NULL;
+  if (!aligned16(X) || !aligned16(dA_i) || !aligned16(dW_i) || (db_i && !aligned16(db_i)))
+    return TP_ERR_ALIGN;
+  const size_t need = grad_weight_ws(M, H, Fk, dtype);
+  if (need && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  Regions in, out;
+  in.add(X, size_t(M) * size_t(H) * e);
+  in.add(dA_i, size_t(M) * size_t(Fk) * e);
+  out.add(dW_i, size_t(H) * size_t(Fk) * 4);
+  out.add(db_i, size_t(Fk) * 4);
+  out.add(workspace, need);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return col_weight_step(X, dA_i, dW_i, db_i, M, H, Fk, dtype, workspace,
+                         (flags & TP_GRAD_ACCUMULATE) != 0, static_cast<hipStream_t>(stream));
+}
+
+int tp_mlp_grad_input_partial(const void* dA_i, const void* W_i, float* dX_i, int64_t M,
+                              int64_t Fk, int64_t H, int dtype, unsigned flags, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (flags & ~TP_ACCUMULATE) return TP_ERR_FLAGS;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (M == 0) return TP_OK;
+  if (!dA_i || !W_i || !dX_i) return TP_ERR_NULL;
+  if (!aligned16(dA_i) || !aligned16(W_i) || !aligned16(dX_i)) return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  Regions in, out;
+  in.add(dA_i, size_t(M) * size_t(Fk) * e);
+  in.add(W_i, size_t(H) * size_t(Fk) * e);
+  out.add(dX_i, size_t(M) * size_t(H) * 4);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return input_grad_step(dA_i, W_i, dX_i, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
+                         static_cast<hipStream_t>(stream));
+}
+
+size_t tp_mlp_backward_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dtype,
+                                       unsigned flags) {
+  if (k < 1 || k > TP_MAX_SHARDS || check_dtype(dtype) || check_dims(M, H, Fk)) return 0;
+  if (flags & ~(TP_FUSED_ACCUM | TP_GRAD_ACCUMULATE)) return 0;
+  const size_t act = round_up(size_t(M) * size_t(Fk) * elt_size(dtype), kWsAlign);
+  size_t bytes = 2 * act + grad_weight_ws(M, H, Fk, dtype);
+  if (!(flags & TP_FUSED_ACCUM)) bytes += size_t(k - 1) * round_up(size_t(M) * size_t(H) * 4, kWsAlign);
+  return bytes;
+}
+
+int tp_mlp_shard_backward(const void* X, const void* const* W, const void* const* b,
+                          const void* const* V, const void* dZ, int k, int64_t M, int64_t H,
+                          int64_t Fk, int dtype, void* workspace, size_t workspace_bytes,
+                          float* dX, float* const* dW, float* const* db, float* const* dV,
+                          unsigned flags, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (flags & ~(TP_FUSED_ACCUM | TP_GRAD_ACCUMULATE)) return TP_ERR_FLAGS;
+  if (k < 1 || k > TP_MAX_SHARDS) return TP_ERR_SHAPE;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (!W || !V || !dW || !dV || (M > 0 && (!X || !dZ || !dX))) return TP_ERR_NULL;
+  for (int i = 0; i < k; ++i) {
+    if (!W[i] || !V[i] || !dW[i] || !dV[i] || (b && !b[i]) || (db && !db[i])) return TP_ERR_NULL;
+    if (!aligned16(W[i]) || !aligned16(V[i]) || !aligned16(dW[i]) || !aligned16(dV[i]) ||
+        (b && !aligned16(b[i])) || (db && !aligned16(db[i])))
+      return TP_ERR_ALIGN;
+  }
+  if (!aligned16(X) || !aligned16(dZ) || (dX && !aligned16(dX))) return TP_ERR_ALIGN;
+  const size_t need = tp_mlp_backward_workspace_bytes(k, M, H, Fk, dtype, flags);
+  if (need && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  const size_t nx = size_t(M) * size_t(H) * 4;
+  Regions in, out;
+  in.add(X, size_t(M) * size_t(H) * e);
+  in.add(dZ, size_t(M) * size_t(H) * e);
+  for (int i = 0; i < k; ++i) {
+    in.add(W[i], size_t(H) * size_t(Fk) * e);
+    in.add(V[i], size_t(Fk) * size_t(H) * e);
+    if (b) in.add(b[i], size_t(Fk) * e);
+    out.add(dW[i], size_t(H) * size_t(Fk) * 4);
+    out.add(dV[i], size_t(Fk) * size_t(H) * 4);
+    if (db) out.add(db[i], size_t(Fk) * 4);
+  }
+  out.add(dX, nx);
+  out.add(workspace, need);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fused = (flags & TP_FUSED_ACCUM) != 0;
+  const bool acc_grads = (flags & TP_GRAD_ACCUMULATE) != 0;
+  char* ws = static_cast<char*>(workspace);
+  const size_t act = round_up(size_t(M) * size_t(Fk) * e, kWsAlign);
+  void* Y = ws;
+  void* G = ws + act;  // G_i, then dA_i in place
+  void* wws = ws + 2 * act;
+  const size_t part_bytes = round_up(nx, kWsAlign);
+  char* part_base = ws + 2 * act + grad_weight_ws(M, H, Fk, dtype);
+  const float* parts[TP_MAX_SHARDS];
+
+  for (int i = 0; i < k; ++i) {
+    if (M > 0) {
+      if ((st = col_step(X, W[i], b ? b[i] : nullptr, Y, G, M, H, Fk, dtype, s))) return st;
+      if ((st = act_grad_step(dZ, V[i], G, G, M, H, Fk, dtype, s))) return st;
+    }
+    if ((st = row_weight_step(Y, dZ, dV[i], M, Fk, H, dtype, wws, acc_grads, s))) return st;
+    if ((st = col_weight_step(X, G, dW[i], db ? db[i] : nullptr, M, H, Fk, dtype, wws, acc_grads, s)))
+      return st;
+    if (M == 0) continue;
+    float* P;
+    bool accumulate = false;
+    if (i == 0) {
+      P = dX;
+    } else if (fused) {
+      P = dX;
+      accumulate = true;
+    } else {
+      P = reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
+    }
+    parts[i] = P;
+    if ((st = input_grad_step(G, W[i], P, M, Fk, H, dtype, accumulate, s))) return st;
+  }
+  if (M > 0 && !fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, dX, M * H, s));
   return TP_OK;
 }
 

@@ -1,6 +1,6 @@
 // Internal launch interface between the C ABI (tp_mlp_abi.cpp) and the gfx950
-// kernels (tp_mlp_kernels.hip).  Arguments are validated by the ABI layer
-// before any of these is called.
+// kernels.  Arguments are validated by the ABI layer before any of these is
+// called.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,23 +8,62 @@
 
 namespace tpmlp {
 
-// Epilogues of the tiled GEMM C[M,N] = A[M,K] B[K,N].
+// Epilogues of the tiled GEMM C[M,N] = A B, applied to the float32
+// accumulator; "operand dtype" is bf16 for the bf16 GEMM, float32 for the
+// float32 one.  aux is an [M, N] array with the leading dimension of C.
 enum Epilogue : int {
-  kEpiBiasGelu = 0,  // C = GeLU(acc + bias[n]) in the input dtype
-  kEpiStoreF32 = 1,  // C = acc (float32)
-  kEpiAccumF32 = 2,  // C = C + acc (float32)
+  kEpiBiasGelu = 0,      // C = GeLU(acc + bias[n])                          (operand dtype)
+  kEpiStoreF32 = 1,      // C = acc                                          (float32)
+  kEpiAccumF32 = 2,      // C = C + acc                                      (float32)
+  kEpiBiasGeluSave = 3,  // C = GeLU(acc + bias[n]), aux = GeLU'(acc + bias[n]) (operand dtype)
+  kEpiMulAux = 4,        // C = acc * aux[m, n]; C may be aux itself         (operand dtype)
 };
 
-// bf16 operands (raw 16-bit patterns), float32 accumulate.
-hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, const uint16_t* bias, void* C,
-                            int64_t M, int64_t N, int64_t K, Epilogue epi, hipStream_t s);
+// Operand layouts.  A is logically [M, K] and B [K, N]:
+//   kNN: A[m, k] at A[m * lda + k],  B[k, n] at B[k * ldb + n]
+//   kNT: A[m, k] at A[m * lda + k],  B[k, n] at B[n * ldb + k]   (B stored transposed)
+//   kTN: A[m, k] at A[k * lda + m],  B[k, n] at B[k * ldb + n]   (A stored transposed)
+enum Layout : int { kNN = 0, kNT = 1, kTN = 2 };
 
-// float32 operands, float32 accumulate.
-hipError_t launch_gemm_f32(const float* A, const float* B, const float* bias, void* C, int64_t M,
-                           int64_t N, int64_t K, Epilogue epi, hipStream_t s);
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  const void* bias;  // [N], kEpiBiasGelu / kEpiBiasGeluSave; may be null
+  void* C;           // [M, N], row m at C + m * ldc
+  void* aux;         // [M, N] with leading dimension ldc: kEpiBiasGeluSave / kEpiMulAux
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc;
+  Layout layout;
+  Epilogue epi;
+};
+
+// bf16 operands (raw 16-bit patterns), float32 accumulate.  Requires the
+// contiguous dimension of A, B and C to be a multiple of 8 elements, every
+// leading dimension at most 2^22 elements, and 16-byte aligned pointers.
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+
+// float32 operands, float32 accumulate (same rules).
+hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
+
+// K-split of a GEMM with a float32 output (kEpiStoreF32 / kEpiAccumF32) whose
+// output has too few tiles to fill the chip (the weight gradients, where K is
+// the token count): slice 0 writes (or adds into) C, slices 1..S-1 write
+// float32 partials into `ws`, and the slices are then added into C in slice
+// order, so the result does not depend on timing.
+int gemm_k_slices(bool bf16, int64_t M, int64_t N, int64_t K);
+size_t gemm_split_workspace_bytes(bool bf16, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_split(const GemmArgs& g, bool bf16, void* ws, hipStream_t s);
 
 // Z[e] = sum_i parts[i][e], i = 0..k-1 in order; Z may equal parts[0].
 hipError_t launch_shard_reduce(const float* const* parts, int k, float* Z, int64_t n,
                                hipStream_t s);
+
+// out[n] (+)= sum_m A[m, n] for A [M, N] row-major (bf16 when `bf16`, else
+// float32), N a multiple of 8.  Deterministic: rows are summed in fixed
+// blocks whose float32 partials go to `partials` and are then added in order.
+// `partials` holds colsum_partials_floats(M, N) floats.
+int64_t colsum_partials_floats(int64_t M, int64_t N);
+hipError_t launch_colsum(const void* A, bool bf16, int64_t M, int64_t N, float* out,
+                         bool accumulate, float* partials, hipStream_t s);
 
 }  // namespace tpmlp

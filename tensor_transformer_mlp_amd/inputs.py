@@ -22,7 +22,9 @@ long_seq       1x32768      8192   32768  8   4096   bf16   0.01
 =============  ===========  =====  =====  ==  =====  =====  =======
 
 X ~ N(0, 1); W, b, V ~ N(0, std) (the second parameter is the standard
-deviation).  Streams: X = 0, W = 1, b = 2, V = 3 under base seed 42.  The full
+deviation).  For the backward, the gradient of the block output is
+dZ ~ N(0, 1) (the gradient of L = sum(Z * R) for a standard normal R).
+Streams: X = 0, W = 1, b = 2, V = 3, dZ = 4 under base seed 42.  The full
 W, b and V are drawn first and shards are slices of them, so the same weights
 serve every shard count k.  bf16 workloads store the float32 draw rounded to
 nearest-even bfloat16 (as raw uint16 bit patterns on the host).
@@ -40,7 +42,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "csrc", "synth_inputs.c")
 _LIB_PATH = os.path.join(_HERE, "libtpsynth.so")
 
-STREAM_X, STREAM_W, STREAM_B, STREAM_V = 0, 1, 2, 3
+STREAM_X, STREAM_W, STREAM_B, STREAM_V, STREAM_DZ = 0, 1, 2, 3, 4
 BASE_SEED = 42
 
 

@@ -13,6 +13,21 @@ Error model (u = unit roundoff: 2^-24 for float32, 2^-8 for bfloat16):
 * row step from the GPU's own Y_i:  |Z_gpu - Z| <= 2 (K + 2) u32 (|Y_i| |V_i|).
 * whole forward:  |Z_gpu - Z| <= tolY |V| + 2 (Fk + k + 4) u32 (|Y| |V|), with
   tolY the column-step bound of every shard, side by side.
+
+Backward (dY = dZ V_i^T, dA = dY * G, G = GeLU'(A)):
+
+* G_i from the training-mode column step:
+    |G_gpu - G| <= u_out |G| + (1 + u_out) (0.8 errA + 5e-7),
+  errA = 2 (K + 2) u32 S the pre-activation's accumulation bound, 0.8 >=
+  max |GeLU''| = 2 phi(0), and 5e-7 the absolute error of the float32 GeLU'
+  evaluation (0.75e-7 from the erfc approximation, a few float32 roundings of
+  Phi <= 1 and of x phi(x) <= 0.25).
+* dA_i = round(float32(dY) * G_used): with errdY = 2 (H + 2) u32 |dZ| |V_i|^T
+  and errG the error of the G the kernel used,
+    |dA_gpu - dA| <= u_out |dA| + (1 + u_out) (errdY |G| + |dY| errG
+                     + errdY errG + u32 |dY| |G|).
+* a float32 GEMM over K terms of operands with errors e_a, e_b:
+    |C_gpu - C| <= e_a^T |b| + |a|^T e_b + 2 (K + 2) u32 (|a| + e_a)^T (|b| + e_b).
 """
 from __future__ import annotations
 
@@ -94,3 +109,56 @@ def assert_within(got, ref, bound, what: str, max_report: int = 5):
             t = tuple(ix)
             lines.append("  at %s: got %.9g ref %.9g err %.3g bound %.3g" % (t, got[t], ref[t], err[t], bound[t]))
         raise AssertionError("\n".join(lines))
+
+
+GELU2_MAX = 0.8
+G_EVAL = 5e-7
+
+
+def grad_g_bound(S, G, K: int, dtype: str):
+    """Bound on the GPU's G = GeLU'(A); S = |X| |W_i| + |b_i|, K = H."""
+    u_out = U16 if dtype == "bf16" else 0.0
+    errA = 2 * (K + 2) * U32 * S
+    return u_out * np.abs(G) + (1 + u_out) * (GELU2_MAX * errA + G_EVAL) + 1e-30
+
+
+def act_grad_bound(dY, G, errdY, errG, dtype: str):
+    u_out = U16 if dtype == "bf16" else 0.0
+    aY, aG = np.abs(dY), np.abs(G)
+    return (u_out * aY * aG + (1 + u_out) * (errdY * aG + aY * errG + errdY * errG + U32 * aY * aG)
+            + 1e-30)
+
+
+def gemm_bound(a, b, K: int, ea=None, eb=None):
+    """Bound of a float32-accumulated a @ b (K terms) with operand errors ea, eb."""
+    aa, ab = np.abs(a), np.abs(b)
+    out = 0.0
+    if ea is not None:
+        out = out + ea @ ab
+        aa = aa + ea
+    if eb is not None:
+        out = out + np.abs(a) @ eb
+        ab = ab + eb
+    return out + 2 * (K + 2) * U32 * (aa @ ab) + 1e-30
+
+
+def backward_terms(orc, Xr, Wc, bc, Vc, dZr, dtype: str):
+    """Magnitudes and error bounds of the backward's intermediates, for the
+    bounds only (expected values come from the oracle), for rows Xr of X and
+    columns Wc of W (bc of b, rows Vc of V): a dict with float64 A, Y, G, dY,
+    dA and the GPU-error bounds tolY (Y), errG (G) and errdA (dA)."""
+    X64, W64, V64, dZ64 = f64(Xr), f64(Wc), f64(Vc), f64(dZr)
+    b64 = f64(bc) if bc is not None else None
+    H = X64.shape[1]
+    A = X64 @ W64 + (b64[None, :] if b64 is not None else 0.0)
+    S = np.abs(X64) @ np.abs(W64) + (np.abs(b64)[None, :] if b64 is not None else 0.0)
+    Y = orc.gelu(A)
+    G = orc.gelu_grad(A)
+    dY = dZ64 @ V64.T
+    errdY = 2 * (H + 2) * U32 * (np.abs(dZ64) @ np.abs(V64).T)
+    u_out = U16 if dtype == "bf16" else 0.0
+    tolY = ((1 + u_out) * (GELU_LIP * 2 * (H + 2) * U32 * S + 8 * U32 * (2 + A * A) * np.abs(Y)
+                           + 2e-7 * np.abs(A)) + u_out * np.abs(Y) + 1e-30)
+    errG = grad_g_bound(S, G, H, dtype)
+    errdA = act_grad_bound(dY, G, errdY, errG, dtype)
+    return dict(A=A, Y=Y, G=G, dY=dY, dA=dY * G, tolY=tolY, errG=errG, errdA=errdA)

@@ -39,7 +39,10 @@ def test_exports_every_declared_symbol(L):
     names = _declared()
     assert names == {"tp_mlp_col_gelu", "tp_mlp_row_partial", "tp_shard_reduce",
                      "tp_mlp_workspace_bytes", "tp_mlp_shard_forward", "tp_status_string",
-                     "tp_mlp_version"}
+                     "tp_mlp_version", "tp_mlp_col_gelu_save", "tp_mlp_grad_act",
+                     "tp_mlp_grad_weight_workspace_bytes", "tp_mlp_grad_row_weight",
+                     "tp_mlp_grad_col_weight", "tp_mlp_grad_input_partial",
+                     "tp_mlp_backward_workspace_bytes", "tp_mlp_shard_backward"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -47,7 +50,8 @@ def test_exports_every_declared_symbol(L):
 def test_python_constants_match_header():
     import tensor_transformer_mlp_amd as tpm
     c = _header_constants()
-    for n in ("TP_F32", "TP_BF16", "TP_ACCUMULATE", "TP_FUSED_ACCUM", "TP_MAX_SHARDS"):
+    for n in ("TP_F32", "TP_BF16", "TP_ACCUMULATE", "TP_FUSED_ACCUM", "TP_GRAD_ACCUMULATE",
+              "TP_MAX_SHARDS"):
         assert getattr(tpm, n) == c[n], n
 
 
@@ -78,7 +82,8 @@ def test_col_gelu_errors(L):
     ok_args = lambda: [_p(0), _p(1), _p(2), _p(3), 16, 64, 128, 1, None]
     a = ok_args(); a[7] = 7
     assert f(*a) == c["TP_ERR_DTYPE"]
-    for idx, val in [(5, 60), (5, 0), (6, 12), (6, 0), (4, -1), (5, -8)]:
+    for idx, val in [(5, 60), (5, 0), (6, 12), (6, 0), (4, -1), (5, -8), (5, (1 << 22) + 8),
+                     (6, (1 << 22) + 8), (4, 1 << 31)]:
         a = ok_args(); a[idx] = val
         assert f(*a) == c["TP_ERR_SHAPE"], (idx, val)
     for idx in (0, 1, 3):
@@ -193,3 +198,155 @@ def test_binding_rejects_cpu_tensors(L):
     W = torch.zeros(64, 128)
     with pytest.raises(ValueError, match="GPU tensor"):
         tpm.tp_mlp_col_gelu(X, W, None, Y_i=torch.zeros(4, 128))
+
+
+def test_col_gelu_save_errors(L):
+    c = _header_constants()
+    f = L.tp_mlp_col_gelu_save
+    ok_args = lambda: [_p(0), _p(1), _p(2), _p(3), _p(4), 16, 64, 128, 1, None]
+    a = ok_args(); a[8] = 2
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    a = ok_args(); a[6] = 20
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    for idx in (0, 1, 3, 4):
+        a = ok_args(); a[idx] = None
+        assert f(*a) == c["TP_ERR_NULL"], idx
+    a = ok_args(); a[4] = ctypes.c_void_p(P * 5 + 8)
+    assert f(*a) == c["TP_ERR_ALIGN"]
+    a = ok_args(); a[4] = _p(3)  # G == Y
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = ok_args(); a[4] = _p(1)  # G overlaps W_i
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = ok_args(); a[5] = 0
+    assert f(*a) == c["TP_OK"]
+
+
+def test_grad_act_errors(L):
+    c = _header_constants()
+    f = L.tp_mlp_grad_act
+    ok_args = lambda: [_p(0), _p(1), _p(2), _p(3), 16, 64, 128, 1, None]
+    a = ok_args(); a[7] = 5
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    a = ok_args(); a[5] = 7
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    for idx in range(4):
+        a = ok_args(); a[idx] = None
+        assert f(*a) == c["TP_ERR_NULL"], idx
+    a = ok_args(); a[3] = ctypes.c_void_p(P * 4 + 2)
+    assert f(*a) == c["TP_ERR_ALIGN"]
+    a = ok_args(); a[3] = _p(0)  # dA overlaps dZ
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = ok_args(); a[3] = ctypes.c_void_p(P * 3 + 64)  # dA partly over G (not in place)
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = ok_args(); a[4] = 0
+    assert f(*a) == c["TP_OK"]
+
+
+def test_grad_weight_errors(L):
+    c = _header_constants()
+    need = L.tp_mlp_grad_weight_workspace_bytes(16, 64, 128, 1)
+    ws = ctypes.c_void_p(1 << 40)
+    f = L.tp_mlp_grad_row_weight  # (Y_i, dZ, dV_i, M, Fk, H, dtype, ws, ws_bytes, flags, stream)
+    ok = lambda: [_p(0), _p(1), _p(2), 16, 128, 64, 1, ws, need, 0, None]
+    a = ok(); a[9] = 1  # TP_ACCUMULATE is not a weight-gradient flag
+    assert f(*a) == c["TP_ERR_FLAGS"]
+    a = ok(); a[6] = 3
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    a = ok(); a[4] = 0
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = ok(); a[2] = None
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = ok(); a[2] = ctypes.c_void_p(P * 3 + 4)
+    assert f(*a) == c["TP_ERR_ALIGN"]
+    a = ok(); a[2] = _p(1)
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    if need:
+        a = ok(); a[8] = need - 1
+        assert f(*a) == c["TP_ERR_WORKSPACE"]
+    g = L.tp_mlp_grad_col_weight  # (X, dA_i, dW_i, db_i, M, H, Fk, dtype, ws, ws_bytes, flags, stream)
+    ok = lambda: [_p(0), _p(1), _p(2), _p(3), 16, 64, 128, 1, ws, need, 2, None]
+    a = ok(); a[10] = 3
+    assert f is not g and g(*a) == c["TP_ERR_FLAGS"]
+    a = ok(); a[3] = ctypes.c_void_p(P * 4 + 8)
+    assert g(*a) == c["TP_ERR_ALIGN"]
+    a = ok(); a[3] = ctypes.c_void_p(P * 3 + 16)  # db inside dW
+    assert g(*a) == c["TP_ERR_ALIAS"]
+    assert need > 0  # the column-sum partials
+    a = ok(); a[8] = ctypes.c_void_p(P * 2)  # workspace over dA
+    assert g(*a) == c["TP_ERR_ALIAS"]
+    a = ok(); a[0] = None
+    assert g(*a) == c["TP_ERR_NULL"]
+
+
+def test_grad_input_partial_errors(L):
+    c = _header_constants()
+    f = L.tp_mlp_grad_input_partial  # (dA_i, W_i, dX_i, M, Fk, H, dtype, flags, stream)
+    ok = lambda: [_p(0), _p(1), _p(2), 16, 128, 64, 1, 0, None]
+    a = ok(); a[7] = 2
+    assert f(*a) == c["TP_ERR_FLAGS"]
+    a = ok(); a[5] = 4
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = ok(); a[1] = None
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = ok(); a[2] = _p(0)
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = ok(); a[3] = 0
+    assert f(*a) == c["TP_OK"]
+
+
+def test_backward_workspace_bytes(L):
+    f = L.tp_mlp_backward_workspace_bytes
+    gw = L.tp_mlp_grad_weight_workspace_bytes
+    for (k, M, H, Fk, dt) in [(4, 8192, 768, 768, 1), (8, 8192, 4096, 2048, 1), (2, 40, 64, 128, 0),
+                              (1, 3, 8, 8, 1)]:
+        e = 2 if dt == 1 else 4
+        act = -(-M * Fk * e // 256) * 256
+        part = -(-M * H * 4 // 256) * 256
+        w = gw(M, H, Fk, dt)
+        assert w % 256 == 0
+        assert f(k, M, H, Fk, dt, 0) == 2 * act + w + (k - 1) * part
+        assert f(k, M, H, Fk, dt, 1) == 2 * act + w
+        assert f(k, M, H, Fk, dt, 3) == 2 * act + w
+    # the weight-gradient workspace covers the column-sum partials at least
+    assert gw(8192, 768, 768, 1) >= 768 * 4
+    assert f(0, 8, 64, 128, 0, 0) == 0
+    assert f(2, 8, 60, 128, 0, 0) == 0
+    assert f(2, 8, 64, 128, 0, 4) == 0
+    assert gw(8, 64, 128, 7) == 0
+    assert f(2, 0, 64, 128, 0, 0) == 0
+
+
+def test_shard_backward_errors(L):
+    c = _header_constants()
+    f = L.tp_mlp_shard_backward
+    k = 2
+    arr = lambda *xs: (ctypes.c_void_p * k)(*xs)
+    W, V, b = arr(10 * P, 11 * P), arr(12 * P, 13 * P), arr(14 * P, 15 * P)
+    dW, dV, db = arr(20 * P, 21 * P), arr(22 * P, 23 * P), arr(24 * P, 25 * P)
+    need = L.tp_mlp_backward_workspace_bytes(k, 8, 64, 128, 1, 0)
+    ws, dX, X, dZ = (ctypes.c_void_p(1 << s) for s in (40, 41, 42, 43))
+    base = lambda: [X, W, b, V, dZ, k, 8, 64, 128, 1, ws, need, dX, dW, db, dV, 0, None]
+    a = base(); a[16] = 4
+    assert f(*a) == c["TP_ERR_FLAGS"]
+    a = base(); a[5] = 0
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[7] = 12
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[11] = need - 1
+    assert f(*a) == c["TP_ERR_WORKSPACE"]
+    a = base(); a[13] = arr(20 * P, None)
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = base(); a[14] = arr(24 * P, None)
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = base(); a[4] = None
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = base(); a[15] = arr(22 * P + 4, 23 * P)
+    assert f(*a) == c["TP_ERR_ALIGN"]
+    a = base(); a[15] = arr(22 * P, 22 * P)  # two shards' dV on one buffer
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[13] = arr(20 * P, 10 * P)  # dW[1] over W[0]
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[12] = ctypes.c_void_p((1 << 40) + 512)  # dX inside the workspace
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[9] = 2
+    assert f(*a) == c["TP_ERR_DTYPE"]

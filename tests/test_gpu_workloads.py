@@ -115,3 +115,102 @@ def test_workload_parity(name):
     err = rel_fro(Z1r, Zr)
     say("  %s: rel_fro on sampled rows = %.3e (bar %.0e)" % (name, err, tol))
     assert err <= tol
+
+
+def _cols(F, k, n_random=8, seed=11):
+    Fk = F // k
+    base = {0, Fk - 1, Fk, F - 1, F // 2}
+    rng = np.random.default_rng(seed)
+    base.update(int(x) for x in rng.integers(0, F, size=n_random))
+    return np.array(sorted(base))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_workload_backward_parity(name):
+    """The whole backward (tp_mlp_shard_backward, both variants) at full size:
+    sampled rows of dX and sampled columns of dW, db and dV (one column of the
+    parameter gradients depends only on that column of W, entry of b and row
+    of V, over all M rows) against the oracle, element by element."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle
+    import tensor_transformer_mlp_amd as tpm
+    from tensor_transformer_mlp_amd import inputs
+    from _helpers import U32, backward_terms, gemm_bound
+
+    w = inputs.WORKLOADS[name]
+    tol = 1e-2 if w.dtype == "bf16" else 1e-5
+    say("backward workload %s: M=%d H=%d F=%d k=%d %s" % (name, w.M, w.H, w.F, w.k, w.dtype))
+    inp = inputs.make_inputs(w)
+    X, W, b, V = inp["X"], inp["W"], inp["b"], inp["V"]
+    dZ = inputs.draw(inputs.STREAM_DZ, (w.M, w.H), 1.0, w.dtype)
+    Fk, k, M = w.Fk, w.k, w.M
+    dev = torch.device("cuda")
+    Xd, dZd = to_dev(X), to_dev(dZ)
+    Wd, bd, Vd = to_dev(W), to_dev(b), to_dev(V)
+    Ws = [Wd[:, i * Fk:(i + 1) * Fk].contiguous() for i in range(k)]
+    bs = [bd[i * Fk:(i + 1) * Fk].contiguous() for i in range(k)]
+    Vs = [Vd[i * Fk:(i + 1) * Fk, :].contiguous() for i in range(k)]
+    del Wd, bd, Vd
+
+    say("  %s: backward literal x2, fused" % name)
+    r1 = tpm.tp_mlp_shard_backward(Xd, Ws, bs, Vs, dZd, fused=False)
+    torch.cuda.synchronize()
+    rows = _rows(M)
+    cols = _cols(w.F, k)
+    rows_t = torch.from_numpy(rows).to(dev)
+    dXr = from_dev(r1[0].index_select(0, rows_t)).astype(np.float64)
+    gW = np.stack([from_dev(r1[1][c // Fk][:, c % Fk]) for c in cols]).astype(np.float64)
+    gb = np.array([from_dev(r1[2][c // Fk][c % Fk:c % Fk + 1])[0] for c in cols], dtype=np.float64)
+    gV = np.stack([from_dev(r1[3][c // Fk][c % Fk]) for c in cols]).astype(np.float64)
+    assert bool(torch.isfinite(r1[0]).all())
+    for grp in r1[1:]:
+        assert all(bool(torch.isfinite(t).all()) for t in grp)
+    r2 = tpm.tp_mlp_shard_backward(Xd, Ws, bs, Vs, dZd, fused=False)
+    torch.cuda.synchronize()
+    same = torch.equal(r1[0], r2[0]) and all(torch.equal(a, c) for g1, g2 in zip(r1[1:], r2[1:])
+                                            for a, c in zip(g1, g2))
+    assert same, "run-to-run results differ"
+    del r2
+    rf = tpm.tp_mlp_shard_backward(Xd, Ws, bs, Vs, dZd, fused=True)
+    torch.cuda.synchronize()
+    same = torch.equal(r1[0], rf[0]) and all(torch.equal(a, c) for g1, g2 in zip(r1[1:], rf[1:])
+                                            for a, c in zip(g1, g2))
+    assert same, "literal and fused variants differ"
+    del rf, r1
+    torch.cuda.empty_cache()
+
+    # dX on sampled rows: every shard's dA_i on those rows.
+    say("  %s: oracle dX on %d rows" % (name, rows.size))
+    Xr, dZr = X[rows], dZ[rows]
+    ref = oracle.backward_rows(Xr, W, b, V, dZr, k)
+    bound = np.zeros_like(ref)
+    for i in range(k):
+        sl = slice(i * Fk, (i + 1) * Fk)
+        t = backward_terms(oracle, Xr, W[:, sl], b[sl], V[sl], dZr, w.dtype)
+        Wi64 = f64(W[:, sl])
+        bound += gemm_bound(t["dA"], Wi64.T, Fk, ea=t["errdA"])
+        bound += (k + 2) * U32 * ((np.abs(t["dA"]) + t["errdA"]) @ np.abs(Wi64).T)
+    assert_within(dXr, ref, bound, "%s dX" % name)
+    err = rel_fro(dXr, ref)
+    say("  %s: dX rel_fro on sampled rows = %.3e (bar %.0e)" % (name, err, tol))
+    assert err <= tol
+
+    # Parameter gradients on sampled columns, over all M rows.
+    say("  %s: oracle dW, db, dV on %d columns" % (name, cols.size))
+    rW, rb, rV = oracle.backward_cols(X, W, b, V, dZ, cols)
+    t = backward_terms(oracle, X, W[:, cols], b[cols], V[cols], dZ, w.dtype)
+    X64, dZ64 = f64(X), f64(dZ)
+    bW = gemm_bound(t["dA"].T, X64, M, ea=t["errdA"].T)
+    bb = t["errdA"].sum(axis=0) + 2 * (M + 2) * U32 * (np.abs(t["dA"]) + t["errdA"]).sum(axis=0) + 1e-30
+    bV = gemm_bound(t["Y"].T, dZ64, M, ea=t["tolY"].T)
+    del X64, dZ64
+    assert_within(gW, rW, bW, "%s dW columns" % name)
+    assert_within(gb, rb, bb, "%s db" % name)
+    assert_within(gV, rV, bV, "%s dV rows" % name)
+    for nm, g, r in (("dW", gW, rW), ("db", gb, rb), ("dV", gV, rV)):
+        err = rel_fro(g, r)
+        say("  %s: %s rel_fro on sampled columns = %.3e" % (name, nm, err))
+        assert err <= tol
