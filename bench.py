@@ -3,12 +3,17 @@
 
 One step = one call of tp_mlp_shard_forward: for each of the k shards the
 column GEMM + bias + GeLU and the row GEMM, then the on-device shard sum, over
-one batch of seeded synthetic inputs already resident in HBM.
+one batch of seeded synthetic inputs already resident in HBM.  `value` is the
+forward's throughput.  The backward of the same block (tp_mlp_shard_backward:
+per shard the training-mode column step, dA, dV, dW + db and the partial dX,
+then the dX shard sum) is timed the same way and reported under "backward".
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant literal|fused]
+                    [--no-backward]
 
 Prints ONE JSON line (metric, value in TFLOP/s, ms_per_step, roofline of the
-dominant kernel, CPU-oracle baseline) on stdout; diagnostics go to stderr.
+dominant kernel, CPU-oracle baseline, backward) on stdout; diagnostics go to
+stderr.
 """
 from __future__ import annotations
 
@@ -42,6 +47,7 @@ def parse():
                     help="target CPU time of the oracle sample (0 disables the CPU leg)")
     ap.add_argument("--kernel-steps", type=int, default=None,
                     help="steps of the per-kernel timing pass (default: --steps)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain float32 copy kernel (y = x * 1) over MIB MiB, 5 times: "
                          "the known-size reference for the HBM byte counters")
@@ -49,22 +55,86 @@ def parse():
 
 
 def kernel_bytes(kind, w, elt):
+    """Algorithmic HBM bytes of one launch of `kind` (each operand read once,
+    each result written once)."""
     M, H, Fk, k = w.M, w.H, w.Fk, w.k
-    if kind == "col_gelu":
-        return (M * H + H * Fk + Fk + M * Fk) * elt
-    if kind == "row_partial":
-        return (M * Fk + Fk * H) * elt + M * H * 4
-    if kind == "row_partial_accum":
-        return (M * Fk + Fk * H) * elt + 2 * M * H * 4
-    if kind == "shard_reduce":
-        return (k + 1) * M * H * 4
-    raise KeyError(kind)
+    table = {
+        "col_gelu": (M * H + H * Fk + Fk + M * Fk) * elt,
+        "row_partial": (M * Fk + Fk * H) * elt + M * H * 4,
+        "row_partial_accum": (M * Fk + Fk * H) * elt + 2 * M * H * 4,
+        "shard_reduce": (k + 1) * M * H * 4,
+        "col_gelu_save": (M * H + H * Fk + Fk + 2 * M * Fk) * elt,
+        "grad_act": (M * H + Fk * H + 2 * M * Fk) * elt,
+        "grad_row_weight": (M * Fk + M * H) * elt + Fk * H * 4,
+        "grad_col_weight": (M * H + M * Fk) * elt + (H * Fk + Fk) * 4,
+        "grad_input": (M * Fk + H * Fk) * elt + M * H * 4,
+        "grad_input_accum": (M * Fk + H * Fk) * elt + 2 * M * H * 4,
+    }
+    return table[kind]
 
 
 def kernel_flops(kind, w):
-    if kind.startswith("col_gelu") or kind.startswith("row_partial"):
-        return 2 * w.M * w.H * w.Fk
-    return (w.k - 1) * w.M * w.H
+    if kind == "shard_reduce":
+        return (w.k - 1) * w.M * w.H
+    return 2 * w.M * w.H * w.Fk
+
+
+def time_kinds(kinds, launch, nlaunch, steps, warmup, w, elt):
+    """Per-kind timing: each kind's launches of one step run back to back
+    between one HIP event pair on the stream they are launched on; a spin
+    kernel queued first keeps the GPU busy while the host enqueues, so no host
+    gap falls inside a pair.  Returns {kind: {avg_ms, ms_per_step, ...}}."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+    durs = {kd: [] for kd in kinds}
+    spin = getattr(torch.cuda, "_sleep", None)
+    for it in range(warmup + steps):
+        if spin is not None:
+            spin(3_000_000)
+        rec = []
+        for kind in kinds:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch(kind)
+            b.record(stream)
+            rec.append((kind, a, b))
+        torch.cuda.synchronize()
+        if it >= warmup:
+            for kind, a, b in rec:
+                durs[kind].append(a.elapsed_time(b) / nlaunch[kind])
+    kern = {}
+    for kind, d in durs.items():
+        if not d:
+            continue
+        avg = float(np.mean(d))
+        kern[kind] = {"launches_per_step": nlaunch[kind], "avg_ms": avg, "ms_per_step": avg * nlaunch[kind],
+                      "flop": kernel_flops(kind, w), "bytes": kernel_bytes(kind, w, elt)}
+        log("  %-18s %2d/step  avg %.4f ms  (%.4f ms/step)  %.1f TFLOP/s  %.0f GB/s" % (
+            kind, nlaunch[kind], avg, avg * nlaunch[kind], kernel_flops(kind, w) / avg / 1e9,
+            kernel_bytes(kind, w, elt) / avg / 1e6))
+    return kern
+
+
+def roofline(kern, w, variant, dtype):
+    """Roofline entry of the kind with the largest share of the step."""
+    dom = max(kern, key=lambda k_: kern[k_]["ms_per_step"])
+    d = kern[dom]
+    peak_f = PEAK_TFLOPS[dtype]
+    t_mfma = d["flop"] / (peak_f * 1e12)
+    t_hbm = d["bytes"] / (PEAK_HBM_GBS * 1e9)
+    if dom != "shard_reduce" and t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": d["flop"] / (d["avg_ms"] * 1e-3) / 1e12, "peak": peak_f,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": d["bytes"] / (d["avg_ms"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(w.name, variant, dom)
+    roof["kernel"] = dom
+    roof["avg_ms"] = d["avg_ms"]
+    return roof
 
 
 def main():
@@ -142,17 +212,12 @@ def main():
         raise RuntimeError("non-finite output")
 
     # Per-kernel pass: the kernels of one step through the per-kernel entry
-    # points, in the same launch configuration; each kind's launches of the
-    # step run back to back between one HIP event pair on the stream they are
-    # launched on, and a spin kernel queued first keeps the GPU busy while the
-    # host enqueues, so no host gap falls inside a pair.
-    stream = torch.cuda.current_stream()
+    # points, in the same launch configuration.
     ks = args.kernel_steps or args.steps
     Y = torch.empty(w.M, Fk, dtype=tdt, device=dev)
     parts = [torch.empty(w.M, w.H, dtype=torch.float32, device=dev) for _ in range(w.k)]
     kinds = ["col_gelu", "row_partial"] + (["row_partial_accum"] if fused and w.k > 1 else []) + \
         (["shard_reduce"] if not fused and w.k > 1 else [])
-    durs = {kd: [] for kd in kinds}
     nlaunch = {"col_gelu": w.k, "row_partial": 1 if fused else w.k, "row_partial_accum": w.k - 1,
                "shard_reduce": 1}
 
@@ -169,48 +234,13 @@ def main():
         else:
             tpm.tp_shard_reduce(parts, Z=Z)
 
-    spin = getattr(torch.cuda, "_sleep", None)
-    for it in range(args.warmup + ks):
-        if spin is not None:
-            spin(3_000_000)
-        rec = []
-        for kind in kinds:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            launch(kind)
-            b.record(stream)
-            rec.append((kind, a, b))
-        torch.cuda.synchronize()
-        if it >= args.warmup:
-            for kind, a, b in rec:
-                durs[kind].append(a.elapsed_time(b) / nlaunch[kind])
-    kern = {}
-    for kind, d in durs.items():
-        if not d:
-            continue
-        avg = float(np.mean(d))
-        per_step = avg * nlaunch[kind]
-        kern[kind] = {"launches_per_step": nlaunch[kind], "avg_ms": avg, "ms_per_step": per_step,
-                      "flop": kernel_flops(kind, w), "bytes": kernel_bytes(kind, w, elt)}
-        log("  %-18s %2d/step  avg %.4f ms  (%.4f ms/step)  %.1f TFLOP/s  %.0f GB/s" % (
-            kind, nlaunch[kind], avg, per_step, kernel_flops(kind, w) / avg / 1e9,
-            kernel_bytes(kind, w, elt) / avg / 1e6))
-    dom = max(kern, key=lambda k_: kern[k_]["ms_per_step"])
-    d = kern[dom]
-    peak_f = PEAK_TFLOPS[w.dtype]
-    t_mfma = d["flop"] / (peak_f * 1e12)
-    t_hbm = d["bytes"] / (PEAK_HBM_GBS * 1e9)
-    if dom != "shard_reduce" and t_mfma >= t_hbm:
-        roof = {"bound": "mfma", "achieved": d["flop"] / (d["avg_ms"] * 1e-3) / 1e12, "peak": peak_f,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": d["bytes"] / (d["avg_ms"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(w.name, args.variant, dom)
-    roof["kernel"] = dom
-    roof["avg_ms"] = d["avg_ms"]
+    kern = time_kinds(kinds, launch, nlaunch, ks, args.warmup, w, elt)
+    roof = roofline(kern, w, args.variant, w.dtype)
+    del Y, parts
+
+    bwd = None
+    if not args.no_backward:
+        bwd = bench_backward(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt)
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
@@ -226,23 +256,103 @@ def main():
         "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"]}
                     for k_, v in kern.items()},
         "cpu_baseline": cpu,
+        "backward": bwd,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_backward(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt):
+    """Time tp_mlp_shard_backward (recomputing Y_i and G_i from X) and its
+    kernels by kind.  FLOPs counted: 5 GEMMs of 2 M H Fk per shard (the
+    recompute, dA, dV, dW, dX)."""
+    import numpy as np
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    dev = X.device
+    Fk, k, M, H = w.Fk, w.k, w.M, w.H
+    dZ_h = inputs.draw(inputs.STREAM_DZ, (M, H), 1.0, w.dtype)
+    dZ = torch.from_numpy(dZ_h.view(np.int16) if dZ_h.dtype == np.uint16 else dZ_h).to(dev)
+    if dZ_h.dtype == np.uint16:
+        dZ = dZ.view(torch.bfloat16)
+    dX = torch.empty(M, H, dtype=torch.float32, device=dev)
+    dW = [torch.empty(H, Fk, dtype=torch.float32, device=dev) for _ in range(k)]
+    db = [torch.empty(Fk, dtype=torch.float32, device=dev) for _ in range(k)]
+    dV = [torch.empty(Fk, H, dtype=torch.float32, device=dev) for _ in range(k)]
+    dt = tpm.TP_BF16 if w.dtype == "bf16" else tpm.TP_F32
+    flags = tpm.TP_FUSED_ACCUM if fused else 0
+    need = tpm.tp_mlp_backward_workspace_bytes(k, M, H, Fk, dt, flags)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        tpm.tp_mlp_shard_backward(X, Ws, bs, Vs, dZ, dX=dX, dW=dW, db=db, dV=dV, workspace=ws, fused=fused)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    flop = 10 * M * H * w.F
+    tflops = flop / (ms * 1e-3) / 1e12
+    log("backward: %.4f ms/step, %.1f TFLOP/s (%.1f%% of %s peak)" % (ms, tflops, 100 * tflops / PEAK_TFLOPS[w.dtype],
+                                                                    w.dtype))
+    if not bool(torch.isfinite(dX).all()):
+        raise RuntimeError("non-finite backward output")
+
+    Y = torch.empty(M, Fk, dtype=tdt, device=dev)
+    G = torch.empty(M, Fk, dtype=tdt, device=dev)
+    parts = [torch.empty(M, H, dtype=torch.float32, device=dev) for _ in range(k)]
+    gws = torch.empty(max(tpm.tp_mlp_grad_weight_workspace_bytes(M, H, Fk, dt), 1), dtype=torch.uint8,
+                      device=dev)
+    kinds = ["col_gelu_save", "grad_act", "grad_row_weight", "grad_col_weight", "grad_input"] + \
+        (["grad_input_accum"] if fused and k > 1 else []) + (["shard_reduce"] if not fused and k > 1 else [])
+    nlaunch = {"col_gelu_save": k, "grad_act": k, "grad_row_weight": k, "grad_col_weight": k,
+               "grad_input": 1 if fused else k, "grad_input_accum": k - 1, "shard_reduce": 1}
+
+    def launch(kind):
+        if kind == "col_gelu_save":
+            for i in range(k):
+                tpm.tp_mlp_col_gelu_save(X, Ws[i], bs[i], Y_i=Y, G_i=G)
+        elif kind == "grad_act":
+            for i in range(k):
+                tpm.tp_mlp_grad_act(dZ, Vs[i], G, dA_i=G)
+        elif kind == "grad_row_weight":
+            for i in range(k):
+                tpm.tp_mlp_grad_row_weight(Y, dZ, dV_i=dV[i], workspace=gws)
+        elif kind == "grad_col_weight":
+            for i in range(k):
+                tpm.tp_mlp_grad_col_weight(X, G, dW_i=dW[i], db_i=db[i], workspace=gws)
+        elif kind == "grad_input":
+            for i in range(nlaunch["grad_input"]):
+                tpm.tp_mlp_grad_input_partial(G, Ws[i], dX_i=dX if fused else parts[i])
+        elif kind == "grad_input_accum":
+            for i in range(1, k):
+                tpm.tp_mlp_grad_input_partial(G, Ws[i], dX_i=dX, accumulate=True)
+        else:
+            tpm.tp_shard_reduce(parts, Z=dX)
+
+    kern = time_kinds(kinds, launch, nlaunch, args.kernel_steps or args.steps, args.warmup, w, elt)
+    roof = roofline(kern, w, args.variant, w.dtype)
+    return {"metric": "TP-shard MLP backward TFLOP/s (5 GEMMs of 2 M H F/k per shard, incl. recompute)",
+            "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+            "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "roofline": roof,
+            "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"]}
+                        for k_, v in kern.items()}}
 
 
 def measured_traffic(workload, variant, kind):
     """HBM bytes per launch of `kind` from the committed counter summary
     (profiles/traffic.json), or None if that summary does not cover this
     kernel or was taken on a different kernel source."""
-    import hashlib
+    from tensor_transformer_mlp_amd.profiling import kernel_source_sha256
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "tensor_transformer_mlp_amd", "csrc", "tp_mlp_kernels.hip")
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     e = rec.get("entries", {}).get("%s/%s/%s" % (workload, variant, kind))
     if not e:

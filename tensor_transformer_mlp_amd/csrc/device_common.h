@@ -68,15 +68,14 @@ __device__ __forceinline__ void gelu_and_grad_f32(float x, float& y, float& g) {
   g = fmaf(x * 0.3989422804014327f, e, Phi);
 }
 
-// Map the linear workgroup id to a (tile_m, tile_n) pair.  Workgroups are
+// Map the linear workgroup id bid (of nb) to a (tile_m, tile_n) pair.  Workgroups are
 // dispatched round-robin over the 8 XCDs, so ids are first regrouped so that
 // each XCD receives a contiguous range of logical tiles, and logical tiles are
 // walked in column strips of `kGroupM` tile rows so that the tiles resident on
 // one XCD at a time share rows of A and columns of B in that XCD's L2.
 template <int kGroupM>
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int bid = blockIdx.x;
-  const int nb = gridDim.x;
+__device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
   const int full = nb - nb % kNumXcd;
   int logical = bid;
   if (bid < full) logical = (bid % kNumXcd) * (full / kNumXcd) + bid / kNumXcd;
@@ -98,24 +97,30 @@ __device__ __forceinline__ i32x4_t buffer_desc(const void* base, uint32_t bytes)
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane l's data lands
-// at LDS byte address `lds + 16 l` (lds is wave-uniform); out-of-range lanes
-// write zeros.  Written as inline assembly so that the compiler does not track
-// the LDS write itself: its conservative alias tracking of in-flight LDS DMA
-// would otherwise insert vmcnt(0) waits before fragment reads of other stage
-// buffers.  Completion is waited for explicitly (vmcnt) before the barrier
-// that publishes a stage; the "memory" clobber keeps LDS accesses in order
-// around it.  M0 is set here for the instruction; no compiler-generated code
-// in the kernels that use this relies on M0.
-__device__ __forceinline__ void lds_dma16(i32x4_t desc, char* lds, uint32_t voff) {
-  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds));
+// at LDS byte address `lds_addr + 16 l` (lds_addr is a wave-uniform LDS
+// offset); out-of-range lanes write zeros.  Written as inline assembly so that
+// the compiler does not track the LDS write itself: its conservative alias
+// tracking of in-flight LDS DMA would otherwise insert vmcnt(0) waits before
+// fragment reads of other stage buffers.  Completion is waited for explicitly
+// (vmcnt) before the barrier that publishes a stage; the "memory" clobber
+// keeps LDS accesses in order around it.  M0 is set here for the instruction
+// (one wait state between the M0 write and the LDS DMA); no compiler-generated
+// code in the kernels that use this relies on M0.
+__device__ __forceinline__ void lds_dma16(i32x4_t desc, uint32_t lds_addr, uint32_t voff) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %1, %2, 0 offen lds"
       :
-      : "s"(lds_addr), "v"(voff), "s"(desc)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(desc)
       : "memory", "m0");
+}
+
+// LDS byte offset of a __shared__ object (no null check: the object is known
+// to live in LDS).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_offset(T* shared_obj) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(char*)shared_obj);
 }
 
 // Two ds_read_b64_tr_b16 transpose reads joined into one 8 x bf16 operand.

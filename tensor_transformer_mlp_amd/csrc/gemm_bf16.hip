@@ -20,10 +20,12 @@ bool c_is_bf16(Epilogue e) {
 //   * 256x256 (8 waves, 4 stages) when it fills at least two rounds of the 256
 //     CUs, or 192..255 tiles (a 0.75 round still beats the smaller tiles);
 //   * otherwise 128x256 with 3 stages (two workgroups per CU) when N > 128;
-//   * otherwise 128x128 (two workgroups per CU).
+//   * otherwise 128x128 (two workgroups per CU);
+//   * K % 32 != 0 (K ends inside a 32-deep stage): the ragged-K variant of the
+//     128x128 tile.
 int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K) {
   (void)layout;
-  (void)K;
+  if (K % 32) return kTailTile;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= 512 || (t256 >= 192 && t256 < 256)) return 0;
   if (N > 128) return 6;
@@ -37,21 +39,22 @@ hipError_t launch_gemm_bf16_tile(int tile, const GemmArgs& g, hipStream_t s) {
   const int64_t tiles_n = (g.N + c.bn - 1) / c.bn;
   const int64_t rows_per_launch = (kMaxTilesPerLaunch / tiles_n) * c.bm;
   const bool a_kmajor = g.layout != kTN;
-  const bool b_kmajor = g.layout == kNT;
   const size_t c_elt = c_is_bf16(g.epi) ? 2 : 4;
   const uint16_t* A = static_cast<const uint16_t*>(g.A);
   const uint16_t* B = static_cast<const uint16_t*>(g.B);
   GemmParams p;
   p.B = B;
   p.bias = static_cast<const uint16_t*>(g.bias);
-  p.a_end = reinterpret_cast<const char*>(A + (a_kmajor ? g.M * g.lda : g.K * g.lda));
-  p.b_end = reinterpret_cast<const char*>(B + (b_kmajor ? g.N * g.ldb : g.K * g.ldb));
   p.lda = g.lda;
   p.ldb = g.ldb;
   p.ldc = g.ldc;
   p.N = (int)g.N;
   p.K = (int)g.K;
   p.tiles_n = (int)tiles_n;
+  p.slices = 1;
+  p.k_slice = p.K;
+  p.part = nullptr;
+  p.part_stride = 0;
   for (int64_t r0 = 0; r0 < g.M; r0 += rows_per_launch) {
     const int64_t Mc = g.M - r0 < rows_per_launch ? g.M - r0 : rows_per_launch;
     p.A = a_kmajor ? A + r0 * g.lda : A + r0;
@@ -76,9 +79,11 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // K-split.  The bf16 slices use the 128x128 tile (two workgroups per CU), the
-// float32 ones the 64x64 tile; K is halved while the output has fewer than
-// 256 tiles per slice count and every slice keeps at least 1024 of K, up to
-// 16 slices.
+// float32 ones the 64x64 tile.  The slice count doubles while the grid has
+// fewer than 256 workgroups and each slice keeps at least 2048 of K, or while
+// it has fewer than 128 and each slice keeps at least 1024 (up to 16 slices).
+// Measured on MI355X for the weight gradients of the MLP shards (for example
+// 768 x 768 x 8192: 4 slices 409 TFLOP/s, 8 slices 311, no split 196).
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -105,7 +110,9 @@ GemmArgs slice_args(const GemmArgs& g, bool bf16, int64_t k0, int64_t kn) {
 int gemm_k_slices(bool bf16, int64_t M, int64_t N, int64_t K) {
   const int64_t t = bf16 ? ((M + 127) / 128) * ((N + 127) / 128) : ((M + 63) / 64) * ((N + 63) / 64);
   int S = 1;
-  while (t * S < 256 && K / (2 * S) >= 1024 && S < 16) S *= 2;
+  while (S < 16 && t * S < 256 &&
+         (K / (2 * S) >= 2048 || (t * S < 128 && K / (2 * S) >= 1024)))
+    S *= 2;
   return S;
 }
 
@@ -118,22 +125,55 @@ hipError_t launch_gemm_split(const GemmArgs& g, bool bf16, void* ws, hipStream_t
   const int S = gemm_k_slices(bf16, g.M, g.N, g.K);
   if (S == 1) return bf16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
   const int64_t ks = split_slice_len(g.K, S);
+  const int n = (int)((g.K + ks - 1) / ks);  // slices actually used (<= S)
   const size_t part = round256(size_t(g.M) * size_t(g.N) * 4);
-  const float* parts[16];
-  int n = 0;
-  for (int64_t k0 = 0; k0 < g.K; k0 += ks, ++n) {
-    GemmArgs a = slice_args(g, bf16, k0, g.K - k0 < ks ? g.K - k0 : ks);
-    if (n > 0) {
-      a.C = static_cast<char*>(ws) + size_t(n - 1) * part;
-      a.ldc = g.N;
-      a.epi = kEpiStoreF32;
+  if (bf16) {
+    // One launch: the grid holds n copies of the tile grid (few tiles by
+    // construction, so no launch splitting is needed).
+    const TileCfg& c = kTiles[kSplitTile];
+    GemmParams p;
+    p.A = static_cast<const uint16_t*>(g.A);
+    p.B = static_cast<const uint16_t*>(g.B);
+    p.bias = nullptr;
+    p.C = g.C;
+    p.aux = nullptr;
+    p.lda = g.lda;
+    p.ldb = g.ldb;
+    p.ldc = g.ldc;
+    p.M = (int)g.M;
+    p.N = (int)g.N;
+    p.K = (int)g.K;
+    p.tiles_m = (int)((g.M + c.bm - 1) / c.bm);
+    p.tiles_n = (int)((g.N + c.bn - 1) / c.bn);
+    p.slices = n;
+    p.k_slice = (int)ks;
+    p.part = static_cast<float*>(ws);
+    p.part_stride = (int64_t)(part / 4);
+    hipError_t e;
+    switch (g.layout) {
+      case kNN: e = launch_bf16_nn(kSplitTile, p, g.epi, s); break;
+      case kNT: e = launch_bf16_nt(kSplitTile, p, g.epi, s); break;
+      default: e = launch_bf16_tn(kSplitTile, p, g.epi, s); break;
     }
-    parts[n] = static_cast<const float*>(a.C);
-    const hipError_t e = bf16 ? launch_gemm_bf16_tile(kSplitTile, a, s) : launch_gemm_f32(a, s);
     if (e != hipSuccess) return e;
+  } else {
+    for (int i = 0; i < n; ++i) {
+      const int64_t k0 = i * ks;
+      GemmArgs a = slice_args(g, bf16, k0, g.K - k0 < ks ? g.K - k0 : ks);
+      if (i > 0) {
+        a.C = static_cast<char*>(ws) + size_t(i - 1) * part;
+        a.ldc = g.N;
+        a.epi = kEpiStoreF32;
+      }
+      const hipError_t e = launch_gemm_f32(a, s);
+      if (e != hipSuccess) return e;
+    }
   }
-  if (n == 1) return hipSuccess;
   // C must be dense ([M, N] with ldc == N) for the element-wise sum.
+  const float* parts[16];
+  parts[0] = static_cast<const float*>(g.C);
+  for (int i = 1; i < n; ++i)
+    parts[i] = reinterpret_cast<const float*>(static_cast<const char*>(ws) + size_t(i - 1) * part);
   return launch_shard_reduce(parts, n, static_cast<float*>(g.C), g.M * g.N, s);
 }
 

@@ -52,11 +52,17 @@ struct GemmParams {
   const uint16_t* bias;
   void* C;
   void* aux;
-  const char* a_end;  // one past the last byte of A / B (bounds the buffer descriptors)
-  const char* b_end;
   int64_t lda, ldb, ldc;
   int M, N, K;
   int tiles_m, tiles_n;
+  // K-split (float32 store / accumulate epilogues only): the grid holds
+  // `slices` copies of the tile grid; slice s covers k in
+  // [s k_slice, min(K, (s + 1) k_slice)).  Slice 0 applies the epilogue to C,
+  // slice s > 0 stores its partial to part + (s - 1) part_stride (leading
+  // dimension N).  slices == 1: no split.
+  int slices, k_slice;
+  float* part;
+  int64_t part_stride;
 };
 
 // Workgroup tile configurations (index = tile id used by the picker).
@@ -94,8 +100,9 @@ __device__ __forceinline__ int swzK(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int swzMN(int k) { return 4 * (k & 3); }
 
 // One operand's tile: R rows of the operand (rows of A, or columns of B) by
-// 32 k per stage, loaded by NW waves.
-template <int R, bool KMAJ, int NW>
+// 32 k per stage, loaded by NW waves.  KTAIL: K may end inside a stage, so the
+// chunks of the last stage are masked per lane by their k.
+template <int R, bool KMAJ, int NW, bool KTAIL>
 struct OperandTile {
   static constexpr int kBytes = R * 64;  // R x 32 x 2 bytes
   static constexpr int kPerWave = kBytes / 1024 / NW;
@@ -105,20 +112,23 @@ struct OperandTile {
   static_assert(kBytes % (1024 * NW) == 0, "DMA split");
   static_assert(KMAJ || (R % 128 == 0 && R <= 512), "MN-major tiles need 16-chunk row groups");
 
-  uint64_t base;     // global address of (tile row 0, k = 0)
-  uint64_t end;      // one past the operand's last byte
-  uint64_t kstride;  // bytes per unit of k
+  // Global address of (tile row 0, first k of the next stage to be issued);
+  // stages are issued in order, so it advances by `step` bytes per stage.
+  uint64_t cur;
+  uint64_t step;
   uint32_t src[kPerWave];  // byte offset of the lane's chunk from (tile row 0, stage k 0)
-  int kidx[kPerWave];      // first k (within a stage) of the lane's chunk
+  int kidx[kPerWave];      // first k (within a stage) of the lane's chunk (KTAIL only)
 
   // r0: first row (K-major) or column (MN-major) of the tile; rtot: the
   // operand's extent in that dimension; ld: leading dimension in elements.
-  __device__ __forceinline__ void init(const uint16_t* ptr, const char* ptr_end, int64_t ld, int r0,
-                                       int rtot, int wave, int lane) {
-    end = reinterpret_cast<uint64_t>(ptr_end);
+  // A chunk outside the operand gets offset kOob and reads as zeros; every
+  // other offset addresses memory inside the operand, so the descriptors
+  // need no exact size.
+  __device__ __forceinline__ void init(const uint16_t* ptr, int64_t ld, int r0, int rtot, int wave,
+                                       int lane) {
     if constexpr (KMAJ) {
-      base = reinterpret_cast<uint64_t>(ptr + (int64_t)r0 * ld);
-      kstride = 2;
+      cur = reinterpret_cast<uint64_t>(ptr + (int64_t)r0 * ld);
+      step = 64;  // 32 k x 2 bytes
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) {
         const int row = (wave * kPerWave + i) * 16 + (lane >> 2);
@@ -127,8 +137,8 @@ struct OperandTile {
         kidx[i] = c * 8;
       }
     } else {
-      base = reinterpret_cast<uint64_t>(ptr + r0);
-      kstride = (uint64_t)ld * 2u;
+      cur = reinterpret_cast<uint64_t>(ptr + r0);
+      step = (uint64_t)ld * 64u;  // 32 k-rows
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) {
         const int row = (wave * kPerWave + i) * kRowsPerBlock + lane / kLanesPerRow;
@@ -139,17 +149,19 @@ struct OperandTile {
     }
   }
 
-  // Loads of stage k0 .. k0 + 31 into `lds`; kleft = K - k0 (<= 0: nothing
-  // valid, every lane writes zeros and no memory is read).
-  __device__ __forceinline__ void issue(char* lds, int wave, int k0, int kleft) const {
-    const bool live = kleft > 0;
-    const uint64_t addr = base + (live ? (uint64_t)k0 * kstride : 0);
-    const uint64_t rem = end > addr ? end - addr : 0;
-    const uint32_t rec = live ? (uint32_t)(rem < 0x7FFFFFF0ull ? rem : 0x7FFFFFF0ull) : 0u;
-    const i32x4_t desc = buffer_desc(reinterpret_cast<const void*>(addr), rec);
+  // Loads of the next stage (k0 .. k0 + 31) into the LDS block at lds_addr;
+  // kleft = K - k0.  A stage past the end (kleft <= 0) gets an empty
+  // descriptor: every lane writes zeros and no memory is read.
+  __device__ __forceinline__ void issue(uint32_t lds_addr, int wave, int kleft) {
+    const i32x4_t desc =
+        buffer_desc(reinterpret_cast<const void*>(cur), kleft > 0 ? 0x7FFFFFF0u : 0u);
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i)
-      lds_dma16(desc, lds + (wave * kPerWave + i) * 1024, kidx[i] < kleft ? src[i] : kOob);
+    for (int i = 0; i < kPerWave; ++i) {
+      uint32_t off = src[i];
+      if constexpr (KTAIL) off = kidx[i] < kleft ? off : kOob;
+      lds_dma16(desc, lds_addr + (uint32_t)((wave * kPerWave + i) * 1024), off);
+    }
+    cur += step;
   }
 };
 
@@ -192,7 +204,7 @@ struct OperandFrags {
   }
 };
 
-template <int EPI, int LAYOUT, int BM, int BN, int WM, int WN, int NBUF>
+template <int EPI, int LAYOUT, int BM, int BN, int WM, int WN, int NBUF, bool KTAIL>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   constexpr bool AK = LAYOUT != kTN;  // A K-major
   constexpr bool BK = LAYOUT == kNT;  // B K-major
@@ -200,8 +212,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  using TA = OperandTile<BM, AK, NW>;
-  using TB = OperandTile<BN, BK, NW>;
+  using TA = OperandTile<BM, AK, NW, KTAIL>;
+  using TB = OperandTile<BN, BK, NW, KTAIL>;
   using RA = OperandFrags<BM, AK, FM>;
   using RB = OperandFrags<BN, BK, FN>;
   constexpr int A_BYTES = TA::kBytes, STAGE = TA::kBytes + TB::kBytes;
@@ -229,27 +241,51 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
     else if constexpr (b == 4) return st4;
     else return st5;
   };
+  auto stage_lds = [&](auto bset) -> uint32_t {
+    constexpr int b = decltype(bset)::value;
+    if constexpr (b == 0) return lds_offset(st0);
+    else if constexpr (b == 1) return lds_offset(st1);
+    else if constexpr (b == 2) return lds_offset(st2);
+    else if constexpr (b == 3) return lds_offset(st3);
+    else if constexpr (b == 4) return lds_offset(st4);
+    else return lds_offset(st5);
+  };
 
   int tm, tn;
-  tile_coords<8>(p.tiles_m, p.tiles_n, tm, tn);
+  const int tiles = p.tiles_m * p.tiles_n;
+  int bid = blockIdx.x, slice = 0;
+  if (p.slices > 1) {
+    slice = bid / tiles;
+    bid -= slice * tiles;
+  }
+  tile_coords<8>(bid, tiles, p.tiles_m, p.tiles_n, tm, tn);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int m0 = tm * BM;
   const int n0 = tn * BN;
-  const int K = p.K;
+  int K = p.K;
+  const uint16_t* Ap = p.A;
+  const uint16_t* Bp = p.B;
+  if (p.slices > 1) {
+    const int kb = slice * p.k_slice;
+    K = min(K - kb, p.k_slice);
+    Ap += AK ? (int64_t)kb : (int64_t)kb * p.lda;
+    Bp += BK ? (int64_t)kb : (int64_t)kb * p.ldb;
+  }
   const int nk = (K + 31) / 32;
 
   TA ta;
   TB tb;
-  ta.init(p.A, p.a_end, p.lda, m0, p.M, wave, lane);
-  tb.init(p.B, p.b_end, p.ldb, n0, p.N, wave, lane);
+  ta.init(Ap, p.lda, m0, p.M, wave, lane);
+  tb.init(Bp, p.ldb, n0, p.N, wave, lane);
+  // Stages are issued in increasing order: kt = 0, 1, 2, ...
   auto issue_stage = [&](auto bset, int kt) {
-    char* S = stage(bset);
-    const int k0 = kt * 32;
-    ta.issue(S, wave, k0, K - k0);
-    tb.issue(S + A_BYTES, wave, k0, K - k0);
+    const uint32_t S = stage_lds(bset);
+    const int kleft = K - kt * 32;
+    ta.issue(S, wave, kleft);
+    tb.issue(S + A_BYTES, wave, kleft);
   };
 
   RA ra;
@@ -344,10 +380,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   // multiplier or the old value of C) is issued before any store, so the
   // loads overlap; each element is read and written by the same lane only,
   // so this order is also correct when C is aux.  The bias is loaded once.
+  // Tiles wholly inside C take a path without per-store bounds checks.
   const int l32 = lane & 31;
   const int hcol = 4 * (lane >> 5);
   const int M = p.M, N = p.N;
-  const int64_t ldc = p.ldc;
+  int64_t ldc = p.ldc;
+  void* Cout = p.C;
+  bool accumulate = EPI == kEpiAccumF32;
+  if (slice > 0) {  // a K-split partial: plain float32 store
+    Cout = p.part + (int64_t)(slice - 1) * p.part_stride;
+    ldc = N;
+    accumulate = false;
+  }
   constexpr bool kBias = EPI == kEpiBiasGelu || EPI == kEpiBiasGeluSave;
   f32x4_t bias4[FN][4];
   if constexpr (kBias) {
@@ -362,88 +406,98 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
                                bf16_bits_to_f32(bb[1] & 0xFFFFu), bf16_bits_to_f32(bb[1] >> 16)};
       }
   }
+  auto epilogue = [&](auto guard) {
+    constexpr bool G = decltype(guard)::value;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + l32;
-    const bool mrow = m < M;
-    const int64_t row = (int64_t)m * ldc;
-    u32x2_t aux2[FN][4];
-    f32x4_t old4[FN][4];
-    if constexpr (EPI == kEpiMulAux || EPI == kEpiAccumF32) {
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm * WTM + i * 32 + l32;
+      const bool mrow = !G || m < M;
+      const int64_t row = (int64_t)m * ldc;
+      u32x2_t aux2[FN][4];
+      f32x4_t old4[FN][4];
+      if constexpr (EPI == kEpiMulAux || EPI == kEpiAccumF32) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
+            const bool ok = !G || (mrow && n < N);
+            if constexpr (EPI == kEpiMulAux) {
+              aux2[j][gq] = u32x2_t{0u, 0u};
+              if (ok)
+                aux2[j][gq] =
+                    *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(p.aux) + row + n);
+            } else {
+              old4[j][gq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              if (ok && accumulate)
+                old4[j][gq] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(Cout) + row + n);
+            }
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
-          if constexpr (EPI == kEpiMulAux) {
-            aux2[j][gq] = u32x2_t{0u, 0u};
-            if (mrow && n < N)
-              aux2[j][gq] = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(p.aux) + row + n);
-          } else {
-            old4[j][gq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (mrow && n < N)
-              old4[j][gq] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.C) + row + n);
-          }
-        }
-    }
+          if (G && (!mrow || n >= N)) continue;
+          const int64_t idx = row + n;
+          f32x4_t v = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                              acc[i][j][4 * gq + 3]};
+          if constexpr (kBias) {
+            v += bias4[j][gq];
+            if constexpr (EPI == kEpiBiasGelu) {
+              u32x2_t o;
+              o[0] = f32_to_bf16_bits(gelu_f32(v[0])) | (f32_to_bf16_bits(gelu_f32(v[1])) << 16);
+              o[1] = f32_to_bf16_bits(gelu_f32(v[2])) | (f32_to_bf16_bits(gelu_f32(v[3])) << 16);
+              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = o;
+            } else {
+              float y[4], g[4];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
-        if (!mrow || n >= N) continue;
-        const int64_t idx = row + n;
-        f32x4_t v = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
-                            acc[i][j][4 * gq + 3]};
-        if constexpr (kBias) {
-          v += bias4[j][gq];
-          if constexpr (EPI == kEpiBiasGelu) {
+              for (int e = 0; e < 4; ++e) gelu_and_grad_f32(v[e], y[e], g[e]);
+              u32x2_t oy, og;
+              oy[0] = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+              oy[1] = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
+              og[0] = f32_to_bf16_bits(g[0]) | (f32_to_bf16_bits(g[1]) << 16);
+              og[1] = f32_to_bf16_bits(g[2]) | (f32_to_bf16_bits(g[3]) << 16);
+              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = oy;
+              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.aux) + idx) = og;
+            }
+          } else if constexpr (EPI == kEpiMulAux) {
+            const u32x2_t gg = aux2[j][gq];
             u32x2_t o;
-            o[0] = f32_to_bf16_bits(gelu_f32(v[0])) | (f32_to_bf16_bits(gelu_f32(v[1])) << 16);
-            o[1] = f32_to_bf16_bits(gelu_f32(v[2])) | (f32_to_bf16_bits(gelu_f32(v[3])) << 16);
-            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.C) + idx) = o;
+            o[0] = f32_to_bf16_bits(v[0] * bf16_bits_to_f32(gg[0] & 0xFFFFu)) |
+                   (f32_to_bf16_bits(v[1] * bf16_bits_to_f32(gg[0] >> 16)) << 16);
+            o[1] = f32_to_bf16_bits(v[2] * bf16_bits_to_f32(gg[1] & 0xFFFFu)) |
+                   (f32_to_bf16_bits(v[3] * bf16_bits_to_f32(gg[1] >> 16)) << 16);
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = o;
+          } else if constexpr (EPI == kEpiStoreF32) {
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(Cout) + idx) = v;
           } else {
-            float y[4], g[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) gelu_and_grad_f32(v[e], y[e], g[e]);
-            u32x2_t oy, og;
-            oy[0] = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
-            oy[1] = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
-            og[0] = f32_to_bf16_bits(g[0]) | (f32_to_bf16_bits(g[1]) << 16);
-            og[1] = f32_to_bf16_bits(g[2]) | (f32_to_bf16_bits(g[3]) << 16);
-            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.C) + idx) = oy;
-            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.aux) + idx) = og;
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(Cout) + idx) = old4[j][gq] + v;
           }
-        } else if constexpr (EPI == kEpiMulAux) {
-          const u32x2_t gg = aux2[j][gq];
-          u32x2_t o;
-          o[0] = f32_to_bf16_bits(v[0] * bf16_bits_to_f32(gg[0] & 0xFFFFu)) |
-                 (f32_to_bf16_bits(v[1] * bf16_bits_to_f32(gg[0] >> 16)) << 16);
-          o[1] = f32_to_bf16_bits(v[2] * bf16_bits_to_f32(gg[1] & 0xFFFFu)) |
-                 (f32_to_bf16_bits(v[3] * bf16_bits_to_f32(gg[1] >> 16)) << 16);
-          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.C) + idx) = o;
-        } else if constexpr (EPI == kEpiStoreF32) {
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.C) + idx) = v;
-        } else {
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.C) + idx) = old4[j][gq] + v;
         }
       }
     }
-  }
+  };
+  if (m0 + BM <= M && n0 + BN <= N)
+    epilogue(std::false_type{});
+  else
+    epilogue(std::true_type{});
 }
 
 // Launch one tile configuration of one layout (p.tiles_m / p.tiles_n set).
-template <int LAYOUT, int T>
+template <int LAYOUT, int T, bool KTAIL>
 hipError_t launch_bf16_tile(const GemmParams& p, Epilogue epi, hipStream_t s) {
   constexpr TileCfg c = kTiles[T];
-  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n), block(c.wm * c.wn * 64);
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.slices),
+      block(c.wm * c.wn * 64);
   bool done = false;
   [&]<int... e>(std::integer_sequence<int, e...>) {
     (([&] {
        if constexpr (layout_has_epi(LAYOUT, e)) {
          if (epi == e) {
-           hipLaunchKernelGGL((gemm_bf16_kernel<e, LAYOUT, c.bm, c.bn, c.wm, c.wn, c.nbuf>), grid,
-                              block, 0, s, p);
+           hipLaunchKernelGGL((gemm_bf16_kernel<e, LAYOUT, c.bm, c.bn, c.wm, c.wn, c.nbuf, KTAIL>),
+                              grid, block, 0, s, p);
            done = true;
          }
        }
@@ -453,11 +507,16 @@ hipError_t launch_bf16_tile(const GemmParams& p, Epilogue epi, hipStream_t s) {
   return done ? hipGetLastError() : hipErrorInvalidValue;
 }
 
+// K % 32 != 0 runs on the ragged-K variant of one tile (kTailTile) only.
+constexpr int kTailTile = 8;
+
 template <int LAYOUT>
 hipError_t launch_bf16_layout_tile(int tile, const GemmParams& p, Epilogue epi, hipStream_t s) {
+  if (p.K % 32) return tile == kTailTile ? launch_bf16_tile<LAYOUT, kTailTile, true>(p, epi, s)
+                                         : hipErrorInvalidValue;
   hipError_t r = hipErrorInvalidValue;
   [&]<int... t>(std::integer_sequence<int, t...>) {
-    ((tile == t ? (r = launch_bf16_tile<LAYOUT, t>(p, epi, s), 0) : 0), ...);
+    ((tile == t ? (r = launch_bf16_tile<LAYOUT, t, false>(p, epi, s), 0) : 0), ...);
   }(std::make_integer_sequence<int, kNumTiles>{});
   return r;
 }

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
   __shared__ __attribute__((aligned(16))) float Bs[BK][BN + PAD];
 
   int tm, tn;
-  tile_coords<8>(p.tiles_m, p.tiles_n, tm, tn);
+  tile_coords<8>(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;

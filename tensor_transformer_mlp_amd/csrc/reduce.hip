@@ -95,7 +95,9 @@ hipError_t launch_reduce_u(const PartPtrs& pp, int k, float* Z, int64_t n, int64
 //      [256 cb, 256 cb + 256): 32 column groups of 8 x 8 row lanes, each lane
 //      a running float32 sum over every 8th row, then the 8 row lanes are
 //      added in order through LDS; the result is partials[rb][n];
-//   2. out[n] = (out[n] +) partials[0][n] + partials[1][n] + ... in order.
+//   2. out[n] = (out[n] +) the partials of column n, in a fixed order: four
+//      consecutive runs of row blocks, each summed in order, then the four
+//      run sums in order.
 // The row-block count depends only on (M, N), so the result is reproducible.
 // ---------------------------------------------------------------------------
 constexpr int kColsPerBlock = 256;
@@ -124,6 +126,7 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const void* __restr
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.f;
   if (n < N) {
+#pragma unroll 8
     for (int64_t r = r0 + rl; r < r1; r += 8) {
       if constexpr (BF16) {
         const u32x4_t v =
@@ -157,14 +160,40 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const void* __restr
   }
 }
 
+// Pass 2: 64 columns per workgroup, 4 row groups of 64 lanes; group g adds
+// partial rows [g q, (g + 1) q) in order, and the four group sums are then
+// added in group order (q = ceil(rb / 4)), so the order is fixed by (M, N).
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ partials,
                                                            int64_t rb, int64_t N,
                                                            float* __restrict__ out, int accumulate) {
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  float t = accumulate ? out[n] : 0.f;
-  for (int64_t i = 0; i < rb; ++i) t += partials[i * N + n];
-  out[n] = t;
+  __shared__ float red[4][64];
+  const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 64 + c;
+  const int64_t q = (rb + 3) / 4;
+  const int64_t i0 = g * q;
+  const int64_t i1 = i0 + q < rb ? i0 + q : rb;
+  float t = 0.f;
+  if (n < N) {
+    int64_t i = i0;
+    for (; i + 8 <= i1; i += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = partials[(i + u) * N + n];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t += v[u];
+    }
+    for (; i < i1; ++i) t += partials[i * N + n];
+  }
+  red[g][c] = t;
+  __syncthreads();
+  if (g == 0 && n < N) {
+    float r = accumulate ? out[n] : 0.f;
+    r += red[0][c];
+    r += red[1][c];
+    r += red[2][c];
+    r += red[3][c];
+    out[n] = r;
+  }
 }
 
 }  // namespace
@@ -192,7 +221,7 @@ hipError_t launch_colsum(const void* A, bool bf16, int64_t M, int64_t N, float* 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s,
                      partials, rb, N, out, accumulate ? 1 : 0);
   return hipGetLastError();
 }

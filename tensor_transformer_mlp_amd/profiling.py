@@ -26,21 +26,41 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-KERNEL_SRC = os.path.join(HERE, "csrc", "tp_mlp_kernels.hip")
+CSRC = os.path.join(HERE, "csrc")
 
-_EPI_KIND = {"0": "col_gelu", "1": "row_partial", "2": "row_partial_accum"}
+# Kernel kinds by (epilogue, operand layout) template arguments of the GEMMs:
+# epilogues 0 bias+GeLU, 1 fp32 store, 2 fp32 accumulate, 3 bias+GeLU+GeLU',
+# 4 multiply by aux; layouts 0 NN, 1 NT, 2 TN.
+_GEMM_KIND = {("0", "0"): "col_gelu", ("1", "0"): "row_partial", ("2", "0"): "row_partial_accum",
+              ("3", "0"): "col_gelu_save", ("4", "1"): "grad_act", ("1", "1"): "grad_input",
+              ("2", "1"): "grad_input_accum", ("1", "2"): "grad_weight", ("2", "2"): "grad_weight_accum"}
+
+
+def kernel_sources():
+    """The device and host sources of libtpmlp.so (what the counters depend on)."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith((".hip", ".h", ".cpp")) and not f.startswith("synth"))
+
+
+def kernel_source_sha256() -> str:
+    h = hashlib.sha256()
+    for path in kernel_sources():
+        h.update(os.path.basename(path).encode() + b"\0")
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def kernel_kind(name: str):
     """Benchmark kernel kind of a device kernel name, or None."""
     if "shard_reduce_kernel" in name:
         return "shard_reduce"
-    m = re.search(r"gemm_(?:bf16(?:_dma)?|f32)_kernel<([^>]*)>", name)
+    if "colsum_" in name:
+        return "colsum"
+    m = re.search(r"gemm_(?:bf16|f32)_kernel<([^>]*)>", name)
     if not m:
         return None
     args = [a.strip() for a in m.group(1).split(",")]
-    epi = args[0] if "gemm_f32_kernel" in name else args[4]
-    return _EPI_KIND.get(epi)
+    return _GEMM_KIND.get((args[0], args[1]))
 
 
 def short_name(name: str) -> str:
@@ -124,7 +144,7 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_byt
         k = kernel_kind(name)
         if k:
             kinds[k]["write"] += vals
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    sha = kernel_source_sha256()
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path))
