@@ -140,8 +140,9 @@ int tp_mlp_row_partial(const void* Y_i, const void* V_i, float* Z_i, int64_t M, 
 int tp_shard_reduce(const float* const* Z_parts, int k, float* Z, int64_t n, void* stream);
 
 /*
- * Bytes of device workspace tp_mlp_shard_forward needs: room for one Y_i
- * [M, Fk] (reused by every shard), plus k - 1 fp32 partials [M, H] unless
+ * Bytes of device workspace tp_mlp_shard_forward needs: one Y_i [M, Fk] per
+ * shard of a batch (the shards run in batches of up to 16, each step of a
+ * batch in one launch), plus k - 1 fp32 partials [M, H] unless
  * TP_FUSED_ACCUM is set (partial 0 is written into Z).  Returns 0 for invalid
  * arguments or M == 0.
  */
@@ -159,9 +160,11 @@ size_t tp_mlp_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dtype
  *
  * flags = 0: every P_i is materialised (P_0 in Z, the rest in the workspace)
  * and tp_shard_reduce sums them; this is the literal one-GPU stand-in for the
- * all-reduce.  flags = TP_FUSED_ACCUM: shard 0's row GEMM writes Z and shard
- * i > 0 adds its product into Z in its epilogue.  Both perform the same float32
- * additions in the same order and give bit-identical Z.
+ * all-reduce.  flags = TP_FUSED_ACCUM: the row GEMMs of a batch of shards run
+ * as one kernel in which every output tile forms each shard's product in its
+ * own float32 accumulator and adds them into Z in shard order, so no partial
+ * goes through memory.  Both perform the same float32 additions in the same
+ * order and give bit-identical Z.
  */
 int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const* b,
                          const void* const* V, int k, int64_t M, int64_t H, int64_t Fk,
@@ -244,9 +247,9 @@ int tp_mlp_grad_input_partial(const void* dA_i, const void* W_i, float* dX_i, in
 
 /*
  * Bytes of device workspace tp_mlp_shard_backward needs: Y_i and G_i / dA_i
- * [M, Fk] (reused by every shard), the weight-gradient workspace, and k - 1
- * float32 partials [M, H] unless TP_FUSED_ACCUM is set.  Returns 0 for
- * invalid arguments.
+ * [M, Fk] for every shard of a batch (up to 16), the weight-gradient
+ * workspace of a batch, and k - 1 float32 partials [M, H] unless
+ * TP_FUSED_ACCUM is set.  Returns 0 for invalid arguments.
  */
 size_t tp_mlp_backward_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dtype,
                                        unsigned flags);

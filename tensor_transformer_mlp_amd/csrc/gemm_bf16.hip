@@ -1,4 +1,5 @@
-// Host side of the bf16 GEMM: tile choice and launch splitting.
+// Host side of the bf16 GEMM: tile choice, batches of per-shard GEMMs, the
+// group sum, the K-split and launch splitting.
 #include "gemm_bf16_impl.h"
 
 namespace tpmlp {
@@ -13,68 +14,126 @@ bool c_is_bf16(Epilogue e) {
   return e == kEpiBiasGelu || e == kEpiBiasGeluSave || e == kEpiMulAux;
 }
 
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+int64_t tiles_of(int tile, int64_t M, int64_t N) {
+  return ((M + kTiles[tile].bm - 1) / kTiles[tile].bm) * ((N + kTiles[tile].bn - 1) / kTiles[tile].bn);
+}
+
+hipError_t launch_layout(Layout layout, int tile, const GemmParams& p, Epilogue epi, bool gsum,
+                         hipStream_t s) {
+  switch (layout) {
+    case kNN: return launch_bf16_nn(tile, p, epi, gsum, s);
+    case kNT: return launch_bf16_nt(tile, p, epi, gsum, s);
+    default: return launch_bf16_tn(tile, p, epi, gsum, s);
+  }
+}
+
+GemmParams base_params(const GemmBatch& b, int tile) {
+  GemmParams p{};
+  for (int g = 0; g < b.groups; ++g) {
+    p.t.A[g] = static_cast<const uint16_t*>(b.A[g]);
+    p.t.B[g] = static_cast<const uint16_t*>(b.B[g]);
+    p.t.bias[g] = static_cast<const uint16_t*>(b.bias[g]);
+    p.t.C[g] = b.C[g];
+    p.t.aux[g] = b.aux[g];
+  }
+  p.groups = b.groups;
+  p.lda = b.lda;
+  p.ldb = b.ldb;
+  p.ldc = b.ldc;
+  p.M = (int)b.M;
+  p.N = (int)b.N;
+  p.K = (int)b.K;
+  p.tiles_m = (int)((b.M + kTiles[tile].bm - 1) / kTiles[tile].bm);
+  p.tiles_n = (int)((b.N + kTiles[tile].bn - 1) / kTiles[tile].bn);
+  p.slices = 1;
+  p.k_slice = p.K;
+  p.part = nullptr;
+  p.part_stride = 0;
+  return p;
+}
+
 }  // namespace
 
 // Tile choice, from the per-shard GEMMs of the five workloads measured on
-// MI355X (random bf16 data):
+// MI355X (random bf16 data), counting the workgroups of the whole batch:
 //   * 256x256 (8 waves, 4 stages) when it fills at least two rounds of the 256
 //     CUs, or 192..255 tiles (a 0.75 round still beats the smaller tiles);
 //   * otherwise 128x256 with 3 stages (two workgroups per CU) when N > 128;
 //   * otherwise 128x128 (two workgroups per CU);
 //   * K % 32 != 0 (K ends inside a 32-deep stage): the ragged-K variant of the
 //     128x128 tile.
-int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K) {
+// A group sum keeps two accumulator sets, so it uses tiles of at most
+// 4 fragments per wave: 128x256 when it gives at least 192 workgroups, else
+// the 4-wave 128x128 tile (two workgroups per CU).
+int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K, int groups, bool group_sum) {
   (void)layout;
   if (K % 32) return kTailTile;
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (group_sum) return tiles_of(6, M, N) >= 192 ? 6 : 7;
+  const int64_t t256 = tiles_of(0, M, N) * groups;
   if (t256 >= 512 || (t256 >= 192 && t256 < 256)) return 0;
   if (N > 128) return 6;
   return 8;
 }
 
-hipError_t launch_gemm_bf16_tile(int tile, const GemmArgs& g, hipStream_t s) {
-  if (tile < 0 || tile >= kNumTiles) return hipErrorInvalidValue;
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+hipError_t launch_gemm_bf16_batch_tile(int tile, const GemmBatch& b, hipStream_t s) {
+  if (tile < 0 || tile >= kNumTiles || b.groups < 1 || b.groups > kMaxGroups) return hipErrorInvalidValue;
+  if (b.group_sum && !tile_allows_group_sum(tile)) return hipErrorInvalidValue;
+  if (b.M <= 0 || b.N <= 0) return hipSuccess;
   const TileCfg& c = kTiles[tile];
-  const int64_t tiles_n = (g.N + c.bn - 1) / c.bn;
-  const int64_t rows_per_launch = (kMaxTilesPerLaunch / tiles_n) * c.bm;
-  const bool a_kmajor = g.layout != kTN;
-  const size_t c_elt = c_is_bf16(g.epi) ? 2 : 4;
-  const uint16_t* A = static_cast<const uint16_t*>(g.A);
-  const uint16_t* B = static_cast<const uint16_t*>(g.B);
-  GemmParams p;
-  p.B = B;
-  p.bias = static_cast<const uint16_t*>(g.bias);
-  p.lda = g.lda;
-  p.ldb = g.ldb;
-  p.ldc = g.ldc;
-  p.N = (int)g.N;
-  p.K = (int)g.K;
-  p.tiles_n = (int)tiles_n;
-  p.slices = 1;
-  p.k_slice = p.K;
-  p.part = nullptr;
-  p.part_stride = 0;
-  for (int64_t r0 = 0; r0 < g.M; r0 += rows_per_launch) {
-    const int64_t Mc = g.M - r0 < rows_per_launch ? g.M - r0 : rows_per_launch;
-    p.A = a_kmajor ? A + r0 * g.lda : A + r0;
-    p.C = static_cast<char*>(g.C) + size_t(r0) * size_t(g.ldc) * c_elt;
-    p.aux = g.aux ? static_cast<char*>(g.aux) + size_t(r0) * size_t(g.ldc) * 2 : nullptr;
+  GemmParams p = base_params(b, tile);
+  const int64_t per_row = (int64_t)p.tiles_n * (b.group_sum ? 1 : b.groups);
+  const int64_t rows_per_launch = (kMaxTilesPerLaunch / per_row) * c.bm;
+  const bool a_kmajor = b.layout != kTN;
+  const size_t c_elt = c_is_bf16(b.epi) ? 2 : 4;
+  for (int64_t r0 = 0; r0 < b.M; r0 += rows_per_launch) {
+    const int64_t Mc = b.M - r0 < rows_per_launch ? b.M - r0 : rows_per_launch;
+    for (int g = 0; g < b.groups; ++g) {
+      const uint16_t* A = static_cast<const uint16_t*>(b.A[g]);
+      p.t.A[g] = a_kmajor ? A + r0 * b.lda : A + r0;
+      p.t.C[g] = static_cast<char*>(b.C[g]) + size_t(r0) * size_t(b.ldc) * c_elt;
+      p.t.aux[g] = b.aux[g] ? static_cast<char*>(b.aux[g]) + size_t(r0) * size_t(b.ldc) * 2 : nullptr;
+    }
     p.M = (int)Mc;
     p.tiles_m = (int)((Mc + c.bm - 1) / c.bm);
-    hipError_t e;
-    switch (g.layout) {
-      case kNN: e = launch_bf16_nn(tile, p, g.epi, s); break;
-      case kNT: e = launch_bf16_nt(tile, p, g.epi, s); break;
-      default: e = launch_bf16_tn(tile, p, g.epi, s); break;
-    }
+    const hipError_t e = launch_layout(b.layout, tile, p, b.epi, b.group_sum, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+hipError_t launch_gemm_bf16_batch(const GemmBatch& b, hipStream_t s) {
+  return launch_gemm_bf16_batch_tile(
+      pick_bf16_tile(b.layout, b.M, b.N, b.K, b.groups, b.group_sum), b, s);
+}
+
+GemmBatch single_batch(const GemmArgs& g) {
+  GemmBatch b{};
+  b.A[0] = g.A;
+  b.B[0] = g.B;
+  b.bias[0] = g.bias;
+  b.C[0] = g.C;
+  b.aux[0] = g.aux;
+  b.groups = 1;
+  b.group_sum = false;
+  b.M = g.M;
+  b.N = g.N;
+  b.K = g.K;
+  b.lda = g.lda;
+  b.ldb = g.ldb;
+  b.ldc = g.ldc;
+  b.layout = g.layout;
+  b.epi = g.epi;
+  return b;
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
-  return launch_gemm_bf16_tile(pick_bf16_tile(g.layout, g.M, g.N, g.K), g, s);
+  return launch_gemm_bf16_batch(single_batch(g), s);
+}
+
+hipError_t launch_gemm_bf16_tile(int tile, const GemmArgs& g, hipStream_t s) {
+  return launch_gemm_bf16_batch_tile(tile, single_batch(g), s);
 }
 
 // ---------------------------------------------------------------------------
@@ -89,92 +148,75 @@ namespace {
 
 constexpr int kSplitTile = 8;  // 128x128, 2x4 waves
 
-size_t round256(size_t x) { return (x + 255) / 256 * 256; }
-
 int64_t split_slice_len(int64_t K, int S) { return ((K + S - 1) / S + 31) / 32 * 32; }
 
-// The operands of slice [k0, ...): A and B advanced by k0 along K.
-GemmArgs slice_args(const GemmArgs& g, bool bf16, int64_t k0, int64_t kn) {
-  GemmArgs a = g;
-  const size_t e = bf16 ? 2 : 4;
-  const int64_t a_off = g.layout == kTN ? k0 * g.lda : k0;
-  const int64_t b_off = g.layout == kNT ? k0 : k0 * g.ldb;
-  a.A = static_cast<const char*>(g.A) + size_t(a_off) * e;
-  a.B = static_cast<const char*>(g.B) + size_t(b_off) * e;
-  a.K = kn;
-  return a;
+int64_t split_tiles(bool bf16, int groups, int64_t M, int64_t N) {
+  return groups * (bf16 ? tiles_of(kSplitTile, M, N) : ((M + 63) / 64) * ((N + 63) / 64));
 }
 
 }  // namespace
 
-int gemm_k_slices(bool bf16, int64_t M, int64_t N, int64_t K) {
-  const int64_t t = bf16 ? ((M + 127) / 128) * ((N + 127) / 128) : ((M + 63) / 64) * ((N + 63) / 64);
+int gemm_k_slices(bool bf16, int64_t tiles, int64_t K) {
+  (void)bf16;
   int S = 1;
-  while (S < 16 && t * S < 256 &&
-         (K / (2 * S) >= 2048 || (t * S < 128 && K / (2 * S) >= 1024)))
+  while (S < 16 && tiles * S < 256 &&
+         (K / (2 * S) >= 2048 || (tiles * S < 128 && K / (2 * S) >= 1024)))
     S *= 2;
   return S;
 }
 
-size_t gemm_split_workspace_bytes(bool bf16, int64_t M, int64_t N, int64_t K) {
-  const int S = gemm_k_slices(bf16, M, N, K);
-  return size_t(S - 1) * round256(size_t(M) * size_t(N) * 4);
+size_t gemm_split_workspace_bytes(bool bf16, int groups, int64_t M, int64_t N, int64_t K) {
+  const int S = gemm_k_slices(bf16, split_tiles(bf16, groups, M, N), K);
+  return size_t(groups) * size_t(S - 1) * round256(size_t(M) * size_t(N) * 4);
 }
 
-hipError_t launch_gemm_split(const GemmArgs& g, bool bf16, void* ws, hipStream_t s) {
-  const int S = gemm_k_slices(bf16, g.M, g.N, g.K);
-  if (S == 1) return bf16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
-  const int64_t ks = split_slice_len(g.K, S);
-  const int n = (int)((g.K + ks - 1) / ks);  // slices actually used (<= S)
-  const size_t part = round256(size_t(g.M) * size_t(g.N) * 4);
+hipError_t launch_gemm_split(const GemmBatch& b, bool bf16, void* ws, hipStream_t s) {
+  const int S = gemm_k_slices(bf16, split_tiles(bf16, b.groups, b.M, b.N), b.K);
+  if (S == 1) return bf16 ? launch_gemm_bf16_batch(b, s) : launch_gemm_f32_batch(b, s);
+  const int64_t ks = split_slice_len(b.K, S);
+  const int n = (int)((b.K + ks - 1) / ks);  // slices actually used (<= S)
+  const size_t part = round256(size_t(b.M) * size_t(b.N) * 4);
+  // group g's partial of slice i > 0 sits at ws + (g (n - 1) + i - 1) part
+  auto part_ptr = [&](int g, int i) {
+    return reinterpret_cast<float*>(static_cast<char*>(ws) + (size_t(g) * (n - 1) + i - 1) * part);
+  };
   if (bf16) {
-    // One launch: the grid holds n copies of the tile grid (few tiles by
-    // construction, so no launch splitting is needed).
-    const TileCfg& c = kTiles[kSplitTile];
-    GemmParams p;
-    p.A = static_cast<const uint16_t*>(g.A);
-    p.B = static_cast<const uint16_t*>(g.B);
-    p.bias = nullptr;
-    p.C = g.C;
-    p.aux = nullptr;
-    p.lda = g.lda;
-    p.ldb = g.ldb;
-    p.ldc = g.ldc;
-    p.M = (int)g.M;
-    p.N = (int)g.N;
-    p.K = (int)g.K;
-    p.tiles_m = (int)((g.M + c.bm - 1) / c.bm);
-    p.tiles_n = (int)((g.N + c.bn - 1) / c.bn);
+    // One launch: the grid holds groups x n copies of the tile grid (few
+    // tiles by construction, so no launch splitting is needed).
+    GemmParams p = base_params(b, kSplitTile);
     p.slices = n;
     p.k_slice = (int)ks;
     p.part = static_cast<float*>(ws);
     p.part_stride = (int64_t)(part / 4);
-    hipError_t e;
-    switch (g.layout) {
-      case kNN: e = launch_bf16_nn(kSplitTile, p, g.epi, s); break;
-      case kNT: e = launch_bf16_nt(kSplitTile, p, g.epi, s); break;
-      default: e = launch_bf16_tn(kSplitTile, p, g.epi, s); break;
-    }
+    const hipError_t e = launch_layout(b.layout, kSplitTile, p, b.epi, false, s);
     if (e != hipSuccess) return e;
   } else {
-    for (int i = 0; i < n; ++i) {
-      const int64_t k0 = i * ks;
-      GemmArgs a = slice_args(g, bf16, k0, g.K - k0 < ks ? g.K - k0 : ks);
-      if (i > 0) {
-        a.C = static_cast<char*>(ws) + size_t(i - 1) * part;
-        a.ldc = g.N;
-        a.epi = kEpiStoreF32;
+    for (int g = 0; g < b.groups; ++g) {
+      for (int i = 0; i < n; ++i) {
+        const int64_t k0 = i * ks;
+        const int64_t a_off = b.layout == kTN ? k0 * b.lda : k0;
+        const int64_t b_off = b.layout == kNT ? k0 : k0 * b.ldb;
+        GemmArgs a{static_cast<const float*>(b.A[g]) + a_off, static_cast<const float*>(b.B[g]) + b_off,
+                   nullptr, b.C[g], nullptr, b.M, b.N, b.K - k0 < ks ? b.K - k0 : ks,
+                   b.lda, b.ldb, b.ldc, b.layout, b.epi};
+        if (i > 0) {
+          a.C = part_ptr(g, i);
+          a.ldc = b.N;
+          a.epi = kEpiStoreF32;
+        }
+        const hipError_t e = launch_gemm_f32(a, s);
+        if (e != hipSuccess) return e;
       }
-      const hipError_t e = launch_gemm_f32(a, s);
-      if (e != hipSuccess) return e;
     }
   }
-  // C must be dense ([M, N] with ldc == N) for the element-wise sum.
-  const float* parts[16];
-  parts[0] = static_cast<const float*>(g.C);
-  for (int i = 1; i < n; ++i)
-    parts[i] = reinterpret_cast<const float*>(static_cast<const char*>(ws) + size_t(i - 1) * part);
-  return launch_shard_reduce(parts, n, static_cast<float*>(g.C), g.M * g.N, s);
+  for (int g = 0; g < b.groups; ++g) {
+    const float* parts[16];
+    parts[0] = static_cast<const float*>(b.C[g]);
+    for (int i = 1; i < n; ++i) parts[i] = part_ptr(g, i);
+    const hipError_t e = launch_shard_reduce(parts, n, static_cast<float*>(b.C[g]), b.M * b.N, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace tpmlp

@@ -46,20 +46,27 @@
 
 namespace tpmlp {
 
+// Per-group operands of a batch of same-shaped GEMMs (the per-shard GEMMs of
+// one step launched together); entries may repeat (the shared X).
+struct GroupTable {
+  const uint16_t* A[kMaxGroups];
+  const uint16_t* B[kMaxGroups];
+  const uint16_t* bias[kMaxGroups];
+  void* C[kMaxGroups];
+  void* aux[kMaxGroups];
+};
+
 struct GemmParams {
-  const uint16_t* A;
-  const uint16_t* B;
-  const uint16_t* bias;
-  void* C;
-  void* aux;
+  GroupTable t;
+  int groups;
   int64_t lda, ldb, ldc;
   int M, N, K;
   int tiles_m, tiles_n;
-  // K-split (float32 store / accumulate epilogues only): the grid holds
-  // `slices` copies of the tile grid; slice s covers k in
-  // [s k_slice, min(K, (s + 1) k_slice)).  Slice 0 applies the epilogue to C,
-  // slice s > 0 stores its partial to part + (s - 1) part_stride (leading
-  // dimension N).  slices == 1: no split.
+  // K-split (float32 store / accumulate epilogues only): each group's grid
+  // holds `slices` copies of the tile grid; slice s covers k in
+  // [s k_slice, min(K, (s + 1) k_slice)).  Slice 0 applies the epilogue to
+  // C, slice s > 0 stores its partial to part + ((g (slices - 1) + s - 1)
+  // part_stride (leading dimension N).  slices == 1: no split.
   int slices, k_slice;
   float* part;
   int64_t part_stride;
@@ -116,6 +123,7 @@ struct OperandTile {
   // stages are issued in order, so it advances by `step` bytes per stage.
   uint64_t cur;
   uint64_t step;
+  uint64_t tile_off;  // bytes from the operand's start to tile row 0
   uint32_t src[kPerWave];  // byte offset of the lane's chunk from (tile row 0, stage k 0)
   int kidx[kPerWave];      // first k (within a stage) of the lane's chunk (KTAIL only)
 
@@ -126,8 +134,9 @@ struct OperandTile {
   // need no exact size.
   __device__ __forceinline__ void init(const uint16_t* ptr, int64_t ld, int r0, int rtot, int wave,
                                        int lane) {
+    static_assert(sizeof(uint64_t) == sizeof(ptr), "64-bit pointers");
     if constexpr (KMAJ) {
-      cur = reinterpret_cast<uint64_t>(ptr + (int64_t)r0 * ld);
+      tile_off = (uint64_t)r0 * (uint64_t)ld * 2u;
       step = 64;  // 32 k x 2 bytes
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) {
@@ -137,7 +146,7 @@ struct OperandTile {
         kidx[i] = c * 8;
       }
     } else {
-      cur = reinterpret_cast<uint64_t>(ptr + r0);
+      tile_off = (uint64_t)r0 * 2u;
       step = (uint64_t)ld * 64u;  // 32 k-rows
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) {
@@ -147,6 +156,12 @@ struct OperandTile {
         kidx[i] = row;
       }
     }
+    rebase(ptr);
+  }
+
+  // Continue with another operand of the same shape (the next group).
+  __device__ __forceinline__ void rebase(const uint16_t* ptr) {
+    cur = reinterpret_cast<uint64_t>(ptr) + tile_off;
   }
 
   // Loads of the next stage (k0 .. k0 + 31) into the LDS block at lds_addr;
@@ -204,7 +219,13 @@ struct OperandFrags {
   }
 };
 
-template <int EPI, int LAYOUT, int BM, int BN, int WM, int WN, int NBUF, bool KTAIL>
+// GSUM: the groups are summed instead of launched side by side: each output
+// tile runs its K loop through every group in turn, with a fresh float32
+// accumulator per group that is added, in group order, into a running sum z
+// (z starts as group 0's product, or as C itself with kEpiAccumF32), and z is
+// stored once.  Each group's product is bit-identical to that group's own
+// GEMM, so this equals storing every product and summing them left to right.
+template <int EPI, int LAYOUT, int BM, int BN, int WM, int WN, int NBUF, bool KTAIL, bool GSUM>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   constexpr bool AK = LAYOUT != kTN;  // A K-major
   constexpr bool BK = LAYOUT == kNT;  // B K-major
@@ -222,6 +243,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   static_assert(NBUF >= 3 && NBUF <= 6, "stage count");
   static_assert((D - 1) * L <= 63, "vmcnt immediate");
   static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
+  static_assert(!GSUM || EPI == kEpiStoreF32 || EPI == kEpiAccumF32, "group sum stores float32");
 
   // One array per stage: distinct LDS objects get distinct alias scopes, so
   // the compiler can tell that fragment reads of one stage do not depend on
@@ -253,10 +275,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
 
   int tm, tn;
   const int tiles = p.tiles_m * p.tiles_n;
-  int bid = blockIdx.x, slice = 0;
-  if (p.slices > 1) {
-    slice = bid / tiles;
-    bid -= slice * tiles;
+  int bid = blockIdx.x, slice = 0, grp = 0;
+  if constexpr (!GSUM) {
+    if (p.groups > 1) {
+      const int per_group = tiles * p.slices;
+      grp = bid / per_group;
+      bid -= grp * per_group;
+    }
+    if (p.slices > 1) {
+      slice = bid / tiles;
+      bid -= slice * tiles;
+    }
   }
   tile_coords<8>(bid, tiles, p.tiles_m, p.tiles_n, tm, tn);
   const int tid = threadIdx.x;
@@ -266,26 +295,42 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   const int m0 = tm * BM;
   const int n0 = tn * BN;
   int K = p.K;
-  const uint16_t* Ap = p.A;
-  const uint16_t* Bp = p.B;
+  int kb = 0;  // first k of this workgroup's slice
   if (p.slices > 1) {
-    const int kb = slice * p.k_slice;
+    kb = slice * p.k_slice;
     K = min(K - kb, p.k_slice);
-    Ap += AK ? (int64_t)kb : (int64_t)kb * p.lda;
-    Bp += BK ? (int64_t)kb : (int64_t)kb * p.ldb;
   }
-  const int nk = (K + 31) / 32;
+  const int nk = (K + 31) / 32;                 // stages per group
+  const int ngroups = GSUM ? p.groups : 1;      // groups this workgroup runs through
+  const int nstages = nk * ngroups;
+  // Start of group g's operands at k = kb.
+  auto a_ptr = [&](int g) {
+    return p.t.A[g] + (AK ? (int64_t)kb : (int64_t)kb * p.lda);
+  };
+  auto b_ptr = [&](int g) {
+    return p.t.B[g] + (BK ? (int64_t)kb : (int64_t)kb * p.ldb);
+  };
 
   TA ta;
   TB tb;
-  ta.init(Ap, p.lda, m0, p.M, wave, lane);
-  tb.init(Bp, p.ldb, n0, p.N, wave, lane);
-  // Stages are issued in increasing order: kt = 0, 1, 2, ...
-  auto issue_stage = [&](auto bset, int kt) {
+  ta.init(a_ptr(grp), p.lda, m0, p.M, wave, lane);
+  tb.init(b_ptr(grp), p.ldb, n0, p.N, wave, lane);
+  // Stages are issued in order: (group 0, stage 0 .. nk - 1), (group 1, ...).
+  int iss_g = 0, iss_kt = 0;
+  auto issue_stage = [&](auto bset) {
     const uint32_t S = stage_lds(bset);
-    const int kleft = K - kt * 32;
+    const int kleft = iss_g < ngroups ? K - iss_kt * 32 : 0;
     ta.issue(S, wave, kleft);
     tb.issue(S + A_BYTES, wave, kleft);
+    if (++iss_kt == nk) {
+      iss_kt = 0;
+      if (GSUM && ++iss_g < ngroups) {
+        ta.rebase(a_ptr(iss_g));
+        tb.rebase(b_ptr(iss_g));
+      } else if (!GSUM) {
+        iss_g = 1;
+      }
+    }
   };
 
   RA ra;
@@ -300,6 +345,54 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  // Group sum: z, the running sum over groups (same fragment layout as acc).
+  f32x16_t z[GSUM ? FM : 1][GSUM ? FN : 1];
+  const bool z_from_c = GSUM && EPI == kEpiAccumF32;
+  if constexpr (GSUM) {
+    if (z_from_c) {
+      const int l32 = lane & 31, hcol = 4 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WTM + i * 32 + l32;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
+            f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (m < p.M && n < p.N)
+              v = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.t.C[0]) +
+                                                    (int64_t)m * p.ldc + n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[i][j][4 * gq + e] = v[e];
+          }
+      }
+    }
+  }
+  int cmp_g = 0, cmp_kt = 0;
+  // After the last stage of a group: z (+)= acc, acc = 0.
+  auto fold = [&]() {
+    if (++cmp_kt < nk) return;
+    cmp_kt = 0;
+    if (cmp_g == 0 && !z_from_c) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) z[i][j] = acc[i][j];
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) z[i][j] = z[i][j] + acc[i][j];
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    ++cmp_g;
+  };
 
   bf16x8_t fa[2][FM], fb[2][FN];
   auto read_frags = [&](auto fset, auto bset, int ks) {
@@ -326,7 +419,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   constexpr int kWaitNext = (kWaitN & 15) | ((kWaitN >> 4) << 14) | (7 << 4);
 
   [&]<int... b>(std::integer_sequence<int, b...>) {
-    (issue_stage(std::integral_constant<int, b>{}, b), ...);
+    (issue_stage(std::integral_constant<int, b>{}), ...);
   }(std::make_integer_sequence<int, D>{});
   __builtin_amdgcn_s_waitcnt(kWaitNext);
   asm volatile("s_barrier" ::: "memory");
@@ -334,13 +427,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
 
   // One K step of 32 on stage buffer c (static, so that every LDS access
   // names its buffer at compile time).
-  auto kstep = [&](auto cset, int kt) {
+  auto kstep = [&](auto cset) {
     constexpr int c = decltype(cset)::value;
     using Refill = std::integral_constant<int, (c + D) % NBUF>;
     using Next = std::integral_constant<int, (c + 1) % NBUF>;
-    // k16 step 0: refill the buffer freed by stage kt - 1 with stage kt + D,
-    // read step 1's fragments, MFMAs of step 0.
-    issue_stage(Refill{}, kt + D);
+    // k16 step 0: refill the buffer freed by the previous stage with the
+    // stage D ahead, read step 1's fragments, MFMAs of step 0.
+    issue_stage(Refill{});
     read_frags(I1{}, cset, 1);
     mfmas(I0{});
 #pragma unroll
@@ -350,8 +443,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
       if (m < L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // k16 step 1: once stage kt + 1 has landed for every wave, read its step
-    // 0 fragments while the MFMAs of step 1 run.
+    // k16 step 1: once the next stage has landed for every wave, read its
+    // step 0 fragments while the MFMAs of step 1 run.
     __builtin_amdgcn_s_waitcnt(kWaitNext);
     asm volatile("s_barrier" ::: "memory");
     read_frags(I0{}, Next{}, 0);
@@ -362,14 +455,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
       if (m < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (GSUM) fold();
   };
   // The loop body walks the NBUF buffers in order; an early exit handles a
-  // step count that is not a multiple of NBUF (uniform across the workgroup).
-  for (int kt = 0; kt < nk; kt += NBUF) {
+  // stage count that is not a multiple of NBUF (uniform across the workgroup).
+  for (int st = 0; st < nstages; st += NBUF) {
     bool more = true;
     [&]<int... b>(std::integer_sequence<int, b...>) {
-      ((more = more && (kt + b < nk), more ? (kstep(std::integral_constant<int, b>{}, kt + b), 0) : 0),
-       ...);
+      ((more = more && (st + b < nstages), more ? (kstep(std::integral_constant<int, b>{}), 0) : 0), ...);
     }(std::make_integer_sequence<int, NBUF>{});
   }
   // The last stages' loads (out of range, writing zeros) must have landed
@@ -385,10 +478,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   const int hcol = 4 * (lane >> 5);
   const int M = p.M, N = p.N;
   int64_t ldc = p.ldc;
-  void* Cout = p.C;
-  bool accumulate = EPI == kEpiAccumF32;
+  void* Cout = p.t.C[grp];
+  void* aux = p.t.aux[grp];
+  const uint16_t* bias = p.t.bias[grp];
+  bool accumulate = EPI == kEpiAccumF32 && !GSUM;  // (the group sum already holds C)
   if (slice > 0) {  // a K-split partial: plain float32 store
-    Cout = p.part + (int64_t)(slice - 1) * p.part_stride;
+    Cout = p.part + ((int64_t)grp * (p.slices - 1) + slice - 1) * p.part_stride;
     ldc = N;
     accumulate = false;
   }
@@ -401,7 +496,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
       for (int gq = 0; gq < 4; ++gq) {
         const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
         u32x2_t bb = u32x2_t{0u, 0u};
-        if (p.bias && n < N) bb = *reinterpret_cast<const u32x2_t*>(p.bias + n);
+        if (bias && n < N) bb = *reinterpret_cast<const u32x2_t*>(bias + n);
         bias4[j][gq] = f32x4_t{bf16_bits_to_f32(bb[0] & 0xFFFFu), bf16_bits_to_f32(bb[0] >> 16),
                                bf16_bits_to_f32(bb[1] & 0xFFFFu), bf16_bits_to_f32(bb[1] >> 16)};
       }
@@ -426,7 +521,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
               aux2[j][gq] = u32x2_t{0u, 0u};
               if (ok)
                 aux2[j][gq] =
-                    *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(p.aux) + row + n);
+                    *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(aux) + row + n);
             } else {
               old4[j][gq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
               if (ok && accumulate)
@@ -441,8 +536,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
           const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
           if (G && (!mrow || n >= N)) continue;
           const int64_t idx = row + n;
-          f32x4_t v = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
-                              acc[i][j][4 * gq + 3]};
+          f32x4_t v;
+          if constexpr (GSUM)
+            v = f32x4_t{z[i][j][4 * gq], z[i][j][4 * gq + 1], z[i][j][4 * gq + 2], z[i][j][4 * gq + 3]};
+          else
+            v = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                        acc[i][j][4 * gq + 3]};
           if constexpr (kBias) {
             v += bias4[j][gq];
             if constexpr (EPI == kEpiBiasGelu) {
@@ -460,7 +559,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
               og[0] = f32_to_bf16_bits(g[0]) | (f32_to_bf16_bits(g[1]) << 16);
               og[1] = f32_to_bf16_bits(g[2]) | (f32_to_bf16_bits(g[3]) << 16);
               *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = oy;
-              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.aux) + idx) = og;
+              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(aux) + idx) = og;
             }
           } else if constexpr (EPI == kEpiMulAux) {
             const u32x2_t gg = aux2[j][gq];
@@ -485,18 +584,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
     epilogue(std::true_type{});
 }
 
+// A group sum holds two accumulator sets per wave: tiles with at most 4
+// fragments per wave.
+constexpr bool tile_allows_group_sum(int t) {
+  return (kTiles[t].bm / kTiles[t].wm / 32) * (kTiles[t].bn / kTiles[t].wn / 32) <= 4;
+}
+
 // Launch one tile configuration of one layout (p.tiles_m / p.tiles_n set).
-template <int LAYOUT, int T, bool KTAIL>
+template <int LAYOUT, int T, bool KTAIL, bool GSUM>
 hipError_t launch_bf16_tile(const GemmParams& p, Epilogue epi, hipStream_t s) {
   constexpr TileCfg c = kTiles[T];
-  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)p.slices),
-      block(c.wm * c.wn * 64);
+  const unsigned copies = GSUM ? 1u : (unsigned)p.groups * (unsigned)p.slices;
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n * copies), block(c.wm * c.wn * 64);
   bool done = false;
   [&]<int... e>(std::integer_sequence<int, e...>) {
     (([&] {
-       if constexpr (layout_has_epi(LAYOUT, e)) {
+       if constexpr (layout_has_epi(LAYOUT, e) && (!GSUM || e == kEpiStoreF32 || e == kEpiAccumF32)) {
          if (epi == e) {
-           hipLaunchKernelGGL((gemm_bf16_kernel<e, LAYOUT, c.bm, c.bn, c.wm, c.wn, c.nbuf, KTAIL>),
+           hipLaunchKernelGGL((gemm_bf16_kernel<e, LAYOUT, c.bm, c.bn, c.wm, c.wn, c.nbuf, KTAIL, GSUM>),
                               grid, block, 0, s, p);
            done = true;
          }
@@ -507,26 +612,44 @@ hipError_t launch_bf16_tile(const GemmParams& p, Epilogue epi, hipStream_t s) {
   return done ? hipGetLastError() : hipErrorInvalidValue;
 }
 
-// K % 32 != 0 runs on the ragged-K variant of one tile (kTailTile) only.
+// K % 32 != 0 runs on the ragged-K variant of one tile (kTailTile) only; the
+// group sum is compiled for the row-step layouts (NN, NT).
 constexpr int kTailTile = 8;
 
 template <int LAYOUT>
-hipError_t launch_bf16_layout_tile(int tile, const GemmParams& p, Epilogue epi, hipStream_t s) {
-  if (p.K % 32) return tile == kTailTile ? launch_bf16_tile<LAYOUT, kTailTile, true>(p, epi, s)
-                                         : hipErrorInvalidValue;
+hipError_t launch_bf16_layout_tile(int tile, const GemmParams& p, Epilogue epi, bool gsum,
+                                   hipStream_t s) {
+  constexpr bool kHasGsum = LAYOUT != kTN;
+  if (p.K % 32) {
+    if (tile != kTailTile) return hipErrorInvalidValue;
+    if (gsum) {
+      if constexpr (kHasGsum) return launch_bf16_tile<LAYOUT, kTailTile, true, true>(p, epi, s);
+      return hipErrorInvalidValue;
+    }
+    return launch_bf16_tile<LAYOUT, kTailTile, true, false>(p, epi, s);
+  }
   hipError_t r = hipErrorInvalidValue;
   [&]<int... t>(std::integer_sequence<int, t...>) {
-    ((tile == t ? (r = launch_bf16_tile<LAYOUT, t, false>(p, epi, s), 0) : 0), ...);
+    (([&] {
+       if (tile != t) return;
+       if (!gsum) {
+         r = launch_bf16_tile<LAYOUT, t, false, false>(p, epi, s);
+       } else if constexpr (kHasGsum && tile_allows_group_sum(t)) {
+         r = launch_bf16_tile<LAYOUT, t, false, true>(p, epi, s);
+       }
+     }()),
+     ...);
   }(std::make_integer_sequence<int, kNumTiles>{});
   return r;
 }
 
-// Per-layout entry points (one translation unit each), and the launcher that
-// splits a large problem into launches of at most kMaxTilesPerLaunch tiles.
-hipError_t launch_bf16_nn(int tile, const GemmParams& p, Epilogue epi, hipStream_t s);
-hipError_t launch_bf16_nt(int tile, const GemmParams& p, Epilogue epi, hipStream_t s);
-hipError_t launch_bf16_tn(int tile, const GemmParams& p, Epilogue epi, hipStream_t s);
+// Per-layout entry points (one translation unit each).
+hipError_t launch_bf16_nn(int tile, const GemmParams& p, Epilogue epi, bool gsum, hipStream_t s);
+hipError_t launch_bf16_nt(int tile, const GemmParams& p, Epilogue epi, bool gsum, hipStream_t s);
+hipError_t launch_bf16_tn(int tile, const GemmParams& p, Epilogue epi, bool gsum, hipStream_t s);
+// Launch with an explicit tile, and the tile the library picks.
 hipError_t launch_gemm_bf16_tile(int tile, const GemmArgs& g, hipStream_t s);
-int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_bf16_batch_tile(int tile, const GemmBatch& b, hipStream_t s);
+int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K, int groups, bool group_sum);
 
 }  // namespace tpmlp

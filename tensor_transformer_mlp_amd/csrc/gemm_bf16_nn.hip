@@ -3,8 +3,8 @@
 
 namespace tpmlp {
 
-hipError_t launch_bf16_nn(int tile, const GemmParams& p, Epilogue epi, hipStream_t s) {
-  return launch_bf16_layout_tile<kNN>(tile, p, epi, s);
+hipError_t launch_bf16_nn(int tile, const GemmParams& p, Epilogue epi, bool gsum, hipStream_t s) {
+  return launch_bf16_layout_tile<kNN>(tile, p, epi, gsum, s);
 }
 
 }  // namespace tpmlp

@@ -207,4 +207,15 @@ hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
   return hipSuccess;
 }
 
+hipError_t launch_gemm_f32_batch(const GemmBatch& b, hipStream_t s) {
+  for (int g = 0; g < b.groups; ++g) {
+    GemmArgs a{b.A[g], b.B[g], b.bias[g], b.group_sum ? b.C[0] : b.C[g], b.aux[g], b.M, b.N, b.K,
+               b.lda, b.ldb, b.ldc, b.layout, b.epi};
+    if (b.group_sum && g > 0) a.epi = kEpiAccumF32;  // C[0] += A[g] B[g], in group order
+    const hipError_t e = launch_gemm_f32(a, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace tpmlp

@@ -66,97 +66,138 @@ bool any_overlap(const Regions& outs, const Regions& ins) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
 
-hipError_t gemm(const GemmArgs& g, int dtype, hipStream_t s) {
-  return dtype == TP_BF16 ? tpmlp::launch_gemm_bf16(g, s) : tpmlp::launch_gemm_f32(g, s);
+using tpmlp::GemmBatch;
+using tpmlp::kMaxGroups;
+
+// The shards of a step are launched together in batches of up to kMaxGroups.
+int batch_size(int k) { return k < kMaxGroups ? k : kMaxGroups; }
+
+GemmBatch batch(int n, tpmlp::Layout layout, tpmlp::Epilogue epi, int64_t M, int64_t N, int64_t K,
+                int64_t lda, int64_t ldb) {
+  GemmBatch b{};
+  b.groups = n;
+  b.group_sum = false;
+  b.M = M;
+  b.N = N;
+  b.K = K;
+  b.lda = lda;
+  b.ldb = ldb;
+  b.ldc = N;
+  b.layout = layout;
+  b.epi = epi;
+  return b;
 }
 
-GemmArgs args(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
-              int64_t ldb, tpmlp::Layout layout, tpmlp::Epilogue epi) {
-  GemmArgs g;
-  g.A = A;
-  g.B = B;
-  g.bias = nullptr;
-  g.C = C;
-  g.aux = nullptr;
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  g.lda = lda;
-  g.ldb = ldb;
-  g.ldc = N;
-  g.layout = layout;
-  g.epi = epi;
-  return g;
+int run(const GemmBatch& b, int dtype, hipStream_t s) {
+  return hip_status(dtype == TP_BF16 ? tpmlp::launch_gemm_bf16_batch(b, s)
+                                     : tpmlp::launch_gemm_f32_batch(b, s));
 }
 
-// The steps, after validation.
+// The steps, after validation; arrays hold the n shards of one batch.
 // Y_i (and G_i) = act(X W_i + b_i): [M, H] x [H, Fk], both row-major.
-int col_step(const void* X, const void* W_i, const void* b_i, void* Y_i, void* G_i, int64_t M,
-             int64_t H, int64_t Fk, int dtype, hipStream_t s) {
-  GemmArgs g = args(X, W_i, Y_i, M, Fk, H, H, Fk, tpmlp::kNN,
-                    G_i ? tpmlp::kEpiBiasGeluSave : tpmlp::kEpiBiasGelu);
-  g.bias = b_i;
-  g.aux = G_i;
-  return hip_status(gemm(g, dtype, s));
+int col_steps(const void* X, const void* const* W, const void* const* b, void* const* Y,
+              void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype, hipStream_t s) {
+  GemmBatch g = batch(n, tpmlp::kNN, G ? tpmlp::kEpiBiasGeluSave : tpmlp::kEpiBiasGelu, M, Fk, H, H, Fk);
+  for (int i = 0; i < n; ++i) {
+    g.A[i] = X;
+    g.B[i] = W[i];
+    g.bias[i] = b ? b[i] : nullptr;
+    g.C[i] = Y[i];
+    g.aux[i] = G ? G[i] : nullptr;
+  }
+  return run(g, dtype, s);
 }
 
-// Z_i (+)= Y_i V_i: [M, Fk] x [Fk, H].
-int row_step(const void* Y_i, const void* V_i, float* Z_i, int64_t M, int64_t Fk, int64_t H,
-             int dtype, bool accumulate, hipStream_t s) {
-  return hip_status(gemm(args(Y_i, V_i, Z_i, M, H, Fk, Fk, H, tpmlp::kNN,
-                              accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32),
-                         dtype, s));
+// Z_i (+)= Y_i V_i: [M, Fk] x [Fk, H], one output per shard (sum == false),
+// or Z (+)= sum_i Y_i V_i in shard order into Z[0] (sum == true).
+int row_steps(const void* const* Y, const void* const* V, float* const* Z, int n, bool sum,
+              int64_t M, int64_t Fk, int64_t H, int dtype, bool accumulate, hipStream_t s) {
+  GemmBatch g = batch(n, tpmlp::kNN, accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32, M, H, Fk,
+                      Fk, H);
+  g.group_sum = sum;
+  for (int i = 0; i < n; ++i) {
+    g.A[i] = Y[i];
+    g.B[i] = V[i];
+    g.C[i] = sum ? Z[0] : Z[i];
+  }
+  return run(g, dtype, s);
 }
 
 // dA_i = (dZ V_i^T) * G_i: [M, H] x ([Fk, H] read as its transpose).
-int act_grad_step(const void* dZ, const void* V_i, const void* G_i, void* dA_i, int64_t M,
-                  int64_t H, int64_t Fk, int dtype, hipStream_t s) {
-  GemmArgs g = args(dZ, V_i, dA_i, M, Fk, H, H, H, tpmlp::kNT, tpmlp::kEpiMulAux);
-  g.aux = const_cast<void*>(G_i);
-  return hip_status(gemm(g, dtype, s));
+int act_grad_steps(const void* dZ, const void* const* V, const void* const* G, void* const* dA, int n,
+                   int64_t M, int64_t H, int64_t Fk, int dtype, hipStream_t s) {
+  GemmBatch g = batch(n, tpmlp::kNT, tpmlp::kEpiMulAux, M, Fk, H, H, H);
+  for (int i = 0; i < n; ++i) {
+    g.A[i] = dZ;
+    g.B[i] = V[i];
+    g.C[i] = dA[i];
+    g.aux[i] = const_cast<void*>(G[i]);
+  }
+  return run(g, dtype, s);
 }
 
-// Weight-gradient workspace: the larger K-split of the two weight GEMMs and
-// the column-sum partials, side by side.
-size_t split_bytes(int64_t M, int64_t H, int64_t Fk, int dtype) {
+// Weight-gradient workspace for a batch of `groups` shards: the larger
+// K-split of the two weight GEMMs, then the column-sum partials of one shard.
+size_t split_bytes(int groups, int64_t M, int64_t H, int64_t Fk, int dtype) {
   const bool bf16 = dtype == TP_BF16;
-  const size_t a = tpmlp::gemm_split_workspace_bytes(bf16, Fk, H, M);
-  const size_t b = tpmlp::gemm_split_workspace_bytes(bf16, H, Fk, M);
-  return a > b ? a : b;
+  const size_t a = tpmlp::gemm_split_workspace_bytes(bf16, groups, Fk, H, M);
+  const size_t b = tpmlp::gemm_split_workspace_bytes(bf16, groups, H, Fk, M);
+  return round_up(a > b ? a : b, kWsAlign);
 }
 size_t colsum_bytes(int64_t M, int64_t Fk) {
   return round_up(size_t(tpmlp::colsum_partials_floats(M, Fk)) * 4, kWsAlign);
 }
-size_t grad_weight_ws(int64_t M, int64_t H, int64_t Fk, int dtype) {
-  return round_up(split_bytes(M, H, Fk, dtype), kWsAlign) + colsum_bytes(M, Fk);
+size_t grad_weight_ws(int groups, int64_t M, int64_t H, int64_t Fk, int dtype) {
+  return split_bytes(groups, M, H, Fk, dtype) + colsum_bytes(M, Fk);
 }
 
 // dV_i (+)= Y_i^T dZ: ([M, Fk] read as its transpose) x [M, H], K = M.
-int row_weight_step(const void* Y_i, const void* dZ, float* dV_i, int64_t M, int64_t Fk, int64_t H,
-                    int dtype, void* ws, bool accumulate, hipStream_t s) {
-  const GemmArgs g = args(Y_i, dZ, dV_i, Fk, H, M, Fk, H, tpmlp::kTN,
-                          accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32);
+int row_weight_steps(const void* const* Y, const void* dZ, float* const* dV, int n, int64_t M,
+                     int64_t Fk, int64_t H, int dtype, void* ws, bool accumulate, hipStream_t s) {
+  GemmBatch g = batch(n, tpmlp::kTN, accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32, Fk, H, M,
+                      Fk, H);
+  for (int i = 0; i < n; ++i) {
+    g.A[i] = Y[i];
+    g.B[i] = dZ;
+    g.C[i] = dV[i];
+  }
   return hip_status(tpmlp::launch_gemm_split(g, dtype == TP_BF16, ws, s));
 }
 
 // dW_i (+)= X^T dA_i and db_i (+)= colsum(dA_i).
-int col_weight_step(const void* X, const void* dA_i, float* dW_i, float* db_i, int64_t M,
-                    int64_t H, int64_t Fk, int dtype, void* ws, bool accumulate, hipStream_t s) {
-  const GemmArgs g = args(X, dA_i, dW_i, H, Fk, M, H, Fk, tpmlp::kTN,
-                          accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32);
+int col_weight_steps(const void* X, const void* const* dA, float* const* dW, float* const* db, int n,
+                     int64_t M, int64_t H, int64_t Fk, int dtype, void* ws, bool accumulate,
+                     hipStream_t s) {
+  GemmBatch g = batch(n, tpmlp::kTN, accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32, H, Fk, M,
+                      H, Fk);
+  for (int i = 0; i < n; ++i) {
+    g.A[i] = X;
+    g.B[i] = dA[i];
+    g.C[i] = dW[i];
+  }
   int st = hip_status(tpmlp::launch_gemm_split(g, dtype == TP_BF16, ws, s));
-  if (st || !db_i) return st;
-  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                             round_up(split_bytes(M, H, Fk, dtype), kWsAlign));
-  return hip_status(tpmlp::launch_colsum(dA_i, dtype == TP_BF16, M, Fk, db_i, accumulate, partials, s));
+  if (st || !db) return st;
+  float* partials =
+      reinterpret_cast<float*>(static_cast<char*>(ws) + split_bytes(n, M, H, Fk, dtype));
+  for (int i = 0; i < n && !st; ++i)
+    st = hip_status(
+        tpmlp::launch_colsum(dA[i], dtype == TP_BF16, M, Fk, db[i], accumulate, partials, s));
+  return st;
 }
 
-// dX_i (+)= dA_i W_i^T: [M, Fk] x ([H, Fk] read as its transpose).
-int input_grad_step(const void* dA_i, const void* W_i, float* dX_i, int64_t M, int64_t Fk,
-                    int64_t H, int dtype, bool accumulate, hipStream_t s) {
-  return hip_status(gemm(args(dA_i, W_i, dX_i, M, H, Fk, Fk, Fk, tpmlp::kNT,
-                              accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32),
-                         dtype, s));
+// dX_i (+)= dA_i W_i^T: [M, Fk] x ([H, Fk] read as its transpose); one output
+// per shard, or the shard-order sum into dX[0] (sum == true).
+int input_grad_steps(const void* const* dA, const void* const* W, float* const* dX, int n, bool sum,
+                     int64_t M, int64_t Fk, int64_t H, int dtype, bool accumulate, hipStream_t s) {
+  GemmBatch g = batch(n, tpmlp::kNT, accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32, M, H, Fk,
+                      Fk, Fk);
+  g.group_sum = sum;
+  for (int i = 0; i < n; ++i) {
+    g.A[i] = dA[i];
+    g.B[i] = W[i];
+    g.C[i] = sum ? dX[0] : dX[i];
+  }
+  return run(g, dtype, s);
 }
 
 }  // namespace
@@ -197,7 +238,7 @@ int tp_mlp_col_gelu(const void* X, const void* W_i, const void* b_i, void* Y_i, 
   in.add(b_i, size_t(Fk) * e);
   out.add(Y_i, size_t(M) * size_t(Fk) * e);
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return col_step(X, W_i, b_i, Y_i, nullptr, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+  return col_steps(X, &W_i, &b_i, &Y_i, nullptr, 1, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
 }
 
 int tp_mlp_col_gelu_save(const void* X, const void* W_i, const void* b_i, void* Y_i, void* G_i,
@@ -218,7 +259,7 @@ int tp_mlp_col_gelu_save(const void* X, const void* W_i, const void* b_i, void* 
   out.add(Y_i, size_t(M) * size_t(Fk) * e);
   out.add(G_i, size_t(M) * size_t(Fk) * e);
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return col_step(X, W_i, b_i, Y_i, G_i, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+  return col_steps(X, &W_i, &b_i, &Y_i, &G_i, 1, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
 }
 
 int tp_mlp_row_partial(const void* Y_i, const void* V_i, float* Z_i, int64_t M, int64_t Fk,
@@ -236,8 +277,8 @@ int tp_mlp_row_partial(const void* Y_i, const void* V_i, float* Z_i, int64_t M, 
   in.add(V_i, size_t(Fk) * size_t(H) * e);
   out.add(Z_i, size_t(M) * size_t(H) * 4);
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return row_step(Y_i, V_i, Z_i, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
-                  static_cast<hipStream_t>(stream));
+  return row_steps(&Y_i, &V_i, &Z_i, 1, false, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
+                   static_cast<hipStream_t>(stream));
 }
 
 int tp_shard_reduce(const float* const* Z_parts, int k, float* Z, int64_t n, void* stream) {
@@ -262,7 +303,7 @@ size_t tp_mlp_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dtype
   if (k < 1 || k > TP_MAX_SHARDS || check_dtype(dtype) || check_dims(M, H, Fk)) return 0;
   if (flags & ~TP_FUSED_ACCUM) return 0;
   if (M == 0) return 0;
-  size_t bytes = round_up(size_t(M) * size_t(Fk) * elt_size(dtype), kWsAlign);
+  size_t bytes = size_t(batch_size(k)) * round_up(size_t(M) * size_t(Fk) * elt_size(dtype), kWsAlign);
   if (!(flags & TP_FUSED_ACCUM)) bytes += size_t(k - 1) * round_up(size_t(M) * size_t(H) * 4, kWsAlign);
   return bytes;
 }
@@ -302,27 +343,33 @@ int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const*
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fused = (flags & TP_FUSED_ACCUM) != 0;
   char* ws = static_cast<char*>(workspace);
-  void* Y = ws;
+  const int G = batch_size(k);
   const size_t y_bytes = round_up(size_t(M) * size_t(Fk) * e, kWsAlign);
   const size_t part_bytes = round_up(nz, kWsAlign);
+  void* Y[kMaxGroups];
+  for (int j = 0; j < G; ++j) Y[j] = ws + size_t(j) * y_bytes;
+  char* part_base = ws + size_t(G) * y_bytes;
   const float* parts[TP_MAX_SHARDS];
+  float* P[kMaxGroups];
 
-  for (int i = 0; i < k; ++i) {
-    // Column-parallel linear + bias + GeLU of shard i into the shared Y buffer.
-    if ((st = col_step(X, W[i], b ? b[i] : nullptr, Y, nullptr, M, H, Fk, dtype, s))) return st;
-    // Row-parallel partial of shard i.
-    float* P;
-    bool accumulate = false;
-    if (i == 0) {
-      P = Z;
-    } else if (fused) {
-      P = Z;
-      accumulate = true;
+  for (int i0 = 0; i0 < k; i0 += G) {
+    const int n = k - i0 < G ? k - i0 : G;
+    // Column-parallel linear + bias + GeLU of shards i0 .. i0 + n - 1.
+    if ((st = col_steps(X, W + i0, b ? b + i0 : nullptr, Y, nullptr, n, M, H, Fk, dtype, s))) return st;
+    if (fused) {
+      // Row-parallel products of the batch, summed in shard order into Z
+      // (after the previous batches' sum).
+      P[0] = Z;
+      if ((st = row_steps(Y, V + i0, P, n, true, M, Fk, H, dtype, i0 > 0, s))) return st;
     } else {
-      P = reinterpret_cast<float*>(ws + y_bytes + size_t(i - 1) * part_bytes);
+      // Row-parallel partials: P_0 in Z, the rest in the workspace.
+      for (int j = 0; j < n; ++j) {
+        const int i = i0 + j;
+        P[j] = i == 0 ? Z : reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
+        parts[i] = P[j];
+      }
+      if ((st = row_steps(Y, V + i0, P, n, false, M, Fk, H, dtype, false, s))) return st;
     }
-    parts[i] = P;
-    if ((st = row_step(Y, V[i], P, M, Fk, H, dtype, accumulate, s))) return st;
   }
   if (!fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
   return TP_OK;
@@ -343,12 +390,12 @@ int tp_mlp_grad_act(const void* dZ, const void* V_i, const void* G_i, void* dA_i
   if (dA_i != G_i) in.add(G_i, size_t(M) * size_t(Fk) * e);
   out.add(dA_i, size_t(M) * size_t(Fk) * e);
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return act_grad_step(dZ, V_i, G_i, dA_i, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+  return act_grad_steps(dZ, &V_i, &G_i, &dA_i, 1, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
 }
 
 size_t tp_mlp_grad_weight_workspace_bytes(int64_t M, int64_t H, int64_t Fk, int dtype) {
   if (check_dtype(dtype) || check_dims(M, H, Fk)) return 0;
-  return grad_weight_ws(M, H, Fk, dtype);
+  return grad_weight_ws(1, M, H, Fk, dtype);
 }
 
 int tp_mlp_grad_row_weight(const void* Y_i, const void* dZ, float* dV_i, int64_t M, int64_t Fk,
@@ -360,7 +407,7 @@ int tp_mlp_grad_row_weight(const void* Y_i, const void* dZ, float* dV_i, int64_t
   if ((st = check_dims(M, H, Fk))) return st;
   if (!dV_i || (M > 0 && (!Y_i || !dZ))) return TP_ERR_NULL;
   if (!aligned16(Y_i) || !aligned16(dZ) || !aligned16(dV_i)) return TP_ERR_ALIGN;
-  const size_t need = grad_weight_ws(M, H, Fk, dtype);
+  const size_t need = grad_weight_ws(1, M, H, Fk, dtype);
   if (need && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return TP_ERR_ALIGN;
   const size_t e = elt_size(dtype);
@@ -370,7 +417,7 @@ int tp_mlp_grad_row_weight(const void* Y_i, const void* dZ, float* dV_i, int64_t
   out.add(dV_i, size_t(Fk) * size_t(H) * 4);
   out.add(workspace, need);
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return row_weight_step(Y_i, dZ, dV_i, M, Fk, H, dtype, workspace,
+  return row_weight_steps(&Y_i, dZ, &dV_i, 1, M, Fk, H, dtype, workspace,
                          (flags & TP_GRAD_ACCUMULATE) != 0, static_cast<hipStream_t>(stream));
 }
 
@@ -384,7 +431,7 @@ int tp_mlp_grad_col_weight(const void* X, const void* dA_i, float* dW_i, float* 
   if (!dW_i || (M > 0 && (!X || !dA_i))) return TP_ERR_NULL;
   if (!aligned16(X) || !aligned16(dA_i) || !aligned16(dW_i) || (db_i && !aligned16(db_i)))
     return TP_ERR_ALIGN;
-  const size_t need = grad_weight_ws(M, H, Fk, dtype);
+  const size_t need = grad_weight_ws(1, M, H, Fk, dtype);
   if (need && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return TP_ERR_ALIGN;
   const size_t e = elt_size(dtype);
@@ -395,7 +442,7 @@ int tp_mlp_grad_col_weight(const void* X, const void* dA_i, float* dW_i, float* 
   out.add(db_i, size_t(Fk) * 4);
   out.add(workspace, need);
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return col_weight_step(X, dA_i, dW_i, db_i, M, H, Fk, dtype, workspace,
+  return col_weight_steps(X, &dA_i, &dW_i, db_i ? &db_i : nullptr, 1, M, H, Fk, dtype, workspace,
                          (flags & TP_GRAD_ACCUMULATE) != 0, static_cast<hipStream_t>(stream));
 }
 
@@ -414,7 +461,7 @@ int tp_mlp_grad_input_partial(const void* dA_i, const void* W_i, float* dX_i, in
   in.add(W_i, size_t(H) * size_t(Fk) * e);
   out.add(dX_i, size_t(M) * size_t(H) * 4);
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return input_grad_step(dA_i, W_i, dX_i, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
+  return input_grad_steps(&dA_i, &W_i, &dX_i, 1, false, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
                          static_cast<hipStream_t>(stream));
 }
 
@@ -423,7 +470,8 @@ size_t tp_mlp_backward_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, 
   if (k < 1 || k > TP_MAX_SHARDS || check_dtype(dtype) || check_dims(M, H, Fk)) return 0;
   if (flags & ~(TP_FUSED_ACCUM | TP_GRAD_ACCUMULATE)) return 0;
   const size_t act = round_up(size_t(M) * size_t(Fk) * elt_size(dtype), kWsAlign);
-  size_t bytes = 2 * act + grad_weight_ws(M, H, Fk, dtype);
+  const int G = batch_size(k);
+  size_t bytes = 2 * size_t(G) * act + grad_weight_ws(G, M, H, Fk, dtype);
   if (!(flags & TP_FUSED_ACCUM)) bytes += size_t(k - 1) * round_up(size_t(M) * size_t(H) * 4, kWsAlign);
   return bytes;
 }
@@ -470,35 +518,43 @@ int tp_mlp_shard_backward(const void* X, const void* const* W, const void* const
   const bool fused = (flags & TP_FUSED_ACCUM) != 0;
   const bool acc_grads = (flags & TP_GRAD_ACCUMULATE) != 0;
   char* ws = static_cast<char*>(workspace);
+  const int G = batch_size(k);
   const size_t act = round_up(size_t(M) * size_t(Fk) * e, kWsAlign);
-  void* Y = ws;
-  void* G = ws + act;  // G_i, then dA_i in place
-  void* wws = ws + 2 * act;
+  void* Y[kMaxGroups];
+  void* Gb[kMaxGroups];  // G_i, then dA_i in place
+  for (int j = 0; j < G; ++j) {
+    Y[j] = ws + size_t(j) * act;
+    Gb[j] = ws + size_t(G + j) * act;
+  }
+  void* wws = ws + 2 * size_t(G) * act;
   const size_t part_bytes = round_up(nx, kWsAlign);
-  char* part_base = ws + 2 * act + grad_weight_ws(M, H, Fk, dtype);
+  char* part_base = ws + 2 * size_t(G) * act + grad_weight_ws(G, M, H, Fk, dtype);
   const float* parts[TP_MAX_SHARDS];
+  float* P[kMaxGroups];
 
-  for (int i = 0; i < k; ++i) {
+  for (int i0 = 0; i0 < k; i0 += G) {
+    const int n = k - i0 < G ? k - i0 : G;
     if (M > 0) {
-      if ((st = col_step(X, W[i], b ? b[i] : nullptr, Y, G, M, H, Fk, dtype, s))) return st;
-      if ((st = act_grad_step(dZ, V[i], G, G, M, H, Fk, dtype, s))) return st;
+      // Recompute Y_i and G_i, then dA_i = (dZ V_i^T) * G_i in place.
+      if ((st = col_steps(X, W + i0, b ? b + i0 : nullptr, Y, Gb, n, M, H, Fk, dtype, s))) return st;
+      if ((st = act_grad_steps(dZ, V + i0, Gb, Gb, n, M, H, Fk, dtype, s))) return st;
     }
-    if ((st = row_weight_step(Y, dZ, dV[i], M, Fk, H, dtype, wws, acc_grads, s))) return st;
-    if ((st = col_weight_step(X, G, dW[i], db ? db[i] : nullptr, M, H, Fk, dtype, wws, acc_grads, s)))
+    if ((st = row_weight_steps(Y, dZ, dV + i0, n, M, Fk, H, dtype, wws, acc_grads, s))) return st;
+    if ((st = col_weight_steps(X, Gb, dW + i0, db ? db + i0 : nullptr, n, M, H, Fk, dtype, wws,
+                               acc_grads, s)))
       return st;
     if (M == 0) continue;
-    float* P;
-    bool accumulate = false;
-    if (i == 0) {
-      P = dX;
-    } else if (fused) {
-      P = dX;
-      accumulate = true;
+    if (fused) {
+      P[0] = dX;
+      if ((st = input_grad_steps(Gb, W + i0, P, n, true, M, Fk, H, dtype, i0 > 0, s))) return st;
     } else {
-      P = reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
+      for (int j = 0; j < n; ++j) {
+        const int i = i0 + j;
+        P[j] = i == 0 ? dX : reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
+        parts[i] = P[j];
+      }
+      if ((st = input_grad_steps(Gb, W + i0, P, n, false, M, Fk, H, dtype, false, s))) return st;
     }
-    parts[i] = P;
-    if ((st = input_grad_step(G, W[i], P, M, Fk, H, dtype, accumulate, s))) return st;
   }
   if (M > 0 && !fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, dX, M * H, s));
   return TP_OK;

@@ -37,22 +37,47 @@ struct GemmArgs {
   Epilogue epi;
 };
 
+// A batch of same-shaped GEMMs (the per-shard GEMMs of one step), launched
+// together: group g computes C[g] = epi(A[g] B[g]) with bias[g] and aux[g]
+// (entries may repeat, such as a shared X).  group_sum: instead, C[0] =
+// sum_g A[g] B[g] with one float32 accumulator per group added in group
+// order (kEpiAccumF32: C[0] + sum, in the same order), which is bit-identical
+// to storing every product and summing them left to right.
+constexpr int kMaxGroups = 16;
+struct GemmBatch {
+  const void* A[kMaxGroups];
+  const void* B[kMaxGroups];
+  const void* bias[kMaxGroups];
+  void* C[kMaxGroups];
+  void* aux[kMaxGroups];
+  int groups;
+  bool group_sum;
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc;
+  Layout layout;
+  Epilogue epi;
+};
+
 // bf16 operands (raw 16-bit patterns), float32 accumulate.  Requires the
 // contiguous dimension of A, B and C to be a multiple of 8 elements, every
 // leading dimension at most 2^22 elements, and 16-byte aligned pointers.
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_bf16_batch(const GemmBatch& b, hipStream_t s);
 
-// float32 operands, float32 accumulate (same rules).
+// float32 operands, float32 accumulate (same rules).  Batches run group by
+// group (a group sum accumulates into C[0] in group order).
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_f32_batch(const GemmBatch& b, hipStream_t s);
 
-// K-split of a GEMM with a float32 output (kEpiStoreF32 / kEpiAccumF32) whose
-// output has too few tiles to fill the chip (the weight gradients, where K is
-// the token count): slice 0 writes (or adds into) C, slices 1..S-1 write
-// float32 partials into `ws`, and the slices are then added into C in slice
-// order, so the result does not depend on timing.
-int gemm_k_slices(bool bf16, int64_t M, int64_t N, int64_t K);
-size_t gemm_split_workspace_bytes(bool bf16, int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_split(const GemmArgs& g, bool bf16, void* ws, hipStream_t s);
+// K-split of the GEMMs of a batch with a float32 output (kEpiStoreF32 /
+// kEpiAccumF32) whose output has too few tiles to fill the chip (the weight
+// gradients, where K is the token count): slice 0 writes (or adds into)
+// C[g], slices 1..S-1 write float32 partials into `ws`, and each group's
+// slices are then added into C[g] in slice order, so the result does not
+// depend on timing.  C[g] must be dense (ldc == N).
+int gemm_k_slices(bool bf16, int64_t tiles, int64_t K);
+size_t gemm_split_workspace_bytes(bool bf16, int groups, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_split(const GemmBatch& b, bool bf16, void* ws, hipStream_t s);
 
 // Z[e] = sum_i parts[i][e], i = 0..k-1 in order; Z may equal parts[0].
 hipError_t launch_shard_reduce(const float* const* parts, int k, float* Z, int64_t n,

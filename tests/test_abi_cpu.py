@@ -140,19 +140,21 @@ def test_shard_reduce_errors(L):
 
 def test_workspace_bytes(L):
     f = L.tp_mlp_workspace_bytes
-    # Y buffer (M*Fk*elt rounded to 256) + (k-1) fp32 partials of M*H
-    assert f(4, 8192, 768, 768, 1, 0) == 8192 * 768 * 2 + 3 * 8192 * 768 * 4
-    assert f(4, 8192, 768, 768, 1, 1) == 8192 * 768 * 2
-    assert f(2, 8, 64, 128, 0, 0) == 8 * 128 * 4 + 8 * 64 * 4
+    # one Y buffer per shard of a batch of min(k, 16) shards (M*Fk*elt rounded
+    # to 256), plus (k-1) fp32 partials of M*H unless fused
+    assert f(4, 8192, 768, 768, 1, 0) == 4 * 8192 * 768 * 2 + 3 * 8192 * 768 * 4
+    assert f(4, 8192, 768, 768, 1, 1) == 4 * 8192 * 768 * 2
+    assert f(2, 8, 64, 128, 0, 0) == 2 * 8 * 128 * 4 + 8 * 64 * 4
     assert f(1, 3, 8, 8, 1, 0) == 256
-    assert f(2, 3, 8, 8, 1, 0) == 256 + 256
+    assert f(2, 3, 8, 8, 1, 0) == 2 * 256 + 256
+    assert f(64, 3, 8, 8, 1, 1) == 16 * 256
     assert f(0, 8, 64, 128, 0, 0) == 0
     assert f(2, 8, 60, 128, 0, 0) == 0
     assert f(2, 8, 64, 128, 5, 0) == 0
     assert f(2, 8, 64, 128, 0, 4) == 0
     assert f(2, 0, 64, 128, 0, 0) == 0
     big = f(8, 32768, 8192, 4096, 1, 0)
-    assert big == 32768 * 4096 * 2 + 7 * 32768 * 8192 * 4
+    assert big == 8 * 32768 * 4096 * 2 + 7 * 32768 * 8192 * 4
 
 
 def test_shard_forward_errors(L):
@@ -298,16 +300,19 @@ def test_backward_workspace_bytes(L):
     f = L.tp_mlp_backward_workspace_bytes
     gw = L.tp_mlp_grad_weight_workspace_bytes
     for (k, M, H, Fk, dt) in [(4, 8192, 768, 768, 1), (8, 8192, 4096, 2048, 1), (2, 40, 64, 128, 0),
-                              (1, 3, 8, 8, 1)]:
+                              (1, 3, 8, 8, 1), (20, 64, 64, 64, 1)]:
         e = 2 if dt == 1 else 4
+        G = min(k, 16)
         act = -(-M * Fk * e // 256) * 256
         part = -(-M * H * 4 // 256) * 256
-        w = gw(M, H, Fk, dt)
-        assert w % 256 == 0
-        assert f(k, M, H, Fk, dt, 0) == 2 * act + w + (k - 1) * part
-        assert f(k, M, H, Fk, dt, 1) == 2 * act + w
-        assert f(k, M, H, Fk, dt, 3) == 2 * act + w
-    # the weight-gradient workspace covers the column-sum partials at least
+        lit = f(k, M, H, Fk, dt, 0)
+        fused = f(k, M, H, Fk, dt, 1)
+        assert lit - fused == (k - 1) * part
+        assert f(k, M, H, Fk, dt, 3) == fused
+        # two activation buffers per shard of a batch, then the weight-gradient
+        # workspace of the batch, which covers at least the single-shard one
+        assert fused >= 2 * G * act + gw(M, H, Fk, dt)
+        assert (fused - 2 * G * act) % 256 == 0
     assert gw(8192, 768, 768, 1) >= 768 * 4
     assert f(0, 8, 64, 128, 0, 0) == 0
     assert f(2, 8, 60, 128, 0, 0) == 0
