@@ -54,36 +54,37 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_bytes(kind, w, elt):
-    """Algorithmic HBM bytes of one launch of `kind` (each operand read once,
-    each result written once)."""
+def kernel_bytes(kind, w, elt, n):
+    """Algorithmic HBM bytes of one launch of `kind` over n shards (each
+    operand read once, each result written once; shared operands once)."""
     M, H, Fk, k = w.M, w.H, w.Fk, w.k
     table = {
-        "col_gelu": (M * H + H * Fk + Fk + M * Fk) * elt,
-        "row_partial": (M * Fk + Fk * H) * elt + M * H * 4,
-        "row_partial_accum": (M * Fk + Fk * H) * elt + 2 * M * H * 4,
+        "col_gelu": M * H * elt + n * (H * Fk + Fk + M * Fk) * elt,
+        "row_partial": n * ((M * Fk + Fk * H) * elt + M * H * 4),
+        "row_sum": n * (M * Fk + Fk * H) * elt + M * H * 4,
         "shard_reduce": (k + 1) * M * H * 4,
-        "col_gelu_save": (M * H + H * Fk + Fk + 2 * M * Fk) * elt,
-        "grad_act": (M * H + Fk * H + 2 * M * Fk) * elt,
-        "grad_row_weight": (M * Fk + M * H) * elt + Fk * H * 4,
-        "grad_col_weight": (M * H + M * Fk) * elt + (H * Fk + Fk) * 4,
-        "grad_input": (M * Fk + H * Fk) * elt + M * H * 4,
-        "grad_input_accum": (M * Fk + H * Fk) * elt + 2 * M * H * 4,
+        "col_gelu_save": M * H * elt + n * (H * Fk + Fk + 2 * M * Fk) * elt,
+        "grad_act": M * H * elt + n * (Fk * H + 2 * M * Fk) * elt,
+        "grad_row_weight": M * H * elt + n * (M * Fk * elt + Fk * H * 4),
+        "grad_col_weight": M * H * elt + n * (M * Fk * elt + (H * Fk + Fk) * 4),
+        "grad_input": n * ((M * Fk + H * Fk) * elt + M * H * 4),
+        "grad_input_sum": n * (M * Fk + H * Fk) * elt + M * H * 4,
     }
     return table[kind]
 
 
-def kernel_flops(kind, w):
+def kernel_flops(kind, w, n):
     if kind == "shard_reduce":
         return (w.k - 1) * w.M * w.H
-    return 2 * w.M * w.H * w.Fk
+    return n * 2 * w.M * w.H * w.Fk
 
 
-def time_kinds(kinds, launch, nlaunch, steps, warmup, w, elt):
+def time_kinds(kinds, launch, nlaunch, nshards, steps, warmup, w, elt):
     """Per-kind timing: each kind's launches of one step run back to back
     between one HIP event pair on the stream they are launched on; a spin
     kernel queued first keeps the GPU busy while the host enqueues, so no host
-    gap falls inside a pair.  Returns {kind: {avg_ms, ms_per_step, ...}}."""
+    gap falls inside a pair.  nshards[kind]: shards per launch.
+    Returns {kind: {avg_ms, ms_per_step, flop, bytes, ...}} per launch."""
     import numpy as np
     import torch
     stream = torch.cuda.current_stream()
@@ -109,11 +110,13 @@ def time_kinds(kinds, launch, nlaunch, steps, warmup, w, elt):
         if not d:
             continue
         avg = float(np.mean(d))
-        kern[kind] = {"launches_per_step": nlaunch[kind], "avg_ms": avg, "ms_per_step": avg * nlaunch[kind],
-                      "flop": kernel_flops(kind, w), "bytes": kernel_bytes(kind, w, elt)}
-        log("  %-18s %2d/step  avg %.4f ms  (%.4f ms/step)  %.1f TFLOP/s  %.0f GB/s" % (
-            kind, nlaunch[kind], avg, avg * nlaunch[kind], kernel_flops(kind, w) / avg / 1e9,
-            kernel_bytes(kind, w, elt) / avg / 1e6))
+        n = nshards[kind]
+        kern[kind] = {"launches_per_step": nlaunch[kind], "shards_per_launch": n, "avg_ms": avg,
+                      "ms_per_step": avg * nlaunch[kind], "flop": kernel_flops(kind, w, n),
+                      "bytes": kernel_bytes(kind, w, elt, n)}
+        log("  %-16s %2d/step x %2d shards  avg %.4f ms  (%.4f ms/step)  %.1f TFLOP/s  %.0f GB/s" % (
+            kind, nlaunch[kind], n, avg, avg * nlaunch[kind], kernel_flops(kind, w, n) / avg / 1e9,
+            kernel_bytes(kind, w, elt, n) / avg / 1e6))
     return kern
 
 
@@ -211,32 +214,36 @@ def main():
     if not bool(torch.isfinite(Z).all()):
         raise RuntimeError("non-finite output")
 
-    # Per-kernel pass: the kernels of one step through the per-kernel entry
-    # points, in the same launch configuration.
+    # Per-kernel pass: the launches of one step through the batched per-step
+    # entry points, in the same launch configuration as the step (the shards
+    # run in batches of up to TP_MAX_BATCH, one launch per step and batch).
     ks = args.kernel_steps or args.steps
-    Y = torch.empty(w.M, Fk, dtype=tdt, device=dev)
-    parts = [torch.empty(w.M, w.H, dtype=torch.float32, device=dev) for _ in range(w.k)]
-    kinds = ["col_gelu", "row_partial"] + (["row_partial_accum"] if fused and w.k > 1 else []) + \
-        (["shard_reduce"] if not fused and w.k > 1 else [])
-    nlaunch = {"col_gelu": w.k, "row_partial": 1 if fused else w.k, "row_partial_accum": w.k - 1,
+    G = min(w.k, tpm.TP_MAX_BATCH)
+    batches = [(i0, min(G, w.k - i0)) for i0 in range(0, w.k, G)]
+    Yb = [torch.empty(w.M, Fk, dtype=tdt, device=dev) for _ in range(G)]
+    parts = [Z] + [torch.empty(w.M, w.H, dtype=torch.float32, device=dev) for _ in range(w.k - 1)]
+    if fused:
+        kinds = ["col_gelu", "row_sum"]
+    else:
+        kinds = ["col_gelu", "row_partial"] + (["shard_reduce"] if w.k > 1 else [])
+    nlaunch = {"col_gelu": len(batches), "row_partial": len(batches), "row_sum": len(batches),
                "shard_reduce": 1}
+    nshards = {"col_gelu": G, "row_partial": G, "row_sum": G, "shard_reduce": w.k}
 
     def launch(kind):
-        if kind == "col_gelu":
-            for i in range(w.k):
-                tpm.tp_mlp_col_gelu(X, Ws[i], bs[i], Y_i=Y)
-        elif kind == "row_partial":
-            for i in range(nlaunch["row_partial"]):
-                tpm.tp_mlp_row_partial(Y, Vs[i], Z_i=Z if fused else parts[i])
-        elif kind == "row_partial_accum":
-            for i in range(1, w.k):
-                tpm.tp_mlp_row_partial(Y, Vs[i], Z_i=Z, accumulate=True)
-        else:
+        for i0, n in batches:
+            if kind == "col_gelu":
+                tpm.tp_mlp_col_gelu_shards(X, Ws[i0:i0 + n], bs[i0:i0 + n], Yb[:n])
+            elif kind == "row_partial":
+                tpm.tp_mlp_row_partial_shards(Yb[:n], Vs[i0:i0 + n], parts[i0:i0 + n])
+            elif kind == "row_sum":
+                tpm.tp_mlp_row_partial_shards(Yb[:n], Vs[i0:i0 + n], [Z], sum_shards=True, accumulate=i0 > 0)
+        if kind == "shard_reduce":
             tpm.tp_shard_reduce(parts, Z=Z)
 
-    kern = time_kinds(kinds, launch, nlaunch, ks, args.warmup, w, elt)
+    kern = time_kinds(kinds, launch, nlaunch, nshards, ks, args.warmup, w, elt)
     roof = roofline(kern, w, args.variant, w.dtype)
-    del Y, parts
+    del Yb, parts
 
     bwd = None
     if not args.no_backward:
@@ -253,8 +260,8 @@ def main():
         "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2),
         "config": dict(w.describe(), variant=args.variant, parallelism="tp%d shards on 1 GPU" % w.k),
         "roofline": roof,
-        "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"]}
-                    for k_, v in kern.items()},
+        "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],
+                         "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()},
         "cpu_baseline": cpu,
         "backward": bwd,
     }
@@ -301,45 +308,46 @@ def bench_backward(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt):
     if not bool(torch.isfinite(dX).all()):
         raise RuntimeError("non-finite backward output")
 
-    Y = torch.empty(M, Fk, dtype=tdt, device=dev)
-    G = torch.empty(M, Fk, dtype=tdt, device=dev)
-    parts = [torch.empty(M, H, dtype=torch.float32, device=dev) for _ in range(k)]
-    gws = torch.empty(max(tpm.tp_mlp_grad_weight_workspace_bytes(M, H, Fk, dt), 1), dtype=torch.uint8,
+    Gn = min(k, tpm.TP_MAX_BATCH)
+    batches = [(i0, min(Gn, k - i0)) for i0 in range(0, k, Gn)]
+    Y = [torch.empty(M, Fk, dtype=tdt, device=dev) for _ in range(Gn)]
+    Gb = [torch.empty(M, Fk, dtype=tdt, device=dev) for _ in range(Gn)]
+    parts = [dX] + [torch.empty(M, H, dtype=torch.float32, device=dev) for _ in range(k - 1)]
+    gws = torch.empty(max(tpm.tp_mlp_grad_weight_workspace_bytes_shards(Gn, M, H, Fk, dt), 1), dtype=torch.uint8,
                       device=dev)
-    kinds = ["col_gelu_save", "grad_act", "grad_row_weight", "grad_col_weight", "grad_input"] + \
-        (["grad_input_accum"] if fused and k > 1 else []) + (["shard_reduce"] if not fused and k > 1 else [])
-    nlaunch = {"col_gelu_save": k, "grad_act": k, "grad_row_weight": k, "grad_col_weight": k,
-               "grad_input": 1 if fused else k, "grad_input_accum": k - 1, "shard_reduce": 1}
+    kinds = ["col_gelu_save", "grad_act", "grad_row_weight", "grad_col_weight"] + \
+        (["grad_input_sum"] if fused else ["grad_input"] + (["shard_reduce"] if k > 1 else []))
+    nb = len(batches)
+    nlaunch = {"col_gelu_save": nb, "grad_act": nb, "grad_row_weight": nb, "grad_col_weight": nb,
+               "grad_input": nb, "grad_input_sum": nb, "shard_reduce": 1}
+    nshards = {kd: Gn for kd in nlaunch}
+    nshards["shard_reduce"] = k
 
     def launch(kind):
-        if kind == "col_gelu_save":
-            for i in range(k):
-                tpm.tp_mlp_col_gelu_save(X, Ws[i], bs[i], Y_i=Y, G_i=G)
-        elif kind == "grad_act":
-            for i in range(k):
-                tpm.tp_mlp_grad_act(dZ, Vs[i], G, dA_i=G)
-        elif kind == "grad_row_weight":
-            for i in range(k):
-                tpm.tp_mlp_grad_row_weight(Y, dZ, dV_i=dV[i], workspace=gws)
-        elif kind == "grad_col_weight":
-            for i in range(k):
-                tpm.tp_mlp_grad_col_weight(X, G, dW_i=dW[i], db_i=db[i], workspace=gws)
-        elif kind == "grad_input":
-            for i in range(nlaunch["grad_input"]):
-                tpm.tp_mlp_grad_input_partial(G, Ws[i], dX_i=dX if fused else parts[i])
-        elif kind == "grad_input_accum":
-            for i in range(1, k):
-                tpm.tp_mlp_grad_input_partial(G, Ws[i], dX_i=dX, accumulate=True)
-        else:
+        for i0, n in batches:
+            sl = slice(i0, i0 + n)
+            if kind == "col_gelu_save":
+                tpm.tp_mlp_col_gelu_shards(X, Ws[sl], bs[sl], Y[:n], Gb[:n])
+            elif kind == "grad_act":
+                tpm.tp_mlp_grad_act_shards(dZ, Vs[sl], Gb[:n], Gb[:n])
+            elif kind == "grad_row_weight":
+                tpm.tp_mlp_grad_row_weight_shards(Y[:n], dZ, dV[sl], workspace=gws)
+            elif kind == "grad_col_weight":
+                tpm.tp_mlp_grad_col_weight_shards(X, Gb[:n], dW[sl], db[sl], workspace=gws)
+            elif kind == "grad_input":
+                tpm.tp_mlp_grad_input_shards(Gb[:n], Ws[sl], parts[sl])
+            elif kind == "grad_input_sum":
+                tpm.tp_mlp_grad_input_shards(Gb[:n], Ws[sl], [dX], sum_shards=True, accumulate=i0 > 0)
+        if kind == "shard_reduce":
             tpm.tp_shard_reduce(parts, Z=dX)
 
-    kern = time_kinds(kinds, launch, nlaunch, args.kernel_steps or args.steps, args.warmup, w, elt)
+    kern = time_kinds(kinds, launch, nlaunch, nshards, args.kernel_steps or args.steps, args.warmup, w, elt)
     roof = roofline(kern, w, args.variant, w.dtype)
     return {"metric": "TP-shard MLP backward TFLOP/s (5 GEMMs of 2 M H F/k per shard, incl. recompute)",
             "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
             "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "roofline": roof,
-            "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"]}
-                        for k_, v in kern.items()}}
+            "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],
+                             "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()}}
 
 
 def measured_traffic(workload, variant, kind):

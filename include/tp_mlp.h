@@ -94,11 +94,13 @@ extern "C" {
 #define TP_ERR_ALIAS (-8)     /* an output overlaps an input it may not overlap */
 
 #define TP_MAX_SHARDS 64
+#define TP_MAX_BATCH 16 /* shards per call of the *_shards entry points */
 
 /* Flags. */
 #define TP_ACCUMULATE 1u  /* tp_mlp_row_partial, tp_mlp_grad_input_partial: add into the output */
 #define TP_FUSED_ACCUM 1u /* tp_mlp_shard_forward / _backward: fold the shard sum into the GEMMs */
 #define TP_GRAD_ACCUMULATE 2u /* weight-gradient entry points: add into dW, db, dV */
+#define TP_SUM_SHARDS 4u      /* row / input-gradient batches: one output, the shard-order sum */
 
 /*
  * Column-parallel linear + bias + GeLU of one shard (ColumnParallelLinear
@@ -280,6 +282,60 @@ int tp_mlp_shard_backward(const void* X, const void* const* W, const void* const
                           int64_t Fk, int dtype, void* workspace, size_t workspace_bytes,
                           float* dX, float* const* dW, float* const* db, float* const* dV,
                           unsigned flags, void* stream);
+
+/*
+ * Batched steps.  Each *_shards call runs one step for n shards
+ * (1 <= n <= TP_MAX_BATCH) of the same shapes as one launch, so that the
+ * small per-shard GEMMs of a narrow layer fill the chip; it gives the same
+ * results, bit for bit, as n calls of the single-shard entry point.  Array
+ * arguments are HOST arrays of n device pointers; every rule of the
+ * single-shard call applies to each shard, and no output may overlap an
+ * input or another output.
+ */
+
+/* tp_mlp_col_gelu (G == NULL) or tp_mlp_col_gelu_save for shards 0..n-1:
+ * X shared; W[i], b[i] (b == NULL: no bias), Y[i] and G[i] per shard. */
+int tp_mlp_col_gelu_shards(const void* X, const void* const* W, const void* const* b, void* const* Y,
+                           void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype,
+                           void* stream);
+
+/* tp_mlp_row_partial for shards 0..n-1: Z[i] (+)= Y[i] V[i].  With
+ * TP_SUM_SHARDS, Z[0] = Y[0] V[0] + ... + Y[n-1] V[n-1] (or Z[0] + ... with
+ * TP_ACCUMULATE), each product in its own float32 accumulator and the sum
+ * formed in shard order: the same values as n partials followed by
+ * tp_shard_reduce (only Z[0] is used). */
+int tp_mlp_row_partial_shards(const void* const* Y, const void* const* V, float* const* Z, int n,
+                              int64_t M, int64_t Fk, int64_t H, int dtype, unsigned flags,
+                              void* stream);
+
+/* tp_mlp_grad_act for shards 0..n-1 (dZ shared; dA[i] may be G[i]). */
+int tp_mlp_grad_act_shards(const void* dZ, const void* const* V, const void* const* G,
+                           void* const* dA, int n, int64_t M, int64_t H, int64_t Fk, int dtype,
+                           void* stream);
+
+/* Workspace of tp_mlp_grad_row_weight_shards / tp_mlp_grad_col_weight_shards
+ * for n shards (n == 1: tp_mlp_grad_weight_workspace_bytes).  0 on invalid
+ * arguments. */
+size_t tp_mlp_grad_weight_workspace_bytes_shards(int n, int64_t M, int64_t H, int64_t Fk,
+                                                 int dtype);
+
+/* tp_mlp_grad_row_weight for shards 0..n-1 (dZ shared). */
+int tp_mlp_grad_row_weight_shards(const void* const* Y, const void* dZ, float* const* dV, int n,
+                                  int64_t M, int64_t Fk, int64_t H, int dtype, void* workspace,
+                                  size_t workspace_bytes, unsigned flags, void* stream);
+
+/* tp_mlp_grad_col_weight for shards 0..n-1 (X shared; db == NULL: no bias
+ * gradients). */
+int tp_mlp_grad_col_weight_shards(const void* X, const void* const* dA, float* const* dW,
+                                  float* const* db, int n, int64_t M, int64_t H, int64_t Fk,
+                                  int dtype, void* workspace, size_t workspace_bytes,
+                                  unsigned flags, void* stream);
+
+/* tp_mlp_grad_input_partial for shards 0..n-1; TP_SUM_SHARDS as for
+ * tp_mlp_row_partial_shards (the backward all-reduce of dX folded in). */
+int tp_mlp_grad_input_shards(const void* const* dA, const void* const* W, float* const* dX, int n,
+                             int64_t M, int64_t Fk, int64_t H, int dtype, unsigned flags,
+                             void* stream);
 
 /* Static text for a status code. */
 const char* tp_status_string(int status);

@@ -19,6 +19,9 @@ Backward (dZ = dL/dZ):
     dW_i = X^T dA_i, db_i = colsum     tp_mlp_grad_col_weight
     dX_i = dA_i W_i^T                  tp_mlp_grad_input_partial
     all of the above, k shards, + dX   tp_mlp_shard_backward
+
+Every per-step call has a *_shards form that runs the step for up to
+TP_MAX_BATCH shards in one launch (what the k-shard calls do inside).
 """
 from __future__ import annotations
 
@@ -31,7 +34,10 @@ __all__ = [
     "tp_shard_reduce", "tp_mlp_workspace_bytes", "tp_mlp_shard_forward", "TP_GRAD_ACCUMULATE",
     "tp_mlp_col_gelu_save", "tp_mlp_grad_act", "tp_mlp_grad_weight_workspace_bytes",
     "tp_mlp_grad_row_weight", "tp_mlp_grad_col_weight", "tp_mlp_grad_input_partial",
-    "tp_mlp_backward_workspace_bytes", "tp_mlp_shard_backward",
+    "tp_mlp_backward_workspace_bytes", "tp_mlp_shard_backward", "TP_SUM_SHARDS", "TP_MAX_BATCH",
+    "tp_mlp_col_gelu_shards", "tp_mlp_row_partial_shards", "tp_mlp_grad_act_shards",
+    "tp_mlp_grad_weight_workspace_bytes_shards", "tp_mlp_grad_row_weight_shards",
+    "tp_mlp_grad_col_weight_shards", "tp_mlp_grad_input_shards",
 ]
 
 TP_F32 = 0
@@ -39,7 +45,9 @@ TP_BF16 = 1
 TP_ACCUMULATE = 1
 TP_FUSED_ACCUM = 1
 TP_GRAD_ACCUMULATE = 2
+TP_SUM_SHARDS = 4
 TP_MAX_SHARDS = 64
+TP_MAX_BATCH = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtpmlp.so")
@@ -92,6 +100,17 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_shard_backward.argtypes = [vp, vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, vp, vp,
                                             vp, vp, cu, vp]
         L.tp_mlp_shard_backward.restype = ci
+        L.tp_mlp_col_gelu_shards.argtypes = [vp, vp, vp, vp, vp, ci, i64, i64, i64, ci, vp]
+        L.tp_mlp_row_partial_shards.argtypes = [vp, vp, vp, ci, i64, i64, i64, ci, cu, vp]
+        L.tp_mlp_grad_act_shards.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp]
+        L.tp_mlp_grad_weight_workspace_bytes_shards.argtypes = [ci, i64, i64, i64, ci]
+        L.tp_mlp_grad_weight_workspace_bytes_shards.restype = sz
+        L.tp_mlp_grad_row_weight_shards.argtypes = [vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, cu, vp]
+        L.tp_mlp_grad_col_weight_shards.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, cu, vp]
+        L.tp_mlp_grad_input_shards.argtypes = [vp, vp, vp, ci, i64, i64, i64, ci, cu, vp]
+        for f in (L.tp_mlp_col_gelu_shards, L.tp_mlp_row_partial_shards, L.tp_mlp_grad_act_shards,
+                  L.tp_mlp_grad_row_weight_shards, L.tp_mlp_grad_col_weight_shards, L.tp_mlp_grad_input_shards):
+            f.restype = ci
         _lib = L
     return _lib
 
@@ -421,3 +440,111 @@ def tp_mlp_shard_backward(X, W, b, V, dZ, dX=None, dW=None, db=None, dV=None, wa
                                        None if db is None else arr(db, "db"), arr(dV, "dV"), flags,
                                        _stream(stream)), "tp_mlp_shard_backward")
     return dX, dW, db, dV
+
+
+# ---------------------------------------------------------------------------
+# Batched steps: one launch for n <= TP_MAX_BATCH shards.
+
+def _ptrs(ts, name, allow_none=False):
+    if ts is None:
+        return None
+    vals = []
+    for i, t in enumerate(ts):
+        if t is None and allow_none:
+            vals.append(None)
+        else:
+            vals.append(_dev(t, "%s[%d]" % (name, i)))
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def _batch_n(n):
+    if not 1 <= n <= TP_MAX_BATCH:
+        raise ValueError("a batch holds 1..%d shards, got %d" % (TP_MAX_BATCH, n))
+    return n
+
+
+def tp_mlp_col_gelu_shards(X, W, b, Y, G=None, stream=None):
+    """Y[i] = GeLU(X W[i] + b[i]) (and G[i] = GeLU'(.) when G is given) for
+    every shard i of the lists, in one launch; b may be None."""
+    n = _batch_n(len(W))
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = W[0].shape[-1]
+    _check(lib().tp_mlp_col_gelu_shards(_dev(X, "X"), _ptrs(W, "W"), _ptrs(b, "b"), _ptrs(Y, "Y"),
+                                        _ptrs(G, "G"), n, M, H, Fk, _dtype_code(X), _stream(stream)),
+           "tp_mlp_col_gelu_shards")
+    return Y, G
+
+
+def tp_mlp_row_partial_shards(Y, V, Z, sum_shards=False, accumulate=False, stream=None):
+    """Z[i] (+)= Y[i] V[i] for every shard, or Z[0] (+)= sum_i Y[i] V[i] in shard
+    order with sum_shards=True (Z may then hold just Z[0])."""
+    n = _batch_n(len(Y))
+    Fk = Y[0].shape[-1]
+    M = Y[0].numel() // Fk if Fk else 0
+    H = V[0].shape[-1]
+    Zl = list(Z) + [None] * (n - len(Z)) if sum_shards else list(Z)
+    flags = (TP_SUM_SHARDS if sum_shards else 0) | (TP_ACCUMULATE if accumulate else 0)
+    _check(lib().tp_mlp_row_partial_shards(_ptrs(Y, "Y"), _ptrs(V, "V"), _ptrs(Zl, "Z", allow_none=True), n,
+                                           M, Fk, H, _dtype_code(Y[0]), flags, _stream(stream)),
+           "tp_mlp_row_partial_shards")
+    return Z
+
+
+def tp_mlp_grad_act_shards(dZ, V, G, dA, stream=None):
+    """dA[i] = (dZ V[i]^T) * G[i] for every shard (dA[i] may be G[i])."""
+    n = _batch_n(len(V))
+    H = dZ.shape[-1]
+    M = dZ.numel() // H if H else 0
+    Fk = V[0].shape[0]
+    _check(lib().tp_mlp_grad_act_shards(_dev(dZ, "dZ"), _ptrs(V, "V"), _ptrs(G, "G"), _ptrs(dA, "dA"), n, M, H,
+                                        Fk, _dtype_code(dZ), _stream(stream)), "tp_mlp_grad_act_shards")
+    return dA
+
+
+def tp_mlp_grad_weight_workspace_bytes_shards(n: int, M: int, H: int, Fk: int, dtype: int) -> int:
+    return int(lib().tp_mlp_grad_weight_workspace_bytes_shards(n, M, H, Fk, dtype))
+
+
+def tp_mlp_grad_row_weight_shards(Y, dZ, dV, workspace=None, accumulate=False, stream=None):
+    """dV[i] (+)= Y[i]^T dZ for every shard."""
+    n = _batch_n(len(Y))
+    Fk = Y[0].shape[-1]
+    M = Y[0].numel() // Fk if Fk else 0
+    H = dZ.shape[-1]
+    dt = _dtype_code(dZ)
+    workspace = _workspace(workspace, tp_mlp_grad_weight_workspace_bytes_shards(n, M, H, Fk, dt), dZ.device)
+    _check(lib().tp_mlp_grad_row_weight_shards(_ptrs(Y, "Y"), _dev(dZ, "dZ"), _ptrs(dV, "dV"), n, M, Fk, H, dt,
+                                               _dev(workspace, "workspace"), workspace.numel(),
+                                               TP_GRAD_ACCUMULATE if accumulate else 0, _stream(stream)),
+           "tp_mlp_grad_row_weight_shards")
+    return dV
+
+
+def tp_mlp_grad_col_weight_shards(X, dA, dW, db=None, workspace=None, accumulate=False, stream=None):
+    """dW[i] (+)= X^T dA[i] and db[i] (+)= colsum(dA[i]) for every shard."""
+    n = _batch_n(len(dA))
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = dA[0].shape[-1]
+    dt = _dtype_code(X)
+    workspace = _workspace(workspace, tp_mlp_grad_weight_workspace_bytes_shards(n, M, H, Fk, dt), X.device)
+    _check(lib().tp_mlp_grad_col_weight_shards(_dev(X, "X"), _ptrs(dA, "dA"), _ptrs(dW, "dW"), _ptrs(db, "db"),
+                                               n, M, H, Fk, dt, _dev(workspace, "workspace"), workspace.numel(),
+                                               TP_GRAD_ACCUMULATE if accumulate else 0, _stream(stream)),
+           "tp_mlp_grad_col_weight_shards")
+    return dW, db
+
+
+def tp_mlp_grad_input_shards(dA, W, dX, sum_shards=False, accumulate=False, stream=None):
+    """dX[i] (+)= dA[i] W[i]^T for every shard, or the shard-order sum into dX[0]."""
+    n = _batch_n(len(dA))
+    Fk = dA[0].shape[-1]
+    M = dA[0].numel() // Fk if Fk else 0
+    H = W[0].shape[0]
+    dXl = list(dX) + [None] * (n - len(dX)) if sum_shards else list(dX)
+    flags = (TP_SUM_SHARDS if sum_shards else 0) | (TP_ACCUMULATE if accumulate else 0)
+    _check(lib().tp_mlp_grad_input_shards(_ptrs(dA, "dA"), _ptrs(W, "W"), _ptrs(dXl, "dX", allow_none=True), n,
+                                          M, Fk, H, _dtype_code(dA[0]), flags, _stream(stream)),
+           "tp_mlp_grad_input_shards")
+    return dX

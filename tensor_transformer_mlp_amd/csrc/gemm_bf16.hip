@@ -65,12 +65,16 @@ GemmParams base_params(const GemmBatch& b, int tile) {
 //   * K % 32 != 0 (K ends inside a 32-deep stage): the ragged-K variant of the
 //     128x128 tile.
 // A group sum keeps two accumulator sets, so it uses tiles of at most
-// 4 fragments per wave: 128x256 when it gives at least 192 workgroups, else
-// the 4-wave 128x128 tile (two workgroups per CU).
+// 4 fragments per wave: 128x256 (4 stages from 512 workgroups up, 3 stages
+// below) when it gives at least 192 workgroups, else the 4-wave 128x128 tile
+// (two workgroups per CU).
 int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K, int groups, bool group_sum) {
   (void)layout;
   if (K % 32) return kTailTile;
-  if (group_sum) return tiles_of(6, M, N) >= 192 ? 6 : 7;
+  if (group_sum) {
+    const int64_t t = tiles_of(6, M, N);
+    return t >= 512 ? 5 : t >= 192 ? 6 : 7;
+  }
   const int64_t t256 = tiles_of(0, M, N) * groups;
   if (t256 >= 512 || (t256 >= 192 && t256 < 256)) return 0;
   if (N > 128) return 6;
@@ -103,7 +107,26 @@ hipError_t launch_gemm_bf16_batch_tile(int tile, const GemmBatch& b, hipStream_t
   return hipSuccess;
 }
 
+GemmBatch single_batch(const GemmArgs& g);
+
+// A group sum whose per-group GEMM alone fills the chip four times over with
+// 256x256 tiles runs group by group instead: group 0 applies the epilogue to
+// C[0] and each later group adds its product into C[0] (the same float32
+// additions in the same order), keeping the larger tile (measured on the
+// row step of the 32768 x 8192 x 4096 shards: 2.09 ms per shard for the
+// 256x256 GEMM that adds into C, 2.14 ms per shard for the 128x256 group sum).
+constexpr int64_t kSequentialSumTiles = 1024;
+
 hipError_t launch_gemm_bf16_batch(const GemmBatch& b, hipStream_t s) {
+  if (b.group_sum && b.groups > 1 && b.K % 32 == 0 && tiles_of(0, b.M, b.N) >= kSequentialSumTiles) {
+    for (int g = 0; g < b.groups; ++g) {
+      GemmArgs a{b.A[g], b.B[g], nullptr, b.C[0], nullptr, b.M, b.N, b.K, b.lda, b.ldb, b.ldc,
+                 b.layout, g == 0 ? b.epi : kEpiAccumF32};
+      const hipError_t e = launch_gemm_bf16(a, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   return launch_gemm_bf16_batch_tile(
       pick_bf16_tile(b.layout, b.M, b.N, b.K, b.groups, b.group_sum), b, s);
 }
@@ -138,9 +161,10 @@ hipError_t launch_gemm_bf16_tile(int tile, const GemmArgs& g, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // K-split.  The bf16 slices use the 128x128 tile (two workgroups per CU), the
-// float32 ones the 64x64 tile.  The slice count doubles while the grid has
-// fewer than 256 workgroups and each slice keeps at least 2048 of K, or while
-// it has fewer than 128 and each slice keeps at least 1024 (up to 16 slices).
+// float32 ones the 64x64 tile.  The slice count doubles while one group's
+// grid has fewer than 256 workgroups and each slice keeps at least 2048 of K,
+// or while it has fewer than 128 and each slice keeps at least 1024 (up to
+// 16 slices).
 // Measured on MI355X for the weight gradients of the MLP shards (for example
 // 768 x 768 x 8192: 4 slices 409 TFLOP/s, 8 slices 311, no split 196).
 // ---------------------------------------------------------------------------
@@ -150,8 +174,10 @@ constexpr int kSplitTile = 8;  // 128x128, 2x4 waves
 
 int64_t split_slice_len(int64_t K, int S) { return ((K + S - 1) / S + 31) / 32 * 32; }
 
-int64_t split_tiles(bool bf16, int groups, int64_t M, int64_t N) {
-  return groups * (bf16 ? tiles_of(kSplitTile, M, N) : ((M + 63) / 64) * ((N + 63) / 64));
+// The slice count depends on one group's shape only, so a shard's result
+// does not depend on how many shards share the launch.
+int64_t split_tiles(bool bf16, int64_t M, int64_t N) {
+  return bf16 ? tiles_of(kSplitTile, M, N) : ((M + 63) / 64) * ((N + 63) / 64);
 }
 
 }  // namespace
@@ -166,12 +192,12 @@ int gemm_k_slices(bool bf16, int64_t tiles, int64_t K) {
 }
 
 size_t gemm_split_workspace_bytes(bool bf16, int groups, int64_t M, int64_t N, int64_t K) {
-  const int S = gemm_k_slices(bf16, split_tiles(bf16, groups, M, N), K);
+  const int S = gemm_k_slices(bf16, split_tiles(bf16, M, N), K);
   return size_t(groups) * size_t(S - 1) * round256(size_t(M) * size_t(N) * 4);
 }
 
 hipError_t launch_gemm_split(const GemmBatch& b, bool bf16, void* ws, hipStream_t s) {
-  const int S = gemm_k_slices(bf16, split_tiles(bf16, b.groups, b.M, b.N), b.K);
+  const int S = gemm_k_slices(bf16, split_tiles(bf16, b.M, b.N), b.K);
   if (S == 1) return bf16 ? launch_gemm_bf16_batch(b, s) : launch_gemm_f32_batch(b, s);
   const int64_t ks = split_slice_len(b.K, S);
   const int n = (int)((b.K + ks - 1) / ks);  // slices actually used (<= S)

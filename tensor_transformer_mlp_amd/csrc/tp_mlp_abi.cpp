@@ -220,65 +220,76 @@ const char* tp_status_string(int status) {
   }
 }
 
-int tp_mlp_version(void) { return 110; }
+int tp_mlp_version(void) { return 120; }
 
-int tp_mlp_col_gelu(const void* X, const void* W_i, const void* b_i, void* Y_i, int64_t M,
-                    int64_t H, int64_t Fk, int dtype, void* stream) {
+int tp_mlp_col_gelu_shards(const void* X, const void* const* W, const void* const* b, void* const* Y,
+                           void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype,
+                           void* stream) {
   int st = check_dtype(dtype);
   if (st) return st;
   if ((st = check_dims(M, H, Fk))) return st;
+  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
   if (M == 0) return TP_OK;
-  if (!X || !W_i || !Y_i) return TP_ERR_NULL;
-  if (!aligned16(X) || !aligned16(W_i) || !aligned16(Y_i) || (b_i && !aligned16(b_i)))
-    return TP_ERR_ALIGN;
+  if (!X || !W || !Y) return TP_ERR_NULL;
+  if (!aligned16(X)) return TP_ERR_ALIGN;
   const size_t e = elt_size(dtype);
   Regions in, out;
   in.add(X, size_t(M) * size_t(H) * e);
-  in.add(W_i, size_t(H) * size_t(Fk) * e);
-  in.add(b_i, size_t(Fk) * e);
-  out.add(Y_i, size_t(M) * size_t(Fk) * e);
+  for (int i = 0; i < n; ++i) {
+    if (!W[i] || !Y[i] || (b && !b[i]) || (G && !G[i])) return TP_ERR_NULL;
+    if (!aligned16(W[i]) || !aligned16(Y[i]) || (b && !aligned16(b[i])) || (G && !aligned16(G[i])))
+      return TP_ERR_ALIGN;
+    in.add(W[i], size_t(H) * size_t(Fk) * e);
+    if (b) in.add(b[i], size_t(Fk) * e);
+    out.add(Y[i], size_t(M) * size_t(Fk) * e);
+    if (G) out.add(G[i], size_t(M) * size_t(Fk) * e);
+  }
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return col_steps(X, &W_i, &b_i, &Y_i, nullptr, 1, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+  return col_steps(X, W, b, Y, G, n, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+}
+
+int tp_mlp_col_gelu(const void* X, const void* W_i, const void* b_i, void* Y_i, int64_t M,
+                    int64_t H, int64_t Fk, int dtype, void* stream) {
+  return tp_mlp_col_gelu_shards(X, &W_i, b_i ? &b_i : nullptr, &Y_i, nullptr, 1, M, H, Fk, dtype,
+                                stream);
 }
 
 int tp_mlp_col_gelu_save(const void* X, const void* W_i, const void* b_i, void* Y_i, void* G_i,
                          int64_t M, int64_t H, int64_t Fk, int dtype, void* stream) {
+  return tp_mlp_col_gelu_shards(X, &W_i, b_i ? &b_i : nullptr, &Y_i, &G_i, 1, M, H, Fk, dtype,
+                                stream);
+}
+
+int tp_mlp_row_partial_shards(const void* const* Y, const void* const* V, float* const* Z, int n,
+                              int64_t M, int64_t Fk, int64_t H, int dtype, unsigned flags,
+                              void* stream) {
   int st = check_dtype(dtype);
   if (st) return st;
+  if (flags & ~(TP_ACCUMULATE | TP_SUM_SHARDS)) return TP_ERR_FLAGS;
   if ((st = check_dims(M, H, Fk))) return st;
+  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
   if (M == 0) return TP_OK;
-  if (!X || !W_i || !Y_i || !G_i) return TP_ERR_NULL;
-  if (!aligned16(X) || !aligned16(W_i) || !aligned16(Y_i) || !aligned16(G_i) ||
-      (b_i && !aligned16(b_i)))
-    return TP_ERR_ALIGN;
+  const bool sum = (flags & TP_SUM_SHARDS) != 0;
+  if (!Y || !V || !Z) return TP_ERR_NULL;
   const size_t e = elt_size(dtype);
   Regions in, out;
-  in.add(X, size_t(M) * size_t(H) * e);
-  in.add(W_i, size_t(H) * size_t(Fk) * e);
-  in.add(b_i, size_t(Fk) * e);
-  out.add(Y_i, size_t(M) * size_t(Fk) * e);
-  out.add(G_i, size_t(M) * size_t(Fk) * e);
+  for (int i = 0; i < n; ++i) {
+    if (!Y[i] || !V[i] || ((!sum || i == 0) && !Z[i])) return TP_ERR_NULL;
+    if (!aligned16(Y[i]) || !aligned16(V[i]) || ((!sum || i == 0) && !aligned16(Z[i])))
+      return TP_ERR_ALIGN;
+    in.add(Y[i], size_t(M) * size_t(Fk) * e);
+    in.add(V[i], size_t(Fk) * size_t(H) * e);
+    if (!sum || i == 0) out.add(Z[i], size_t(M) * size_t(H) * 4);
+  }
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return col_steps(X, &W_i, &b_i, &Y_i, &G_i, 1, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+  return row_steps(Y, V, Z, n, sum, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
+                   static_cast<hipStream_t>(stream));
 }
 
 int tp_mlp_row_partial(const void* Y_i, const void* V_i, float* Z_i, int64_t M, int64_t Fk,
                        int64_t H, int dtype, unsigned flags, void* stream) {
-  int st = check_dtype(dtype);
-  if (st) return st;
-  if (flags & ~TP_ACCUMULATE) return TP_ERR_FLAGS;
-  if ((st = check_dims(M, H, Fk))) return st;
-  if (M == 0) return TP_OK;
-  if (!Y_i || !V_i || !Z_i) return TP_ERR_NULL;
-  if (!aligned16(Y_i) || !aligned16(V_i) || !aligned16(Z_i)) return TP_ERR_ALIGN;
-  const size_t e = elt_size(dtype);
-  Regions in, out;
-  in.add(Y_i, size_t(M) * size_t(Fk) * e);
-  in.add(V_i, size_t(Fk) * size_t(H) * e);
-  out.add(Z_i, size_t(M) * size_t(H) * 4);
-  if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return row_steps(&Y_i, &V_i, &Z_i, 1, false, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
-                   static_cast<hipStream_t>(stream));
+  if (flags & ~TP_ACCUMULATE) return check_dtype(dtype) ? check_dtype(dtype) : TP_ERR_FLAGS;
+  return tp_mlp_row_partial_shards(&Y_i, &V_i, &Z_i, 1, M, Fk, H, dtype, flags, stream);
 }
 
 int tp_shard_reduce(const float* const* Z_parts, int k, float* Z, int64_t n, void* stream) {
@@ -375,94 +386,151 @@ int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const*
   return TP_OK;
 }
 
-int tp_mlp_grad_act(const void* dZ, const void* V_i, const void* G_i, void* dA_i, int64_t M,
-                    int64_t H, int64_t Fk, int dtype, void* stream) {
+int tp_mlp_grad_act_shards(const void* dZ, const void* const* V, const void* const* G,
+                           void* const* dA, int n, int64_t M, int64_t H, int64_t Fk, int dtype,
+                           void* stream) {
   int st = check_dtype(dtype);
   if (st) return st;
   if ((st = check_dims(M, H, Fk))) return st;
+  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
   if (M == 0) return TP_OK;
-  if (!dZ || !V_i || !G_i || !dA_i) return TP_ERR_NULL;
-  if (!aligned16(dZ) || !aligned16(V_i) || !aligned16(G_i) || !aligned16(dA_i)) return TP_ERR_ALIGN;
+  if (!dZ || !V || !G || !dA) return TP_ERR_NULL;
+  if (!aligned16(dZ)) return TP_ERR_ALIGN;
   const size_t e = elt_size(dtype);
+  const size_t na = size_t(M) * size_t(Fk) * e;
   Regions in, out;
   in.add(dZ, size_t(M) * size_t(H) * e);
-  in.add(V_i, size_t(Fk) * size_t(H) * e);
-  if (dA_i != G_i) in.add(G_i, size_t(M) * size_t(Fk) * e);
-  out.add(dA_i, size_t(M) * size_t(Fk) * e);
+  for (int i = 0; i < n; ++i) {
+    if (!V[i] || !G[i] || !dA[i]) return TP_ERR_NULL;
+    if (!aligned16(V[i]) || !aligned16(G[i]) || !aligned16(dA[i])) return TP_ERR_ALIGN;
+    in.add(V[i], size_t(Fk) * size_t(H) * e);
+    out.add(dA[i], na);
+  }
+  // G[i] may be dA[i] itself, but no other output
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < out.n; ++j)
+      if (!(j == i && G[i] == dA[i]) && overlap(G[i], na, out.r[j].p, out.r[j].n)) return TP_ERR_ALIAS;
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return act_grad_steps(dZ, &V_i, &G_i, &dA_i, 1, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+  return act_grad_steps(dZ, V, G, dA, n, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+}
+
+int tp_mlp_grad_act(const void* dZ, const void* V_i, const void* G_i, void* dA_i, int64_t M,
+                    int64_t H, int64_t Fk, int dtype, void* stream) {
+  return tp_mlp_grad_act_shards(dZ, &V_i, &G_i, &dA_i, 1, M, H, Fk, dtype, stream);
+}
+
+size_t tp_mlp_grad_weight_workspace_bytes_shards(int n, int64_t M, int64_t H, int64_t Fk,
+                                                 int dtype) {
+  if (n < 1 || n > TP_MAX_BATCH || check_dtype(dtype) || check_dims(M, H, Fk)) return 0;
+  return grad_weight_ws(n, M, H, Fk, dtype);
 }
 
 size_t tp_mlp_grad_weight_workspace_bytes(int64_t M, int64_t H, int64_t Fk, int dtype) {
-  if (check_dtype(dtype) || check_dims(M, H, Fk)) return 0;
-  return grad_weight_ws(1, M, H, Fk, dtype);
+  return tp_mlp_grad_weight_workspace_bytes_shards(1, M, H, Fk, dtype);
+}
+
+int tp_mlp_grad_row_weight_shards(const void* const* Y, const void* dZ, float* const* dV, int n,
+                                  int64_t M, int64_t Fk, int64_t H, int dtype, void* workspace,
+                                  size_t workspace_bytes, unsigned flags, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (flags & ~TP_GRAD_ACCUMULATE) return TP_ERR_FLAGS;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
+  if (!Y || !dV || (M > 0 && !dZ)) return TP_ERR_NULL;
+  if (!aligned16(dZ)) return TP_ERR_ALIGN;
+  const size_t need = grad_weight_ws(n, M, H, Fk, dtype);
+  if (need && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  Regions in, out;
+  in.add(dZ, size_t(M) * size_t(H) * e);
+  for (int i = 0; i < n; ++i) {
+    if (!dV[i] || (M > 0 && !Y[i])) return TP_ERR_NULL;
+    if (!aligned16(Y[i]) || !aligned16(dV[i])) return TP_ERR_ALIGN;
+    in.add(Y[i], size_t(M) * size_t(Fk) * e);
+    out.add(dV[i], size_t(Fk) * size_t(H) * 4);
+  }
+  out.add(workspace, need);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return row_weight_steps(Y, dZ, dV, n, M, Fk, H, dtype, workspace,
+                          (flags & TP_GRAD_ACCUMULATE) != 0, static_cast<hipStream_t>(stream));
 }
 
 int tp_mlp_grad_row_weight(const void* Y_i, const void* dZ, float* dV_i, int64_t M, int64_t Fk,
                            int64_t H, int dtype, void* workspace, size_t workspace_bytes,
                            unsigned flags, void* stream) {
-  int st = check_dtype(dtype);
-  if (st) return st;
-  if (flags & ~TP_GRAD_ACCUMULATE) return TP_ERR_FLAGS;
-  if ((st = check_dims(M, H, Fk))) return st;
-  if (!dV_i || (M > 0 && (!Y_i || !dZ))) return TP_ERR_NULL;
-  if (!aligned16(Y_i) || !aligned16(dZ) || !aligned16(dV_i)) return TP_ERR_ALIGN;
-  const size_t need = grad_weight_ws(1, M, H, Fk, dtype);
-  if (need && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
-  if (workspace && !aligned16(workspace)) return TP_ERR_ALIGN;
-  const size_t e = elt_size(dtype);
-  Regions in, out;
-  in.add(Y_i, size_t(M) * size_t(Fk) * e);
-  in.add(dZ, size_t(M) * size_t(H) * e);
-  out.add(dV_i, size_t(Fk) * size_t(H) * 4);
-  out.add(workspace, need);
-  if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return row_weight_steps(&Y_i, dZ, &dV_i, 1, M, Fk, H, dtype, workspace,
-                         (flags & TP_GRAD_ACCUMULATE) != 0, static_cast<hipStream_t>(stream));
+  return tp_mlp_grad_row_weight_shards(&Y_i, dZ, &dV_i, 1, M, Fk, H, dtype, workspace,
+                                       workspace_bytes, flags, stream);
 }
 
-int tp_mlp_grad_col_weight(const void* X, const void* dA_i, float* dW_i, float* db_i, int64_t M,
-                           int64_t H, int64_t Fk, int dtype, void* workspace,
-                           size_t workspace_bytes, unsigned flags, void* stream) {
+int tp_mlp_grad_col_weight_shards(const void* X, const void* const* dA, float* const* dW,
+                                  float* const* db, int n, int64_t M, int64_t H, int64_t Fk,
+                                  int dtype, void* workspace, size_t workspace_bytes,
+                                  unsigned flags, void* stream) {
   int st = check_dtype(dtype);
   if (st) return st;
   if (flags & ~TP_GRAD_ACCUMULATE) return TP_ERR_FLAGS;
   if ((st = check_dims(M, H, Fk))) return st;
-  if (!dW_i || (M > 0 && (!X || !dA_i))) return TP_ERR_NULL;
-  if (!aligned16(X) || !aligned16(dA_i) || !aligned16(dW_i) || (db_i && !aligned16(db_i)))
-    return TP_ERR_ALIGN;
-  const size_t need = grad_weight_ws(1, M, H, Fk, dtype);
+  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
+  if (!dA || !dW || (M > 0 && !X)) return TP_ERR_NULL;
+  if (!aligned16(X)) return TP_ERR_ALIGN;
+  const size_t need = grad_weight_ws(n, M, H, Fk, dtype);
   if (need && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return TP_ERR_ALIGN;
   const size_t e = elt_size(dtype);
   Regions in, out;
   in.add(X, size_t(M) * size_t(H) * e);
-  in.add(dA_i, size_t(M) * size_t(Fk) * e);
-  out.add(dW_i, size_t(H) * size_t(Fk) * 4);
-  out.add(db_i, size_t(Fk) * 4);
+  for (int i = 0; i < n; ++i) {
+    if (!dW[i] || (M > 0 && !dA[i]) || (db && !db[i])) return TP_ERR_NULL;
+    if (!aligned16(dA[i]) || !aligned16(dW[i]) || (db && !aligned16(db[i]))) return TP_ERR_ALIGN;
+    in.add(dA[i], size_t(M) * size_t(Fk) * e);
+    out.add(dW[i], size_t(H) * size_t(Fk) * 4);
+    if (db) out.add(db[i], size_t(Fk) * 4);
+  }
   out.add(workspace, need);
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return col_weight_steps(X, &dA_i, &dW_i, db_i ? &db_i : nullptr, 1, M, H, Fk, dtype, workspace,
-                         (flags & TP_GRAD_ACCUMULATE) != 0, static_cast<hipStream_t>(stream));
+  return col_weight_steps(X, dA, dW, db, n, M, H, Fk, dtype, workspace,
+                          (flags & TP_GRAD_ACCUMULATE) != 0, static_cast<hipStream_t>(stream));
+}
+
+int tp_mlp_grad_col_weight(const void* X, const void* dA_i, float* dW_i, float* db_i, int64_t M,
+                           int64_t H, int64_t Fk, int dtype, void* workspace,
+                           size_t workspace_bytes, unsigned flags, void* stream) {
+  return tp_mlp_grad_col_weight_shards(X, &dA_i, &dW_i, db_i ? &db_i : nullptr, 1, M, H, Fk, dtype,
+                                       workspace, workspace_bytes, flags, stream);
+}
+
+int tp_mlp_grad_input_shards(const void* const* dA, const void* const* W, float* const* dX, int n,
+                             int64_t M, int64_t Fk, int64_t H, int dtype, unsigned flags,
+                             void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (flags & ~(TP_ACCUMULATE | TP_SUM_SHARDS)) return TP_ERR_FLAGS;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
+  if (M == 0) return TP_OK;
+  const bool sum = (flags & TP_SUM_SHARDS) != 0;
+  if (!dA || !W || !dX) return TP_ERR_NULL;
+  const size_t e = elt_size(dtype);
+  Regions in, out;
+  for (int i = 0; i < n; ++i) {
+    if (!dA[i] || !W[i] || ((!sum || i == 0) && !dX[i])) return TP_ERR_NULL;
+    if (!aligned16(dA[i]) || !aligned16(W[i]) || ((!sum || i == 0) && !aligned16(dX[i])))
+      return TP_ERR_ALIGN;
+    in.add(dA[i], size_t(M) * size_t(Fk) * e);
+    in.add(W[i], size_t(H) * size_t(Fk) * e);
+    if (!sum || i == 0) out.add(dX[i], size_t(M) * size_t(H) * 4);
+  }
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return input_grad_steps(dA, W, dX, n, sum, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
+                          static_cast<hipStream_t>(stream));
 }
 
 int tp_mlp_grad_input_partial(const void* dA_i, const void* W_i, float* dX_i, int64_t M,
                               int64_t Fk, int64_t H, int dtype, unsigned flags, void* stream) {
-  int st = check_dtype(dtype);
-  if (st) return st;
-  if (flags & ~TP_ACCUMULATE) return TP_ERR_FLAGS;
-  if ((st = check_dims(M, H, Fk))) return st;
-  if (M == 0) return TP_OK;
-  if (!dA_i || !W_i || !dX_i) return TP_ERR_NULL;
-  if (!aligned16(dA_i) || !aligned16(W_i) || !aligned16(dX_i)) return TP_ERR_ALIGN;
-  const size_t e = elt_size(dtype);
-  Regions in, out;
-  in.add(dA_i, size_t(M) * size_t(Fk) * e);
-  in.add(W_i, size_t(H) * size_t(Fk) * e);
-  out.add(dX_i, size_t(M) * size_t(H) * 4);
-  if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return input_grad_steps(&dA_i, &W_i, &dX_i, 1, false, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
-                         static_cast<hipStream_t>(stream));
+  if (flags & ~TP_ACCUMULATE) return check_dtype(dtype) ? check_dtype(dtype) : TP_ERR_FLAGS;
+  return tp_mlp_grad_input_shards(&dA_i, &W_i, &dX_i, 1, M, Fk, H, dtype, flags, stream);
 }
 
 size_t tp_mlp_backward_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dtype,

@@ -28,12 +28,20 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 
-# Kernel kinds by (epilogue, operand layout) template arguments of the GEMMs:
-# epilogues 0 bias+GeLU, 1 fp32 store, 2 fp32 accumulate, 3 bias+GeLU+GeLU',
-# 4 multiply by aux; layouts 0 NN, 1 NT, 2 TN.
+# Kernel kinds by (epilogue, operand layout, group sum) template arguments of
+# the GEMMs: epilogues 0 bias+GeLU, 1 fp32 store, 2 fp32 accumulate,
+# 3 bias+GeLU+GeLU', 4 multiply by aux; layouts 0 NN, 1 NT, 2 TN.
 _GEMM_KIND = {("0", "0"): "col_gelu", ("1", "0"): "row_partial", ("2", "0"): "row_partial_accum",
               ("3", "0"): "col_gelu_save", ("4", "1"): "grad_act", ("1", "1"): "grad_input",
               ("2", "1"): "grad_input_accum", ("1", "2"): "grad_weight", ("2", "2"): "grad_weight_accum"}
+_GSUM_KIND = {"0": "row_sum", "1": "grad_input_sum"}
+
+
+def _targ(a: str) -> str:
+    """A template argument as printed by the demangler: '(tpmlp::Epilogue)1', '1', 'true'."""
+    a = a.strip()
+    a = re.sub(r"^\([^)]*\)", "", a)
+    return {"true": "1", "false": "0"}.get(a, a)
 
 
 def kernel_sources():
@@ -59,7 +67,9 @@ def kernel_kind(name: str):
     m = re.search(r"gemm_(?:bf16|f32)_kernel<([^>]*)>", name)
     if not m:
         return None
-    args = [a.strip() for a in m.group(1).split(",")]
+    args = [_targ(a) for a in m.group(1).split(",")]
+    if "gemm_bf16_kernel" in name and len(args) >= 9 and args[8] == "1":
+        return _GSUM_KIND.get(args[1])
     return _GEMM_KIND.get((args[0], args[1]))
 
 

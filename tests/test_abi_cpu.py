@@ -42,7 +42,10 @@ def test_exports_every_declared_symbol(L):
                      "tp_mlp_version", "tp_mlp_col_gelu_save", "tp_mlp_grad_act",
                      "tp_mlp_grad_weight_workspace_bytes", "tp_mlp_grad_row_weight",
                      "tp_mlp_grad_col_weight", "tp_mlp_grad_input_partial",
-                     "tp_mlp_backward_workspace_bytes", "tp_mlp_shard_backward"}
+                     "tp_mlp_backward_workspace_bytes", "tp_mlp_shard_backward",
+                     "tp_mlp_col_gelu_shards", "tp_mlp_row_partial_shards", "tp_mlp_grad_act_shards",
+                     "tp_mlp_grad_weight_workspace_bytes_shards", "tp_mlp_grad_row_weight_shards",
+                     "tp_mlp_grad_col_weight_shards", "tp_mlp_grad_input_shards"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -51,7 +54,7 @@ def test_python_constants_match_header():
     import tensor_transformer_mlp_amd as tpm
     c = _header_constants()
     for n in ("TP_F32", "TP_BF16", "TP_ACCUMULATE", "TP_FUSED_ACCUM", "TP_GRAD_ACCUMULATE",
-              "TP_MAX_SHARDS"):
+              "TP_SUM_SHARDS", "TP_MAX_SHARDS", "TP_MAX_BATCH"):
         assert getattr(tpm, n) == c[n], n
 
 
@@ -355,3 +358,55 @@ def test_shard_backward_errors(L):
     assert f(*a) == c["TP_ERR_ALIAS"]
     a = base(); a[9] = 2
     assert f(*a) == c["TP_ERR_DTYPE"]
+
+
+def test_shards_entry_point_errors(L):
+    c = _header_constants()
+    arr = lambda *xs: (ctypes.c_void_p * len(xs))(*xs)
+    X = ctypes.c_void_p(1 << 40)
+    W, b, Y, G = arr(10 * P, 11 * P), arr(12 * P, 13 * P), arr(14 * P, 15 * P), arr(16 * P, 17 * P)
+    f = L.tp_mlp_col_gelu_shards  # (X, W, b, Y, G, n, M, H, Fk, dtype, stream)
+    ok = lambda: [X, W, b, Y, G, 2, 16, 64, 128, 1, None]
+    a = ok(); a[5] = 0
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = ok(); a[5] = c["TP_MAX_BATCH"] + 1
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = ok(); a[3] = arr(14 * P, None)
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = ok(); a[4] = arr(16 * P, 17 * P + 4)
+    assert f(*a) == c["TP_ERR_ALIGN"]
+    a = ok(); a[3] = arr(14 * P, 14 * P)  # two shards write one Y
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = ok(); a[4] = arr(16 * P, 11 * P)  # G[1] over W[1]
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = ok(); a[6] = 0
+    assert f(*a) == c["TP_OK"]
+    r = L.tp_mlp_row_partial_shards  # (Y, V, Z, n, M, Fk, H, dtype, flags, stream)
+    Z = arr(20 * P, None)
+    ok = lambda: [Y, W, arr(20 * P, 21 * P), 2, 16, 128, 64, 1, 0, None]
+    a = ok(); a[8] = 8
+    assert r(*a) == c["TP_ERR_FLAGS"]
+    a = ok(); a[2] = Z  # Z[1] needed without TP_SUM_SHARDS
+    assert r(*a) == c["TP_ERR_NULL"]
+    a = ok(); a[2] = arr(20 * P, 20 * P)
+    assert r(*a) == c["TP_ERR_ALIAS"]
+    a = ok(); a[4] = 0
+    assert r(*a) == c["TP_OK"]
+    # the single-shard call rejects the batch-only flag
+    assert L.tp_mlp_row_partial(_p(0), _p(1), _p(2), 16, 128, 64, 1, c["TP_SUM_SHARDS"], None) == c["TP_ERR_FLAGS"]
+    g = L.tp_mlp_grad_act_shards  # (dZ, V, G, dA, n, M, H, Fk, dtype, stream)
+    ok = lambda: [X, W, G, arr(16 * P, 17 * P), 2, 16, 64, 128, 1, None]  # in place
+    a = ok(); a[3] = arr(17 * P, 16 * P)  # dA[0] over G[1]: not in place
+    assert g(*a) == c["TP_ERR_ALIAS"]
+    a = ok(); a[1] = None
+    assert g(*a) == c["TP_ERR_NULL"]
+    w = L.tp_mlp_grad_weight_workspace_bytes_shards
+    assert w(0, 16, 64, 128, 1) == 0 and w(17, 16, 64, 128, 1) == 0
+    assert w(1, 8192, 768, 768, 1) == L.tp_mlp_grad_weight_workspace_bytes(8192, 768, 768, 1)
+    assert w(4, 8192, 768, 768, 1) >= w(1, 8192, 768, 768, 1)
+    d = L.tp_mlp_grad_input_shards  # (dA, W, dX, n, M, Fk, H, dtype, flags, stream)
+    ok = lambda: [Y, W, Z, 2, 16, 128, 64, 1, c["TP_SUM_SHARDS"], None]
+    a = ok(); a[8] = 16
+    assert d(*a) == c["TP_ERR_FLAGS"]
+    a = ok(); a[2] = arr(11 * P, None)  # dX[0] over W[1]
+    assert d(*a) == c["TP_ERR_ALIAS"]
