@@ -235,14 +235,10 @@ hipError_t launch_gemm_split(const GemmBatch& b, bool bf16, void* ws, hipStream_
       }
     }
   }
-  for (int g = 0; g < b.groups; ++g) {
-    const float* parts[16];
-    parts[0] = static_cast<const float*>(b.C[g]);
-    for (int i = 1; i < n; ++i) parts[i] = part_ptr(g, i);
-    const hipError_t e = launch_shard_reduce(parts, n, static_cast<float*>(b.C[g]), b.M * b.N, s);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  float* C[kMaxGroups];
+  for (int g = 0; g < b.groups; ++g) C[g] = static_cast<float*>(b.C[g]);
+  return launch_split_reduce(C, b.groups, static_cast<const float*>(ws), (int64_t)(part / 4), n,
+                             b.M * b.N, s);
 }
 
 }  // namespace tpmlp

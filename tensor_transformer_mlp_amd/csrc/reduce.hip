@@ -112,11 +112,19 @@ int64_t colsum_row_blocks(int64_t M, int64_t N) {
   return rb < 1 ? 1 : rb;
 }
 
+struct ColsumPtrs {
+  const void* A[kMaxGroups];
+  float* out[kMaxGroups];
+};
+
+// blockIdx.z: the group (shard) whose A is summed into partials + z rb N.
 template <bool BF16>
-__global__ __launch_bounds__(256) void colsum_partial_kernel(const void* __restrict__ A, int64_t M,
-                                                             int64_t N, int64_t rows_per_block,
-                                                             float* __restrict__ partials) {
+__global__ __launch_bounds__(256) void colsum_partial_kernel(ColsumPtrs pp, int64_t M, int64_t N,
+                                                             int64_t rows_per_block,
+                                                             float* __restrict__ partials_all) {
   __shared__ float red[8][kColsPerBlock + 4];
+  const void* __restrict__ A = pp.A[blockIdx.z];
+  float* __restrict__ partials = partials_all + (int64_t)blockIdx.z * gridDim.y * N;
   const int cg = threadIdx.x & 31, rl = threadIdx.x >> 5;
   const int64_t n = (int64_t)blockIdx.x * kColsPerBlock + cg * 8;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
@@ -163,10 +171,11 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const void* __restr
 // Pass 2: 64 columns per workgroup, 4 row groups of 64 lanes; group g adds
 // partial rows [g q, (g + 1) q) in order, and the four group sums are then
 // added in group order (q = ceil(rb / 4)), so the order is fixed by (M, N).
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ partials,
-                                                           int64_t rb, int64_t N,
-                                                           float* __restrict__ out, int accumulate) {
+__global__ __launch_bounds__(256) void colsum_final_kernel(ColsumPtrs pp, const float* __restrict__ partials_all,
+                                                           int64_t rb, int64_t N, int accumulate) {
   __shared__ float red[4][64];
+  const float* __restrict__ partials = partials_all + (int64_t)blockIdx.y * rb * N;
+  float* __restrict__ out = pp.out[blockIdx.y];
   const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int64_t n = (int64_t)blockIdx.x * 64 + c;
   const int64_t q = (rb + 3) / 4;
@@ -207,22 +216,112 @@ hipError_t launch_shard_reduce(const float* const* parts, int k, float* Z, int64
 
 int64_t colsum_partials_floats(int64_t M, int64_t N) { return colsum_row_blocks(M, N) * N; }
 
-hipError_t launch_colsum(const void* A, bool bf16, int64_t M, int64_t N, float* out,
-                         bool accumulate, float* partials, hipStream_t s) {
-  if (N <= 0) return hipSuccess;
+hipError_t launch_colsum(const void* const* A, int groups, bool bf16, int64_t M, int64_t N,
+                         float* const* out, bool accumulate, float* partials, hipStream_t s) {
+  if (N <= 0 || groups < 1) return hipSuccess;
+  if (groups > kMaxGroups) return hipErrorInvalidValue;
+  ColsumPtrs pp{};
+  for (int g = 0; g < groups; ++g) {
+    pp.A[g] = A[g];
+    pp.out[g] = out[g];
+  }
   const int64_t rb = colsum_row_blocks(M, N);
   if (rb > 0) {
     const int64_t rows = (M + rb - 1) / rb;
-    const dim3 grid((unsigned)((N + kColsPerBlock - 1) / kColsPerBlock), (unsigned)rb), block(256);
+    const dim3 grid((unsigned)((N + kColsPerBlock - 1) / kColsPerBlock), (unsigned)rb, (unsigned)groups);
     if (bf16)
-      hipLaunchKernelGGL(colsum_partial_kernel<true>, grid, block, 0, s, A, M, N, rows, partials);
+      hipLaunchKernelGGL(colsum_partial_kernel<true>, grid, dim3(256), 0, s, pp, M, N, rows, partials);
     else
-      hipLaunchKernelGGL(colsum_partial_kernel<false>, grid, block, 0, s, A, M, N, rows, partials);
+      hipLaunchKernelGGL(colsum_partial_kernel<false>, grid, dim3(256), 0, s, pp, M, N, rows, partials);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s,
-                     partials, rb, N, out, accumulate ? 1 : 0);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)groups), dim3(256), 0,
+                     s, pp, partials, rb, N, accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// K-split sums: C[g] = C[g] + part[g (n - 1)] + ... + part[g (n - 1) + n - 2]
+// for every group g, in slice order, one launch (blockIdx.y = group).
+// ---------------------------------------------------------------------------
+struct SplitPtrs {
+  float* C[kMaxGroups];
+};
+
+template <int NC>
+__global__ __launch_bounds__(256) void split_reduce_kernel(SplitPtrs pp, const float* __restrict__ part,
+                                                           int64_t part_stride, int n, int64_t count) {
+  constexpr int U = 4;
+  const int nn = NC > 0 ? NC : n;
+  const int g = blockIdx.y;
+  float* __restrict__ C = pp.C[g];
+  const float* __restrict__ base = part + (int64_t)g * (nn - 1) * part_stride;
+  const int64_t n4 = count >> 2;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * U;
+  for (int64_t v0 = (int64_t)blockIdx.x * blockDim.x * U + threadIdx.x; v0 < n4; v0 += stride) {
+    f32x4_t acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + (int64_t)u * blockDim.x;
+      acc[u] = v < n4 ? reinterpret_cast<const f32x4_t*>(C)[v] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (NC > 0) {
+      f32x4_t t[NC > 1 ? NC - 1 : 1][U];
+#pragma unroll
+      for (int i = 1; i < NC; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + (int64_t)u * blockDim.x;
+          t[i - 1][u] = v < n4 ? __builtin_nontemporal_load(
+                                     reinterpret_cast<const f32x4_t*>(base + (i - 1) * part_stride) + v)
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int i = 1; i < NC; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = acc[u] + t[i - 1][u];
+    } else {
+      for (int i = 1; i < nn; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + (int64_t)u * blockDim.x;
+          if (v < n4)
+            acc[u] = acc[u] + __builtin_nontemporal_load(
+                                  reinterpret_cast<const f32x4_t*>(base + (i - 1) * part_stride) + v);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + (int64_t)u * blockDim.x;
+      if (v < n4) reinterpret_cast<f32x4_t*>(C)[v] = acc[u];
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (count & 3)) {
+    const int64_t e = (n4 << 2) + threadIdx.x;
+    float t = C[e];
+    for (int i = 1; i < nn; ++i) t = t + base[(i - 1) * part_stride + e];
+    C[e] = t;
+  }
+}
+
+hipError_t launch_split_reduce(float* const* C, int groups, const float* part, int64_t part_stride,
+                               int n, int64_t count, hipStream_t s) {
+  if (n <= 1 || count <= 0 || groups < 1) return hipSuccess;
+  if (groups > kMaxGroups) return hipErrorInvalidValue;
+  SplitPtrs pp{};
+  for (int g = 0; g < groups; ++g) pp.C[g] = C[g];
+  int64_t blocks = ((count >> 2) + 1023) / 1024;
+  const int64_t cap = 2048 / groups + 1;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks, (unsigned)groups), block(256);
+  switch (n) {
+    case 2: hipLaunchKernelGGL(split_reduce_kernel<2>, grid, block, 0, s, pp, part, part_stride, n, count); break;
+    case 4: hipLaunchKernelGGL(split_reduce_kernel<4>, grid, block, 0, s, pp, part, part_stride, n, count); break;
+    case 8: hipLaunchKernelGGL(split_reduce_kernel<8>, grid, block, 0, s, pp, part, part_stride, n, count); break;
+    default: hipLaunchKernelGGL(split_reduce_kernel<0>, grid, block, 0, s, pp, part, part_stride, n, count); break;
+  }
   return hipGetLastError();
 }
 

@@ -137,18 +137,18 @@ int act_grad_steps(const void* dZ, const void* const* V, const void* const* G, v
 }
 
 // Weight-gradient workspace for a batch of `groups` shards: the larger
-// K-split of the two weight GEMMs, then the column-sum partials of one shard.
+// K-split of the two weight GEMMs, then the column-sum partials of the batch.
 size_t split_bytes(int groups, int64_t M, int64_t H, int64_t Fk, int dtype) {
   const bool bf16 = dtype == TP_BF16;
   const size_t a = tpmlp::gemm_split_workspace_bytes(bf16, groups, Fk, H, M);
   const size_t b = tpmlp::gemm_split_workspace_bytes(bf16, groups, H, Fk, M);
   return round_up(a > b ? a : b, kWsAlign);
 }
-size_t colsum_bytes(int64_t M, int64_t Fk) {
-  return round_up(size_t(tpmlp::colsum_partials_floats(M, Fk)) * 4, kWsAlign);
+size_t colsum_bytes(int groups, int64_t M, int64_t Fk) {
+  return round_up(size_t(groups) * size_t(tpmlp::colsum_partials_floats(M, Fk)) * 4, kWsAlign);
 }
 size_t grad_weight_ws(int groups, int64_t M, int64_t H, int64_t Fk, int dtype) {
-  return split_bytes(groups, M, H, Fk, dtype) + colsum_bytes(M, Fk);
+  return split_bytes(groups, M, H, Fk, dtype) + colsum_bytes(groups, M, Fk);
 }
 
 // dV_i (+)= Y_i^T dZ: ([M, Fk] read as its transpose) x [M, H], K = M.
@@ -179,10 +179,8 @@ int col_weight_steps(const void* X, const void* const* dA, float* const* dW, flo
   if (st || !db) return st;
   float* partials =
       reinterpret_cast<float*>(static_cast<char*>(ws) + split_bytes(n, M, H, Fk, dtype));
-  for (int i = 0; i < n && !st; ++i)
-    st = hip_status(
-        tpmlp::launch_colsum(dA[i], dtype == TP_BF16, M, Fk, db[i], accumulate, partials, s));
-  return st;
+  return hip_status(
+      tpmlp::launch_colsum(dA, n, dtype == TP_BF16, M, Fk, db, accumulate, partials, s));
 }
 
 // dX_i (+)= dA_i W_i^T: [M, Fk] x ([H, Fk] read as its transpose); one output

@@ -83,12 +83,19 @@ hipError_t launch_gemm_split(const GemmBatch& b, bool bf16, void* ws, hipStream_
 hipError_t launch_shard_reduce(const float* const* parts, int k, float* Z, int64_t n,
                                hipStream_t s);
 
-// out[n] (+)= sum_m A[m, n] for A [M, N] row-major (bf16 when `bf16`, else
-// float32), N a multiple of 8.  Deterministic: rows are summed in fixed
-// blocks whose float32 partials go to `partials` and are then added in order.
-// `partials` holds colsum_partials_floats(M, N) floats.
+// out[g][n] (+)= sum_m A[g][m, n] for `groups` matrices A[g] [M, N] row-major
+// (bf16 when `bf16`, else float32), N a multiple of 8, in one pass of two
+// launches.  Deterministic: rows are summed in fixed blocks whose float32
+// partials go to `partials` and are then added in a fixed order.
+// `partials` holds groups * colsum_partials_floats(M, N) floats.
 int64_t colsum_partials_floats(int64_t M, int64_t N);
-hipError_t launch_colsum(const void* A, bool bf16, int64_t M, int64_t N, float* out,
-                         bool accumulate, float* partials, hipStream_t s);
+hipError_t launch_colsum(const void* const* A, int groups, bool bf16, int64_t M, int64_t N,
+                         float* const* out, bool accumulate, float* partials, hipStream_t s);
+
+// C[g][e] = C[g][e] + part[g (n-1)][e] + ... + part[g (n-1) + n-2][e] for
+// 0 <= e < count and every group, in slice order (the K-split sums); part
+// entries are part_stride floats apart.
+hipError_t launch_split_reduce(float* const* C, int groups, const float* part, int64_t part_stride,
+                               int n, int64_t count, hipStream_t s);
 
 }  // namespace tpmlp
