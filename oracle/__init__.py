@@ -19,13 +19,25 @@ Backward for dZ = dL/dZ (chain rule through the same steps):
   dV_i = Y_i^T dZ,  dW_i = X^T dA_i,  db_i = colsum(dA_i),
   dX = sum_i dA_i W_i^T.
 
+Sequence parallelism: the all-reduce becomes a reduce-scatter over row
+blocks of the sequence, with the block's residual added to each block:
+  O_r = X[r Mb:(r+1) Mb] + (sum_i Z_i)[r Mb:(r+1) Mb],  Mb = M / k.
+SwiGLU variant (no biases):
+  Y_i = SiLU(X Wg_i) * (X Wu_i),  SiLU(x) = x / (1 + exp(-x)),  Z = sum_i Y_i V_i.
+
 Every forward function here is pinned by tests/test_oracle_pins.py (brute
 force in exact rational arithmetic with 50-digit erf, the column-split and
 row-split identities, GeLU closed forms, special cases that reduce to library
 routines, row independence and exact scaling); every backward function by
 tests/test_oracle_backward_pins.py (50-digit numerical differentiation of the
 exact forward, float64 autograd of an independent implementation, GeLU' closed
-forms, the ones-column identity between db and dW, k-invariance, linearity).
+forms, the ones-column identity between db and dW, k-invariance, linearity);
+the sequence-parallel and SwiGLU functions by tests/test_oracle_sp_swiglu_pins.py
+(exact small-integer sums and a hand-worked block split, the all-gather of the
+blocks against the all-reduce, residual-only and zero-residual cases, row
+locality; SiLU closed forms and 50-digit values, exact rational brute force,
+gate/up asymmetry, the column- and row-split identities and k-invariance, an
+independent numpy implementation).
 """
 from __future__ import annotations
 
@@ -67,6 +79,12 @@ def _L():
         lib.oracle_shard_reduce.argtypes = [vp, ci, i64, vp]
         lib.oracle_forward_rows.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp, i64, vp]
         lib.oracle_max_threads.restype = ci
+        lib.oracle_sp_reduce_scatter.argtypes = [vp, ci, vp, ci, i64, i64, vp]
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_silu_array.argtypes = [vp, i64, vp]
+        lib.oracle_swiglu_col.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        lib.oracle_swiglu_forward_rows.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp, i64, vp]
         lib.oracle_gelu_grad.argtypes = [ctypes.c_double]
         lib.oracle_gelu_grad.restype = ctypes.c_double
         lib.oracle_gelu_grad_array.argtypes = [vp, i64, vp]
@@ -81,7 +99,9 @@ def _L():
                   lib.oracle_row_partial, lib.oracle_shard_reduce, lib.oracle_forward_rows,
                   lib.oracle_gelu_grad_array, lib.oracle_col_gelu_grad, lib.oracle_act_grad,
                   lib.oracle_row_weight_grad, lib.oracle_col_weight_grad,
-                  lib.oracle_input_grad_partial, lib.oracle_backward_rows, lib.oracle_backward_cols):
+                  lib.oracle_input_grad_partial, lib.oracle_backward_rows, lib.oracle_backward_cols,
+                  lib.oracle_sp_reduce_scatter, lib.oracle_silu_array, lib.oracle_swiglu_col,
+                  lib.oracle_swiglu_forward_rows):
             f.restype = None
         _lib = lib
     return _lib
@@ -338,3 +358,94 @@ def backward(X, W, b, V, dZ, k: int):
         parts.append(input_grad_partial(dAi, W, k, i))
     dX = shard_reduce(parts)
     return dX, dW, db, dV
+
+
+# ---------------------------------------------------------------------------
+# Sequence parallelism.
+
+def sp_reduce_scatter(parts, R, k: int):
+    """Blocks O_r = R[r Mb:(r+1) Mb] + (parts[0] + ... )[r Mb:(r+1) Mb] for
+    r < k, Mb = M / k; float64 [Mb, H] each.  R may be None (no residual)."""
+    ws = [np.ascontiguousarray(widen(p)) for p in parts]
+    if not ws:
+        raise ValueError("need at least one part")
+    M, H = ws[0].shape
+    assert all(w.shape == (M, H) for w in ws)
+    if k < 1 or M % k:
+        raise ValueError("k must be >= 1 and divide M")
+    R64 = np.ascontiguousarray(widen(R)) if R is not None else None
+    if R64 is not None:
+        assert R64.shape == (M, H)
+    outs = [np.empty((M // k, H)) for _ in range(k)]
+    pp = (ctypes.c_void_p * len(ws))(*[w.ctypes.data for w in ws])
+    po = (ctypes.c_void_p * k)(*[o.ctypes.data for o in outs])
+    if M:
+        _L().oracle_sp_reduce_scatter(pp, len(ws), _p(R64), k, M, H, po)
+    return outs
+
+
+def sp_forward(X, W, b, V, k: int):
+    """Sequence-parallel block output: the k blocks of X + sum_i Z_i."""
+    X64 = widen(X)
+    parts = [row_partial(col_gelu(X64, W, b, k, i), V, k, i) for i in range(k)]
+    return sp_reduce_scatter(parts, X64, k)
+
+
+def sp_forward_rows(X, W, b, V, k: int, rows) -> np.ndarray:
+    """Rows `rows` (indices into the gathered [M, H]) of the blocks' union,
+    X[rows] + Z[rows], float64."""
+    X64 = widen(X)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    Z = forward_rows(X64, W, b, V, k, r)
+    return sp_reduce_scatter([Z], X64[r], 1)[0]
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU.
+
+def silu_scalar(x: float) -> float:
+    return float(_L().oracle_silu(float(x)))
+
+
+def silu(x) -> np.ndarray:
+    x = widen(x)
+    y = np.empty_like(x)
+    _L().oracle_silu_array(_p(x), x.size, _p(y))
+    return y
+
+
+def swiglu_col(X, Wg, Wu, k: int, i: int) -> np.ndarray:
+    """Y_i = SiLU(X Wg_i) * (X Wu_i), float64 [M, F/k]."""
+    X, Wg, Wu = widen(X), widen(Wg), widen(Wu)
+    M, H = X.shape
+    F = Wg.shape[1]
+    assert Wg.shape == (H, F) and Wu.shape == (H, F)
+    _check_shard(F, k, i)
+    Y = np.empty((M, F // k))
+    _L().oracle_swiglu_col(_p(X), _p(Wg), _p(Wu), M, H, F, k, i, _p(Y))
+    return Y
+
+
+def swiglu_forward_rows(X, Wg, Wu, V, k: int, rows=None) -> np.ndarray:
+    """Z[rows, :] of the SwiGLU forward, float64 (all rows if None)."""
+    X, Wg, Wu, V = widen(X), widen(Wg), widen(Wu), widen(V)
+    M, H = X.shape
+    F = Wg.shape[1]
+    assert Wg.shape == (H, F) and Wu.shape == (H, F) and V.shape == (F, H)
+    _check_shard(F, k, 0)
+    if rows is None:
+        r, nrows = None, M
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        if r.size and (r.min() < 0 or r.max() >= M):
+            raise IndexError("row index out of range")
+        nrows = r.size
+    Z = np.empty((nrows, H))
+    if nrows:
+        _L().oracle_swiglu_forward_rows(_p(X), _p(Wg), _p(Wu), _p(V), H, F, k, _p(r), nrows, _p(Z))
+    return Z
+
+
+def swiglu_forward(X, Wg, Wu, V, k: int) -> np.ndarray:
+    """Z = sum_i (SiLU(X Wg_i) * (X Wu_i)) V_i, float64 [M, H]."""
+    return swiglu_forward_rows(X, Wg, Wu, V, k, None)

@@ -40,6 +40,27 @@
  *  10. dX = dX_0 + ... + dX_{k-1}: X feeds every shard, so its gradient is the
  *      sum over shards (the backward all-reduce).
  *
+ * Sequence parallelism (Megatron's split of the block's non-TP region along
+ * the sequence, "AI大模型分布式训练：张量并行与流水线并行深度实践" §4.2, with
+ * LayerNorm/Dropout sharded along the sequence: "大模型分布式训练四维并行：DDP、
+ * ZeRO、张量、流水线与上下文" §4.3):
+ *  11. the all-reduce of step 5 is a reduce-scatter followed by an all-gather
+ *      (the ring decomposition, §2.1 of that page); under sequence
+ *      parallelism each of the k ranks keeps only its reduce-scatter block,
+ *      the sum over its rows [r M/k, (r+1) M/k) of the sequence;
+ *  12. the block's residual connection x + mlp(x) (the TransformerBlock of
+ *      §3.4 on the page above) is added to that block:
+ *      O_r = X[rows of r] + Z[rows of r].
+ *
+ * SwiGLU variant of the block (gate_proj and up_proj column-parallel,
+ * down_proj row-parallel: §6.1 of the page above; gate_up_proj column- and
+ * down_proj row-parallel for Llama-2-70B: "大模型分布式优化技术（一）"
+ * §5.1, which names the SwiGLU activation in §3.3); the formula is not on
+ * the pages and is taken as Llama's, without biases:
+ *  13. Y_i = SiLU(X Wg_i) * (X Wu_i), SiLU(x) = x sigma(x) = x / (1 + e^-x),
+ *      with Wg_i, Wu_i the column blocks i of Wg, Wu [H, F]; steps 4 and 5
+ *      are unchanged (Z_i = Y_i V_i, Z = sum_i Z_i).
+ *
  * All arrays are row-major doubles; the Python wrapper widens bf16/f32 inputs
  * to double exactly before calling.  Sums run in index order.  Parallelism is
  * over output rows only (OpenMP), which does not change any value.
@@ -321,6 +342,89 @@ void oracle_backward_cols(const double* X, const double* W, const double* b, con
     }
     free(y);
     free(da);
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Sequence parallelism (steps 11-12).                                     */
+
+/* For each rank r < k, rows [r*Mb, (r+1)*Mb) with Mb = M / k (k divides M):
+   out[r][m*H + n] = R[(r*Mb + m)*H + n] + sum_i parts[i][(r*Mb + m)*H + n],
+   the sum over parts in index order.  R == NULL: no residual. */
+void oracle_sp_reduce_scatter(const double* const* parts, int nparts, const double* R, int k,
+                              int64_t M, int64_t H, double* const* out) {
+  const int64_t Mb = M / k;
+  for (int r = 0; r < k; ++r) {
+    double* o = out[r];
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < Mb; ++m) {
+      const int64_t row = r * Mb + m;
+      for (int64_t n = 0; n < H; ++n) {
+        double s = 0.0;
+        for (int i = 0; i < nparts; ++i) s += parts[i][row * H + n];
+        o[m * H + n] = (R ? R[row * H + n] : 0.0) + s;
+      }
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* SwiGLU (step 13).                                                       */
+
+/* SiLU(x) = x sigma(x) = x / (1 + exp(-x)); for x -> -inf, exp(-x)
+   overflows to +inf and the quotient is (-)0, the limit. */
+double oracle_silu(double x) { return x / (1.0 + exp(-x)); }
+
+void oracle_silu_array(const double* x, int64_t n, double* y) {
+  for (int64_t i = 0; i < n; ++i) y[i] = oracle_silu(x[i]);
+}
+
+/* Y_i[M,Fk] = SiLU(X Wg_i) * (X Wu_i) of shard i. */
+void oracle_swiglu_col(const double* X, const double* Wg, const double* Wu, int64_t M, int64_t H,
+                       int64_t F, int k, int i, double* Y) {
+  const int64_t Fk = F / k;
+#pragma omp parallel
+  {
+    double* u = (double*)malloc(sizeof(double) * (size_t)(Fk > 0 ? Fk : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+      double* y = Y + m * Fk;
+      preact_row(X, Wg, NULL, m, H, F, Fk, i, y);
+      preact_row(X, Wu, NULL, m, H, F, Fk, i, u);
+      for (int64_t j = 0; j < Fk; ++j) y[j] = oracle_silu(y[j]) * u[j];
+    }
+    free(u);
+  }
+}
+
+/* Whole SwiGLU forward for selected rows (steps 13, 4, 5):
+   Z[r, :] = sum_i (SiLU(x Wg_i) * (x Wu_i)) V_i with x = X[rows[r], :]
+   (rows == NULL: 0..nrows-1). */
+void oracle_swiglu_forward_rows(const double* X, const double* Wg, const double* Wu,
+                                const double* V, int64_t H, int64_t F, int k, const int64_t* rows,
+                                int64_t nrows, double* Z) {
+  const int64_t Fk = F / k;
+#pragma omp parallel
+  {
+    double* y = (double*)malloc(sizeof(double) * (size_t)Fk);
+    double* u = (double*)malloc(sizeof(double) * (size_t)Fk);
+    double* zi = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+      const int64_t m = rows ? rows[r] : r;
+      double* z = Z + r * H;
+      for (int64_t n = 0; n < H; ++n) z[n] = 0.0;
+      for (int i = 0; i < k; ++i) {
+        preact_row(X, Wg, NULL, m, H, F, Fk, i, y);
+        preact_row(X, Wu, NULL, m, H, F, Fk, i, u);
+        for (int64_t j = 0; j < Fk; ++j) y[j] = oracle_silu(y[j]) * u[j];
+        partial_row(y, V, H, Fk, i, zi);
+        for (int64_t n = 0; n < H; ++n) z[n] += zi[n];
+      }
+    }
+    free(y);
+    free(u);
+    free(zi);
   }
 }
 
