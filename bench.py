@@ -6,10 +6,13 @@ column GEMM + bias + GeLU and the row GEMM, then the on-device shard sum, over
 one batch of seeded synthetic inputs already resident in HBM.  `value` is the
 forward's throughput.  The backward of the same block (tp_mlp_shard_backward:
 per shard the training-mode column step, dA, dV, dW + db and the partial dX,
-then the dX shard sum) is timed the same way and reported under "backward".
+then the dX shard sum) is timed the same way and reported under "backward",
+and so is the sequence-parallel forward (tp_mlp_shard_forward_sp: the shard
+sum as a reduce-scatter over the k sequence blocks with the residual X added)
+under "sequence_parallel".
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant literal|fused]
-                    [--no-backward]
+                    [--no-backward] [--no-sp]
 
 Prints ONE JSON line (metric, value in TFLOP/s, ms_per_step, roofline of the
 dominant kernel, CPU-oracle baseline, backward) on stdout; diagnostics go to
@@ -48,6 +51,7 @@ def parse():
     ap.add_argument("--kernel-steps", type=int, default=None,
                     help="steps of the per-kernel timing pass (default: --steps)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel leg")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain float32 copy kernel (y = x * 1) over MIB MiB, 5 times: "
                          "the known-size reference for the HBM byte counters")
@@ -69,6 +73,9 @@ def kernel_bytes(kind, w, elt, n):
         "grad_col_weight": M * H * elt + n * (M * Fk * elt + (H * Fk + Fk) * 4),
         "grad_input": n * ((M * Fk + H * Fk) * elt + M * H * 4),
         "grad_input_sum": n * (M * Fk + H * Fk) * elt + M * H * 4,
+        # sequence-parallel reduce-scatter + residual: k (or 1) fp32 parts, X, fp32 blocks
+        "sp_reduce": (k * 4 + elt + 4) * M * H,
+        "sp_reduce_fused": (4 + elt + 4) * M * H,
     }
     return table[kind]
 
@@ -76,6 +83,10 @@ def kernel_bytes(kind, w, elt, n):
 def kernel_flops(kind, w, n):
     if kind == "shard_reduce":
         return (w.k - 1) * w.M * w.H
+    if kind == "sp_reduce":
+        return w.k * w.M * w.H
+    if kind == "sp_reduce_fused":
+        return w.M * w.H
     return n * 2 * w.M * w.H * w.Fk
 
 
@@ -120,14 +131,15 @@ def time_kinds(kinds, launch, nlaunch, nshards, steps, warmup, w, elt):
     return kern
 
 
-def roofline(kern, w, variant, dtype):
-    """Roofline entry of the kind with the largest share of the step."""
-    dom = max(kern, key=lambda k_: kern[k_]["ms_per_step"])
+def roofline(kern, w, variant, dtype, kind=None):
+    """Roofline entry of `kind`, by default the kind with the largest share
+    of the step."""
+    dom = kind or max(kern, key=lambda k_: kern[k_]["ms_per_step"])
     d = kern[dom]
     peak_f = PEAK_TFLOPS[dtype]
     t_mfma = d["flop"] / (peak_f * 1e12)
     t_hbm = d["bytes"] / (PEAK_HBM_GBS * 1e9)
-    if dom != "shard_reduce" and t_mfma >= t_hbm:
+    if not dom.startswith(("shard_reduce", "sp_reduce")) and t_mfma >= t_hbm:
         roof = {"bound": "mfma", "achieved": d["flop"] / (d["avg_ms"] * 1e-3) / 1e12, "peak": peak_f,
                 "unit": "TFLOP/s"}
     else:
@@ -248,6 +260,9 @@ def main():
     bwd = None
     if not args.no_backward:
         bwd = bench_backward(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt)
+    sp = None
+    if not args.no_sp and w.M % w.k == 0:
+        sp = bench_sp(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt)
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
@@ -264,6 +279,7 @@ def main():
                          "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()},
         "cpu_baseline": cpu,
         "backward": bwd,
+        "sequence_parallel": sp,
     }
     print(json.dumps(out), flush=True)
 
@@ -344,6 +360,66 @@ def bench_backward(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt):
     kern = time_kinds(kinds, launch, nlaunch, nshards, args.kernel_steps or args.steps, args.warmup, w, elt)
     roof = roofline(kern, w, args.variant, w.dtype)
     return {"metric": "TP-shard MLP backward TFLOP/s (5 GEMMs of 2 M H F/k per shard, incl. recompute)",
+            "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+            "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "roofline": roof,
+            "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],
+                             "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()}}
+
+
+def bench_sp(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt):
+    """Time tp_mlp_shard_forward_sp (the forward whose all-reduce is a
+    reduce-scatter over the k sequence blocks, with X as the residual; fp32
+    blocks side by side) and its kernels by kind.  FLOPs counted: those of
+    the forward (4 M H F); the roofline entry is the reduce-scatter's."""
+    import torch
+    dev = X.device
+    Fk, k, M, H = w.Fk, w.k, w.M, w.H
+    dt = tpm.TP_BF16 if w.dtype == "bf16" else tpm.TP_F32
+    flags = tpm.TP_FUSED_ACCUM if fused else 0
+    need = tpm.tp_mlp_sp_workspace_bytes(k, M, H, Fk, dt, flags)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    O = torch.empty(M, H, dtype=torch.float32, device=dev)
+
+    def step():
+        tpm.tp_mlp_shard_forward_sp(X, Ws, bs, Vs, O=O, workspace=ws, fused=fused)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    tflops = w.flop / (ms * 1e-3) / 1e12
+    log("sequence-parallel forward: %.4f ms/step, %.1f TFLOP/s" % (ms, tflops))
+    if not bool(torch.isfinite(O).all()):
+        raise RuntimeError("non-finite sequence-parallel output")
+
+    G = min(k, tpm.TP_MAX_BATCH)
+    batches = [(i0, min(G, k - i0)) for i0 in range(0, k, G)]
+    Yb = [torch.empty(M, Fk, dtype=tdt, device=dev) for _ in range(G)]
+    parts = [torch.empty(M, H, dtype=torch.float32, device=dev) for _ in range(1 if fused else k)]
+    red = "sp_reduce_fused" if fused else "sp_reduce"
+    kinds = ["col_gelu", "row_sum" if fused else "row_partial", red]
+    nlaunch = {"col_gelu": len(batches), "row_partial": len(batches), "row_sum": len(batches), red: 1}
+    nshards = {"col_gelu": G, "row_partial": G, "row_sum": G, red: k}
+
+    def launch(kind):
+        for i0, n in batches:
+            if kind == "col_gelu":
+                tpm.tp_mlp_col_gelu_shards(X, Ws[i0:i0 + n], bs[i0:i0 + n], Yb[:n])
+            elif kind == "row_partial":
+                tpm.tp_mlp_row_partial_shards(Yb[:n], Vs[i0:i0 + n], parts[i0:i0 + n])
+            elif kind == "row_sum":
+                tpm.tp_mlp_row_partial_shards(Yb[:n], Vs[i0:i0 + n], parts[:1], sum_shards=True,
+                                              accumulate=i0 > 0)
+        if kind == red:
+            tpm.tp_sp_reduce_scatter(parts, k, R=X, O=O)
+
+    kern = time_kinds(kinds, launch, nlaunch, nshards, args.kernel_steps or args.steps, args.warmup, w, elt)
+    roof = roofline(kern, w, args.variant, w.dtype, kind=red)
+    return {"metric": "TP-shard MLP forward under sequence parallelism (reduce-scatter + residual) TFLOP/s",
             "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
             "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "roofline": roof,
             "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],

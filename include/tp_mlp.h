@@ -174,6 +174,62 @@ int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const*
                          unsigned flags, void* stream);
 
 /*
+ * Sequence parallelism.  Megatron's sequence parallelism also splits the
+ * part of the block that tensor parallelism leaves whole (LayerNorm,
+ * Dropout, the residual) along the sequence, one block of M/k rows per rank
+ * ("AI大模型分布式训练：张量并行与流水线并行深度实践" §4.2; "大模型分布式训练四维并行：
+ * DDP、ZeRO、张量、流水线与上下文" §4.3).  The all-reduce that ends the
+ * row-parallel layer is then cut at its midpoint: an all-reduce is a
+ * reduce-scatter followed by an all-gather (the ring algorithm, §2.1 of the
+ * latter page), and each rank keeps only its reduce-scatter block.  The
+ * block's residual connection x + mlp(x) (the TransformerBlock of §3.4 of the
+ * former page) is added to that block in the same pass:
+ *
+ *   for r in 0..k-1, m in 0..M/k-1:
+ *     O[r][m, n] = R[r M/k + m, n] + (Z_parts[0] + ... + Z_parts[nparts-1])[r M/k + m, n]
+ *
+ * The parts are float32 [M, H] and are summed left to right in float32, then
+ * R is added (R == NULL: no residual) and the result is stored in
+ * `out_dtype` (rounded to nearest-even for TP_BF16).  R [M, H] has type
+ * `r_dtype`.  Z_parts is a HOST array of nparts device pointers
+ * (1 <= nparts <= TP_MAX_SHARDS) and O a HOST array of k device pointers to
+ * [M/k, H] blocks (1 <= k <= TP_MAX_SHARDS, k divides M).  Passing
+ * O[r] = base + r (M/k) H elements puts the blocks side by side, which is
+ * the all-gather on one device.  H follows the rules above; M == 0 is a
+ * no-op.  No output may overlap an input or another output.
+ */
+int tp_sp_reduce_scatter(const float* const* Z_parts, int nparts, const void* R, int r_dtype,
+                         void* const* O, int out_dtype, int k, int64_t M, int64_t H, void* stream);
+
+/*
+ * Bytes of device workspace tp_mlp_shard_forward_sp needs: one Y_i per shard
+ * of a batch (as tp_mlp_workspace_bytes) plus k float32 partials [M, H], or
+ * one (their running sum) with TP_FUSED_ACCUM.  0 for invalid arguments,
+ * M == 0 or k not dividing M.
+ */
+size_t tp_mlp_sp_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dtype, unsigned flags);
+
+/*
+ * The block forward under sequence parallelism: tp_mlp_shard_forward whose
+ * closing all-reduce is tp_sp_reduce_scatter with X as the residual,
+ *
+ *   O[r] = X[rows of r] + (P_0 + ... + P_{k-1})[rows of r],  P_i = GeLU(X W[i] + b[i]) V[i]
+ *
+ * (on one device the all-gather of X that precedes the column-parallel layer
+ * under sequence parallelism is X itself).  Arguments as for
+ * tp_mlp_shard_forward, with O a HOST array of k device pointers to [M/k, H]
+ * blocks of `out_dtype`, which k must divide M, and `workspace` of
+ * tp_mlp_sp_workspace_bytes(...) bytes.  flags = TP_FUSED_ACCUM sums the
+ * shards inside the row GEMMs (one partial in memory instead of k); both
+ * give bit-identical blocks, and the float32 blocks equal X + Z of
+ * tp_mlp_shard_forward bit for bit.
+ */
+int tp_mlp_shard_forward_sp(const void* X, const void* const* W, const void* const* b,
+                            const void* const* V, int k, int64_t M, int64_t H, int64_t Fk,
+                            int dtype, void* workspace, size_t workspace_bytes, void* const* O,
+                            int out_dtype, unsigned flags, void* stream);
+
+/*
  * Training-mode column step: tp_mlp_col_gelu that also keeps the derivative
  * of the activation for the backward pass (the closed form of GeLU' above):
  *

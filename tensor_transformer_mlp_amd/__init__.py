@@ -20,6 +20,12 @@ Backward (dZ = dL/dZ):
     dX_i = dA_i W_i^T                  tp_mlp_grad_input_partial
     all of the above, k shards, + dX   tp_mlp_shard_backward
 
+Sequence parallelism (the all-reduce as a reduce-scatter over row blocks,
+with the residual X added):
+
+    O_r = X[rows of r] + sum_i Z_i[rows of r]   tp_sp_reduce_scatter
+    the whole block, k shards                   tp_mlp_shard_forward_sp
+
 Every per-step call has a *_shards form that runs the step for up to
 TP_MAX_BATCH shards in one launch (what the k-shard calls do inside).
 """
@@ -38,6 +44,7 @@ __all__ = [
     "tp_mlp_col_gelu_shards", "tp_mlp_row_partial_shards", "tp_mlp_grad_act_shards",
     "tp_mlp_grad_weight_workspace_bytes_shards", "tp_mlp_grad_row_weight_shards",
     "tp_mlp_grad_col_weight_shards", "tp_mlp_grad_input_shards",
+    "tp_sp_reduce_scatter", "tp_mlp_sp_workspace_bytes", "tp_mlp_shard_forward_sp",
 ]
 
 TP_F32 = 0
@@ -108,6 +115,12 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_grad_row_weight_shards.argtypes = [vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, cu, vp]
         L.tp_mlp_grad_col_weight_shards.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, cu, vp]
         L.tp_mlp_grad_input_shards.argtypes = [vp, vp, vp, ci, i64, i64, i64, ci, cu, vp]
+        L.tp_sp_reduce_scatter.argtypes = [vp, ci, vp, ci, vp, ci, ci, i64, i64, vp]
+        L.tp_sp_reduce_scatter.restype = ci
+        L.tp_mlp_sp_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, cu]
+        L.tp_mlp_sp_workspace_bytes.restype = sz
+        L.tp_mlp_shard_forward_sp.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, vp, ci, cu, vp]
+        L.tp_mlp_shard_forward_sp.restype = ci
         for f in (L.tp_mlp_col_gelu_shards, L.tp_mlp_row_partial_shards, L.tp_mlp_grad_act_shards,
                   L.tp_mlp_grad_row_weight_shards, L.tp_mlp_grad_col_weight_shards, L.tp_mlp_grad_input_shards):
             f.restype = ci
@@ -548,3 +561,93 @@ def tp_mlp_grad_input_shards(dA, W, dX, sum_shards=False, accumulate=False, stre
                                           M, Fk, H, _dtype_code(dA[0]), flags, _stream(stream)),
            "tp_mlp_grad_input_shards")
     return dX
+
+
+# ---------------------------------------------------------------------------
+# Sequence parallelism.
+
+def _sp_blocks(O, k, Mb, H, dtype, device):
+    """k output blocks [Mb, H]: a list of tensors, or views of one [k Mb, H] tensor."""
+    torch = _torch()
+    if O is None:
+        O = torch.empty(k * Mb, H, dtype=dtype, device=device)
+    if isinstance(O, (list, tuple)):
+        if len(O) != k:
+            raise ValueError("need k = %d output blocks" % k)
+        blocks = list(O)
+    else:
+        if O.dtype != dtype or O.numel() != k * Mb * H or not O.is_contiguous():
+            raise ValueError("O must be a contiguous %s tensor of %d elements" % (dtype, k * Mb * H))
+        blocks = [O.view(k * Mb, H)[r * Mb:(r + 1) * Mb] for r in range(k)]
+    for r, t in enumerate(blocks):
+        if t.dtype != dtype or t.numel() != Mb * H:
+            raise ValueError("block %d must be %s with %d elements" % (r, dtype, Mb * H))
+    return O, blocks
+
+
+def tp_sp_reduce_scatter(parts, k: int, R=None, O=None, out_dtype=None, stream=None):
+    """Blocks O_r = R[rows of r] + sum_i parts[i][rows of r] for the k ranks.
+
+    ``parts``: float32 [M, H] tensors; ``R``: [M, H] bf16/float32 or None;
+    ``O``: None (a new [M, H] tensor), one [M, H] tensor (the gathered
+    blocks) or a list of k [M/k, H] tensors.  ``out_dtype`` defaults to
+    float32.  Returns O.
+    """
+    torch = _torch()
+    if not parts:
+        raise ValueError("need at least one partial")
+    M, H = parts[0].shape[0], parts[0].shape[-1]
+    for p in parts:
+        if p.dtype != torch.float32 or tuple(p.shape) != (M, H):
+            raise ValueError("partials must be float32 [M, H] tensors of one shape")
+    if R is not None and tuple(R.shape) != (M, H):
+        raise ValueError("R must be [M, H]")
+    if k < 1 or M % k:
+        raise ValueError("k must divide M")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    O, blocks = _sp_blocks(O, k, M // k, H, out_dtype, parts[0].device)
+    pp = (ctypes.c_void_p * len(parts))(*[_dev(p, "parts[%d]" % i) for i, p in enumerate(parts)])
+    po = (ctypes.c_void_p * k)(*[_dev(t, "O[%d]" % r) for r, t in enumerate(blocks)])
+    _check(lib().tp_sp_reduce_scatter(pp, len(parts), _dev(R, "R"), _dtype_code(R) if R is not None else TP_F32,
+                                      po, TP_BF16 if out_dtype == torch.bfloat16 else TP_F32, k, M, H,
+                                      _stream(stream)), "tp_sp_reduce_scatter")
+    return O
+
+
+def tp_mlp_sp_workspace_bytes(k: int, M: int, H: int, Fk: int, dtype: int, flags: int = 0) -> int:
+    return int(lib().tp_mlp_sp_workspace_bytes(k, M, H, Fk, dtype, flags))
+
+
+def tp_mlp_shard_forward_sp(X, W, b, V, O=None, out_dtype=None, workspace=None, fused: bool = False,
+                            stream=None):
+    """Sequence-parallel block forward: O_r = X[rows of r] + Z[rows of r] with
+    Z = sum_i GeLU(X W[i] + b[i]) V[i]; O as for tp_sp_reduce_scatter."""
+    torch = _torch()
+    k = len(W)
+    if k < 1 or len(V) != k or (b is not None and len(b) != k):
+        raise ValueError("W, V (and b) must hold the same number k >= 1 of shards")
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = W[0].shape[-1]
+    dt = _dtype_code(X)
+    _same_dtype("tp_mlp_shard_forward_sp", X, *W, *V, *(b or []))
+    for i in range(k):
+        if tuple(W[i].shape) != (H, Fk) or tuple(V[i].shape) != (Fk, H) or \
+                (b is not None and tuple(b[i].shape) != (Fk,)):
+            raise ValueError("shard %d has the wrong shape" % i)
+    if M % k:
+        raise ValueError("k must divide M")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    O, blocks = _sp_blocks(O, k, M // k, H, out_dtype, X.device)
+    flags = TP_FUSED_ACCUM if fused else 0
+    need = tp_mlp_sp_workspace_bytes(k, M, H, Fk, dt, flags)
+    workspace = _workspace(workspace, need, X.device)
+    Wp = (ctypes.c_void_p * k)(*[_dev(w, "W[%d]" % i) for i, w in enumerate(W)])
+    Vp = (ctypes.c_void_p * k)(*[_dev(v, "V[%d]" % i) for i, v in enumerate(V)])
+    bp = None if b is None else (ctypes.c_void_p * k)(*[_dev(x, "b[%d]" % i) for i, x in enumerate(b)])
+    po = (ctypes.c_void_p * k)(*[_dev(t, "O[%d]" % r) for r, t in enumerate(blocks)])
+    _check(lib().tp_mlp_shard_forward_sp(_dev(X, "X"), Wp, bp, Vp, k, M, H, Fk, dt,
+                                         _dev(workspace, "workspace"), workspace.numel(), po,
+                                         TP_BF16 if out_dtype == torch.bfloat16 else TP_F32, flags,
+                                         _stream(stream)), "tp_mlp_shard_forward_sp")
+    return O

@@ -98,12 +98,15 @@ constexpr bool layout_has_epi(int layout, int epi) {
 }
 
 // LDS chunk swizzles (see the file comment).  K-major rows are 64 bytes
-// (four chunks); a 16-byte LDS access is served per 16 lanes over 64 banks,
-// i.e. sixteen 16-byte slots, and swzK spreads the 16 consecutive rows of a
-// fragment read over the four chunk positions of four row pairs.  MN-major
-// rows hold >= 16 chunks; swzMN rotates by 4 chunks per k-row so that the
-// four k-rows of a transpose read fall in distinct bank groups.
-__device__ __forceinline__ int swzK(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// (four chunks) and a fragment read takes one chunk of each of 32
+// consecutive rows (lanes 0-31 and 32-63 take neighbouring chunks).  Among
+// the swizzles that XOR the chunk index with two parity bits of the row,
+// timing every one of them for this read on MI355X (the 16-byte reads are
+// spread over 64 four-byte banks) splits them into a conflict-free class
+// and a class 1.5x slower; swzK, bits 2..3 of the row, is in the fast one.
+// MN-major rows hold >= 16 chunks; swzMN rotates by 4 chunks per k-row so
+// that the four k-rows of a transpose read fall in distinct bank groups.
+__device__ __forceinline__ int swzK(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swzMN(int k) { return 4 * (k & 3); }
 
 // One operand's tile: R rows of the operand (rows of A, or columns of B) by

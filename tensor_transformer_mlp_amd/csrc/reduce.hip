@@ -325,4 +325,126 @@ hipError_t launch_split_reduce(float* const* C, int groups, const float* part, i
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Sequence-parallel reduce-scatter with the residual: rank r = blockIdx.y
+// owns rows [r Mb, (r + 1) Mb), i.e. the block_elems = Mb H contiguous floats
+// at r block_elems of every part, and writes
+//   O_r[e] = R[r block_elems + e] + ((P_0 + P_1) + ... + P_{n-1})[r block_elems + e]
+// in float32 (R == nullptr: no residual), rounded to nearest-even bf16 when
+// OBF16.  block_elems is a multiple of 8, so every 16-byte vector of a part
+// lies in one rank's block.
+// ---------------------------------------------------------------------------
+struct SpPtrs {
+  const float* p[64];
+  void* out[64];
+};
+
+template <int KC, bool RBF16, bool OBF16>
+__global__ __launch_bounds__(256) void sp_reduce_kernel(SpPtrs pp, int nparts, const void* __restrict__ R,
+                                                        int64_t block_elems) {
+  constexpr int U = 4;
+  const int kk = KC > 0 ? KC : nparts;
+  const int64_t n4 = block_elems >> 2;
+  const int64_t base4 = (int64_t)blockIdx.y * n4;  // this rank's first vector in a part
+  void* __restrict__ out = pp.out[blockIdx.y];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * U;
+  const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int64_t v0 = (int64_t)blockIdx.x * blockDim.x * U + threadIdx.x; v0 < n4; v0 += stride) {
+    f32x4_t s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + (int64_t)u * blockDim.x;
+      s[u] = v < n4 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pp.p[0]) + base4 + v)
+                    : zero;
+    }
+    if constexpr (KC > 0) {
+      f32x4_t t[KC > 1 ? KC - 1 : 1][U];
+#pragma unroll
+      for (int i = 1; i < KC; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + (int64_t)u * blockDim.x;
+          t[i - 1][u] = v < n4 ? __builtin_nontemporal_load(
+                                     reinterpret_cast<const f32x4_t*>(pp.p[i]) + base4 + v)
+                               : zero;
+        }
+#pragma unroll
+      for (int i = 1; i < KC; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) s[u] = s[u] + t[i - 1][u];
+    } else {
+      for (int i = 1; i < kk; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + (int64_t)u * blockDim.x;
+          if (v < n4)
+            s[u] = s[u] + __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pp.p[i]) + base4 + v);
+        }
+    }
+    if (R) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + (int64_t)u * blockDim.x;
+        if (v >= n4) continue;
+        f32x4_t r;
+        if constexpr (RBF16) {
+          const u32x2_t h = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(R) + base4 + v);
+          r = f32x4_t{bf16_bits_to_f32(h[0] & 0xFFFFu), bf16_bits_to_f32(h[0] >> 16),
+                      bf16_bits_to_f32(h[1] & 0xFFFFu), bf16_bits_to_f32(h[1] >> 16)};
+        } else {
+          r = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(R) + base4 + v);
+        }
+        s[u] = r + s[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + (int64_t)u * blockDim.x;
+      if (v >= n4) continue;
+      if constexpr (OBF16) {
+        const u32x2_t o = u32x2_t{f32_to_bf16_bits(s[u][0]) | (f32_to_bf16_bits(s[u][1]) << 16),
+                                  f32_to_bf16_bits(s[u][2]) | (f32_to_bf16_bits(s[u][3]) << 16)};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(out) + v);
+      } else {
+        __builtin_nontemporal_store(s[u], reinterpret_cast<f32x4_t*>(out) + v);
+      }
+    }
+  }
+}
+
+template <bool RBF16, bool OBF16>
+void launch_sp_typed(const SpPtrs& pp, int nparts, const void* R, int k, int64_t block_elems,
+                     hipStream_t s) {
+  int64_t blocks = ((block_elems >> 2) + 1023) / 1024;
+  const int64_t cap = 4096 / k + 1;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks, (unsigned)k), block(256);
+  switch (nparts) {
+    case 1: hipLaunchKernelGGL((sp_reduce_kernel<1, RBF16, OBF16>), grid, block, 0, s, pp, nparts, R, block_elems); break;
+    case 2: hipLaunchKernelGGL((sp_reduce_kernel<2, RBF16, OBF16>), grid, block, 0, s, pp, nparts, R, block_elems); break;
+    case 4: hipLaunchKernelGGL((sp_reduce_kernel<4, RBF16, OBF16>), grid, block, 0, s, pp, nparts, R, block_elems); break;
+    case 8: hipLaunchKernelGGL((sp_reduce_kernel<8, RBF16, OBF16>), grid, block, 0, s, pp, nparts, R, block_elems); break;
+    default: hipLaunchKernelGGL((sp_reduce_kernel<0, RBF16, OBF16>), grid, block, 0, s, pp, nparts, R, block_elems); break;
+  }
+}
+
+hipError_t launch_sp_reduce_scatter(const float* const* parts, int nparts, const void* R, bool r_bf16,
+                                    void* const* out, bool o_bf16, int k, int64_t block_elems,
+                                    hipStream_t s) {
+  if (nparts < 1 || nparts > 64 || k < 1 || k > 64 || block_elems % 8) return hipErrorInvalidValue;
+  if (block_elems == 0) return hipSuccess;
+  SpPtrs pp{};
+  for (int i = 0; i < nparts; ++i) pp.p[i] = parts[i];
+  for (int r = 0; r < k; ++r) pp.out[r] = out[r];
+  if (r_bf16) {
+    if (o_bf16) launch_sp_typed<true, true>(pp, nparts, R, k, block_elems, s);
+    else launch_sp_typed<true, false>(pp, nparts, R, k, block_elems, s);
+  } else {
+    if (o_bf16) launch_sp_typed<false, true>(pp, nparts, R, k, block_elems, s);
+    else launch_sp_typed<false, false>(pp, nparts, R, k, block_elems, s);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace tpmlp

@@ -198,6 +198,61 @@ int input_grad_steps(const void* const* dA, const void* const* W, float* const* 
   return run(g, dtype, s);
 }
 
+// The column and row steps of k shards, in batches of up to kMaxGroups
+// shards per launch.  col(i0, n) runs the column step of shards i0 ..
+// i0 + n - 1 into Y[0 .. n-1].  Literal (fused == false): partial i goes to
+// part(i) and its pointer to parts[i].  Fused: the row step of every batch
+// adds its shards, in shard order, into part(0) (the first batch stores).
+template <class Col, class Part>
+int shard_steps(Col col, const void* const* V, int k, int64_t M, int64_t H, int64_t Fk, int dtype,
+                void* const* Y, bool fused, Part part, const float** parts, hipStream_t s) {
+  const int G = batch_size(k);
+  float* P[kMaxGroups];
+  int st;
+  for (int i0 = 0; i0 < k; i0 += G) {
+    const int n = k - i0 < G ? k - i0 : G;
+    if ((st = col(i0, n))) return st;
+    if (fused) {
+      P[0] = part(0);
+      if ((st = row_steps(Y, V + i0, P, n, true, M, Fk, H, dtype, i0 > 0, s))) return st;
+    } else {
+      for (int j = 0; j < n; ++j) {
+        P[j] = part(i0 + j);
+        parts[i0 + j] = P[j];
+      }
+      if ((st = row_steps(Y, V + i0, P, n, false, M, Fk, H, dtype, false, s))) return st;
+    }
+  }
+  return TP_OK;
+}
+
+// Shape and pointer rules of the sequence-parallel reduce-scatter.
+int check_sp(const float* const* parts, int nparts, const void* R, int r_dtype, void* const* O,
+             int out_dtype, int k, int64_t M, int64_t H) {
+  if (check_dtype(r_dtype) || check_dtype(out_dtype)) return TP_ERR_DTYPE;
+  if (nparts < 1 || nparts > TP_MAX_SHARDS || k < 1 || k > TP_MAX_SHARDS) return TP_ERR_SHAPE;
+  if (check_dims(M, H, 8)) return TP_ERR_SHAPE;
+  if (M % k) return TP_ERR_SHAPE;
+  if (M == 0) return TP_OK;
+  if (!parts || !O) return TP_ERR_NULL;
+  for (int i = 0; i < nparts; ++i) {
+    if (!parts[i]) return TP_ERR_NULL;
+    if (!aligned16(parts[i])) return TP_ERR_ALIGN;
+  }
+  for (int r = 0; r < k; ++r) {
+    if (!O[r]) return TP_ERR_NULL;
+    if (!aligned16(O[r])) return TP_ERR_ALIGN;
+  }
+  if (R && !aligned16(R)) return TP_ERR_ALIGN;
+  const size_t nz = size_t(M) * size_t(H);
+  Regions in, out;
+  for (int i = 0; i < nparts; ++i) in.add(parts[i], nz * 4);
+  if (R) in.add(R, nz * elt_size(r_dtype));
+  for (int r = 0; r < k; ++r) out.add(O[r], nz / size_t(k) * elt_size(out_dtype));
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return TP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,7 +273,7 @@ const char* tp_status_string(int status) {
   }
 }
 
-int tp_mlp_version(void) { return 120; }
+int tp_mlp_version(void) { return 130; }
 
 int tp_mlp_col_gelu_shards(const void* X, const void* const* W, const void* const* b, void* const* Y,
                            void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype,
@@ -359,29 +414,90 @@ int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const*
   for (int j = 0; j < G; ++j) Y[j] = ws + size_t(j) * y_bytes;
   char* part_base = ws + size_t(G) * y_bytes;
   const float* parts[TP_MAX_SHARDS];
-  float* P[kMaxGroups];
-
-  for (int i0 = 0; i0 < k; i0 += G) {
-    const int n = k - i0 < G ? k - i0 : G;
-    // Column-parallel linear + bias + GeLU of shards i0 .. i0 + n - 1.
-    if ((st = col_steps(X, W + i0, b ? b + i0 : nullptr, Y, nullptr, n, M, H, Fk, dtype, s))) return st;
-    if (fused) {
-      // Row-parallel products of the batch, summed in shard order into Z
-      // (after the previous batches' sum).
-      P[0] = Z;
-      if ((st = row_steps(Y, V + i0, P, n, true, M, Fk, H, dtype, i0 > 0, s))) return st;
-    } else {
-      // Row-parallel partials: P_0 in Z, the rest in the workspace.
-      for (int j = 0; j < n; ++j) {
-        const int i = i0 + j;
-        P[j] = i == 0 ? Z : reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
-        parts[i] = P[j];
-      }
-      if ((st = row_steps(Y, V + i0, P, n, false, M, Fk, H, dtype, false, s))) return st;
-    }
-  }
+  // P_0 (or the fused sum) in Z, P_1 .. P_{k-1} in the workspace.
+  auto part = [&](int i) {
+    return i == 0 ? Z : reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
+  };
+  auto col = [&](int i0, int n) {
+    return col_steps(X, W + i0, b ? b + i0 : nullptr, Y, nullptr, n, M, H, Fk, dtype, s);
+  };
+  if ((st = shard_steps(col, V, k, M, H, Fk, dtype, Y, fused, part, parts, s))) return st;
   if (!fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
   return TP_OK;
+}
+
+int tp_sp_reduce_scatter(const float* const* Z_parts, int nparts, const void* R, int r_dtype,
+                         void* const* O, int out_dtype, int k, int64_t M, int64_t H, void* stream) {
+  int st = check_sp(Z_parts, nparts, R, r_dtype, O, out_dtype, k, M, H);
+  if (st || M == 0) return st;
+  return hip_status(tpmlp::launch_sp_reduce_scatter(Z_parts, nparts, R, r_dtype == TP_BF16, O,
+                                                    out_dtype == TP_BF16, k, (M / k) * H,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+size_t tp_mlp_sp_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dtype, unsigned flags) {
+  if (k < 1 || k > TP_MAX_SHARDS || check_dtype(dtype) || check_dims(M, H, Fk)) return 0;
+  if (flags & ~TP_FUSED_ACCUM) return 0;
+  if (M == 0 || M % k) return 0;
+  const size_t y = round_up(size_t(M) * size_t(Fk) * elt_size(dtype), kWsAlign);
+  const size_t part = round_up(size_t(M) * size_t(H) * 4, kWsAlign);
+  return size_t(batch_size(k)) * y + size_t((flags & TP_FUSED_ACCUM) ? 1 : k) * part;
+}
+
+int tp_mlp_shard_forward_sp(const void* X, const void* const* W, const void* const* b,
+                            const void* const* V, int k, int64_t M, int64_t H, int64_t Fk,
+                            int dtype, void* workspace, size_t workspace_bytes, void* const* O,
+                            int out_dtype, unsigned flags, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (check_dtype(out_dtype)) return TP_ERR_DTYPE;
+  if (flags & ~TP_FUSED_ACCUM) return TP_ERR_FLAGS;
+  if (k < 1 || k > TP_MAX_SHARDS) return TP_ERR_SHAPE;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (M % k) return TP_ERR_SHAPE;
+  if (M == 0) return TP_OK;
+  if (!X || !W || !V || !O) return TP_ERR_NULL;
+  for (int i = 0; i < k; ++i) {
+    if (!W[i] || !V[i] || (b && !b[i]) || !O[i]) return TP_ERR_NULL;
+    if (!aligned16(W[i]) || !aligned16(V[i]) || (b && !aligned16(b[i])) || !aligned16(O[i]))
+      return TP_ERR_ALIGN;
+  }
+  if (!aligned16(X)) return TP_ERR_ALIGN;
+  const size_t need = tp_mlp_sp_workspace_bytes(k, M, H, Fk, dtype, flags);
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  const size_t nz = size_t(M) * size_t(H);
+  Regions in, out;
+  in.add(X, nz * e);
+  for (int i = 0; i < k; ++i) {
+    in.add(W[i], size_t(H) * size_t(Fk) * e);
+    in.add(V[i], size_t(Fk) * size_t(H) * e);
+    if (b) in.add(b[i], size_t(Fk) * e);
+    out.add(O[i], nz / size_t(k) * elt_size(out_dtype));
+  }
+  out.add(workspace, need);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fused = (flags & TP_FUSED_ACCUM) != 0;
+  char* ws = static_cast<char*>(workspace);
+  const int G = batch_size(k);
+  const size_t y_bytes = round_up(size_t(M) * size_t(Fk) * e, kWsAlign);
+  const size_t part_bytes = round_up(nz * 4, kWsAlign);
+  void* Y[kMaxGroups];
+  for (int j = 0; j < G; ++j) Y[j] = ws + size_t(j) * y_bytes;
+  char* part_base = ws + size_t(G) * y_bytes;
+  const float* parts[TP_MAX_SHARDS];
+  auto part = [&](int i) { return reinterpret_cast<float*>(part_base + size_t(i) * part_bytes); };
+  auto col = [&](int i0, int n) {
+    return col_steps(X, W + i0, b ? b + i0 : nullptr, Y, nullptr, n, M, H, Fk, dtype, s);
+  };
+  if ((st = shard_steps(col, V, k, M, H, Fk, dtype, Y, fused, part, parts, s))) return st;
+  if (fused) parts[0] = part(0);
+  // The reduce-scatter over the k sequence blocks, with X as the residual.
+  return hip_status(tpmlp::launch_sp_reduce_scatter(parts, fused ? 1 : k, X, dtype == TP_BF16, O,
+                                                    out_dtype == TP_BF16, k, (M / k) * H, s));
 }
 
 int tp_mlp_grad_act_shards(const void* dZ, const void* const* V, const void* const* G,

@@ -98,4 +98,12 @@ hipError_t launch_colsum(const void* const* A, int groups, bool bf16, int64_t M,
 hipError_t launch_split_reduce(float* const* C, int groups, const float* part, int64_t part_stride,
                                int n, int64_t count, hipStream_t s);
 
+// Sequence-parallel reduce-scatter with the residual: for r < k,
+// out[r][e] = R[r block_elems + e] + sum_i parts[i][r block_elems + e]
+// (parts in order, then R; R may be null), 0 <= e < block_elems (a multiple
+// of 8).  R is bf16 when r_bf16 (else float32); out[r] bf16 when o_bf16.
+hipError_t launch_sp_reduce_scatter(const float* const* parts, int nparts, const void* R, bool r_bf16,
+                                    void* const* out, bool o_bf16, int k, int64_t block_elems,
+                                    hipStream_t s);
+
 }  // namespace tpmlp

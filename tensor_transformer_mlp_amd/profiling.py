@@ -62,6 +62,9 @@ def kernel_kind(name: str):
     """Benchmark kernel kind of a device kernel name, or None."""
     if "shard_reduce_kernel" in name:
         return "shard_reduce"
+    if "sp_reduce_kernel" in name:
+        m = re.search(r"sp_reduce_kernel<([^,>]*)", name)
+        return "sp_reduce_fused" if m and _targ(m.group(1)) == "1" else "sp_reduce"
     if "colsum_" in name:
         return "colsum"
     m = re.search(r"gemm_(?:bf16|f32)_kernel<([^>]*)>", name)

@@ -45,7 +45,8 @@ def test_exports_every_declared_symbol(L):
                      "tp_mlp_backward_workspace_bytes", "tp_mlp_shard_backward",
                      "tp_mlp_col_gelu_shards", "tp_mlp_row_partial_shards", "tp_mlp_grad_act_shards",
                      "tp_mlp_grad_weight_workspace_bytes_shards", "tp_mlp_grad_row_weight_shards",
-                     "tp_mlp_grad_col_weight_shards", "tp_mlp_grad_input_shards"}
+                     "tp_mlp_grad_col_weight_shards", "tp_mlp_grad_input_shards",
+                     "tp_sp_reduce_scatter", "tp_mlp_sp_workspace_bytes", "tp_mlp_shard_forward_sp"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -410,3 +411,91 @@ def test_shards_entry_point_errors(L):
     assert d(*a) == c["TP_ERR_FLAGS"]
     a = ok(); a[2] = arr(11 * P, None)  # dX[0] over W[1]
     assert d(*a) == c["TP_ERR_ALIAS"]
+
+
+def test_sp_reduce_scatter_errors(L):
+    c = _header_constants()
+    f = L.tp_sp_reduce_scatter
+    parts = (ctypes.c_void_p * 2)(P, 2 * P)
+    O = (ctypes.c_void_p * 4)(20 * P, 21 * P, 22 * P, 23 * P)
+    R = ctypes.c_void_p(30 * P)
+    base = lambda: [parts, 2, R, 1, O, 0, 4, 64, 64, None]
+    a = base(); a[3] = 2
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    a = base(); a[5] = -1
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    a = base(); a[1] = 0
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[1] = 65
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[6] = 0
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[7] = 66            # k = 4 does not divide M
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[8] = 60            # H % 8
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[0] = None
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = base(); a[4] = (ctypes.c_void_p * 4)(20 * P, None, 22 * P, 23 * P)
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = base(); a[4] = (ctypes.c_void_p * 4)(20 * P, 21 * P + 8, 22 * P, 23 * P)
+    assert f(*a) == c["TP_ERR_ALIGN"]
+    a = base(); a[2] = ctypes.c_void_p(30 * P + 4)
+    assert f(*a) == c["TP_ERR_ALIGN"]
+    # an output block inside a part, inside R, or over another block
+    a = base(); a[4] = (ctypes.c_void_p * 4)(20 * P, P + 1024, 22 * P, 23 * P)
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[4] = (ctypes.c_void_p * 4)(20 * P, 21 * P, 30 * P + 16, 23 * P)
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[4] = (ctypes.c_void_p * 4)(20 * P, 20 * P + 256, 22 * P, 23 * P)
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    # blocks side by side (the gathered layout) do not overlap: 16 rows x 64 x 4 bytes each
+    a = base(); a[4] = (ctypes.c_void_p * 4)(*[20 * P + r * 16 * 64 * 4 for r in range(4)])
+    a[7] = 0                          # M == 0: a no-op after the checks
+    assert f(*a) == c["TP_OK"]
+    a = base(); a[7] = 0
+    assert f(*a) == c["TP_OK"]
+
+
+def test_sp_workspace_bytes(L):
+    f = L.tp_mlp_sp_workspace_bytes
+    # one Y per shard of a batch plus k fp32 partials (1 when fused)
+    assert f(4, 8192, 768, 768, 1, 0) == 4 * 8192 * 768 * 2 + 4 * 8192 * 768 * 4
+    assert f(4, 8192, 768, 768, 1, 1) == 4 * 8192 * 768 * 2 + 8192 * 768 * 4
+    assert f(2, 8, 64, 128, 0, 0) == 2 * 8 * 128 * 4 + 2 * 8 * 64 * 4
+    assert f(4, 6, 64, 128, 0, 0) == 0      # k does not divide M
+    assert f(4, 0, 64, 128, 0, 0) == 0
+    assert f(4, 8, 64, 128, 0, 2) == 0
+    assert f(4, 8, 64, 128, 7, 0) == 0
+
+
+def test_shard_forward_sp_errors(L):
+    c = _header_constants()
+    f = L.tp_mlp_shard_forward_sp
+    k = 2
+    W = (ctypes.c_void_p * k)(10 * P, 11 * P)
+    V = (ctypes.c_void_p * k)(12 * P, 13 * P)
+    b = (ctypes.c_void_p * k)(14 * P, 15 * P)
+    O = (ctypes.c_void_p * k)(1 << 41, (1 << 41) + 4 * 64 * 4)
+    need = L.tp_mlp_sp_workspace_bytes(k, 8, 64, 128, 1, 0)
+    ws = ctypes.c_void_p(1 << 40)
+    X = ctypes.c_void_p(1 << 42)
+    base = lambda: [X, W, b, V, k, 8, 64, 128, 1, ws, need, O, 0, 0, None]
+    a = base(); a[13] = 2
+    assert f(*a) == c["TP_ERR_FLAGS"]
+    a = base(); a[12] = 5
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    a = base(); a[5] = 9              # k does not divide M
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[10] = need - 1
+    assert f(*a) == c["TP_ERR_WORKSPACE"]
+    a = base(); a[11] = (ctypes.c_void_p * k)(1 << 41, None)
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = base(); a[11] = (ctypes.c_void_p * k)(1 << 41, (1 << 41) + 16)
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[11] = (ctypes.c_void_p * k)(1 << 41, (1 << 40) + 512)   # block inside the workspace
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[11] = (ctypes.c_void_p * k)((1 << 42) + 64, (1 << 41))  # block over X
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[5] = 0
+    assert f(*a) == c["TP_OK"]
