@@ -9,10 +9,11 @@ per shard the training-mode column step, dA, dV, dW + db and the partial dX,
 then the dX shard sum) is timed the same way and reported under "backward",
 and so is the sequence-parallel forward (tp_mlp_shard_forward_sp: the shard
 sum as a reduce-scatter over the k sequence blocks with the residual X added)
-under "sequence_parallel".
+under "sequence_parallel", and the SwiGLU variant of the block
+(tp_swiglu_shard_forward) under "swiglu".
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant literal|fused]
-                    [--no-backward] [--no-sp]
+                    [--no-backward] [--no-sp] [--no-swiglu]
 
 Prints ONE JSON line (metric, value in TFLOP/s, ms_per_step, roofline of the
 dominant kernel, CPU-oracle baseline, backward) on stdout; diagnostics go to
@@ -52,6 +53,7 @@ def parse():
                     help="steps of the per-kernel timing pass (default: --steps)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel leg")
+    ap.add_argument("--no-swiglu", action="store_true", help="skip the SwiGLU leg")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain float32 copy kernel (y = x * 1) over MIB MiB, 5 times: "
                          "the known-size reference for the HBM byte counters")
@@ -76,6 +78,8 @@ def kernel_bytes(kind, w, elt, n):
         # sequence-parallel reduce-scatter + residual: k (or 1) fp32 parts, X, fp32 blocks
         "sp_reduce": (k * 4 + elt + 4) * M * H,
         "sp_reduce_fused": (4 + elt + 4) * M * H,
+        # SwiGLU column step: X once, gate and up weights, Y
+        "swiglu_col": M * H * elt + n * (2 * H * Fk + M * Fk) * elt,
     }
     return table[kind]
 
@@ -87,6 +91,8 @@ def kernel_flops(kind, w, n):
         return w.k * w.M * w.H
     if kind == "sp_reduce_fused":
         return w.M * w.H
+    if kind == "swiglu_col":
+        return n * 4 * w.M * w.H * w.Fk
     return n * 2 * w.M * w.H * w.Fk
 
 
@@ -263,6 +269,10 @@ def main():
     sp = None
     if not args.no_sp and w.M % w.k == 0:
         sp = bench_sp(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt)
+    del Ws, bs
+    swiglu = None
+    if not args.no_swiglu:
+        swiglu = bench_swiglu(tpm, w, X, Vs, fused, args, elt, tdt)
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
@@ -280,6 +290,7 @@ def main():
         "cpu_baseline": cpu,
         "backward": bwd,
         "sequence_parallel": sp,
+        "swiglu": swiglu,
     }
     print(json.dumps(out), flush=True)
 
@@ -420,6 +431,76 @@ def bench_sp(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt):
     kern = time_kinds(kinds, launch, nlaunch, nshards, args.kernel_steps or args.steps, args.warmup, w, elt)
     roof = roofline(kern, w, args.variant, w.dtype, kind=red)
     return {"metric": "TP-shard MLP forward under sequence parallelism (reduce-scatter + residual) TFLOP/s",
+            "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+            "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "roofline": roof,
+            "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],
+                             "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()}}
+
+
+def bench_swiglu(tpm, w, X, Vs, fused, args, elt, tdt):
+    """Time tp_swiglu_shard_forward (the SwiGLU block: per shard one GEMM with
+    the gate and up weights and the SiLU(gate) * up epilogue, the row GEMM,
+    then the shard sum) on the same X and V with gate and up weights drawn for
+    the workload, and its kernels by kind.  FLOPs counted: 3 GEMMs of
+    2 M H F/k per shard (6 M H F); the roofline entry is the SwiGLU column
+    GEMM's."""
+    import numpy as np
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    dev = X.device
+    Fk, k, M, H = w.Fk, w.k, w.M, w.H
+
+    def up(a):
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+        return t.view(torch.bfloat16) if a.dtype == np.uint16 else t
+
+    Wg = [up(x) for x in inputs.col_slices(inputs.draw(inputs.STREAM_W, (H, w.F), w.std, w.dtype), k)]
+    Wu = [up(x) for x in inputs.col_slices(inputs.draw(inputs.STREAM_WU, (H, w.F), w.std, w.dtype), k)]
+    dt = tpm.TP_BF16 if w.dtype == "bf16" else tpm.TP_F32
+    flags = tpm.TP_FUSED_ACCUM if fused else 0
+    ws = torch.empty(max(tpm.tp_mlp_workspace_bytes(k, M, H, Fk, dt, flags), 1), dtype=torch.uint8, device=dev)
+    Z = torch.empty(M, H, dtype=torch.float32, device=dev)
+
+    def step():
+        tpm.tp_swiglu_shard_forward(X, Wg, Wu, Vs, Z=Z, workspace=ws, fused=fused)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    flop = 6 * M * H * w.F
+    tflops = flop / (ms * 1e-3) / 1e12
+    log("swiglu forward: %.4f ms/step, %.1f TFLOP/s (%.1f%% of %s peak)" % (
+        ms, tflops, 100 * tflops / PEAK_TFLOPS[w.dtype], w.dtype))
+    if not bool(torch.isfinite(Z).all()):
+        raise RuntimeError("non-finite SwiGLU output")
+
+    G = min(k, tpm.TP_MAX_BATCH)
+    batches = [(i0, min(G, k - i0)) for i0 in range(0, k, G)]
+    Yb = [torch.empty(M, Fk, dtype=tdt, device=dev) for _ in range(G)]
+    parts = [Z] + [torch.empty(M, H, dtype=torch.float32, device=dev) for _ in range(k - 1)]
+    kinds = ["swiglu_col"] + (["row_sum"] if fused else ["row_partial"] + (["shard_reduce"] if k > 1 else []))
+    nlaunch = {"swiglu_col": len(batches), "row_partial": len(batches), "row_sum": len(batches), "shard_reduce": 1}
+    nshards = {"swiglu_col": G, "row_partial": G, "row_sum": G, "shard_reduce": k}
+
+    def launch(kind):
+        for i0, n in batches:
+            if kind == "swiglu_col":
+                tpm.tp_swiglu_col_shards(X, Wg[i0:i0 + n], Wu[i0:i0 + n], Yb[:n])
+            elif kind == "row_partial":
+                tpm.tp_mlp_row_partial_shards(Yb[:n], Vs[i0:i0 + n], parts[i0:i0 + n])
+            elif kind == "row_sum":
+                tpm.tp_mlp_row_partial_shards(Yb[:n], Vs[i0:i0 + n], [Z], sum_shards=True, accumulate=i0 > 0)
+        if kind == "shard_reduce":
+            tpm.tp_shard_reduce(parts, Z=Z)
+
+    kern = time_kinds(kinds, launch, nlaunch, nshards, args.kernel_steps or args.steps, args.warmup, w, elt)
+    roof = roofline(kern, w, args.variant, w.dtype, kind="swiglu_col")
+    return {"metric": "TP-shard SwiGLU MLP forward TFLOP/s (3 GEMMs of 2 M H F/k per shard)",
             "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
             "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "roofline": roof,
             "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],

@@ -230,6 +230,39 @@ int tp_mlp_shard_forward_sp(const void* X, const void* const* W, const void* con
                             int out_dtype, unsigned flags, void* stream);
 
 /*
+ * SwiGLU variant of the block (the gated MLP of Llama-style models: gate_proj
+ * and up_proj column-parallel, down_proj row-parallel, "AI大模型分布式训练：张量
+ * 并行与流水线并行深度实践" §6.1; gate_up_proj column- and down_proj
+ * row-parallel, "大模型分布式优化技术（一）" §5.1).  The pages name the SwiGLU
+ * activation (§3.3 of the latter) without its formula; it is taken here as
+ * Llama's, without biases:
+ *
+ *   Y_i = SiLU(X Wg_i) * (X Wu_i),  SiLU(x) = x / (1 + exp(-x))
+ *   Z_i = Y_i V_i,  Z = Z_0 + ... + Z_{k-1}
+ *
+ * Wg_i and Wu_i [H, Fk] are columns [i*Fk, (i+1)*Fk) of the full gate and up
+ * weights [H, F] (type `dtype`, row-major [in, out]); both products of a tile
+ * run in one GEMM and the activation is applied to the two float32
+ * accumulators before Y_i is rounded to `dtype`.  The row step and the shard
+ * sum are those of the GeLU block.
+ *
+ * tp_swiglu_col: one shard's column step, Y_i [M, Fk] must not overlap X,
+ * Wg_i or Wu_i.  tp_swiglu_col_shards: the same for n shards in one launch
+ * (as the other *_shards calls).  tp_swiglu_shard_forward: the whole block,
+ * arguments and flags as tp_mlp_shard_forward (Wg, Wu, V HOST arrays of k
+ * device pointers; workspace of tp_mlp_workspace_bytes(k, M, H, Fk, dtype,
+ * flags) bytes).
+ */
+int tp_swiglu_col(const void* X, const void* Wg_i, const void* Wu_i, void* Y_i, int64_t M, int64_t H,
+                  int64_t Fk, int dtype, void* stream);
+int tp_swiglu_col_shards(const void* X, const void* const* Wg, const void* const* Wu, void* const* Y,
+                         int n, int64_t M, int64_t H, int64_t Fk, int dtype, void* stream);
+int tp_swiglu_shard_forward(const void* X, const void* const* Wg, const void* const* Wu,
+                            const void* const* V, int k, int64_t M, int64_t H, int64_t Fk, int dtype,
+                            void* workspace, size_t workspace_bytes, float* Z, unsigned flags,
+                            void* stream);
+
+/*
  * Training-mode column step: tp_mlp_col_gelu that also keeps the derivative
  * of the activation for the backward pass (the closed form of GeLU' above):
  *

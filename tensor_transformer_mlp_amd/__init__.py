@@ -26,6 +26,11 @@ with the residual X added):
     O_r = X[rows of r] + sum_i Z_i[rows of r]   tp_sp_reduce_scatter
     the whole block, k shards                   tp_mlp_shard_forward_sp
 
+SwiGLU block (Y_i = SiLU(X Wg_i) * (X Wu_i), no biases):
+
+    Y_i                          tp_swiglu_col (tp_swiglu_col_shards)
+    the whole block, k shards    tp_swiglu_shard_forward
+
 Every per-step call has a *_shards form that runs the step for up to
 TP_MAX_BATCH shards in one launch (what the k-shard calls do inside).
 """
@@ -45,6 +50,7 @@ __all__ = [
     "tp_mlp_grad_weight_workspace_bytes_shards", "tp_mlp_grad_row_weight_shards",
     "tp_mlp_grad_col_weight_shards", "tp_mlp_grad_input_shards",
     "tp_sp_reduce_scatter", "tp_mlp_sp_workspace_bytes", "tp_mlp_shard_forward_sp",
+    "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward",
 ]
 
 TP_F32 = 0
@@ -121,6 +127,12 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_sp_workspace_bytes.restype = sz
         L.tp_mlp_shard_forward_sp.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, vp, ci, cu, vp]
         L.tp_mlp_shard_forward_sp.restype = ci
+        L.tp_swiglu_col.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
+        L.tp_swiglu_col.restype = ci
+        L.tp_swiglu_col_shards.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp]
+        L.tp_swiglu_col_shards.restype = ci
+        L.tp_swiglu_shard_forward.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, vp, cu, vp]
+        L.tp_swiglu_shard_forward.restype = ci
         for f in (L.tp_mlp_col_gelu_shards, L.tp_mlp_row_partial_shards, L.tp_mlp_grad_act_shards,
                   L.tp_mlp_grad_row_weight_shards, L.tp_mlp_grad_col_weight_shards, L.tp_mlp_grad_input_shards):
             f.restype = ci
@@ -651,3 +663,66 @@ def tp_mlp_shard_forward_sp(X, W, b, V, O=None, out_dtype=None, workspace=None, 
                                          TP_BF16 if out_dtype == torch.bfloat16 else TP_F32, flags,
                                          _stream(stream)), "tp_mlp_shard_forward_sp")
     return O
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU block.
+
+def tp_swiglu_col(X, Wg_i, Wu_i, Y_i=None, stream=None):
+    """Y_i = SiLU(X Wg_i) * (X Wu_i); X [..., H], Wg_i and Wu_i [H, Fk]."""
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = Wg_i.shape[-1]
+    dt = _dtype_code(X)
+    _same_dtype("tp_swiglu_col", X, Wg_i, Wu_i, Y_i)
+    if tuple(Wg_i.shape) != (H, Fk) or tuple(Wu_i.shape) != (H, Fk):
+        raise ValueError("shape mismatch: X %s, Wg_i %s, Wu_i %s" % (tuple(X.shape), tuple(Wg_i.shape),
+                                                                    tuple(Wu_i.shape)))
+    Y_i = _out(Y_i, (M, Fk), X.dtype, X.device, "Y_i")
+    _check(lib().tp_swiglu_col(_dev(X, "X"), _dev(Wg_i, "Wg_i"), _dev(Wu_i, "Wu_i"), _dev(Y_i, "Y_i"), M, H, Fk,
+                               dt, _stream(stream)), "tp_swiglu_col")
+    return Y_i
+
+
+def tp_swiglu_col_shards(X, Wg, Wu, Y, stream=None):
+    """tp_swiglu_col for the n shards of the lists Wg, Wu, Y in one launch."""
+    n = len(Wg)
+    if n < 1 or len(Wu) != n or len(Y) != n:
+        raise ValueError("Wg, Wu and Y must hold the same number n >= 1 of shards")
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = Wg[0].shape[-1]
+    dt = _dtype_code(X)
+    _same_dtype("tp_swiglu_col_shards", X, *Wg, *Wu, *Y)
+    for i in range(n):
+        if tuple(Wg[i].shape) != (H, Fk) or tuple(Wu[i].shape) != (H, Fk) or Y[i].numel() != M * Fk:
+            raise ValueError("shard %d has the wrong shape" % i)
+    arr = lambda ts, nm: (ctypes.c_void_p * n)(*[_dev(t, "%s[%d]" % (nm, i)) for i, t in enumerate(ts)])
+    _check(lib().tp_swiglu_col_shards(_dev(X, "X"), arr(Wg, "Wg"), arr(Wu, "Wu"), arr(Y, "Y"), n, M, H, Fk, dt,
+                                      _stream(stream)), "tp_swiglu_col_shards")
+    return Y
+
+
+def tp_swiglu_shard_forward(X, Wg, Wu, V, Z=None, workspace=None, fused: bool = False, stream=None):
+    """Z = sum_i (SiLU(X Wg[i]) * (X Wu[i])) V[i] over the k shards."""
+    torch = _torch()
+    k = len(Wg)
+    if k < 1 or len(Wu) != k or len(V) != k:
+        raise ValueError("Wg, Wu and V must hold the same number k >= 1 of shards")
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = Wg[0].shape[-1]
+    dt = _dtype_code(X)
+    _same_dtype("tp_swiglu_shard_forward", X, *Wg, *Wu, *V)
+    for i in range(k):
+        if tuple(Wg[i].shape) != (H, Fk) or tuple(Wu[i].shape) != (H, Fk) or tuple(V[i].shape) != (Fk, H):
+            raise ValueError("shard %d has the wrong shape" % i)
+    flags = TP_FUSED_ACCUM if fused else 0
+    need = tp_mlp_workspace_bytes(k, M, H, Fk, dt, flags)
+    workspace = _workspace(workspace, need, X.device)
+    Z = _out(Z, (M, H), torch.float32, X.device, "Z")
+    arr = lambda ts, nm: (ctypes.c_void_p * k)(*[_dev(t, "%s[%d]" % (nm, i)) for i, t in enumerate(ts)])
+    _check(lib().tp_swiglu_shard_forward(_dev(X, "X"), arr(Wg, "Wg"), arr(Wu, "Wu"), arr(V, "V"), k, M, H, Fk, dt,
+                                         _dev(workspace, "workspace"), workspace.numel(), _dev(Z, "Z"), flags,
+                                         _stream(stream)), "tp_swiglu_shard_forward")
+    return Z

@@ -1,5 +1,5 @@
 // Device helpers shared by the gfx950 kernels: vector types, bf16 rounding,
-// GeLU and its derivative, the XCD-aware tile order, raw buffer descriptors,
+// GeLU and its derivative, SiLU, the XCD-aware tile order, raw buffer descriptors,
 // direct-to-LDS loads and the LDS transpose read.
 #pragma once
 
@@ -66,6 +66,14 @@ __device__ __forceinline__ void gelu_and_grad_f32(float x, float& y, float& g) {
   const float Phi = x < 0.0f ? h : 1.0f - h;
   y = x * Phi;
   g = fmaf(x * 0.3989422804014327f, e, Phi);
+}
+
+// SiLU(x) = x sigma(x) = x / (1 + exp(-x)), with exp(-x) = 2^(-x log2 e) and
+// the reciprocal on the transcendental unit.  For x -> -inf the exponential
+// overflows to +inf and the reciprocal to 0, giving the limit (-)0.
+__device__ __forceinline__ float silu_f32(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // Map the linear workgroup id bid (of nb) to a (tile_m, tile_n) pair.  Workgroups are

@@ -11,13 +11,14 @@ namespace {
 constexpr int64_t kMaxTilesPerLaunch = int64_t(1) << 22;
 
 bool c_is_bf16(Epilogue e) {
-  return e == kEpiBiasGelu || e == kEpiBiasGeluSave || e == kEpiMulAux;
+  return e == kEpiBiasGelu || e == kEpiBiasGeluSave || e == kEpiMulAux || e == kEpiSwiGLU;
 }
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-int64_t tiles_of(int tile, int64_t M, int64_t N) {
-  return ((M + kTiles[tile].bm - 1) / kTiles[tile].bm) * ((N + kTiles[tile].bn - 1) / kTiles[tile].bn);
+int64_t tiles_of(int tile, int64_t M, int64_t N, Epilogue epi = kEpiStoreF32) {
+  const int64_t cols = tile_out_cols(tile, epi);
+  return ((M + kTiles[tile].bm - 1) / kTiles[tile].bm) * ((N + cols - 1) / cols);
 }
 
 hipError_t launch_layout(Layout layout, int tile, const GemmParams& p, Epilogue epi, bool gsum,
@@ -34,6 +35,7 @@ GemmParams base_params(const GemmBatch& b, int tile) {
   for (int g = 0; g < b.groups; ++g) {
     p.t.A[g] = static_cast<const uint16_t*>(b.A[g]);
     p.t.B[g] = static_cast<const uint16_t*>(b.B[g]);
+    p.t.B2[g] = static_cast<const uint16_t*>(b.B2[g]);
     p.t.bias[g] = static_cast<const uint16_t*>(b.bias[g]);
     p.t.C[g] = b.C[g];
     p.t.aux[g] = b.aux[g];
@@ -46,7 +48,8 @@ GemmParams base_params(const GemmBatch& b, int tile) {
   p.N = (int)b.N;
   p.K = (int)b.K;
   p.tiles_m = (int)((b.M + kTiles[tile].bm - 1) / kTiles[tile].bm);
-  p.tiles_n = (int)((b.N + kTiles[tile].bn - 1) / kTiles[tile].bn);
+  const int cols = tile_out_cols(tile, b.epi);
+  p.tiles_n = (int)((b.N + cols - 1) / cols);
   p.slices = 1;
   p.k_slice = p.K;
   p.part = nullptr;
@@ -81,9 +84,20 @@ int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K, int groups, b
   return 8;
 }
 
+// SwiGLU (two B operands, BM x BN/2 output tiles): 256x256 (128 output
+// columns) on the same workgroup-count rule as above, else 128x256 with 3
+// stages, which is also the ragged-K tile.
+int pick_swiglu_tile(int64_t M, int64_t N, int64_t K, int groups) {
+  if (K % 32) return kTailTileSwiGLU;
+  const int64_t t256 = tiles_of(0, M, N, kEpiSwiGLU) * groups;
+  return (t256 >= 512 || (t256 >= 192 && t256 < 256)) ? 0 : 6;
+}
+
 hipError_t launch_gemm_bf16_batch_tile(int tile, const GemmBatch& b, hipStream_t s) {
   if (tile < 0 || tile >= kNumTiles || b.groups < 1 || b.groups > kMaxGroups) return hipErrorInvalidValue;
   if (b.group_sum && !tile_allows_group_sum(tile)) return hipErrorInvalidValue;
+  if (b.epi == kEpiSwiGLU && (b.group_sum || b.layout != kNN || !tile_allows_swiglu(tile)))
+    return hipErrorInvalidValue;
   if (b.M <= 0 || b.N <= 0) return hipSuccess;
   const TileCfg& c = kTiles[tile];
   GemmParams p = base_params(b, tile);
@@ -120,13 +134,14 @@ constexpr int64_t kSequentialSumTiles = 1024;
 hipError_t launch_gemm_bf16_batch(const GemmBatch& b, hipStream_t s) {
   if (b.group_sum && b.groups > 1 && b.K % 32 == 0 && tiles_of(0, b.M, b.N) >= kSequentialSumTiles) {
     for (int g = 0; g < b.groups; ++g) {
-      GemmArgs a{b.A[g], b.B[g], nullptr, b.C[0], nullptr, b.M, b.N, b.K, b.lda, b.ldb, b.ldc,
+      GemmArgs a{b.A[g], b.B[g], nullptr, nullptr, b.C[0], nullptr, b.M, b.N, b.K, b.lda, b.ldb, b.ldc,
                  b.layout, g == 0 ? b.epi : kEpiAccumF32};
       const hipError_t e = launch_gemm_bf16(a, s);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
   }
+  if (b.epi == kEpiSwiGLU) return launch_gemm_bf16_batch_tile(pick_swiglu_tile(b.M, b.N, b.K, b.groups), b, s);
   return launch_gemm_bf16_batch_tile(
       pick_bf16_tile(b.layout, b.M, b.N, b.K, b.groups, b.group_sum), b, s);
 }
@@ -136,6 +151,7 @@ GemmBatch single_batch(const GemmArgs& g) {
   b.A[0] = g.A;
   b.B[0] = g.B;
   b.bias[0] = g.bias;
+  b.B2[0] = g.B2;
   b.C[0] = g.C;
   b.aux[0] = g.aux;
   b.groups = 1;
@@ -223,7 +239,7 @@ hipError_t launch_gemm_split(const GemmBatch& b, bool bf16, void* ws, hipStream_
         const int64_t a_off = b.layout == kTN ? k0 * b.lda : k0;
         const int64_t b_off = b.layout == kNT ? k0 : k0 * b.ldb;
         GemmArgs a{static_cast<const float*>(b.A[g]) + a_off, static_cast<const float*>(b.B[g]) + b_off,
-                   nullptr, b.C[g], nullptr, b.M, b.N, b.K - k0 < ks ? b.K - k0 : ks,
+                   nullptr, nullptr, b.C[g], nullptr, b.M, b.N, b.K - k0 < ks ? b.K - k0 : ks,
                    b.lda, b.ldb, b.ldc, b.layout, b.epi};
         if (i > 0) {
           a.C = part_ptr(g, i);

@@ -51,6 +51,7 @@ namespace tpmlp {
 struct GroupTable {
   const uint16_t* A[kMaxGroups];
   const uint16_t* B[kMaxGroups];
+  const uint16_t* B2[kMaxGroups];  // kEpiSwiGLU: the second B operand (up projection)
   const uint16_t* bias[kMaxGroups];
   void* C[kMaxGroups];
   void* aux[kMaxGroups];
@@ -92,7 +93,7 @@ constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // Epilogues each layout is instantiated with.
 constexpr bool layout_has_epi(int layout, int epi) {
   return layout == kNN ? (epi == kEpiBiasGelu || epi == kEpiBiasGeluSave || epi == kEpiStoreF32 ||
-                          epi == kEpiAccumF32)
+                          epi == kEpiAccumF32 || epi == kEpiSwiGLU)
        : layout == kNT ? (epi == kEpiMulAux || epi == kEpiStoreF32 || epi == kEpiAccumF32)
                        : (epi == kEpiStoreF32 || epi == kEpiAccumF32);
 }
@@ -208,7 +209,8 @@ struct OperandFrags {
   }
 
   // swzK(r + 32 f) == swzK(r) and swzMN(k + 4) == swzMN(k + 16) == swzMN(k).
-  __device__ __forceinline__ void read(const char* S, int ks, bf16x8_t (&dst)[F]) const {
+  // dst: F fragments.
+  __device__ __forceinline__ void read(const char* S, int ks, bf16x8_t* dst) const {
     if constexpr (KMAJ) {
 #pragma unroll
       for (int f = 0; f < F; ++f) dst[f] = *reinterpret_cast<const bf16x8_t*>(S + off[ks] + f * 2048);
@@ -228,20 +230,32 @@ struct OperandFrags {
 // (z starts as group 0's product, or as C itself with kEpiAccumF32), and z is
 // stored once.  Each group's product is bit-identical to that group's own
 // GEMM, so this equals storing every product and summing them left to right.
+//
+// DUAL (kEpiSwiGLU): two B operands, the gate B and the up projection B2, of
+// the same shape.  The stage holds A and two B sub-tiles of BN / 2 columns
+// each (the gate's and the up projection's for the same BN / 2 output
+// columns), every wave reads its FN / 2 gate and FN / 2 up fragments at the
+// same offsets of the two sub-tiles, and the epilogue stores
+// SiLU(gate) * up: a BM x BN / 2 tile of the output.
 template <int EPI, int LAYOUT, int BM, int BN, int WM, int WN, int NBUF, bool KTAIL, bool GSUM>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   constexpr bool AK = LAYOUT != kTN;  // A K-major
   constexpr bool BK = LAYOUT == kNT;  // B K-major
+  constexpr bool DUAL = EPI == kEpiSwiGLU;
   constexpr int D = NBUF - 1;         // prefetch distance in K steps of 32
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int NB = DUAL ? 2 : 1;              // B sub-tiles per stage
+  constexpr int BNO = BN / NB, WTNO = WTN / NB;  // output columns per workgroup / wave
+  constexpr int FNO = FN / NB;                  // output fragments per wave row
   using TA = OperandTile<BM, AK, NW, KTAIL>;
-  using TB = OperandTile<BN, BK, NW, KTAIL>;
+  using TB = OperandTile<BNO, BK, NW, KTAIL>;
   using RA = OperandFrags<BM, AK, FM>;
-  using RB = OperandFrags<BN, BK, FN>;
-  constexpr int A_BYTES = TA::kBytes, STAGE = TA::kBytes + TB::kBytes;
-  constexpr int L = TA::kPerWave + TB::kPerWave;  // DMA instructions per wave per stage
+  using RB = OperandFrags<BNO, BK, FNO>;
+  constexpr int A_BYTES = TA::kBytes, STAGE = TA::kBytes + NB * TB::kBytes;
+  constexpr int L = TA::kPerWave + NB * TB::kPerWave;  // DMA instructions per wave per stage
+  static_assert(!DUAL || (LAYOUT == kNN && FN % 2 == 0 && !GSUM), "SwiGLU: kNN, two fragment sets");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(NBUF >= 3 && NBUF <= 6, "stage count");
   static_assert((D - 1) * L <= 63, "vmcnt immediate");
@@ -296,7 +310,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int m0 = tm * BM;
-  const int n0 = tn * BN;
+  const int n0 = tn * BNO;
   int K = p.K;
   int kb = 0;  // first k of this workgroup's slice
   if (p.slices > 1) {
@@ -315,9 +329,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   };
 
   TA ta;
-  TB tb;
+  TB tb, tb2;
   ta.init(a_ptr(grp), p.lda, m0, p.M, wave, lane);
   tb.init(b_ptr(grp), p.ldb, n0, p.N, wave, lane);
+  if constexpr (DUAL) tb2.init(p.t.B2[grp] + (int64_t)kb * p.ldb, p.ldb, n0, p.N, wave, lane);
   // Stages are issued in order: (group 0, stage 0 .. nk - 1), (group 1, ...).
   int iss_g = 0, iss_kt = 0;
   auto issue_stage = [&](auto bset) {
@@ -325,6 +340,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
     const int kleft = iss_g < ngroups ? K - iss_kt * 32 : 0;
     ta.issue(S, wave, kleft);
     tb.issue(S + A_BYTES, wave, kleft);
+    if constexpr (DUAL) tb2.issue(S + A_BYTES + TB::kBytes, wave, kleft);
     if (++iss_kt == nk) {
       iss_kt = 0;
       if (GSUM && ++iss_g < ngroups) {
@@ -339,7 +355,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   RA ra;
   RB rb;
   ra.init(wm * WTM, lane);
-  rb.init(wn * WTN, lane);
+  rb.init(wn * WTNO, lane);
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -403,6 +419,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
     const char* S = stage(bset);
     ra.read(S, ks, fa[f]);
     rb.read(S + A_BYTES, ks, fb[f]);
+    if constexpr (DUAL) rb.read(S + A_BYTES + TB::kBytes, ks, fb[f] + FNO);
   };
   auto mfmas = [&](auto fset) {
     constexpr int f = decltype(fset)::value;
@@ -415,7 +432,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   constexpr int kMfma = FM * FN;
-  constexpr int kReads = RA::kReads + RB::kReads;
+  constexpr int kReads = RA::kReads + NB * RB::kReads;
   // vmcnt((D - 1) L), expcnt(7), lgkmcnt(0): this wave's loads of the next
   // stage (all but the D - 1 younger stages) and all its LDS reads are done.
   constexpr int kWaitN = (D - 1) * L;
@@ -497,7 +514,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
+        const int n = n0 + wn * WTNO + j * 32 + 8 * gq + hcol;
         u32x2_t bb = u32x2_t{0u, 0u};
         if (bias && n < N) bb = *reinterpret_cast<const u32x2_t*>(bias + n);
         bias4[j][gq] = f32x4_t{bf16_bits_to_f32(bb[0] & 0xFFFFu), bf16_bits_to_f32(bb[0] >> 16),
@@ -518,7 +535,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
-            const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
+            const int n = n0 + wn * WTNO + j * 32 + 8 * gq + hcol;
             const bool ok = !G || (mrow && n < N);
             if constexpr (EPI == kEpiMulAux) {
               aux2[j][gq] = u32x2_t{0u, 0u};
@@ -533,13 +550,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
           }
       }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
+      for (int j = 0; j < FNO; ++j) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
+          const int n = n0 + wn * WTNO + j * 32 + 8 * gq + hcol;
           if (G && (!mrow || n >= N)) continue;
           const int64_t idx = row + n;
           f32x4_t v;
+          if constexpr (DUAL) {
+            // gate fragment j and up fragment FNO + j hold the same columns
+            u32x2_t o;
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = silu_f32(acc[i][j][4 * gq + e]) * acc[i][FNO + j][4 * gq + e];
+            o[0] = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+            o[1] = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = o;
+            continue;
+          }
           if constexpr (GSUM)
             v = f32x4_t{z[i][j][4 * gq], z[i][j][4 * gq + 1], z[i][j][4 * gq + 2], z[i][j][4 * gq + 3]};
           else
@@ -581,7 +609,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
       }
     }
   };
-  if (m0 + BM <= M && n0 + BN <= N)
+  if (m0 + BM <= M && n0 + BNO <= N)
     epilogue(std::false_type{});
   else
     epilogue(std::true_type{});
@@ -593,6 +621,31 @@ constexpr bool tile_allows_group_sum(int t) {
   return (kTiles[t].bm / kTiles[t].wm / 32) * (kTiles[t].bn / kTiles[t].wn / 32) <= 4;
 }
 
+// SwiGLU splits a tile's BN columns into a gate and an up sub-tile of BN / 2
+// columns each (MN-major sub-tiles need 128, 256 or 512 columns) and every
+// wave's fragments into two equal sets.
+constexpr bool tile_allows_swiglu(int t) {
+  return (kTiles[t].bn / 2 == 128 || kTiles[t].bn / 2 == 256) && (kTiles[t].bn / kTiles[t].wn / 32) % 2 == 0;
+}
+
+// Output columns of one workgroup tile.
+constexpr int tile_out_cols(int t, int epi) { return epi == kEpiSwiGLU ? kTiles[t].bn / 2 : kTiles[t].bn; }
+
+// K % 32 != 0 runs on a ragged-K variant of one tile only: kTailTile, or
+// kTailTileSwiGLU for the SwiGLU epilogue.
+constexpr int kTailTile = 8;
+constexpr int kTailTileSwiGLU = 6;
+
+// Which (tile, ragged K, group sum, epilogue) combinations a layout is
+// compiled for.
+constexpr bool instantiated(int layout, int t, bool ktail, bool gsum, int epi) {
+  if (!layout_has_epi(layout, epi)) return false;
+  if (gsum && (layout == kTN || (epi != kEpiStoreF32 && epi != kEpiAccumF32) || !tile_allows_group_sum(t)))
+    return false;
+  if (epi == kEpiSwiGLU) return !gsum && tile_allows_swiglu(t) && (!ktail || t == kTailTileSwiGLU);
+  return !ktail || t == kTailTile;
+}
+
 // Launch one tile configuration of one layout (p.tiles_m / p.tiles_n set).
 template <int LAYOUT, int T, bool KTAIL, bool GSUM>
 hipError_t launch_bf16_tile(const GemmParams& p, Epilogue epi, hipStream_t s) {
@@ -602,7 +655,7 @@ hipError_t launch_bf16_tile(const GemmParams& p, Epilogue epi, hipStream_t s) {
   bool done = false;
   [&]<int... e>(std::integer_sequence<int, e...>) {
     (([&] {
-       if constexpr (layout_has_epi(LAYOUT, e) && (!GSUM || e == kEpiStoreF32 || e == kEpiAccumF32)) {
+       if constexpr (instantiated(LAYOUT, T, KTAIL, GSUM, e)) {
          if (epi == e) {
            hipLaunchKernelGGL((gemm_bf16_kernel<e, LAYOUT, c.bm, c.bn, c.wm, c.wn, c.nbuf, KTAIL, GSUM>),
                               grid, block, 0, s, p);
@@ -611,34 +664,28 @@ hipError_t launch_bf16_tile(const GemmParams& p, Epilogue epi, hipStream_t s) {
        }
      }()),
      ...);
-  }(std::make_integer_sequence<int, 5>{});
+  }(std::make_integer_sequence<int, 6>{});
   return done ? hipGetLastError() : hipErrorInvalidValue;
 }
 
-// K % 32 != 0 runs on the ragged-K variant of one tile (kTailTile) only; the
-// group sum is compiled for the row-step layouts (NN, NT).
-constexpr int kTailTile = 8;
-
+// p.tiles_n counts tiles of tile_out_cols(tile, epi) columns.
 template <int LAYOUT>
 hipError_t launch_bf16_layout_tile(int tile, const GemmParams& p, Epilogue epi, bool gsum,
                                    hipStream_t s) {
-  constexpr bool kHasGsum = LAYOUT != kTN;
-  if (p.K % 32) {
-    if (tile != kTailTile) return hipErrorInvalidValue;
-    if (gsum) {
-      if constexpr (kHasGsum) return launch_bf16_tile<LAYOUT, kTailTile, true, true>(p, epi, s);
-      return hipErrorInvalidValue;
-    }
-    return launch_bf16_tile<LAYOUT, kTailTile, true, false>(p, epi, s);
-  }
+  const bool ktail = p.K % 32 != 0;
   hipError_t r = hipErrorInvalidValue;
   [&]<int... t>(std::integer_sequence<int, t...>) {
     (([&] {
        if (tile != t) return;
-       if (!gsum) {
-         r = launch_bf16_tile<LAYOUT, t, false, false>(p, epi, s);
-       } else if constexpr (kHasGsum && tile_allows_group_sum(t)) {
+       if (ktail) {
+         if constexpr (t == kTailTile || t == kTailTileSwiGLU) {
+           if (gsum) r = launch_bf16_tile<LAYOUT, t, true, true>(p, epi, s);
+           else r = launch_bf16_tile<LAYOUT, t, true, false>(p, epi, s);
+         }
+       } else if (gsum) {
          r = launch_bf16_tile<LAYOUT, t, false, true>(p, epi, s);
+       } else {
+         r = launch_bf16_tile<LAYOUT, t, false, false>(p, epi, s);
        }
      }()),
      ...);

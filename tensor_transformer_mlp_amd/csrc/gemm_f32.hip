@@ -6,6 +6,10 @@
 // layout in memory (a K-major operand is transposed on its way into LDS), so
 // both MFMA operands are read as consecutive words across lanes.  This is the
 // full-precision path; the bf16 kernels carry the throughput.
+//
+// kEpiSwiGLU (kNN only) multiplies A by two B operands, B and B2, in the same
+// K loop (a second B tile in LDS and a second accumulator set) and stores
+// SiLU(A B) * (A B2).
 #include <type_traits>
 #include <utility>
 
@@ -19,6 +23,7 @@ namespace {
 struct F32Params {
   const float* A;
   const float* B;
+  const float* B2;  // kEpiSwiGLU
   const float* bias;
   float* C;
   float* aux;
@@ -33,8 +38,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
   constexpr int BM = 64, BN = 64, BK = 16, PAD = 4;
   constexpr bool AK = LAYOUT != kTN;  // A K-major
   constexpr bool BKM = LAYOUT == kNT; // B K-major
+  constexpr bool DUAL = EPI == kEpiSwiGLU;
+  static_assert(!DUAL || LAYOUT == kNN, "SwiGLU: kNN");
   __shared__ __attribute__((aligned(16))) float As[BK][BM + PAD];
   __shared__ __attribute__((aligned(16))) float Bs[BK][BN + PAD];
+  __shared__ __attribute__((aligned(16))) float Bs2[DUAL ? BK : 1][BN + PAD];
 
   int tm, tn;
   tile_coords<8>(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
@@ -47,11 +55,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
   const int64_t M = p.M;
   const int N = p.N, K = p.K;
 
-  f32x4_t acc[2][2];
+  f32x4_t acc[2][2], acc2[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = acc2[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // A K-major / B K-major: thread loads 4 consecutive k of row (tid / 4).
   // A M-major / B N-major: thread loads 4 consecutive m (n) of k-row (tid / 16).
@@ -59,7 +67,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
   const int xr = tid >> 4, xc = (tid & 15) * 4;
   const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < K; k0 += BK) {
-    f32x4_t va = zero, vb = zero;
+    f32x4_t va = zero, vb = zero, vb2 = zero;
     if constexpr (AK) {
       if (m0 + kr < M && k0 + kc < K)
         va = *reinterpret_cast<const f32x4_t*>(p.A + (m0 + kr) * p.lda + k0 + kc);
@@ -71,8 +79,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
       if (n0 + kr < N && k0 + kc < K)
         vb = *reinterpret_cast<const f32x4_t*>(p.B + (n0 + kr) * p.ldb + k0 + kc);
     } else {
-      if (k0 + xr < K && n0 + xc < N)
+      if (k0 + xr < K && n0 + xc < N) {
         vb = *reinterpret_cast<const f32x4_t*>(p.B + (int64_t)(k0 + xr) * p.ldb + n0 + xc);
+        if constexpr (DUAL)
+          vb2 = *reinterpret_cast<const f32x4_t*>(p.B2 + (int64_t)(k0 + xr) * p.ldb + n0 + xc);
+      }
     }
     if constexpr (AK) {
 #pragma unroll
@@ -85,6 +96,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
       for (int j = 0; j < 4; ++j) Bs[kc + j][kr] = vb[j];
     } else {
       *reinterpret_cast<f32x4_t*>(&Bs[xr][xc]) = vb;
+      if constexpr (DUAL) *reinterpret_cast<f32x4_t*>(&Bs2[xr][xc]) = vb2;
     }
     __syncthreads();
 #pragma unroll
@@ -100,6 +112,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_op[j], b_op[i], acc[i][j], 0, 0, 0);
+      if constexpr (DUAL) {
+        float a2_op[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) a2_op[j] = Bs2[kk][wn * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc2[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2_op[j], b_op[i], acc2[i][j], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
@@ -130,6 +152,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
         }
         *reinterpret_cast<f32x4_t*>(p.C + idx) = y;
         if constexpr (EPI == kEpiBiasGeluSave) *reinterpret_cast<f32x4_t*>(p.aux + idx) = g;
+      } else if constexpr (DUAL) {
+        const f32x4_t u = acc2[i][j];
+        f32x4_t y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = silu_f32(v[e]) * u[e];
+        *reinterpret_cast<f32x4_t*>(p.C + idx) = y;
       } else if constexpr (EPI == kEpiMulAux) {
         const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(p.aux + idx);
         *reinterpret_cast<f32x4_t*>(p.C + idx) = v * gg;
@@ -163,6 +191,12 @@ hipError_t launch_f32_layout(const F32Params& p, Epilogue epi, dim3 grid, hipStr
     case kEpiMulAux:
       hipLaunchKernelGGL((gemm_f32_kernel<kEpiMulAux, LAYOUT>), grid, block, 0, s, p);
       break;
+    case kEpiSwiGLU:
+      if constexpr (LAYOUT == kNN) {
+        hipLaunchKernelGGL((gemm_f32_kernel<kEpiSwiGLU, kNN>), grid, block, 0, s, p);
+        break;
+      }
+      return hipErrorInvalidValue;
     default:
       return hipErrorInvalidValue;
   }
@@ -181,6 +215,7 @@ hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
   const float* A = static_cast<const float*>(g.A);
   F32Params p;
   p.B = static_cast<const float*>(g.B);
+  p.B2 = static_cast<const float*>(g.B2);
   p.bias = static_cast<const float*>(g.bias);
   p.lda = g.lda;
   p.ldb = g.ldb;
@@ -209,7 +244,7 @@ hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_gemm_f32_batch(const GemmBatch& b, hipStream_t s) {
   for (int g = 0; g < b.groups; ++g) {
-    GemmArgs a{b.A[g], b.B[g], b.bias[g], b.group_sum ? b.C[0] : b.C[g], b.aux[g], b.M, b.N, b.K,
+    GemmArgs a{b.A[g], b.B[g], b.bias[g], b.B2[g], b.group_sum ? b.C[0] : b.C[g], b.aux[g], b.M, b.N, b.K,
                b.lda, b.ldb, b.ldc, b.layout, b.epi};
     if (b.group_sum && g > 0) a.epi = kEpiAccumF32;  // C[0] += A[g] B[g], in group order
     const hipError_t e = launch_gemm_f32(a, s);

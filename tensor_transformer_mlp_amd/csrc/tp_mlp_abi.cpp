@@ -108,6 +108,20 @@ int col_steps(const void* X, const void* const* W, const void* const* b, void* c
   return run(g, dtype, s);
 }
 
+// SwiGLU column step: Y_i = SiLU(X Wg_i) * (X Wu_i), two [H, Fk] row-major
+// weights per shard in one GEMM.
+int swiglu_col_steps(const void* X, const void* const* Wg, const void* const* Wu, void* const* Y, int n,
+                     int64_t M, int64_t H, int64_t Fk, int dtype, hipStream_t s) {
+  GemmBatch g = batch(n, tpmlp::kNN, tpmlp::kEpiSwiGLU, M, Fk, H, H, Fk);
+  for (int i = 0; i < n; ++i) {
+    g.A[i] = X;
+    g.B[i] = Wg[i];
+    g.B2[i] = Wu[i];
+    g.C[i] = Y[i];
+  }
+  return run(g, dtype, s);
+}
+
 // Z_i (+)= Y_i V_i: [M, Fk] x [Fk, H], one output per shard (sum == false),
 // or Z (+)= sum_i Y_i V_i in shard order into Z[0] (sum == true).
 int row_steps(const void* const* Y, const void* const* V, float* const* Z, int n, bool sum,
@@ -498,6 +512,85 @@ int tp_mlp_shard_forward_sp(const void* X, const void* const* W, const void* con
   // The reduce-scatter over the k sequence blocks, with X as the residual.
   return hip_status(tpmlp::launch_sp_reduce_scatter(parts, fused ? 1 : k, X, dtype == TP_BF16, O,
                                                     out_dtype == TP_BF16, k, (M / k) * H, s));
+}
+
+int tp_swiglu_col_shards(const void* X, const void* const* Wg, const void* const* Wu, void* const* Y,
+                         int n, int64_t M, int64_t H, int64_t Fk, int dtype, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
+  if (M == 0) return TP_OK;
+  if (!X || !Wg || !Wu || !Y) return TP_ERR_NULL;
+  if (!aligned16(X)) return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  Regions in, out;
+  in.add(X, size_t(M) * size_t(H) * e);
+  for (int i = 0; i < n; ++i) {
+    if (!Wg[i] || !Wu[i] || !Y[i]) return TP_ERR_NULL;
+    if (!aligned16(Wg[i]) || !aligned16(Wu[i]) || !aligned16(Y[i])) return TP_ERR_ALIGN;
+    in.add(Wg[i], size_t(H) * size_t(Fk) * e);
+    in.add(Wu[i], size_t(H) * size_t(Fk) * e);
+    out.add(Y[i], size_t(M) * size_t(Fk) * e);
+  }
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return swiglu_col_steps(X, Wg, Wu, Y, n, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+}
+
+int tp_swiglu_col(const void* X, const void* Wg_i, const void* Wu_i, void* Y_i, int64_t M, int64_t H,
+                  int64_t Fk, int dtype, void* stream) {
+  return tp_swiglu_col_shards(X, &Wg_i, &Wu_i, &Y_i, 1, M, H, Fk, dtype, stream);
+}
+
+int tp_swiglu_shard_forward(const void* X, const void* const* Wg, const void* const* Wu,
+                            const void* const* V, int k, int64_t M, int64_t H, int64_t Fk, int dtype,
+                            void* workspace, size_t workspace_bytes, float* Z, unsigned flags,
+                            void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (flags & ~TP_FUSED_ACCUM) return TP_ERR_FLAGS;
+  if (k < 1 || k > TP_MAX_SHARDS) return TP_ERR_SHAPE;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (M == 0) return TP_OK;
+  if (!X || !Wg || !Wu || !V || !Z) return TP_ERR_NULL;
+  for (int i = 0; i < k; ++i) {
+    if (!Wg[i] || !Wu[i] || !V[i]) return TP_ERR_NULL;
+    if (!aligned16(Wg[i]) || !aligned16(Wu[i]) || !aligned16(V[i])) return TP_ERR_ALIGN;
+  }
+  if (!aligned16(X) || !aligned16(Z)) return TP_ERR_ALIGN;
+  const size_t need = tp_mlp_workspace_bytes(k, M, H, Fk, dtype, flags);
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  const size_t nz = size_t(M) * size_t(H) * 4;
+  Regions in, out;
+  in.add(X, size_t(M) * size_t(H) * e);
+  for (int i = 0; i < k; ++i) {
+    in.add(Wg[i], size_t(H) * size_t(Fk) * e);
+    in.add(Wu[i], size_t(H) * size_t(Fk) * e);
+    in.add(V[i], size_t(Fk) * size_t(H) * e);
+  }
+  out.add(Z, nz);
+  out.add(workspace, need);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fused = (flags & TP_FUSED_ACCUM) != 0;
+  char* ws = static_cast<char*>(workspace);
+  const int G = batch_size(k);
+  const size_t y_bytes = round_up(size_t(M) * size_t(Fk) * e, kWsAlign);
+  const size_t part_bytes = round_up(nz, kWsAlign);
+  void* Y[kMaxGroups];
+  for (int j = 0; j < G; ++j) Y[j] = ws + size_t(j) * y_bytes;
+  char* part_base = ws + size_t(G) * y_bytes;
+  const float* parts[TP_MAX_SHARDS];
+  auto part = [&](int i) {
+    return i == 0 ? Z : reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
+  };
+  auto col = [&](int i0, int n) { return swiglu_col_steps(X, Wg + i0, Wu + i0, Y, n, M, H, Fk, dtype, s); };
+  if ((st = shard_steps(col, V, k, M, H, Fk, dtype, Y, fused, part, parts, s))) return st;
+  if (!fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
+  return TP_OK;
 }
 
 int tp_mlp_grad_act_shards(const void* dZ, const void* const* V, const void* const* G,

@@ -17,6 +17,7 @@ enum Epilogue : int {
   kEpiAccumF32 = 2,      // C = C + acc                                      (float32)
   kEpiBiasGeluSave = 3,  // C = GeLU(acc + bias[n]), aux = GeLU'(acc + bias[n]) (operand dtype)
   kEpiMulAux = 4,        // C = acc * aux[m, n]; C may be aux itself         (operand dtype)
+  kEpiSwiGLU = 5,        // C = SiLU(A B) * (A B2), two B operands (kNN)     (operand dtype)
 };
 
 // Operand layouts.  A is logically [M, K] and B [K, N]:
@@ -29,6 +30,7 @@ struct GemmArgs {
   const void* A;
   const void* B;
   const void* bias;  // [N], kEpiBiasGelu / kEpiBiasGeluSave; may be null
+  const void* B2;    // second B operand (same layout as B): kEpiSwiGLU
   void* C;           // [M, N], row m at C + m * ldc
   void* aux;         // [M, N] with leading dimension ldc: kEpiBiasGeluSave / kEpiMulAux
   int64_t M, N, K;
@@ -42,11 +44,13 @@ struct GemmArgs {
 // (entries may repeat, such as a shared X).  group_sum: instead, C[0] =
 // sum_g A[g] B[g] with one float32 accumulator per group added in group
 // order (kEpiAccumF32: C[0] + sum, in the same order), which is bit-identical
-// to storing every product and summing them left to right.
+// to storing every product and summing them left to right.  kEpiSwiGLU
+// groups also take a second B operand, B2[g].
 constexpr int kMaxGroups = 16;
 struct GemmBatch {
   const void* A[kMaxGroups];
   const void* B[kMaxGroups];
+  const void* B2[kMaxGroups];
   const void* bias[kMaxGroups];
   void* C[kMaxGroups];
   void* aux[kMaxGroups];

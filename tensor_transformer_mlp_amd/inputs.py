@@ -42,7 +42,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "csrc", "synth_inputs.c")
 _LIB_PATH = os.path.join(_HERE, "libtpsynth.so")
 
-STREAM_X, STREAM_W, STREAM_B, STREAM_V, STREAM_DZ = 0, 1, 2, 3, 4
+STREAM_X, STREAM_W, STREAM_B, STREAM_V, STREAM_DZ, STREAM_WU = 0, 1, 2, 3, 4, 5
 BASE_SEED = 42
 
 
@@ -188,6 +188,32 @@ def make_custom(M: int, H: int, F: int, dtype: str, std: float = 0.02, x_std: fl
         "b": draw(STREAM_B, (F,), std, dtype, seed),
         "V": draw(STREAM_V, (F, H), std, dtype, seed),
     }
+
+
+def make_swiglu(w: Workload | None = None, seed: int = BASE_SEED, M: int | None = None, H: int | None = None,
+                F: int | None = None, dtype: str | None = None, std: float | None = None) -> dict:
+    """Inputs of the SwiGLU block: X[M,H], gate Wg[H,F] (the W stream), up
+    Wu[H,F] (its own stream) and V[F,H], for a workload or a custom shape."""
+    M = M if M is not None else w.M
+    H = H if H is not None else w.H
+    F = F if F is not None else w.F
+    dtype = dtype if dtype is not None else w.dtype
+    std = std if std is not None else w.std
+    return {
+        "X": draw(STREAM_X, (M, H), 1.0, dtype, seed),
+        "Wg": draw(STREAM_W, (H, F), std, dtype, seed),
+        "Wu": draw(STREAM_WU, (H, F), std, dtype, seed),
+        "V": draw(STREAM_V, (F, H), std, dtype, seed),
+    }
+
+
+def col_slices(W: np.ndarray, k: int):
+    """Contiguous column blocks W_i = W[:, i*Fk:(i+1)*Fk] (data placement only)."""
+    F = W.shape[1]
+    if F % k:
+        raise ValueError("k must divide F")
+    Fk = F // k
+    return [np.ascontiguousarray(W[:, i * Fk:(i + 1) * Fk]) for i in range(k)]
 
 
 def shard_slices(W: np.ndarray, b: np.ndarray, V: np.ndarray, k: int):

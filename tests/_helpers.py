@@ -26,6 +26,12 @@ Backward (dY = dZ V_i^T, dA = dY * G, G = GeLU'(A)):
   and errG the error of the G the kernel used,
     |dA_gpu - dA| <= u_out |dA| + (1 + u_out) (errdY |G| + |dY| errG
                      + errdY errG + u32 |dY| |G|).
+* SwiGLU column step, per element of Y_i = SiLU(g) u with g = X Wg_i,
+  u = X Wu_i accumulated in float32 (errors e_g, e_u <= 2 (K + 2) u32 S_g, S_u):
+    |Y_gpu - Y| <= u_out |Y| + (1 + u_out) (1.1 |u| e_g + |SiLU(g)| e_u + 1.1 e_g e_u
+                                            + (4 + 2 |g|) u32 |Y|)
+  with 1.1 >= max |SiLU'| and (4 + 2 |g|) u32 the relative error of the
+  float32 SiLU (the exponential's argument rounding grows with |g|).
 * a float32 GEMM over K terms of operands with errors e_a, e_b:
     |C_gpu - C| <= e_a^T |b| + |a|^T e_b + 2 (K + 2) u32 (|a| + e_a)^T (|b| + e_b).
 """
@@ -162,3 +168,20 @@ def backward_terms(orc, Xr, Wc, bc, Vc, dZr, dtype: str):
     errG = grad_g_bound(S, G, H, dtype)
     errdA = act_grad_bound(dY, G, errdY, errG, dtype)
     return dict(A=A, Y=Y, G=G, dY=dY, dA=dY * G, tolY=tolY, errG=errG, errdA=errdA)
+
+
+SILU_LIP = 1.1
+
+
+def swiglu_bound(X64, Wg64, Wu64, G, U, Y, dtype: str):
+    """Element-wise bound for the SwiGLU Y_i (see module docstring); G, U the
+    exact gate and up pre-activations, Y the exact output."""
+    K = X64.shape[1]
+    aX = np.abs(X64)
+    eg = 2 * (K + 2) * U32 * (aX @ np.abs(Wg64))
+    eu = 2 * (K + 2) * U32 * (aX @ np.abs(Wu64))
+    s = G / (1.0 + np.exp(-G))
+    u_out = U16 if dtype == "bf16" else 0.0
+    aY = np.abs(Y)
+    return (u_out * aY + (1 + u_out) * (SILU_LIP * np.abs(U) * eg + np.abs(s) * eu + SILU_LIP * eg * eu
+                                        + (4 + 2 * np.abs(G)) * U32 * aY) + 1e-30)

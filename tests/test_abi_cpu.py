@@ -46,7 +46,8 @@ def test_exports_every_declared_symbol(L):
                      "tp_mlp_col_gelu_shards", "tp_mlp_row_partial_shards", "tp_mlp_grad_act_shards",
                      "tp_mlp_grad_weight_workspace_bytes_shards", "tp_mlp_grad_row_weight_shards",
                      "tp_mlp_grad_col_weight_shards", "tp_mlp_grad_input_shards",
-                     "tp_sp_reduce_scatter", "tp_mlp_sp_workspace_bytes", "tp_mlp_shard_forward_sp"}
+                     "tp_sp_reduce_scatter", "tp_mlp_sp_workspace_bytes", "tp_mlp_shard_forward_sp",
+                     "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -499,3 +500,37 @@ def test_shard_forward_sp_errors(L):
     assert f(*a) == c["TP_ERR_ALIAS"]
     a = base(); a[5] = 0
     assert f(*a) == c["TP_OK"]
+
+
+def test_swiglu_errors(L):
+    c = _header_constants()
+    f = L.tp_swiglu_col
+    X, Wg, Wu, Y = _p(0), _p(1), _p(2), _p(3)
+    assert f(X, Wg, Wu, Y, 8, 64, 128, 2, None) == c["TP_ERR_DTYPE"]
+    assert f(X, Wg, Wu, Y, 8, 60, 128, 1, None) == c["TP_ERR_SHAPE"]
+    assert f(X, None, Wu, Y, 8, 64, 128, 1, None) == c["TP_ERR_NULL"]
+    assert f(X, Wg, None, Y, 8, 64, 128, 1, None) == c["TP_ERR_NULL"]
+    assert f(X, Wg, ctypes.c_void_p(3 * P + 8), Y, 8, 64, 128, 1, None) == c["TP_ERR_ALIGN"]
+    assert f(X, Wg, Wu, ctypes.c_void_p(2 * P + 64), 8, 64, 128, 1, None) == c["TP_ERR_ALIAS"]  # Y over Wu
+    assert f(X, Wg, Wu, Y, 0, 64, 128, 1, None) == c["TP_OK"]
+    fs = L.tp_swiglu_col_shards
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    assert fs(X, arr(P, 2 * P), arr(3 * P, 4 * P), arr(5 * P, 6 * P), 0, 8, 64, 128, 1, None) == c["TP_ERR_SHAPE"]
+    assert fs(X, arr(P, 2 * P), arr(3 * P, 4 * P), arr(5 * P, 5 * P + 16), 2, 8, 64, 128, 1, None) == \
+        c["TP_ERR_ALIAS"]
+    ff = L.tp_swiglu_shard_forward
+    k = 2
+    need = L.tp_mlp_workspace_bytes(k, 8, 64, 128, 1, 0)
+    ws, Z = ctypes.c_void_p(1 << 40), ctypes.c_void_p(1 << 41)
+    base = lambda: [ctypes.c_void_p(1 << 42), arr(10 * P, 11 * P), arr(12 * P, 13 * P), arr(14 * P, 15 * P), k, 8,
+                    64, 128, 1, ws, need, Z, 0, None]
+    a = base(); a[12] = 2
+    assert ff(*a) == c["TP_ERR_FLAGS"]
+    a = base(); a[10] = need - 1
+    assert ff(*a) == c["TP_ERR_WORKSPACE"]
+    a = base(); a[2] = arr(12 * P, None)
+    assert ff(*a) == c["TP_ERR_NULL"]
+    a = base(); a[11] = ctypes.c_void_p(12 * P + 256)      # Z over an up weight
+    assert ff(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[5] = 0
+    assert ff(*a) == c["TP_OK"]
