@@ -25,6 +25,12 @@ blocks of the sequence, with the block's residual added to each block:
 SwiGLU variant (no biases):
   Y_i = SiLU(X Wg_i) * (X Wu_i),  SiLU(x) = x / (1 + exp(-x)),  Z = sum_i Y_i V_i.
 
+Tensor-parallel attention (heads split over the k shards, hk = n_heads / k
+per shard, d = H / n_heads, Hk = hk d):
+  QKV_i = X [Wq_i | Wk_i | Wv_i] + [bq_i | bk_i | bv_i]   (column blocks i)
+  per head: softmax(q k^T / sqrt d, causal or not, within each sequence) v
+  A_i = heads side by side,  Z = sum_i A_i Wo_i  (Wo_i = rows block i of Wo).
+
 Every forward function here is pinned by tests/test_oracle_pins.py (brute
 force in exact rational arithmetic with 50-digit erf, the column-split and
 row-split identities, GeLU closed forms, special cases that reduce to library
@@ -37,7 +43,13 @@ the sequence-parallel and SwiGLU functions by tests/test_oracle_sp_swiglu_pins.p
 blocks against the all-reduce, residual-only and zero-residual cases, row
 locality; SiLU closed forms and 50-digit values, exact rational brute force,
 gate/up asymmetry, the column- and row-split identities and k-invariance, an
-independent numpy implementation).
+independent numpy implementation); the attention functions by
+tests/test_oracle_attn_pins.py (exact-rational projections with 50-digit
+softmax on tiny inputs, one key gives v, a zero query gives the mean of the
+visible values, two-key closed forms with the 1/sqrt(d) scale, causality,
+sequence independence, key permutation invariance without the mask, the
+head split and row split identities, k-invariance, an independent numpy
+implementation).
 """
 from __future__ import annotations
 
@@ -85,6 +97,10 @@ def _L():
         lib.oracle_silu_array.argtypes = [vp, i64, vp]
         lib.oracle_swiglu_col.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
         lib.oracle_swiglu_forward_rows.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp, i64, vp]
+        lib.oracle_attn_qkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, vp]
+        lib.oracle_attn_core.argtypes = [vp, i64, i64, ci, i64, ci, vp]
+        lib.oracle_attn_forward_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, vp, i64,
+                                                 vp]
         lib.oracle_gelu_grad.argtypes = [ctypes.c_double]
         lib.oracle_gelu_grad.restype = ctypes.c_double
         lib.oracle_gelu_grad_array.argtypes = [vp, i64, vp]
@@ -101,7 +117,8 @@ def _L():
                   lib.oracle_row_weight_grad, lib.oracle_col_weight_grad,
                   lib.oracle_input_grad_partial, lib.oracle_backward_rows, lib.oracle_backward_cols,
                   lib.oracle_sp_reduce_scatter, lib.oracle_silu_array, lib.oracle_swiglu_col,
-                  lib.oracle_swiglu_forward_rows):
+                  lib.oracle_swiglu_forward_rows, lib.oracle_attn_qkv, lib.oracle_attn_core,
+                  lib.oracle_attn_forward_rows):
             f.restype = None
         _lib = lib
     return _lib
@@ -449,3 +466,72 @@ def swiglu_forward_rows(X, Wg, Wu, V, k: int, rows=None) -> np.ndarray:
 def swiglu_forward(X, Wg, Wu, V, k: int) -> np.ndarray:
     """Z = sum_i (SiLU(X Wg_i) * (X Wu_i)) V_i, float64 [M, H]."""
     return swiglu_forward_rows(X, Wg, Wu, V, k, None)
+
+
+# ---------------------------------------------------------------------------
+# Tensor-parallel attention.
+
+def _attn_dims(H: int, nh: int, k: int):
+    if nh < 1 or H % nh or nh % k:
+        raise ValueError("n_heads must divide H and k must divide n_heads")
+    d = H // nh
+    return d, nh // k, (nh // k) * d
+
+
+def attn_qkv(X, Wq, Wk, Wv, bq, bk, bv, nh: int, k: int, i: int) -> np.ndarray:
+    """[q | k | v] of shard i: float64 [M, 3 Hk]; biases may be None."""
+    X, Wq, Wk, Wv = widen(X), widen(Wq), widen(Wk), widen(Wv)
+    bq, bk, bv = [widen(x) if x is not None else None for x in (bq, bk, bv)]
+    M, H = X.shape
+    assert Wq.shape == Wk.shape == Wv.shape == (H, H)
+    d, hk, Hk = _attn_dims(H, nh, k)
+    if not 0 <= i < k:
+        raise ValueError("shard index out of range")
+    out = np.empty((M, 3 * Hk))
+    if M:
+        _L().oracle_attn_qkv(_p(X), _p(Wq), _p(Wk), _p(Wv), _p(bq), _p(bk), _p(bv), M, H, nh, k, i, _p(out))
+    return out
+
+
+def attn_core(QKV, B: int, S: int, hk: int, d: int, causal: bool = True) -> np.ndarray:
+    """The shard's heads' attention outputs side by side, float64 [B S, hk d]."""
+    Q = np.ascontiguousarray(widen(QKV))
+    assert Q.shape == (B * S, 3 * hk * d)
+    A = np.empty((B * S, hk * d))
+    if B * S:
+        _L().oracle_attn_core(_p(Q), B, S, hk, d, 1 if causal else 0, _p(A))
+    return A
+
+
+def attn_forward_rows(X, Wq, Wk, Wv, bq, bk, bv, Wo, nh: int, S: int, k: int, rows,
+                      causal: bool = True) -> np.ndarray:
+    """Z[rows, :] of the whole attention block, float64 (rows index X = [B S, H])."""
+    X, Wq, Wk, Wv, Wo = widen(X), widen(Wq), widen(Wk), widen(Wv), widen(Wo)
+    bq, bk, bv = [widen(x) if x is not None else None for x in (bq, bk, bv)]
+    M, H = X.shape
+    _attn_dims(H, nh, k)
+    if S < 1 or M % S:
+        raise ValueError("S must divide M")
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    if r.size and (r.min() < 0 or r.max() >= M):
+        raise IndexError("row index out of range")
+    Z = np.empty((r.size, H))
+    if r.size:
+        _L().oracle_attn_forward_rows(_p(X), _p(Wq), _p(Wk), _p(Wv), _p(bq), _p(bk), _p(bv), _p(Wo), S, H, nh, k,
+                                      1 if causal else 0, _p(r), r.size, _p(Z))
+    return Z
+
+
+def attn_forward(X, Wq, Wk, Wv, bq, bk, bv, Wo, nh: int, S: int, k: int, causal: bool = True) -> np.ndarray:
+    """The attention block by shards, in the order of the steps: float64 [M, H]."""
+    X64 = widen(X)
+    M, H = X64.shape
+    d, hk, Hk = _attn_dims(H, nh, k)
+    Wo64 = widen(Wo)
+    parts = []
+    for i in range(k):
+        A = attn_core(attn_qkv(X64, Wq, Wk, Wv, bq, bk, bv, nh, k, i), M // S, S, hk, d, causal)
+        Woi = np.ascontiguousarray(Wo64[i * Hk:(i + 1) * Hk])
+        # Z_i = A_i Wo_i: the row-parallel partial of the MLP oracle with one shard
+        parts.append(row_partial(A, Woi, 1, 0))
+    return shard_reduce(parts)

@@ -61,6 +61,25 @@
  *      with Wg_i, Wu_i the column blocks i of Wg, Wu [H, F]; steps 4 and 5
  *      are unchanged (Z_i = Y_i V_i, Z = sum_i Z_i).
  *
+ * Tensor-parallel attention block (multi-head attention split by heads: the
+ * Q/K/V projections column-parallel, each shard computing its own heads'
+ * attention with no communication, the output projection row-parallel and
+ * summed: "AI大模型分布式训练：张量并行与流水线并行深度实践" §2.3; "千亿参数模型如何拆分
+ * 到多张GPU上训练" 注意力层的切分; "大模型分布式并行策略详解：TP、DP、PP、CP、EP核心原理
+ * 与实战" §4.2).  Given Wq, Wk, Wv, Wo [H, H], biases bq, bk, bv [H], n_heads
+ * heads of d = H / n_heads columns, k shards of hk = n_heads / k heads and
+ * Hk = hk d, rows m = b S + t of X (batch b, position t):
+ *  14. shard i's heads are i hk .. (i+1) hk - 1; its projection output is
+ *      [q | k | v] = X [Wq_i | Wk_i | Wv_i] + [bq_i | bk_i | bv_i] with
+ *      Wq_i = Wq[:, i Hk:(i+1) Hk] (and so on), the chunk-in-three layout of
+ *      the shard's ColumnParallelLinear(H, 3H) output;
+ *  15. per head h, scaled dot-product attention within each sequence:
+ *      s_tj = q_t . k_j / sqrt(d) for keys j of the same sequence, j <= t
+ *      when causal; p_tj = exp(s_tj) / sum_j' exp(s_tj'); o_t = sum_j p_tj v_j;
+ *  16. A_i = the shard's heads side by side [M, Hk]; Z_i = A_i Wo_i with
+ *      Wo_i = Wo[i Hk:(i+1) Hk, :] (RowParallelLinear, no bias);
+ *  17. Z = Z_0 + ... + Z_{k-1}.
+ *
  * All arrays are row-major doubles; the Python wrapper widens bf16/f32 inputs
  * to double exactly before calling.  Sums run in index order.  Parallelism is
  * over output rows only (OpenMP), which does not change any value.
@@ -425,6 +444,122 @@ void oracle_swiglu_forward_rows(const double* X, const double* Wg, const double*
     free(y);
     free(u);
     free(zi);
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Tensor-parallel attention (steps 14-17).                                 */
+
+/* Step 14 for one row: out[0..3Hk) = [q | k | v] of shard i. */
+static void attn_qkv_row(const double* x, const double* Wq, const double* Wk, const double* Wv,
+                         const double* bq, const double* bk, const double* bv, int64_t H,
+                         int64_t Hk, int64_t i, double* out) {
+  const double* W[3] = {Wq, Wk, Wv};
+  const double* bb[3] = {bq, bk, bv};
+  for (int part = 0; part < 3; ++part) {
+    double* o = out + part * Hk;
+    for (int64_t c = 0; c < Hk; ++c) o[c] = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+      const double xv = x[h];
+      const double* w = W[part] + h * H + i * Hk;
+      for (int64_t c = 0; c < Hk; ++c) o[c] += xv * w[c];
+    }
+    if (bb[part])
+      for (int64_t c = 0; c < Hk; ++c) o[c] += bb[part][i * Hk + c];
+  }
+}
+
+/* QKV_i[M, 3 Hk] of shard i (step 14).  Biases may be NULL. */
+void oracle_attn_qkv(const double* X, const double* Wq, const double* Wk, const double* Wv,
+                     const double* bq, const double* bk, const double* bv, int64_t M, int64_t H,
+                     int nh, int k, int i, double* QKV) {
+  const int64_t Hk = H / nh * (nh / k);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < M; ++m) attn_qkv_row(X + m * H, Wq, Wk, Wv, bq, bk, bv, H, Hk, i, QKV + m * 3 * Hk);
+}
+
+/* Step 15 for one query row t of sequence b and one head h of the shard:
+   qkv is the shard's [M, 3 Hk] projection, o[0..d) the head's output. */
+static void attn_head_row(const double* qkv, int64_t S, int64_t Hk, int64_t d, int64_t b, int64_t t,
+                          int64_t h, int causal, double* p, double* o) {
+  const int64_t ld = 3 * Hk;
+  const double* q = qkv + (b * S + t) * ld + h * d;
+  const int64_t nkeys = causal ? t + 1 : S;
+  const double scale = 1.0 / sqrt((double)d);
+  double mx = -INFINITY;
+  for (int64_t j = 0; j < nkeys; ++j) {
+    const double* kj = qkv + (b * S + j) * ld + Hk + h * d;
+    double s = 0.0;
+    for (int64_t c = 0; c < d; ++c) s += q[c] * kj[c];
+    p[j] = s * scale;
+    if (p[j] > mx) mx = p[j];
+  }
+  /* softmax; subtracting the maximum changes no value in exact arithmetic */
+  double sum = 0.0;
+  for (int64_t j = 0; j < nkeys; ++j) {
+    p[j] = exp(p[j] - mx);
+    sum += p[j];
+  }
+  for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+  for (int64_t j = 0; j < nkeys; ++j) {
+    const double w = p[j] / sum;
+    const double* vj = qkv + (b * S + j) * ld + 2 * Hk + h * d;
+    for (int64_t c = 0; c < d; ++c) o[c] += w * vj[c];
+  }
+}
+
+/* A_i[M, Hk] from the shard's projection QKV_i (step 15), M = B S. */
+void oracle_attn_core(const double* QKV, int64_t B, int64_t S, int hk, int64_t d, int causal,
+                      double* A) {
+  const int64_t Hk = hk * d;
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+#pragma omp for schedule(dynamic, 1) collapse(2)
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t t = 0; t < S; ++t)
+        for (int64_t h = 0; h < hk; ++h) attn_head_row(QKV, S, Hk, d, b, t, h, causal, p, A + (b * S + t) * Hk + h * d);
+    free(p);
+  }
+}
+
+/* The whole block for selected rows (steps 14-17): Z[r, :] for row
+   m = rows[r] = b S + t.  Only the rows the query attends to are projected
+   (positions 0..t of sequence b when causal, the whole sequence otherwise). */
+void oracle_attn_forward_rows(const double* X, const double* Wq, const double* Wk, const double* Wv,
+                              const double* bq, const double* bk, const double* bv, const double* Wo,
+                              int64_t S, int64_t H, int nh, int k, int causal, const int64_t* rows,
+                              int64_t nrows, double* Z) {
+  const int64_t d = H / nh, hk = nh / k, Hk = hk * d;
+#pragma omp parallel
+  {
+    double* qkv = (double*)malloc(sizeof(double) * (size_t)(S * 3 * Hk));
+    double* p = (double*)malloc(sizeof(double) * (size_t)S);
+    double* a = (double*)malloc(sizeof(double) * (size_t)Hk);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+      const int64_t m = rows[r], b = m / S, t = m % S;
+      const int64_t n = causal ? t + 1 : S;
+      double* z = Z + r * H;
+      for (int64_t c = 0; c < H; ++c) z[c] = 0.0;
+      for (int i = 0; i < k; ++i) {
+        /* the shard's projection of rows b S .. b S + n - 1, stored as a
+           one-sequence [n, 3 Hk] block (sequence 0 of length n) */
+        for (int64_t j = 0; j < n; ++j)
+          attn_qkv_row(X + (b * S + j) * H, Wq, Wk, Wv, bq, bk, bv, H, Hk, i, qkv + j * 3 * Hk);
+        for (int64_t h = 0; h < hk; ++h)
+          attn_head_row(qkv, n, Hk, d, 0, t, h, causal, p, a + h * d);
+        /* Z += A_i[m] Wo_i */
+        for (int64_t c = 0; c < Hk; ++c) {
+          const double av = a[c];
+          const double* w = Wo + (i * Hk + c) * H;
+          for (int64_t e = 0; e < H; ++e) z[e] += av * w[e];
+        }
+      }
+    }
+    free(qkv);
+    free(p);
+    free(a);
   }
 }
 
