@@ -10,10 +10,11 @@ then the dX shard sum) is timed the same way and reported under "backward",
 and so is the sequence-parallel forward (tp_mlp_shard_forward_sp: the shard
 sum as a reduce-scatter over the k sequence blocks with the residual X added)
 under "sequence_parallel", and the SwiGLU variant of the block
-(tp_swiglu_shard_forward) under "swiglu".
+(tp_swiglu_shard_forward) under "swiglu", and the causal tensor-parallel
+attention block of the same width (tp_attn_shard_forward) under "attention".
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant literal|fused]
-                    [--no-backward] [--no-sp] [--no-swiglu]
+                    [--no-backward] [--no-sp] [--no-swiglu] [--no-attention]
 
 Prints ONE JSON line (metric, value in TFLOP/s, ms_per_step, roofline of the
 dominant kernel, CPU-oracle baseline, backward) on stdout; diagnostics go to
@@ -54,6 +55,7 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel leg")
     ap.add_argument("--no-swiglu", action="store_true", help="skip the SwiGLU leg")
+    ap.add_argument("--no-attention", action="store_true", help="skip the attention leg")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain float32 copy kernel (y = x * 1) over MIB MiB, 5 times: "
                          "the known-size reference for the HBM byte counters")
@@ -80,6 +82,10 @@ def kernel_bytes(kind, w, elt, n):
         "sp_reduce_fused": (4 + elt + 4) * M * H,
         # SwiGLU column step: X once, gate and up weights, Y
         "swiglu_col": M * H * elt + n * (2 * H * Fk + M * Fk) * elt,
+        # attention block (Hk = H / k per shard): projection, attention, output projection
+        "attn_qkv": M * H * elt + n * (3 * H * (H // k) + 3 * (H // k) + 3 * M * (H // k)) * elt,
+        "attn_core": n * 4 * M * (H // k) * elt,
+        "attn_out": n * ((M * (H // k) + (H // k) * H) * elt + M * H * 4),
     }
     return table[kind]
 
@@ -93,6 +99,13 @@ def kernel_flops(kind, w, n):
         return w.M * w.H
     if kind == "swiglu_col":
         return n * 4 * w.M * w.H * w.Fk
+    if kind == "attn_qkv":
+        return n * 2 * w.M * w.H * 3 * (w.H // w.k)
+    if kind == "attn_core":
+        # causal: query t meets t + 1 keys; 2 d flop for the score, 2 d for the sum
+        return n * 4 * (w.H // w.k) * w.B * (w.S * (w.S + 1) // 2)
+    if kind == "attn_out":
+        return n * 2 * w.M * (w.H // w.k) * w.H
     return n * 2 * w.M * w.H * w.Fk
 
 
@@ -273,6 +286,10 @@ def main():
     swiglu = None
     if not args.no_swiglu:
         swiglu = bench_swiglu(tpm, w, X, Vs, fused, args, elt, tdt)
+    del Vs
+    attn = None
+    if not args.no_attention and w.dtype == "bf16":
+        attn = bench_attention(tpm, w, X, fused, args, elt)
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
@@ -291,6 +308,7 @@ def main():
         "backward": bwd,
         "sequence_parallel": sp,
         "swiglu": swiglu,
+        "attention": attn,
     }
     print(json.dumps(out), flush=True)
 
@@ -503,6 +521,85 @@ def bench_swiglu(tpm, w, X, Vs, fused, args, elt, tdt):
     return {"metric": "TP-shard SwiGLU MLP forward TFLOP/s (3 GEMMs of 2 M H F/k per shard)",
             "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
             "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "roofline": roof,
+            "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],
+                             "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()}}
+
+
+def bench_attention(tpm, w, X, fused, args, elt):
+    """Time tp_attn_shard_forward (the causal tensor-parallel attention block of
+    the workload's width, heads and sequences: per shard the projection of its
+    heads, their attention and the output projection, then the shard sum) on
+    the same X with attention weights drawn for it, and its kernels by kind.
+    FLOPs counted: the three GEMMs (8 M H^2) and the unmasked half of the
+    attention (4 H B S(S+1)/2); the roofline entry is the attention kernel's."""
+    import numpy as np
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    dev = X.device
+    k, M, H, nh = w.k, w.M, w.H, w.heads
+    Hk, d, hk = H // k, H // nh, nh // k
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    inp = inputs.make_attention(w)
+    Wqkv_h, bqkv_h = inputs.qkv_shards(inp["Wq"], inp["Wk"], inp["Wv"], inp["bq"], inp["bk"], inp["bv"], nh, k)
+    Wqkv = [up(x) for x in Wqkv_h]
+    bqkv = [up(x) for x in bqkv_h]
+    Wo = [up(np.ascontiguousarray(inp["Wo"][i * Hk:(i + 1) * Hk])) for i in range(k)]
+    del inp, Wqkv_h, bqkv_h
+    flags = (tpm.TP_FUSED_ACCUM if fused else 0) | tpm.TP_CAUSAL
+    ws = torch.empty(max(tpm.tp_attn_workspace_bytes(k, w.B, w.S, H, nh, tpm.TP_BF16, flags), 1),
+                     dtype=torch.uint8, device=dev)
+    Z = torch.empty(M, H, dtype=torch.float32, device=dev)
+
+    def step():
+        tpm.tp_attn_shard_forward(X, Wqkv, bqkv, Wo, w.B, w.S, nh, Z=Z, workspace=ws, fused=fused, causal=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    flop = 8 * M * H * H + 4 * H * w.B * (w.S * (w.S + 1) // 2)
+    tflops = flop / (ms * 1e-3) / 1e12
+    log("attention forward (%d heads of %d, causal): %.4f ms/step, %.1f TFLOP/s (%.1f%% of bf16 peak)" % (
+        nh, d, ms, tflops, 100 * tflops / PEAK_TFLOPS["bf16"]))
+    if not bool(torch.isfinite(Z).all()):
+        raise RuntimeError("non-finite attention output")
+
+    G = min(k, tpm.TP_MAX_BATCH)
+    batches = [(i0, min(G, k - i0)) for i0 in range(0, k, G)]
+    QKV = [torch.empty(M, 3 * Hk, dtype=torch.bfloat16, device=dev) for _ in range(G)]
+    A = [torch.empty(M, Hk, dtype=torch.bfloat16, device=dev) for _ in range(G)]
+    parts = [Z] + [torch.empty(M, H, dtype=torch.float32, device=dev) for _ in range(k - 1)]
+    kinds = ["attn_qkv", "attn_core", "attn_out"] + (["shard_reduce"] if k > 1 and not fused else [])
+    nlaunch = {"attn_qkv": len(batches), "attn_core": len(batches), "attn_out": len(batches), "shard_reduce": 1}
+    nshards = {"attn_qkv": G, "attn_core": G, "attn_out": G, "shard_reduce": k}
+
+    def launch(kind):
+        for i0, n in batches:
+            if kind == "attn_qkv":
+                tpm.tp_attn_qkv_shards(X, Wqkv[i0:i0 + n], bqkv[i0:i0 + n], QKV[:n])
+            elif kind == "attn_core":
+                tpm.tp_attn_core_shards(QKV[:n], A[:n], w.B, w.S, hk, d, causal=True)
+            elif kind == "attn_out":
+                if fused:
+                    tpm.tp_mlp_row_partial_shards(A[:n], Wo[i0:i0 + n], [Z], sum_shards=True, accumulate=i0 > 0)
+                else:
+                    tpm.tp_mlp_row_partial_shards(A[:n], Wo[i0:i0 + n], parts[i0:i0 + n])
+        if kind == "shard_reduce":
+            tpm.tp_shard_reduce(parts, Z=Z)
+
+    kern = time_kinds(kinds, launch, nlaunch, nshards, args.kernel_steps or args.steps, args.warmup, w, elt)
+    roof = roofline(kern, w, args.variant, "bf16", kind="attn_core")
+    return {"metric": "TP-shard attention block forward TFLOP/s (causal; 3 projections + attention)",
+            "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+            "pct_of_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2), "heads": nh, "head_dim": d,
+            "roofline": roof,
             "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],
                              "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()}}
 

@@ -101,6 +101,7 @@ extern "C" {
 #define TP_FUSED_ACCUM 1u /* tp_mlp_shard_forward / _backward: fold the shard sum into the GEMMs */
 #define TP_GRAD_ACCUMULATE 2u /* weight-gradient entry points: add into dW, db, dV */
 #define TP_SUM_SHARDS 4u      /* row / input-gradient batches: one output, the shard-order sum */
+#define TP_CAUSAL 8u          /* attention: each query attends to keys at or before it only */
 
 /*
  * Column-parallel linear + bias + GeLU of one shard (ColumnParallelLinear
@@ -261,6 +262,49 @@ int tp_swiglu_shard_forward(const void* X, const void* const* Wg, const void* co
                             const void* const* V, int k, int64_t M, int64_t H, int64_t Fk, int dtype,
                             void* workspace, size_t workspace_bytes, float* Z, unsigned flags,
                             void* stream);
+
+/*
+ * Tensor-parallel attention block (multi-head attention split by heads: each
+ * of the k shards owns n_heads / k whole heads, its Q/K/V projection is
+ * column-parallel, its heads' attention needs no communication, and the
+ * output projection is row-parallel and summed: "AI大模型分布式训练：张量并行与流水线
+ * 并行深度实践" §2.3; "千亿参数模型如何拆分到多张GPU上训练" 注意力层的切分;
+ * "大模型分布式并行策略详解：TP、DP、PP、CP、EP核心原理与实战" §4.2).  With
+ * d = H / n_heads (64 or 128), hk = n_heads / k and Hk = hk d, for rows
+ * m = b S + t of X [B S, H]:
+ *
+ *   QKV_i = X Wqkv_i + bqkv_i                [M, 3 Hk]: q | k | v of shard i
+ *   per head h of the shard, within each sequence:
+ *     o_t = sum_j softmax_j(q_t . k_j / sqrt(d)) v_j   (j <= t with TP_CAUSAL)
+ *   A_i = the heads' outputs side by side    [M, Hk]
+ *   Z_i = A_i Wo_i,  Z = Z_0 + ... + Z_{k-1}  (Wo_i [Hk, H], rows block i of Wo)
+ *
+ * Wqkv_i [H, 3 Hk] holds the columns of shard i's heads of the full Wq, Wk and
+ * Wv side by side ([Wq_i | Wk_i | Wv_i], the layout of one
+ * ColumnParallelLinear(H, 3H) shard whose output is chunked into q, k, v);
+ * bqkv_i [3 Hk] likewise (NULL: no bias).  TP_BF16 only for the attention
+ * (TP_ERR_DTYPE otherwise): the projection accumulates in float32 and is
+ * rounded to bf16, the scores, softmax and weighted sum are float32 (the
+ * probabilities rounded to bf16 for the products with V), A_i is rounded to
+ * bf16, Z is float32.
+ *
+ * tp_attn_qkv_shards: the projection for n shards (any dtype; 3 Hk <= 2^22).
+ * tp_attn_core_shards: each shard's attention, QKV[i] [B S, 3 heads d] ->
+ * A[i] [B S, heads d], flags = TP_CAUSAL or 0.  tp_attn_shard_forward: the
+ * block, workspace of tp_attn_workspace_bytes(...) bytes, flags
+ * TP_FUSED_ACCUM (the output projections sum the shards inside the GEMM, as
+ * for the MLP) and TP_CAUSAL.  M == 0 is a no-op; S * 6 Hk < 2^31.
+ */
+int tp_attn_qkv_shards(const void* X, const void* const* Wqkv, const void* const* bqkv, void* const* QKV,
+                       int n, int64_t M, int64_t H, int64_t Hk, int dtype, void* stream);
+int tp_attn_core_shards(const void* const* QKV, void* const* A, int n, int64_t B, int64_t S, int heads,
+                        int head_dim, int dtype, unsigned flags, void* stream);
+size_t tp_attn_workspace_bytes(int k, int64_t B, int64_t S, int64_t H, int n_heads, int dtype,
+                               unsigned flags);
+int tp_attn_shard_forward(const void* X, const void* const* Wqkv, const void* const* bqkv,
+                          const void* const* Wo, int k, int64_t B, int64_t S, int64_t H, int n_heads,
+                          int dtype, void* workspace, size_t workspace_bytes, float* Z, unsigned flags,
+                          void* stream);
 
 /*
  * Training-mode column step: tp_mlp_col_gelu that also keeps the derivative

@@ -31,6 +31,12 @@ SwiGLU block (Y_i = SiLU(X Wg_i) * (X Wu_i), no biases):
     Y_i                          tp_swiglu_col (tp_swiglu_col_shards)
     the whole block, k shards    tp_swiglu_shard_forward
 
+Tensor-parallel attention (heads split over the shards):
+
+    QKV_i = X Wqkv_i + bqkv_i          tp_attn_qkv_shards
+    A_i = softmax(q k^T / sqrt d) v    tp_attn_core_shards (causal or not)
+    Z = sum_i A_i Wo_i, k shards       tp_attn_shard_forward
+
 Every per-step call has a *_shards form that runs the step for up to
 TP_MAX_BATCH shards in one launch (what the k-shard calls do inside).
 """
@@ -50,7 +56,8 @@ __all__ = [
     "tp_mlp_grad_weight_workspace_bytes_shards", "tp_mlp_grad_row_weight_shards",
     "tp_mlp_grad_col_weight_shards", "tp_mlp_grad_input_shards",
     "tp_sp_reduce_scatter", "tp_mlp_sp_workspace_bytes", "tp_mlp_shard_forward_sp",
-    "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward",
+    "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward", "TP_CAUSAL",
+    "tp_attn_qkv_shards", "tp_attn_core_shards", "tp_attn_workspace_bytes", "tp_attn_shard_forward",
 ]
 
 TP_F32 = 0
@@ -59,6 +66,7 @@ TP_ACCUMULATE = 1
 TP_FUSED_ACCUM = 1
 TP_GRAD_ACCUMULATE = 2
 TP_SUM_SHARDS = 4
+TP_CAUSAL = 8
 TP_MAX_SHARDS = 64
 TP_MAX_BATCH = 16
 
@@ -133,6 +141,14 @@ def lib() -> ctypes.CDLL:
         L.tp_swiglu_col_shards.restype = ci
         L.tp_swiglu_shard_forward.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, vp, cu, vp]
         L.tp_swiglu_shard_forward.restype = ci
+        L.tp_attn_qkv_shards.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp]
+        L.tp_attn_qkv_shards.restype = ci
+        L.tp_attn_core_shards.argtypes = [vp, vp, ci, i64, i64, ci, ci, ci, cu, vp]
+        L.tp_attn_core_shards.restype = ci
+        L.tp_attn_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ci, cu]
+        L.tp_attn_workspace_bytes.restype = sz
+        L.tp_attn_shard_forward.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, ci, vp, sz, vp, cu, vp]
+        L.tp_attn_shard_forward.restype = ci
         for f in (L.tp_mlp_col_gelu_shards, L.tp_mlp_row_partial_shards, L.tp_mlp_grad_act_shards,
                   L.tp_mlp_grad_row_weight_shards, L.tp_mlp_grad_col_weight_shards, L.tp_mlp_grad_input_shards):
             f.restype = ci
@@ -725,4 +741,72 @@ def tp_swiglu_shard_forward(X, Wg, Wu, V, Z=None, workspace=None, fused: bool = 
     _check(lib().tp_swiglu_shard_forward(_dev(X, "X"), arr(Wg, "Wg"), arr(Wu, "Wu"), arr(V, "V"), k, M, H, Fk, dt,
                                          _dev(workspace, "workspace"), workspace.numel(), _dev(Z, "Z"), flags,
                                          _stream(stream)), "tp_swiglu_shard_forward")
+    return Z
+
+
+# ---------------------------------------------------------------------------
+# Tensor-parallel attention.
+
+def tp_attn_qkv_shards(X, Wqkv, bqkv, QKV, stream=None):
+    """QKV[i] = X Wqkv[i] + bqkv[i] for the n shards (bqkv may be None)."""
+    n = len(Wqkv)
+    if n < 1 or len(QKV) != n or (bqkv is not None and len(bqkv) != n):
+        raise ValueError("Wqkv, QKV (and bqkv) must hold the same number n >= 1 of shards")
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    N3 = Wqkv[0].shape[-1]
+    if N3 % 3:
+        raise ValueError("Wqkv must have 3 Hk columns")
+    _same_dtype("tp_attn_qkv_shards", X, *Wqkv, *QKV, *(bqkv or []))
+    for i in range(n):
+        if tuple(Wqkv[i].shape) != (H, N3) or QKV[i].numel() != M * N3 or \
+                (bqkv is not None and tuple(bqkv[i].shape) != (N3,)):
+            raise ValueError("shard %d has the wrong shape" % i)
+    _check(lib().tp_attn_qkv_shards(_dev(X, "X"), _ptrs(Wqkv, "Wqkv"), None if bqkv is None else _ptrs(bqkv, "bqkv"),
+                                    _ptrs(QKV, "QKV"), n, M, H, N3 // 3, _dtype_code(X), _stream(stream)),
+           "tp_attn_qkv_shards")
+    return QKV
+
+
+def tp_attn_core_shards(QKV, A, B: int, S: int, heads: int, head_dim: int, causal: bool = True, stream=None):
+    """A[i] = the attention of shard i's heads from its projection QKV[i]."""
+    n = len(QKV)
+    if n < 1 or len(A) != n:
+        raise ValueError("QKV and A must hold the same number n >= 1 of shards")
+    Hk = heads * head_dim
+    for i in range(n):
+        if QKV[i].numel() != B * S * 3 * Hk or A[i].numel() != B * S * Hk:
+            raise ValueError("shard %d has the wrong size" % i)
+    _same_dtype("tp_attn_core_shards", QKV[0], *QKV, *A)
+    _check(lib().tp_attn_core_shards(_ptrs(QKV, "QKV"), _ptrs(A, "A"), n, B, S, heads, head_dim,
+                                     _dtype_code(QKV[0]), TP_CAUSAL if causal else 0, _stream(stream)),
+           "tp_attn_core_shards")
+    return A
+
+
+def tp_attn_workspace_bytes(k: int, B: int, S: int, H: int, n_heads: int, dtype: int, flags: int = 0) -> int:
+    return int(lib().tp_attn_workspace_bytes(k, B, S, H, n_heads, dtype, flags))
+
+
+def tp_attn_shard_forward(X, Wqkv, bqkv, Wo, B: int, S: int, n_heads: int, Z=None, workspace=None,
+                          fused: bool = False, causal: bool = True, stream=None):
+    """Z = sum_i A_i Wo[i] over the k shards of the attention block; X [B S, H]."""
+    torch = _torch()
+    k = len(Wqkv)
+    if k < 1 or len(Wo) != k or (bqkv is not None and len(bqkv) != k):
+        raise ValueError("Wqkv, Wo (and bqkv) must hold the same number k >= 1 of shards")
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    if M != B * S:
+        raise ValueError("X must hold B S rows")
+    dt = _dtype_code(X)
+    _same_dtype("tp_attn_shard_forward", X, *Wqkv, *Wo, *(bqkv or []))
+    flags = (TP_FUSED_ACCUM if fused else 0) | (TP_CAUSAL if causal else 0)
+    need = tp_attn_workspace_bytes(k, B, S, H, n_heads, dt, flags)
+    workspace = _workspace(workspace, need, X.device)
+    Z = _out(Z, (M, H), torch.float32, X.device, "Z")
+    _check(lib().tp_attn_shard_forward(_dev(X, "X"), _ptrs(Wqkv, "Wqkv"), None if bqkv is None else _ptrs(bqkv, "bqkv"),
+                                       _ptrs(Wo, "Wo"), k, B, S, H, n_heads, dt, _dev(workspace, "workspace"),
+                                       workspace.numel(), _dev(Z, "Z"), flags, _stream(stream)),
+           "tp_attn_shard_forward")
     return Z

@@ -1,0 +1,281 @@
+// Scaled dot-product attention of one tensor-parallel shard's heads for
+// gfx950 (bf16 in, fp32 softmax and accumulation, bf16 out), the per-shard
+// step of the tensor-parallel attention block: each shard owns whole heads,
+// so its attention needs no communication.
+//
+// Input: the shard's projection QKV [B S, 3 Hk] (Hk = heads * D): the query of
+// head h at columns h D .. h D + D - 1, its key at Hk + h D, its value at
+// 2 Hk + h D.  Output: A [B S, Hk], head h at columns h D.
+//
+// One workgroup = 4 waves = 128 queries of one (sequence, head); each wave
+// owns 32 queries and walks the keys in blocks of 64 (causal: up to its
+// diagonal), with the online softmax (running maximum m and sum l per query):
+//   S^T = K Q^T    (keys x queries) on v_mfma_f32_32x32x16_bf16, K as the
+//                  instruction's row operand, so every lane holds one query's
+//                  scores and the softmax is lane-local (the two half-waves
+//                  hold the two halves of the keys and exchange one maximum
+//                  per block);
+//   O^T += V^T P^T (D x queries), with P^T taken straight from the score
+//                  registers (rounded to bf16) and V^T read by transpose
+//                  reads, whose key order is chosen to match P's.
+// K and V blocks go global -> LDS by direct-to-LDS loads into two stage
+// buffers ([64 keys][D], 16-byte chunks XOR-swizzled by key), so loading block
+// j + 1 overlaps the MFMAs of block j; the query fragments stay in registers.
+// Keys past the sequence end read as zeros and are masked, as are keys after
+// the query when causal; queries past the end are computed but not stored.
+#include <type_traits>
+#include <utility>
+
+#include "device_common.h"
+#include "tp_mlp_kernels.h"
+
+namespace tpmlp {
+
+namespace {
+
+struct AttnPtrs {
+  const uint16_t* qkv[kMaxGroups];
+  uint16_t* out[kMaxGroups];
+};
+
+struct AttnParams {
+  AttnPtrs t;
+  int groups;
+  int B, S, heads;  // heads of one shard
+  int nqb;          // query blocks of 128 per sequence
+};
+
+constexpr int kBQ = 128, kBK = 64;
+
+// Chunk swizzle of a [keys][D] tile: D = 128 rows are one 256-byte bank row,
+// so the 16 chunks of consecutive keys are rotated by key & 15; D = 64 rows
+// pair up in a bank row, rotated by (key >> 1) & 7.
+template <int D>
+__device__ __forceinline__ int swz(int key) {
+  if constexpr (D == 128) return key & 15;
+  else return (key >> 1) & 7;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
+  constexpr int ROW = 2 * D;                 // bytes per key row in LDS
+  constexpr int TILE = kBK * ROW;            // one K or V block
+  constexpr int STAGE = 2 * TILE;
+  constexpr int CH = D / 8;                  // 16-byte chunks per row
+  constexpr int ROWS_PER_DMA = 1024 / ROW;   // rows per 1 KB direct-to-LDS load
+  constexpr int DMA_PER_WAVE = TILE / 1024 / 4;
+  constexpr int KS = D / 16;                 // MFMA k-steps over D (scores)
+  constexpr int DT = D / 32;                 // output tiles of 32 along D
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+
+  // Heaviest query blocks (the last ones, under the causal mask) first.
+  const int per_qb = p.groups * p.B * p.heads;
+  const int id = blockIdx.x;
+  const int qb = p.nqb - 1 - id / per_qb;
+  int rest = id % per_qb;
+  const int g = rest / (p.B * p.heads);
+  rest -= g * p.B * p.heads;
+  const int b = rest / p.heads;
+  const int head = rest - b * p.heads;
+
+  const int S = p.S;
+  const int Hk = p.heads * D;
+  const int64_t ld = 3 * (int64_t)Hk;
+  const uint16_t* qkv = p.t.qkv[g];
+  const uint16_t* seq = qkv + (int64_t)b * S * ld;  // row 0 of this sequence
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int q0 = qb * kBQ;
+  const int qq = q0 + 32 * wave + l32;  // this lane's query
+
+  // Query fragments (B operand of S^T = K Q^T): dims 16 j + 8 h2 .. + 7.
+  bf16x8_t qf[KS];
+  {
+    const bool ok = qq < S;
+    const uint16_t* qrow = seq + (int64_t)(ok ? qq : 0) * ld + head * D + 8 * h2;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4_t*>(qrow + 16 * j);
+      qf[j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // Direct-to-LDS loads of one K and one V block: this wave's rows of the
+  // 64-row tiles.  Lane offsets from the block's first key row.
+  uint32_t loff[DMA_PER_WAVE];
+  int lrow[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int row = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA + lane / CH;
+    const int c = (lane % CH) ^ swz<D>(row);
+    lrow[i] = row;
+    loff[i] = (uint32_t)row * (uint32_t)(ld * 2) + (uint32_t)c * 16u;
+  }
+  auto issue = [&](uint32_t lds, int k0) {
+    // The descriptors start at the block's first key row (64-bit address
+    // arithmetic here, 32-bit offsets inside the block).
+    const i32x4_t kd = buffer_desc(seq + (int64_t)k0 * ld + Hk + head * D, 0x7FFFFFF0u);
+    const i32x4_t vd = buffer_desc(seq + (int64_t)k0 * ld + 2 * Hk + head * D, 0x7FFFFFF0u);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const uint32_t off = k0 + lrow[i] < S ? loff[i] : kOob;
+      lds_dma16(kd, lds + (uint32_t)((wave * DMA_PER_WAVE + i) * 1024), off);
+      lds_dma16(vd, lds + TILE + (uint32_t)((wave * DMA_PER_WAVE + i) * 1024), off);
+    }
+  };
+
+  // LDS read offsets.  K fragment (A operand of S^T) of 32-key tile u and
+  // k-step j: key 32 u + l32, chunk 2 j + h2 (swz(key) does not depend on u).
+  int koff[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) koff[j] = l32 * ROW + (((2 * j + h2) ^ swz<D>(l32)) << 4);
+  // V^T fragment (A operand of O^T += V^T P^T) of output tile t, k-step jj
+  // (keys 16 jj ..): two transpose reads at keys 16 jj + 4 h2 + 8 r + (q / 4),
+  // columns 32 t + 16 ((lane >> 4) & 1) + 4 (q % 4), q = lane % 16; the
+  // swizzle does not depend on jj.
+  int voff[DT][2];
+  {
+    const int q = lane & 15;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int key = 4 * h2 + 8 * r + (q >> 2);
+        const int col = 32 * t + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+        voff[t][r] = TILE + key * ROW + (((col >> 3) ^ swz<D>(key)) << 4) + ((col >> 2) & 1) * 8;
+      }
+  }
+
+  f32x16_t acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+  float m_run = -1e30f, l_run = 0.f;
+  const float c2 = 1.4426950408889634f / __builtin_sqrtf((float)D);  // log2(e) / sqrt(D)
+
+  const int kend = CAUSAL ? min(q0 + kBQ, S) : S;
+  const int nb = (kend + kBK - 1) / kBK;
+
+  auto block = [&](const char* Sb, int k0) {
+    // S^T for the 64 keys: two 32-key tiles.
+    f32x16_t s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[u][e] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Sb + u * 32 * ROW + koff[j]);
+        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j], s[u], 0, 0, 0);
+      }
+    }
+    // Mask, scale to base 2, block maximum (lane pair l, l ^ 32 hold one query).
+    const bool edge = k0 + kBK > S || (CAUSAL && k0 + kBK - 1 > q0 + 32 * wave);
+    float mx = -1e30f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = s[u][e] * c2;
+        if (edge) {
+          const int kk = k0 + 32 * u + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          if (kk >= S || (CAUSAL && kk > qq)) x = -__builtin_inff();
+        }
+        s[u][e] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x8_t pf[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x4_t pk;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int e = 8 * (jj & 1) + 2 * e2;
+        const float a0 = __builtin_amdgcn_exp2f(s[jj >> 1][e] - m_new);
+        const float a1 = __builtin_amdgcn_exp2f(s[jj >> 1][e + 1] - m_new);
+        psum += a0 + a1;
+        pk[e2] = f32_to_bf16_bits(a0) | (f32_to_bf16_bits(a1) << 16);
+      }
+      pf[jj] = __builtin_bit_cast(bf16x8_t, pk);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] = acc[t] * alpha;
+    // O^T += V^T P^T over the 64 keys (4 k-steps of 16).
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const char* v0 = Sb + voff[t][0] + jj * 16 * ROW;
+        const bf16x8_t vf = ds_read_tr_pair(v0, v0 + (voff[t][1] - voff[t][0]));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[jj], acc[t], 0, 0, 0);
+      }
+  };
+
+  // Two stage buffers: block j + 1 loads while block j is computed.  At the
+  // top of iteration j the only loads in flight are block j's.
+  issue(lds_offset(st0), 0);
+  for (int j = 0; j < nb; ++j) {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): block j has landed
+    asm volatile("s_barrier" ::: "memory");             // visible to all; block j - 1 done
+    const bool odd = j & 1;
+    if (j + 1 < nb) issue(odd ? lds_offset(st0) : lds_offset(st1), (j + 1) * kBK);
+    block(odd ? st1 : st0, j * kBK);
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+
+  // O = O^T / l: lane holds query qq, columns 32 t + 8 (e / 4) + 4 h2 + e % 4.
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qq < S) {
+    const float inv = __builtin_amdgcn_rcpf(l_tot);
+    uint16_t* orow = p.t.out[g] + ((int64_t)b * S + qq) * Hk + head * D + 4 * h2;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        u32x2_t o;
+        o[0] = f32_to_bf16_bits(acc[t][4 * e4] * inv) | (f32_to_bf16_bits(acc[t][4 * e4 + 1] * inv) << 16);
+        o[1] = f32_to_bf16_bits(acc[t][4 * e4 + 2] * inv) | (f32_to_bf16_bits(acc[t][4 * e4 + 3] * inv) << 16);
+        *reinterpret_cast<u32x2_t*>(orow + 32 * t + 8 * e4) = o;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention_bf16(const void* const* qkv, void* const* out, int groups, int64_t B,
+                                 int64_t S, int heads, int d, bool causal, hipStream_t s) {
+  if (groups < 1 || groups > kMaxGroups || (d != 64 && d != 128)) return hipErrorInvalidValue;
+  if (B <= 0 || S <= 0) return hipSuccess;
+  AttnParams p{};
+  for (int gi = 0; gi < groups; ++gi) {
+    p.t.qkv[gi] = static_cast<const uint16_t*>(qkv[gi]);
+    p.t.out[gi] = static_cast<uint16_t*>(out[gi]);
+  }
+  p.groups = groups;
+  p.B = (int)B;
+  p.S = (int)S;
+  p.heads = heads;
+  p.nqb = (int)((S + kBQ - 1) / kBQ);
+  const int64_t blocks = (int64_t)p.nqb * groups * B * heads;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (d == 128) {
+    if (causal) hipLaunchKernelGGL((attention_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<128, false>), grid, block, 0, s, p);
+  } else {
+    if (causal) hipLaunchKernelGGL((attention_kernel<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<64, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tpmlp

@@ -11,7 +11,7 @@ namespace {
 constexpr int64_t kMaxTilesPerLaunch = int64_t(1) << 22;
 
 bool c_is_bf16(Epilogue e) {
-  return e == kEpiBiasGelu || e == kEpiBiasGeluSave || e == kEpiMulAux || e == kEpiSwiGLU;
+  return e == kEpiBiasGelu || e == kEpiBiasGeluSave || e == kEpiMulAux || e == kEpiSwiGLU || e == kEpiBias;
 }
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }

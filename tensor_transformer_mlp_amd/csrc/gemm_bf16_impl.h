@@ -93,7 +93,7 @@ constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // Epilogues each layout is instantiated with.
 constexpr bool layout_has_epi(int layout, int epi) {
   return layout == kNN ? (epi == kEpiBiasGelu || epi == kEpiBiasGeluSave || epi == kEpiStoreF32 ||
-                          epi == kEpiAccumF32 || epi == kEpiSwiGLU)
+                          epi == kEpiAccumF32 || epi == kEpiSwiGLU || epi == kEpiBias)
        : layout == kNT ? (epi == kEpiMulAux || epi == kEpiStoreF32 || epi == kEpiAccumF32)
                        : (epi == kEpiStoreF32 || epi == kEpiAccumF32);
 }
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
     ldc = N;
     accumulate = false;
   }
-  constexpr bool kBias = EPI == kEpiBiasGelu || EPI == kEpiBiasGeluSave;
+  constexpr bool kBias = EPI == kEpiBiasGelu || EPI == kEpiBiasGeluSave || EPI == kEpiBias;
   f32x4_t bias4[FN][4];
   if constexpr (kBias) {
 #pragma unroll
@@ -575,7 +575,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
                         acc[i][j][4 * gq + 3]};
           if constexpr (kBias) {
             v += bias4[j][gq];
-            if constexpr (EPI == kEpiBiasGelu) {
+            if constexpr (EPI == kEpiBias) {
+              u32x2_t o;
+              o[0] = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+              o[1] = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = o;
+            } else if constexpr (EPI == kEpiBiasGelu) {
               u32x2_t o;
               o[0] = f32_to_bf16_bits(gelu_f32(v[0])) | (f32_to_bf16_bits(gelu_f32(v[1])) << 16);
               o[1] = f32_to_bf16_bits(gelu_f32(v[2])) | (f32_to_bf16_bits(gelu_f32(v[3])) << 16);
@@ -664,7 +669,7 @@ hipError_t launch_bf16_tile(const GemmParams& p, Epilogue epi, hipStream_t s) {
        }
      }()),
      ...);
-  }(std::make_integer_sequence<int, 6>{});
+  }(std::make_integer_sequence<int, 7>{});
   return done ? hipGetLastError() : hipErrorInvalidValue;
 }
 

@@ -136,7 +136,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
       if (n >= N) continue;
       const int64_t idx = m * p.ldc + n;
       f32x4_t v = acc[i][j];
-      if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBiasGeluSave) {
+      if constexpr (EPI == kEpiBias) {
+        if (p.bias) v += *reinterpret_cast<const f32x4_t*>(p.bias + n);
+        *reinterpret_cast<f32x4_t*>(p.C + idx) = v;
+      } else if constexpr (EPI == kEpiBiasGelu || EPI == kEpiBiasGeluSave) {
         if (p.bias) v += *reinterpret_cast<const f32x4_t*>(p.bias + n);
         f32x4_t y, g;
 #pragma unroll
@@ -191,6 +194,12 @@ hipError_t launch_f32_layout(const F32Params& p, Epilogue epi, dim3 grid, hipStr
     case kEpiMulAux:
       hipLaunchKernelGGL((gemm_f32_kernel<kEpiMulAux, LAYOUT>), grid, block, 0, s, p);
       break;
+    case kEpiBias:
+      if constexpr (LAYOUT == kNN) {
+        hipLaunchKernelGGL((gemm_f32_kernel<kEpiBias, kNN>), grid, block, 0, s, p);
+        break;
+      }
+      return hipErrorInvalidValue;
     case kEpiSwiGLU:
       if constexpr (LAYOUT == kNN) {
         hipLaunchKernelGGL((gemm_f32_kernel<kEpiSwiGLU, kNN>), grid, block, 0, s, p);

@@ -122,6 +122,33 @@ int swiglu_col_steps(const void* X, const void* const* Wg, const void* const* Wu
   return run(g, dtype, s);
 }
 
+// Attention projection: QKV_i = X Wqkv_i + bqkv_i, [M, H] x [H, 3 Hk].
+int qkv_steps(const void* X, const void* const* W, const void* const* b, void* const* QKV, int n, int64_t M,
+              int64_t H, int64_t Hk, int dtype, hipStream_t s) {
+  GemmBatch g = batch(n, tpmlp::kNN, tpmlp::kEpiBias, M, 3 * Hk, H, H, 3 * Hk);
+  for (int i = 0; i < n; ++i) {
+    g.A[i] = X;
+    g.B[i] = W[i];
+    g.bias[i] = b ? b[i] : nullptr;
+    g.C[i] = QKV[i];
+  }
+  return run(g, dtype, s);
+}
+
+// Shape rules of the attention block: d = H / n_heads in {64, 128}, k | n_heads,
+// and one sequence's projection rows addressable with 32-bit offsets.
+int check_attn(int64_t B, int64_t S, int64_t H, int n_heads, int k) {
+  if (B < 0 || S < 0 || B > kMaxDim || S > kMaxDim) return TP_ERR_SHAPE;
+  if (n_heads < 1 || k < 1 || k > TP_MAX_SHARDS || H % 8 || H < 8 || H > kMaxLd) return TP_ERR_SHAPE;
+  if (H % n_heads || n_heads % k) return TP_ERR_SHAPE;
+  const int64_t d = H / n_heads;
+  if (d != 64 && d != 128) return TP_ERR_SHAPE;
+  const int64_t Hk = d * (n_heads / k);
+  if (S > 0 && S > ((int64_t(1) << 31) - 1) / (6 * Hk)) return TP_ERR_SHAPE;
+  if (B > 0 && S > 0 && B > kMaxDim / S) return TP_ERR_SHAPE;
+  return check_dims(B * S, H, Hk);
+}
+
 // Z_i (+)= Y_i V_i: [M, Fk] x [Fk, H], one output per shard (sum == false),
 // or Z (+)= sum_i Y_i V_i in shard order into Z[0] (sum == true).
 int row_steps(const void* const* Y, const void* const* V, float* const* Z, int n, bool sum,
@@ -589,6 +616,130 @@ int tp_swiglu_shard_forward(const void* X, const void* const* Wg, const void* co
   };
   auto col = [&](int i0, int n) { return swiglu_col_steps(X, Wg + i0, Wu + i0, Y, n, M, H, Fk, dtype, s); };
   if ((st = shard_steps(col, V, k, M, H, Fk, dtype, Y, fused, part, parts, s))) return st;
+  if (!fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
+  return TP_OK;
+}
+
+int tp_attn_qkv_shards(const void* X, const void* const* Wqkv, const void* const* bqkv, void* const* QKV,
+                       int n, int64_t M, int64_t H, int64_t Hk, int dtype, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_dims(M, H, Hk))) return st;
+  if (3 * Hk > kMaxLd) return TP_ERR_SHAPE;
+  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
+  if (M == 0) return TP_OK;
+  if (!X || !Wqkv || !QKV) return TP_ERR_NULL;
+  if (!aligned16(X)) return TP_ERR_ALIGN;
+  const size_t e = elt_size(dtype);
+  Regions in, out;
+  in.add(X, size_t(M) * size_t(H) * e);
+  for (int i = 0; i < n; ++i) {
+    if (!Wqkv[i] || !QKV[i] || (bqkv && !bqkv[i])) return TP_ERR_NULL;
+    if (!aligned16(Wqkv[i]) || !aligned16(QKV[i]) || (bqkv && !aligned16(bqkv[i]))) return TP_ERR_ALIGN;
+    in.add(Wqkv[i], size_t(H) * size_t(3 * Hk) * e);
+    if (bqkv) in.add(bqkv[i], size_t(3 * Hk) * e);
+    out.add(QKV[i], size_t(M) * size_t(3 * Hk) * e);
+  }
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return qkv_steps(X, Wqkv, bqkv, QKV, n, M, H, Hk, dtype, static_cast<hipStream_t>(stream));
+}
+
+int tp_attn_core_shards(const void* const* QKV, void* const* A, int n, int64_t B, int64_t S, int heads,
+                        int head_dim, int dtype, unsigned flags, void* stream) {
+  if (check_dtype(dtype)) return TP_ERR_DTYPE;
+  if (dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (flags & ~TP_CAUSAL) return TP_ERR_FLAGS;
+  if (n < 1 || n > TP_MAX_BATCH || heads < 1) return TP_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return TP_ERR_SHAPE;
+  int st = check_attn(B, S, int64_t(heads) * head_dim, heads, 1);
+  if (st) return st;
+  if (B == 0 || S == 0) return TP_OK;
+  if (!QKV || !A) return TP_ERR_NULL;
+  const size_t M = size_t(B) * size_t(S), Hk = size_t(heads) * size_t(head_dim);
+  Regions in, out;
+  for (int i = 0; i < n; ++i) {
+    if (!QKV[i] || !A[i]) return TP_ERR_NULL;
+    if (!aligned16(QKV[i]) || !aligned16(A[i])) return TP_ERR_ALIGN;
+    in.add(QKV[i], M * 3 * Hk * 2);
+    out.add(A[i], M * Hk * 2);
+  }
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return hip_status(tpmlp::launch_attention_bf16(QKV, A, n, B, S, heads, head_dim, (flags & TP_CAUSAL) != 0,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+size_t tp_attn_workspace_bytes(int k, int64_t B, int64_t S, int64_t H, int n_heads, int dtype, unsigned flags) {
+  if (check_dtype(dtype) || dtype != TP_BF16 || check_attn(B, S, H, n_heads, k)) return 0;
+  if (flags & ~(TP_FUSED_ACCUM | TP_CAUSAL)) return 0;
+  const int64_t M = B * S;
+  if (M == 0) return 0;
+  const int64_t Hk = H / n_heads * (n_heads / k);
+  const size_t qkv = round_up(size_t(M) * size_t(3 * Hk) * 2, kWsAlign);
+  const size_t a = round_up(size_t(M) * size_t(Hk) * 2, kWsAlign);
+  size_t bytes = size_t(batch_size(k)) * (qkv + a);
+  if (!(flags & TP_FUSED_ACCUM)) bytes += size_t(k - 1) * round_up(size_t(M) * size_t(H) * 4, kWsAlign);
+  return bytes;
+}
+
+int tp_attn_shard_forward(const void* X, const void* const* Wqkv, const void* const* bqkv,
+                          const void* const* Wo, int k, int64_t B, int64_t S, int64_t H, int n_heads,
+                          int dtype, void* workspace, size_t workspace_bytes, float* Z, unsigned flags,
+                          void* stream) {
+  if (check_dtype(dtype) || dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (flags & ~(TP_FUSED_ACCUM | TP_CAUSAL)) return TP_ERR_FLAGS;
+  int st = check_attn(B, S, H, n_heads, k);
+  if (st) return st;
+  const int64_t M = B * S;
+  if (M == 0) return TP_OK;
+  const int64_t d = H / n_heads, hk = n_heads / k, Hk = d * hk;
+  if (!X || !Wqkv || !Wo || !Z) return TP_ERR_NULL;
+  for (int i = 0; i < k; ++i) {
+    if (!Wqkv[i] || !Wo[i] || (bqkv && !bqkv[i])) return TP_ERR_NULL;
+    if (!aligned16(Wqkv[i]) || !aligned16(Wo[i]) || (bqkv && !aligned16(bqkv[i]))) return TP_ERR_ALIGN;
+  }
+  if (!aligned16(X) || !aligned16(Z)) return TP_ERR_ALIGN;
+  const size_t need = tp_attn_workspace_bytes(k, B, S, H, n_heads, dtype, flags);
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TP_ERR_ALIGN;
+  const size_t nz = size_t(M) * size_t(H) * 4;
+  Regions in, out;
+  in.add(X, size_t(M) * size_t(H) * 2);
+  for (int i = 0; i < k; ++i) {
+    in.add(Wqkv[i], size_t(H) * size_t(3 * Hk) * 2);
+    in.add(Wo[i], size_t(Hk) * size_t(H) * 2);
+    if (bqkv) in.add(bqkv[i], size_t(3 * Hk) * 2);
+  }
+  out.add(Z, nz);
+  out.add(workspace, need);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fused = (flags & TP_FUSED_ACCUM) != 0;
+  const bool causal = (flags & TP_CAUSAL) != 0;
+  char* ws = static_cast<char*>(workspace);
+  const int G = batch_size(k);
+  const size_t qkv_bytes = round_up(size_t(M) * size_t(3 * Hk) * 2, kWsAlign);
+  const size_t a_bytes = round_up(size_t(M) * size_t(Hk) * 2, kWsAlign);
+  const size_t part_bytes = round_up(nz, kWsAlign);
+  void* QKV[kMaxGroups];
+  void* A[kMaxGroups];
+  for (int j = 0; j < G; ++j) {
+    QKV[j] = ws + size_t(j) * qkv_bytes;
+    A[j] = ws + size_t(G) * qkv_bytes + size_t(j) * a_bytes;
+  }
+  char* part_base = ws + size_t(G) * (qkv_bytes + a_bytes);
+  const float* parts[TP_MAX_SHARDS];
+  auto part = [&](int i) {
+    return i == 0 ? Z : reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
+  };
+  // The "column step" of a batch: the head-split projection, then each
+  // shard's heads' attention into A (the row step's input).
+  auto col = [&](int i0, int n) {
+    int r = qkv_steps(X, Wqkv + i0, bqkv ? bqkv + i0 : nullptr, QKV, n, M, H, Hk, dtype, s);
+    if (r) return r;
+    return hip_status(tpmlp::launch_attention_bf16(QKV, A, n, B, S, (int)hk, (int)d, causal, s));
+  };
+  if ((st = shard_steps(col, Wo, k, M, H, Hk, dtype, A, fused, part, parts, s))) return st;
   if (!fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
   return TP_OK;
 }

@@ -18,6 +18,7 @@ enum Epilogue : int {
   kEpiBiasGeluSave = 3,  // C = GeLU(acc + bias[n]), aux = GeLU'(acc + bias[n]) (operand dtype)
   kEpiMulAux = 4,        // C = acc * aux[m, n]; C may be aux itself         (operand dtype)
   kEpiSwiGLU = 5,        // C = SiLU(A B) * (A B2), two B operands (kNN)     (operand dtype)
+  kEpiBias = 6,          // C = acc + bias[n]                                (operand dtype)
 };
 
 // Operand layouts.  A is logically [M, K] and B [K, N]:
@@ -109,5 +110,13 @@ hipError_t launch_split_reduce(float* const* C, int groups, const float* part, i
 hipError_t launch_sp_reduce_scatter(const float* const* parts, int nparts, const void* R, bool r_bf16,
                                     void* const* out, bool o_bf16, int k, int64_t block_elems,
                                     hipStream_t s);
+
+// Scaled dot-product attention of `heads` heads of dimension d (64 or 128)
+// for `groups` shards at once: qkv[g] [B S, 3 heads d] bf16 (query, key and
+// value of head h at columns h d, heads d + h d, 2 heads d + h d), out[g]
+// [B S, heads d] bf16; causal masks keys after the query.  S <= 2^31 / (6
+// heads d) keeps a sequence's rows within 32-bit offsets.
+hipError_t launch_attention_bf16(const void* const* qkv, void* const* out, int groups, int64_t B,
+                                 int64_t S, int heads, int d, bool causal, hipStream_t s);
 
 }  // namespace tpmlp

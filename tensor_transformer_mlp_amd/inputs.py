@@ -43,6 +43,8 @@ _SRC = os.path.join(_HERE, "csrc", "synth_inputs.c")
 _LIB_PATH = os.path.join(_HERE, "libtpsynth.so")
 
 STREAM_X, STREAM_W, STREAM_B, STREAM_V, STREAM_DZ, STREAM_WU = 0, 1, 2, 3, 4, 5
+# attention block: Wq, Wk, Wv, Wo, bq, bk, bv
+STREAM_WQ, STREAM_WK, STREAM_WV, STREAM_WO, STREAM_BQ, STREAM_BK, STREAM_BV = 6, 7, 8, 9, 10, 11, 12
 BASE_SEED = 42
 
 
@@ -69,6 +71,13 @@ class Workload:
     def flop(self) -> int:
         """Two GEMMs of 2*M*H*(F/k) per shard, k shards: 4*M*H*F."""
         return 4 * self.M * self.H * self.F
+
+    @property
+    def heads(self) -> int:
+        """Attention heads of the model the shape is taken from: 64-wide heads
+        for the GPT-2-small width, 128-wide above (GPT-2 small: 12 heads; 7B:
+        32; GPT-3 175B: 96; the long-sequence layer: 64)."""
+        return self.H // (64 if self.H <= 1024 else 128)
 
     def describe(self) -> dict:
         return {"workload": self.name, "B": self.B, "S": self.S, "M": self.M, "H": self.H,
@@ -205,6 +214,39 @@ def make_swiglu(w: Workload | None = None, seed: int = BASE_SEED, M: int | None 
         "Wu": draw(STREAM_WU, (H, F), std, dtype, seed),
         "V": draw(STREAM_V, (F, H), std, dtype, seed),
     }
+
+
+def make_attention(w: Workload | None = None, seed: int = BASE_SEED, M: int | None = None,
+                   H: int | None = None, dtype: str | None = None, std: float | None = None) -> dict:
+    """Inputs of the attention block: X[M,H], Wq, Wk, Wv, Wo [H,H] and biases
+    bq, bk, bv [H], each from its own stream."""
+    M = M if M is not None else w.M
+    H = H if H is not None else w.H
+    dtype = dtype if dtype is not None else w.dtype
+    std = std if std is not None else w.std
+    out = {"X": draw(STREAM_X, (M, H), 1.0, dtype, seed)}
+    for name, st in (("Wq", STREAM_WQ), ("Wk", STREAM_WK), ("Wv", STREAM_WV), ("Wo", STREAM_WO)):
+        out[name] = draw(st, (H, H), std, dtype, seed)
+    for name, st in (("bq", STREAM_BQ), ("bk", STREAM_BK), ("bv", STREAM_BV)):
+        out[name] = draw(st, (H,), std, dtype, seed)
+    return out
+
+
+def qkv_shards(Wq, Wk, Wv, bq, bk, bv, n_heads: int, k: int):
+    """Per-shard projection weights [Wq_i | Wk_i | Wv_i] [H, 3 Hk] and biases
+    [bq_i | bk_i | bv_i] (columns of the shard's heads side by side; data
+    placement only).  Biases may be None."""
+    H = Wq.shape[0]
+    if n_heads % k or H % n_heads:
+        raise ValueError("k must divide n_heads, n_heads must divide H")
+    Hk = H // n_heads * (n_heads // k)
+    Ws, bs = [], []
+    for i in range(k):
+        sl = slice(i * Hk, (i + 1) * Hk)
+        Ws.append(np.ascontiguousarray(np.concatenate([Wq[:, sl], Wk[:, sl], Wv[:, sl]], axis=1)))
+        if bq is not None:
+            bs.append(np.ascontiguousarray(np.concatenate([bq[sl], bk[sl], bv[sl]])))
+    return Ws, (bs if bq is not None else None)
 
 
 def col_slices(W: np.ndarray, k: int):

@@ -30,12 +30,12 @@ CSRC = os.path.join(HERE, "csrc")
 
 # Kernel kinds by (epilogue, operand layout, group sum) template arguments of
 # the GEMMs: epilogues 0 bias+GeLU, 1 fp32 store, 2 fp32 accumulate,
-# 3 bias+GeLU+GeLU', 4 multiply by aux, 5 SiLU(gate) * up; layouts 0 NN,
-# 1 NT, 2 TN.
+# 3 bias+GeLU+GeLU', 4 multiply by aux, 5 SiLU(gate) * up, 6 bias only;
+# layouts 0 NN, 1 NT, 2 TN.
 _GEMM_KIND = {("0", "0"): "col_gelu", ("1", "0"): "row_partial", ("2", "0"): "row_partial_accum",
               ("3", "0"): "col_gelu_save", ("4", "1"): "grad_act", ("1", "1"): "grad_input",
               ("2", "1"): "grad_input_accum", ("1", "2"): "grad_weight", ("2", "2"): "grad_weight_accum",
-              ("5", "0"): "swiglu_col"}
+              ("5", "0"): "swiglu_col", ("6", "0"): "attn_qkv"}
 _GSUM_KIND = {"0": "row_sum", "1": "grad_input_sum"}
 
 
@@ -64,6 +64,8 @@ def kernel_kind(name: str):
     """Benchmark kernel kind of a device kernel name, or None."""
     if "shard_reduce_kernel" in name:
         return "shard_reduce"
+    if "attention_kernel" in name:
+        return "attn_core"
     if "sp_reduce_kernel" in name:
         m = re.search(r"sp_reduce_kernel<([^,>]*)", name)
         return "sp_reduce_fused" if m and _targ(m.group(1)) == "1" else "sp_reduce"

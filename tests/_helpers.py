@@ -32,6 +32,15 @@ Backward (dY = dZ V_i^T, dA = dY * G, G = GeLU'(A)):
                                             + (4 + 2 |g|) u32 |Y|)
   with 1.1 >= max |SiLU'| and (4 + 2 |g|) u32 the relative error of the
   float32 SiLU (the exponential's argument rounding grows with |g|).
+* attention of one head from given bf16 q, k, v (exact inputs): with
+  p_tj the exact softmax weights and W_t = sum_j p_tj |v_j|,
+    |A_gpu - A| <= 1.5 u16 W_t + 1.01 u16 |A| + 2^-16 W_t
+  (the probabilities are rounded to bf16 for the products with V while the
+  normaliser sums them unrounded, the output is rounded to bf16, and the
+  float32 scores, exp2 and sums add far less).  From the block's inputs the
+  scores also carry the projection's error: |ds_tj| <= e_s = 2 u16 (|q| . |k|)
+  / sqrt(d) + the GEMMs' accumulation bound, which moves each output by at
+  most 2 max_j e_s W_t; the value's rounding adds u16 W_t.
 * a float32 GEMM over K terms of operands with errors e_a, e_b:
     |C_gpu - C| <= e_a^T |b| + |a|^T e_b + 2 (K + 2) u32 (|a| + e_a)^T (|b| + e_b).
 """
@@ -185,3 +194,46 @@ def swiglu_bound(X64, Wg64, Wu64, G, U, Y, dtype: str):
     aY = np.abs(Y)
     return (u_out * aY + (1 + u_out) * (SILU_LIP * np.abs(U) * eg + np.abs(s) * eu + SILU_LIP * eg * eu
                                         + (4 + 2 * np.abs(G)) * U32 * aY) + 1e-30)
+
+
+def attn_weights(qkv64, B: int, S: int, hk: int, d: int, causal: bool):
+    """float64 softmax weights P [B, hk, S, S] of a shard's heads (for bounds only)."""
+    Hk = hk * d
+    q = qkv64[:, :Hk].reshape(B, S, hk, d).transpose(0, 2, 1, 3)
+    k = qkv64[:, Hk:2 * Hk].reshape(B, S, hk, d).transpose(0, 2, 1, 3)
+    s = q @ k.transpose(0, 1, 3, 2) / np.sqrt(d)
+    if causal:
+        s = np.where(np.tril(np.ones((S, S), dtype=bool)), s, -np.inf)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    return p / p.sum(axis=-1, keepdims=True)
+
+
+def attn_core_bound(qkv64, A, B: int, S: int, hk: int, d: int, causal: bool, e_s=None):
+    """Element-wise bound for the GPU attention A [B S, hk d] from exact q, k, v
+    (see the module docstring); e_s [B, hk, S] adds the score-error term."""
+    Hk = hk * d
+    P = attn_weights(qkv64, B, S, hk, d, causal)
+    v = np.abs(qkv64[:, 2 * Hk:]).reshape(B, S, hk, d).transpose(0, 2, 1, 3)
+    W = (P @ v).transpose(0, 2, 1, 3).reshape(B * S, Hk)          # sum_j p_tj |v_j|
+    bound = 1.5 * U16 * W + 1.01 * U16 * np.abs(A) + 2.0 ** -16 * W
+    if e_s is not None:
+        es = np.repeat(e_s.transpose(0, 2, 1).reshape(B * S, hk), d, axis=1)
+        bound = bound + 2 * es * W + U16 * W
+    return bound + 1e-30
+
+
+def attn_score_err(qkv64, B: int, S: int, hk: int, d: int, H: int, X64=None, Wq=None, Wk=None):
+    """max_j of the score error bound e_s [B, hk, S] for bf16 q and k computed
+    by a float32 GEMM over H terms (|X| |W| the GEMM's absolute terms)."""
+    Hk = hk * d
+    aq = np.abs(qkv64[:, :Hk]).reshape(B, S, hk, d).transpose(0, 2, 1, 3)
+    ak = np.abs(qkv64[:, Hk:2 * Hk]).reshape(B, S, hk, d).transpose(0, 2, 1, 3)
+    e = 2 * U16 * (aq @ ak.transpose(0, 1, 3, 2)) / np.sqrt(d)
+    if X64 is not None:
+        gq = 2 * (H + 2) * U32 * (np.abs(X64) @ np.abs(Wq))
+        gk = 2 * (H + 2) * U32 * (np.abs(X64) @ np.abs(Wk))
+        gq = gq.reshape(B, S, hk, d).transpose(0, 2, 1, 3)
+        gk = gk.reshape(B, S, hk, d).transpose(0, 2, 1, 3)
+        e = e + ((gq @ ak.transpose(0, 1, 3, 2)) + (aq @ gk.transpose(0, 1, 3, 2))) / np.sqrt(d)
+    return e.max(axis=-1)

@@ -47,7 +47,9 @@ def test_exports_every_declared_symbol(L):
                      "tp_mlp_grad_weight_workspace_bytes_shards", "tp_mlp_grad_row_weight_shards",
                      "tp_mlp_grad_col_weight_shards", "tp_mlp_grad_input_shards",
                      "tp_sp_reduce_scatter", "tp_mlp_sp_workspace_bytes", "tp_mlp_shard_forward_sp",
-                     "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward"}
+                     "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward",
+                     "tp_attn_qkv_shards", "tp_attn_core_shards", "tp_attn_workspace_bytes",
+                     "tp_attn_shard_forward"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -56,7 +58,7 @@ def test_python_constants_match_header():
     import tensor_transformer_mlp_amd as tpm
     c = _header_constants()
     for n in ("TP_F32", "TP_BF16", "TP_ACCUMULATE", "TP_FUSED_ACCUM", "TP_GRAD_ACCUMULATE",
-              "TP_SUM_SHARDS", "TP_MAX_SHARDS", "TP_MAX_BATCH"):
+              "TP_SUM_SHARDS", "TP_MAX_SHARDS", "TP_MAX_BATCH", "TP_CAUSAL"):
         assert getattr(tpm, n) == c[n], n
 
 
@@ -534,3 +536,48 @@ def test_swiglu_errors(L):
     assert ff(*a) == c["TP_ERR_ALIAS"]
     a = base(); a[5] = 0
     assert ff(*a) == c["TP_OK"]
+
+
+def test_attention_errors(L):
+    c = _header_constants()
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    core = L.tp_attn_core_shards
+    qkv, A = arr(P, 2 * P), arr(3 * P, 4 * P)
+    # B=1, S=8, 2 heads of 64
+    assert core(qkv, A, 2, 1, 8, 2, 64, 0, 8, None) == c["TP_ERR_DTYPE"]        # fp32 attention
+    assert core(qkv, A, 2, 1, 8, 2, 96, 1, 8, None) == c["TP_ERR_SHAPE"]        # head_dim
+    assert core(qkv, A, 2, 1, 8, 2, 64, 1, 16, None) == c["TP_ERR_FLAGS"]
+    assert core(qkv, A, 0, 1, 8, 2, 64, 1, 8, None) == c["TP_ERR_SHAPE"]
+    assert core(arr(P, None), A, 2, 1, 8, 2, 64, 1, 8, None) == c["TP_ERR_NULL"]
+    assert core(qkv, arr(3 * P, 4 * P + 8), 2, 1, 8, 2, 64, 1, 8, None) == c["TP_ERR_ALIGN"]
+    assert core(qkv, arr(3 * P, P + 64), 2, 1, 8, 2, 64, 1, 8, None) == c["TP_ERR_ALIAS"]   # A over QKV
+    assert core(qkv, A, 2, 1, 0, 2, 64, 1, 8, None) == c["TP_OK"]
+    ws_f = L.tp_attn_workspace_bytes
+    # k = 4, B = 8, S = 1024, H = 768, 12 heads: per batch shard QKV [M, 576] and A [M, 192] bf16,
+    # plus 3 fp32 partials [M, 768]
+    M = 8 * 1024
+    assert ws_f(4, 8, 1024, 768, 12, 1, 8) == 4 * (M * 576 * 2 + M * 192 * 2) + 3 * M * 768 * 4
+    assert ws_f(4, 8, 1024, 768, 12, 1, 9) == 4 * (M * 576 * 2 + M * 192 * 2)
+    assert ws_f(4, 8, 1024, 768, 10, 1, 8) == 0       # 768 / 10 is not a head width
+    assert ws_f(5, 8, 1024, 768, 12, 1, 8) == 0       # 5 does not divide 12
+    assert ws_f(4, 8, 1024, 768, 12, 0, 8) == 0       # fp32
+    f = L.tp_attn_shard_forward
+    k = 2
+    need = ws_f(k, 1, 64, 256, 4, 1, 8)
+    ws, Z, X = ctypes.c_void_p(1 << 40), ctypes.c_void_p(1 << 41), ctypes.c_void_p(1 << 42)
+    base = lambda: [X, arr(10 * P, 11 * P), arr(12 * P, 13 * P), arr(14 * P, 15 * P), k, 1, 64, 256, 4, 1, ws,
+                    need, Z, 8, None]
+    a = base(); a[13] = 2
+    assert f(*a) == c["TP_ERR_FLAGS"]
+    a = base(); a[8] = 3
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = base(); a[9] = 0
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    a = base(); a[11] = need - 1
+    assert f(*a) == c["TP_ERR_WORKSPACE"]
+    a = base(); a[3] = arr(14 * P, None)
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = base(); a[12] = ctypes.c_void_p(14 * P + 64)   # Z over an output weight
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    a = base(); a[6] = 0
+    assert f(*a) == c["TP_OK"]

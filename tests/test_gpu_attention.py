@@ -1,0 +1,201 @@
+"""GPU parity of the tensor-parallel attention block (tp_attn_qkv_shards,
+tp_attn_core_shards, tp_attn_shard_forward) against the CPU fp64 oracle,
+element by element: the attention kernel from given bf16 projections at
+small and ragged sizes (sequences shorter than a key block, not a multiple
+of the 128-query block, head widths 64 and 128, causal or not, several heads
+and shards per launch), the projection GEMM with its bias epilogue, and the
+whole block at small sizes and at the workload sizes on sampled rows; plus
+batched == single-shard and fused == literal bit-identities and M = 0.
+Bounds: tests/_helpers.py (the softmax weights for them are an independent
+float64 computation; expected values come from the oracle).
+"""
+import numpy as np
+import pytest
+
+from _helpers import (U32, assert_within, attn_core_bound, attn_score_err, f64, from_dev, gemm_bound,
+                      rel_fro, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tpm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tensor_transformer_mlp_amd as tpm
+    tpm.lib()
+    return tpm
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    return oracle
+
+
+def _guarded(torch, shape, dtype, pad=64):
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * pad,), float("nan"), dtype=dtype, device="cuda")
+    return buf, buf[pad:pad + n].view(*shape)
+
+
+CORE_CASES = [
+    # B, S, heads, d, causal, score std
+    (1, 1, 1, 64, True, 1.0), (1, 7, 1, 64, True, 1.0), (2, 64, 2, 64, False, 1.0), (1, 100, 3, 64, True, 1.5),
+    (2, 129, 1, 128, True, 1.0), (1, 256, 2, 128, False, 1.0), (3, 300, 2, 128, True, 2.0),
+    (1, 1024, 3, 64, True, 1.0), (1, 200, 4, 128, True, 3.0), (2, 65, 2, 64, False, 2.0),
+]
+
+
+@pytest.mark.parametrize("B,S,heads,d,causal,std", CORE_CASES)
+def test_attn_core_parity(tpm, orc, B, S, heads, d, causal, std):
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    say("attn_core B=%d S=%d heads=%d d=%d causal=%s std=%g" % (B, S, heads, d, causal, std))
+    Hk = heads * d
+    M = B * S
+    qkv = inputs.draw(inputs.STREAM_X, (M, 3 * Hk), std, "bf16", seed=B * 1000 + S + heads + d)
+    pad = 64
+    buf, A = _guarded(torch, (M, Hk), torch.bfloat16, pad)
+    tpm.tp_attn_core_shards([to_dev(qkv)], [A], B, S, heads, d, causal=causal)
+    torch.cuda.synchronize()
+    assert bool(torch.all(torch.isnan(buf[:pad]))) and bool(torch.all(torch.isnan(buf[-pad:])))
+    Ag = f64(from_dev(A))
+    assert np.all(np.isfinite(Ag))
+    Ar = orc.attn_core(qkv, B, S, heads, d, causal)
+    assert_within(Ag, Ar, attn_core_bound(f64(qkv), Ar, B, S, heads, d, causal), "A")
+    assert rel_fro(Ag, Ar) <= 1e-2
+
+
+def test_attn_core_shards_equal_single(tpm):
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    B, S, heads, d, n = 2, 300, 2, 128, 5
+    say("attn_core_shards n=%d B=%d S=%d" % (n, B, S))
+    Hk = heads * d
+    qkvs = [to_dev(inputs.draw(inputs.STREAM_X, (B * S, 3 * Hk), 1.0, "bf16", seed=40 + i)) for i in range(n)]
+    A = [torch.empty(B * S, Hk, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    tpm.tp_attn_core_shards(qkvs, A, B, S, heads, d)
+    for i in range(n):
+        Ai = torch.empty_like(A[i])
+        tpm.tp_attn_core_shards([qkvs[i]], [Ai], B, S, heads, d)
+        torch.cuda.synchronize()
+        assert torch.equal(Ai, A[i]), i
+
+
+def _shard_inputs(inp, n_heads, k):
+    from tensor_transformer_mlp_amd import inputs
+    Wqkv, bqkv = inputs.qkv_shards(inp["Wq"], inp["Wk"], inp["Wv"], inp["bq"], inp["bk"], inp["bv"], n_heads, k)
+    H = inp["Wo"].shape[0]
+    Hk = H // k
+    Wo = [np.ascontiguousarray(inp["Wo"][i * Hk:(i + 1) * Hk]) for i in range(k)]
+    return Wqkv, bqkv, Wo
+
+
+def test_attn_qkv_parity(tpm, orc):
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    B, S, H, nh, k = 2, 100, 256, 4, 2
+    say("attn_qkv B=%d S=%d H=%d heads=%d k=%d" % (B, S, H, nh, k))
+    inp = inputs.make_attention(M=B * S, H=H, dtype="bf16", std=0.05, seed=3)
+    Wqkv, bqkv, _ = _shard_inputs(inp, nh, k)
+    Hk = H // k
+    QKV = [torch.empty(B * S, 3 * Hk, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    tpm.tp_attn_qkv_shards(to_dev(inp["X"]), [to_dev(w) for w in Wqkv], [to_dev(x) for x in bqkv], QKV)
+    torch.cuda.synchronize()
+    X64 = f64(inp["X"])
+    for i in range(k):
+        ref = orc.attn_qkv(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["bq"], inp["bk"], inp["bv"], nh, k, i)
+        got = f64(from_dev(QKV[i]))
+        bound = gemm_bound(X64, f64(Wqkv[i]), H) + 2.0 ** -8 * np.abs(ref) + 2 * U32 * np.abs(f64(bqkv[i]))[None, :]
+        assert_within(got, ref, bound, "QKV[%d]" % i)
+
+
+FWD_CASES = [
+    # B, S, H, n_heads, k, causal
+    (1, 64, 256, 4, 2, True), (2, 100, 256, 4, 4, True), (1, 130, 512, 4, 2, False), (2, 48, 768, 12, 4, True),
+    (1, 200, 512, 4, 1, True),
+]
+
+
+@pytest.mark.parametrize("B,S,H,nh,k,causal", FWD_CASES)
+@pytest.mark.parametrize("fused", [False, True])
+def test_attn_shard_forward_parity(tpm, orc, B, S, H, nh, k, causal, fused):
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    say("attn_shard_forward B=%d S=%d H=%d heads=%d k=%d causal=%s fused=%s" % (B, S, H, nh, k, causal, fused))
+    inp = inputs.make_attention(M=B * S, H=H, dtype="bf16", std=0.05, seed=B + S + H + k)
+    Wqkv, bqkv, Wo = _shard_inputs(inp, nh, k)
+    pad = 64
+    buf, Z = _guarded(torch, (B * S, H), torch.float32, pad)
+    tpm.tp_attn_shard_forward(to_dev(inp["X"]), [to_dev(w) for w in Wqkv], [to_dev(x) for x in bqkv],
+                              [to_dev(w) for w in Wo], B, S, nh, Z=Z, fused=fused, causal=causal)
+    torch.cuda.synchronize()
+    assert bool(torch.all(torch.isnan(buf[:pad]))) and bool(torch.all(torch.isnan(buf[-pad:])))
+    Zg = f64(from_dev(Z))
+    assert np.all(np.isfinite(Zg))
+    Zr = orc.attn_forward(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["bq"], inp["bk"], inp["bv"], inp["Wo"],
+                          nh, S, k, causal)
+    # bound: per shard, the attention bound with the projection's score and
+    # value errors, through the output projection
+    d, hk, Hk = H // nh, nh // k, H // k
+    X64 = f64(inp["X"])
+    bound = np.zeros_like(Zr)
+    for i in range(k):
+        qkv = orc.attn_qkv(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["bq"], inp["bk"], inp["bv"], nh, k, i)
+        A = orc.attn_core(qkv, B, S, hk, d, causal)
+        sl = slice(i * Hk, (i + 1) * Hk)
+        es = attn_score_err(qkv, B, S, hk, d, H, X64, f64(inp["Wq"])[:, sl], f64(inp["Wk"])[:, sl])
+        eA = attn_core_bound(qkv, A, B, S, hk, d, causal, e_s=es)
+        bound += gemm_bound(A, f64(Wo[i]), Hk, ea=eA)
+    bound += 2 * (k + 2) * U32 * np.abs(Zr)
+    assert_within(Zg, Zr, bound, "Z")
+    assert rel_fro(Zg, Zr) <= 1e-2
+
+
+def test_attn_fused_equals_literal_and_empty(tpm):
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    B, S, H, nh, k = 2, 200, 512, 4, 4
+    say("attn fused vs literal B=%d S=%d H=%d k=%d" % (B, S, H, k))
+    inp = inputs.make_attention(M=B * S, H=H, dtype="bf16", std=0.05, seed=8)
+    Wqkv, bqkv, Wo = _shard_inputs(inp, nh, k)
+    args = (to_dev(inp["X"]), [to_dev(w) for w in Wqkv], [to_dev(x) for x in bqkv], [to_dev(w) for w in Wo])
+    Z1 = tpm.tp_attn_shard_forward(*args, B, S, nh, fused=False)
+    Z2 = tpm.tp_attn_shard_forward(*args, B, S, nh, fused=True)
+    Z3 = tpm.tp_attn_shard_forward(*args, B, S, nh, fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(Z1, Z2) and torch.equal(Z1, Z3)
+    say("attn M=0")
+    X0 = torch.empty(0, H, dtype=torch.bfloat16, device="cuda")
+    Z0 = tpm.tp_attn_shard_forward(X0, *args[1:], 0, S, nh)
+    torch.cuda.synchronize()
+    assert Z0.numel() == 0
+
+
+@pytest.mark.parametrize("name", ["gpt2_small", "llama7b"])
+def test_attn_workload_sampled_rows(tpm, orc, name):
+    """Full-size causal attention block (the workload's B, S, H and heads) in
+    the benchmark's launch configuration; sampled rows at several positions
+    of several sequences against the oracle (a row at position t needs only
+    the t + 1 rows before it)."""
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    w = inputs.WORKLOADS[name]
+    nh = w.heads
+    say("workload attention %s B=%d S=%d H=%d heads=%d k=%d" % (name, w.B, w.S, w.H, nh, w.k))
+    inp = inputs.make_attention(w)
+    Wqkv, bqkv, Wo = _shard_inputs(inp, nh, w.k)
+    Z = tpm.tp_attn_shard_forward(to_dev(inp["X"]), [to_dev(x) for x in Wqkv], [to_dev(x) for x in bqkv],
+                                  [to_dev(x) for x in Wo], w.B, w.S, nh)
+    torch.cuda.synchronize()
+    pos = [0, 1, 63, 64, 127, 128, 200]
+    rows = np.array(sorted({(r % w.B) * w.S + t for r, t in enumerate(pos)}))
+    Zg = f64(from_dev(Z[torch.from_numpy(rows).cuda()]))
+    Zr = orc.attn_forward_rows(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["bq"], inp["bk"], inp["bv"], inp["Wo"],
+                               nh, w.S, w.k, rows, True)
+    assert np.all(np.isfinite(Zg))
+    assert rel_fro(Zg, Zr) <= 1e-2
+    for j in range(len(rows)):
+        assert rel_fro(Zg[j], Zr[j]) <= 2e-2, rows[j]
