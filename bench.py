@@ -10,11 +10,12 @@ then the dX shard sum) is timed the same way and reported under "backward",
 and so is the sequence-parallel forward (tp_mlp_shard_forward_sp: the shard
 sum as a reduce-scatter over the k sequence blocks with the residual X added)
 under "sequence_parallel", and the SwiGLU variant of the block
-(tp_swiglu_shard_forward) under "swiglu", and the causal tensor-parallel
-attention block of the same width (tp_attn_shard_forward) under "attention".
+(tp_swiglu_shard_forward) under "swiglu"; with --attention, the causal
+tensor-parallel attention block of the same width (tp_attn_shard_forward)
+under "attention".
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant literal|fused]
-                    [--no-backward] [--no-sp] [--no-swiglu] [--no-attention]
+                    [--no-backward] [--no-sp] [--no-swiglu] [--attention]
 
 Prints ONE JSON line (metric, value in TFLOP/s, ms_per_step, roofline of the
 dominant kernel, CPU-oracle baseline, backward) on stdout; diagnostics go to
@@ -55,7 +56,9 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel leg")
     ap.add_argument("--no-swiglu", action="store_true", help="skip the SwiGLU leg")
-    ap.add_argument("--no-attention", action="store_true", help="skip the attention leg")
+    ap.add_argument("--attention", action="store_true",
+                    help="also time the attention block (off by default: its output projection launches the "
+                         "row GEMM kernel at another shape, which would mix into that kernel's profile)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain float32 copy kernel (y = x * 1) over MIB MiB, 5 times: "
                          "the known-size reference for the HBM byte counters")
@@ -288,7 +291,7 @@ def main():
         swiglu = bench_swiglu(tpm, w, X, Vs, fused, args, elt, tdt)
     del Vs
     attn = None
-    if not args.no_attention and w.dtype == "bf16":
+    if args.attention and w.dtype == "bf16":
         attn = bench_attention(tpm, w, X, fused, args, elt)
 
     cpu = None
