@@ -4,7 +4,9 @@
 One step = one call of tp_mlp_shard_forward: for each of the k shards the
 column GEMM + bias + GeLU and the row GEMM, then the on-device shard sum, over
 one batch of seeded synthetic inputs already resident in HBM.  `value` is the
-forward's throughput.  The backward of the same block (tp_mlp_shard_backward:
+forward's throughput (the literal variant by default: fp32 partials and the
+shard-reduce kernel); "variants" also gives the other variant (the shard sum
+folded into the row GEMMs), checked to give the same Z bit for bit.  The backward of the same block (tp_mlp_shard_backward:
 per shard the training-mode column step, dA, dV, dW + db and the partial dX,
 then the dX shard sum) is timed the same way and reported under "backward",
 and so is the sequence-parallel forward (tp_mlp_shard_forward_sp: the shard
@@ -248,6 +250,30 @@ def main():
     if not bool(torch.isfinite(Z).all()):
         raise RuntimeError("non-finite output")
 
+    # The other variant of the same step, timed the same way (reported beside
+    # the headline; bit-identical Z).
+    other = not fused
+    oflags = tpm.TP_FUSED_ACCUM if other else 0
+    ows = torch.empty(max(tpm.tp_mlp_workspace_bytes(w.k, w.M, w.H, Fk, tpm.TP_BF16 if w.dtype == "bf16" else
+                                                     tpm.TP_F32, oflags), 1), dtype=torch.uint8, device=dev)
+    Z2 = torch.empty_like(Z)
+    for _ in range(args.warmup):
+        tpm.tp_mlp_shard_forward(X, Ws, bs, Vs, Z=Z2, workspace=ows, fused=other)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tpm.tp_mlp_shard_forward(X, Ws, bs, Vs, Z=Z2, workspace=ows, fused=other)
+    torch.cuda.synchronize()
+    oms = (time.perf_counter() - t0) * 1e3 / args.steps
+    if not torch.equal(Z, Z2):
+        raise RuntimeError("literal and fused forward differ")
+    variants = {args.variant: {"value": round(tflops, 3), "ms_per_step": round(ms, 5)},
+                ("fused" if other else "literal"): {"value": round(w.flop / (oms * 1e-3) / 1e12, 3),
+                                                    "ms_per_step": round(oms, 5)}}
+    log("other variant (%s): %.4f ms/step, %.1f TFLOP/s" % ("fused" if other else "literal", oms,
+                                                          w.flop / (oms * 1e-3) / 1e12))
+    del ows, Z2
+
     # Per-kernel pass: the launches of one step through the batched per-step
     # entry points, in the same launch configuration as the step (the shards
     # run in batches of up to TP_MAX_BATCH, one launch per step and batch).
@@ -307,6 +333,7 @@ def main():
         "roofline": roof,
         "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],
                          "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()},
+        "variants": variants,
         "cpu_baseline": cpu,
         "backward": bwd,
         "sequence_parallel": sp,
