@@ -169,7 +169,7 @@ def test_shard_forward_sp_fused_equals_literal(tpm):
     assert torch.equal(O1, O2) and torch.equal(O1, O3)
 
 
-@pytest.mark.parametrize("name", ["gpt2_small", "llama7b"])
+@pytest.mark.parametrize("name", ["tiny", "gpt2_small", "llama7b", "gpt3_175b", "long_seq"])
 def test_workload_sp_sampled_rows(tpm, orc, name):
     """Full-size sequence-parallel forward in the benchmark's launch
     configuration; sampled rows of every rank's block against the oracle."""
@@ -186,9 +186,10 @@ def test_workload_sp_sampled_rows(tpm, orc, name):
     torch.cuda.synchronize()
     Mb = w.M // w.k
     rng = np.random.default_rng(5)
-    rows = np.sort(np.concatenate([r * Mb + rng.choice(Mb, 2, replace=False) for r in range(w.k)]))
+    rows = np.sort(np.concatenate([r * Mb + rng.choice(Mb, min(2, Mb), replace=False) for r in range(w.k)]))
     Og = f64(from_dev(O[torch.from_numpy(rows).cuda()]))
     ref = orc.sp_forward_rows(X, W, b, V, w.k, rows)
-    assert rel_fro(Og, ref) <= 1e-2
+    tol = 1e-2 if w.dtype == "bf16" else 1e-5
+    assert rel_fro(Og, ref) <= tol
     # the residual is there: O - X is the MLP output, of a different scale than X
-    assert rel_fro(Og - f64(X[rows]), ref - f64(X[rows])) <= 1e-2
+    assert rel_fro(Og - f64(X[rows]), ref - f64(X[rows])) <= tol

@@ -155,7 +155,7 @@ def test_swiglu_fused_equals_literal_and_empty(tpm):
     assert Z0.numel() == 0 and Y0.numel() == 0
 
 
-@pytest.mark.parametrize("name", ["gpt2_small", "llama7b"])
+@pytest.mark.parametrize("name", ["tiny", "gpt2_small", "llama7b", "gpt3_175b", "long_seq"])
 def test_swiglu_workload_sampled_rows(tpm, orc, name):
     """Full-size SwiGLU forward in the benchmark's launch configuration;
     sampled rows against the oracle."""
@@ -171,8 +171,8 @@ def test_swiglu_workload_sampled_rows(tpm, orc, name):
                                     [to_dev(np.ascontiguousarray(V[i * Fk:(i + 1) * Fk])) for i in range(w.k)])
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
-    rows = np.sort(rng.choice(w.M, 12, replace=False))
+    rows = np.sort(rng.choice(w.M, min(12, w.M), replace=False))
     Zg = f64(from_dev(Z[torch.from_numpy(rows).cuda()]))
     Zr = orc.swiglu_forward_rows(X, Wg, Wu, V, w.k, rows)
-    assert rel_fro(Zg, Zr) <= 1e-2
+    assert rel_fro(Zg, Zr) <= (1e-2 if w.dtype == "bf16" else 1e-5)
     assert np.all(np.isfinite(Zg))
