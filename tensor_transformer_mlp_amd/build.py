@@ -33,8 +33,15 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-source flags.  attention.hip: MFMA accumulators in ordinary VGPRs (the
+# softmax reads and rescales them with VALU instructions every key block; in
+# AGPRs each of those needs a copy out and back).
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc_compile_cmd(src: str, obj: str) -> list:
-    return [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, src]
+    extra = SOURCE_FLAGS.get(os.path.basename(src), [])
+    return [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, src]
 
 
 def hipcc_link_cmd(objs, out: str) -> list:

@@ -47,6 +47,14 @@ struct AttnParams {
 
 constexpr int kBQ = 128, kBK = 64;
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to two round-to-nearest-even bf16 in one 32-bit word (a low).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // Chunk swizzle of a [keys][D] tile: D = 128 rows are one 256-byte bank row,
 // so the 16 chunks of consecutive keys are rotated by key & 15; D = 64 rows
 // pair up in a bank row, rotated by (key >> 1) & 7.
@@ -173,25 +181,29 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
         s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j], s[u], 0, 0, 0);
       }
     }
-    // Mask, scale to base 2, block maximum (lane pair l, l ^ 32 hold one query).
+    // Mask, block maximum of the raw scores (lane pair l, l ^ 32 hold one
+    // query); the running maximum m is kept in base-2 units, m = max s c2.
     const bool edge = k0 + kBK > S || (CAUSAL && k0 + kBK - 1 > q0 + 32 * wave);
+    if (edge) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kk = k0 + 32 * u + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          if (kk >= S || (CAUSAL && kk > qq)) s[u][e] = -__builtin_inff();
+        }
+    }
     float mx = -1e30f;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = s[u][e] * c2;
-        if (edge) {
-          const int kk = k0 + 32 * u + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          if (kk >= S || (CAUSAL && kk > qq)) x = -__builtin_inff();
-        }
-        s[u][e] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, mx * c2);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
+    // p = 2^(s c2 - m), one fused multiply-add per score; a masked score
+    // (-inf) gives 0.
     float psum = 0.f;
     bf16x8_t pf[4];
 #pragma unroll
@@ -200,16 +212,20 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const int e = 8 * (jj & 1) + 2 * e2;
-        const float a0 = __builtin_amdgcn_exp2f(s[jj >> 1][e] - m_new);
-        const float a1 = __builtin_amdgcn_exp2f(s[jj >> 1][e + 1] - m_new);
+        const float a0 = __builtin_amdgcn_exp2f(fmaf(s[jj >> 1][e], c2, -m_new));
+        const float a1 = __builtin_amdgcn_exp2f(fmaf(s[jj >> 1][e + 1], c2, -m_new));
         psum += a0 + a1;
-        pk[e2] = f32_to_bf16_bits(a0) | (f32_to_bf16_bits(a1) << 16);
+        pk[e2] = pack_bf16x2(a0, a1);
       }
       pf[jj] = __builtin_bit_cast(bf16x8_t, pk);
     }
     l_run = l_run * alpha + psum;
+    // The running maximum rarely grows after the first blocks: rescale the
+    // accumulators only when it did for some lane (alpha == 1 is exact).
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int t = 0; t < DT; ++t) acc[t] = acc[t] * alpha;
+      for (int t = 0; t < DT; ++t) acc[t] = acc[t] * alpha;
+    }
     // O^T += V^T P^T over the 64 keys (4 k-steps of 16).
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
@@ -243,8 +259,8 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         u32x2_t o;
-        o[0] = f32_to_bf16_bits(acc[t][4 * e4] * inv) | (f32_to_bf16_bits(acc[t][4 * e4 + 1] * inv) << 16);
-        o[1] = f32_to_bf16_bits(acc[t][4 * e4 + 2] * inv) | (f32_to_bf16_bits(acc[t][4 * e4 + 3] * inv) << 16);
+        o[0] = pack_bf16x2(acc[t][4 * e4] * inv, acc[t][4 * e4 + 1] * inv);
+        o[1] = pack_bf16x2(acc[t][4 * e4 + 2] * inv, acc[t][4 * e4 + 3] * inv);
         *reinterpret_cast<u32x2_t*>(orow + 32 * t + 8 * e4) = o;
       }
   }
