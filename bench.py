@@ -44,11 +44,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def warm(step, args):
+    """Untimed: the step repeated for args.settle_seconds (the GPU raises its
+    clock only after some time under load: the first ~50 gpt2_small steps after
+    an idle period run ~12% slower than the steady state), then args.warmup
+    more steps."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_seconds:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-seconds", type=float, default=0.5,
+                    help="before each leg's warmup steps, repeat its step for this long so that the GPU's clock "
+                         "has left its idle state (untimed; 0 disables)")
     ap.add_argument("--workload", default="gpt2_small")
     ap.add_argument("--variant", choices=["literal", "fused"], default="literal")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
@@ -235,8 +253,7 @@ def main():
     def step():
         tpm.tp_mlp_shard_forward(X, Ws, bs, Vs, Z=Z, workspace=ws, fused=fused)
 
-    for _ in range(args.warmup):
-        step()
+    warm(step, args)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -257,8 +274,7 @@ def main():
     ows = torch.empty(max(tpm.tp_mlp_workspace_bytes(w.k, w.M, w.H, Fk, tpm.TP_BF16 if w.dtype == "bf16" else
                                                      tpm.TP_F32, oflags), 1), dtype=torch.uint8, device=dev)
     Z2 = torch.empty_like(Z)
-    for _ in range(args.warmup):
-        tpm.tp_mlp_shard_forward(X, Ws, bs, Vs, Z=Z2, workspace=ows, fused=other)
+    warm(lambda: tpm.tp_mlp_shard_forward(X, Ws, bs, Vs, Z=Z2, workspace=ows, fused=other), args)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -368,8 +384,7 @@ def bench_backward(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt):
     def step():
         tpm.tp_mlp_shard_backward(X, Ws, bs, Vs, dZ, dX=dX, dW=dW, db=db, dV=dV, workspace=ws, fused=fused)
 
-    for _ in range(args.warmup):
-        step()
+    warm(step, args)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -442,8 +457,7 @@ def bench_sp(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt):
     def step():
         tpm.tp_mlp_shard_forward_sp(X, Ws, bs, Vs, O=O, workspace=ws, fused=fused)
 
-    for _ in range(args.warmup):
-        step()
+    warm(step, args)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -512,8 +526,7 @@ def bench_swiglu(tpm, w, X, Vs, fused, args, elt, tdt):
     def step():
         tpm.tp_swiglu_shard_forward(X, Wg, Wu, Vs, Z=Z, workspace=ws, fused=fused)
 
-    for _ in range(args.warmup):
-        step()
+    warm(step, args)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -586,8 +599,7 @@ def bench_attention(tpm, w, X, fused, args, elt):
     def step():
         tpm.tp_attn_shard_forward(X, Wqkv, bqkv, Wo, w.B, w.S, nh, Z=Z, workspace=ws, fused=fused, causal=True)
 
-    for _ in range(args.warmup):
-        step()
+    warm(step, args)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):

@@ -76,17 +76,20 @@ __device__ __forceinline__ float silu_f32(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// Map the linear workgroup id bid (of nb) to a (tile_m, tile_n) pair.  Workgroups are
-// dispatched round-robin over the 8 XCDs, so ids are first regrouped so that
-// each XCD receives a contiguous range of logical tiles, and logical tiles are
-// walked in column strips of `kGroupM` tile rows so that the tiles resident on
-// one XCD at a time share rows of A and columns of B in that XCD's L2.
-template <int kGroupM>
-__device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_m, int tiles_n, int& tm,
-                                            int& tn) {
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup id b runs
+// on XCD b % 8).  xcd_logical regroups the ids 0 .. nb - 1 so that each XCD
+// receives a contiguous range of logical ids: b -> (b % 8) (nb / 8) + b / 8
+// for the largest multiple of 8 below nb, the rest unchanged (a bijection).
+__device__ __forceinline__ int xcd_logical(int bid, int nb) {
   const int full = nb - nb % kNumXcd;
-  int logical = bid;
-  if (bid < full) logical = (bid % kNumXcd) * (full / kNumXcd) + bid / kNumXcd;
+  return bid < full ? (bid % kNumXcd) * (full / kNumXcd) + bid / kNumXcd : bid;
+}
+
+// Logical tile id -> (tile_m, tile_n), walking the tiles in column strips of
+// `kGroupM` tile rows, so that consecutive ids share rows of A and columns of
+// B.
+template <int kGroupM>
+__device__ __forceinline__ void strip_coords(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int group = kGroupM * tiles_n;
   const int g = logical / group;
   const int first_m = g * kGroupM;
@@ -94,6 +97,16 @@ __device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_m, int ti
   const int local = logical - g * group;
   tm = first_m + local % gm;
   tn = local / gm;
+}
+
+// Map the linear workgroup id bid (of nb, the tiles of one output) to a
+// (tile_m, tile_n) pair: each XCD receives a contiguous range of logical
+// tiles, walked in strips, so that the tiles resident on one XCD at a time
+// share rows of A and columns of B in that XCD's L2.
+template <int kGroupM>
+__device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  strip_coords<kGroupM>(xcd_logical(bid, nb), tiles_m, tiles_n, tm, tn);
 }
 
 // gfx9 raw buffer descriptor (stride 0, num_records = bytes) as four SGPRs.

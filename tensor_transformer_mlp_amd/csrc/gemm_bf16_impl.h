@@ -293,18 +293,28 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   int tm, tn;
   const int tiles = p.tiles_m * p.tiles_n;
   int bid = blockIdx.x, slice = 0, grp = 0;
-  if constexpr (!GSUM) {
-    if (p.groups > 1) {
-      const int per_group = tiles * p.slices;
-      grp = bid / per_group;
-      bid -= grp * per_group;
+  if (!GSUM && p.slices > 1) {
+    // K-split: the whole grid is regrouped so that each XCD runs a contiguous
+    // range of (slice, group, tile) in slice-major order, i.e. the workgroups
+    // on one XCD share one K slab of the operands in its L2.
+    const int sg_tile = xcd_logical(bid, tiles * p.slices * p.groups);
+    const int sg = sg_tile / tiles;
+    grp = sg % p.groups;
+    slice = sg / p.groups;
+    strip_coords<8>(sg_tile - sg * tiles, p.tiles_m, p.tiles_n, tm, tn);
+  } else {
+    if (!GSUM && p.groups > 1) {
+      grp = bid / tiles;
+      bid -= grp * tiles;
     }
-    if (p.slices > 1) {
-      slice = bid / tiles;
-      bid -= slice * tiles;
-    }
+    tile_coords<8>(bid, tiles, p.tiles_m, p.tiles_n, tm, tn);
   }
-  tile_coords<8>(bid, tiles, p.tiles_m, p.tiles_n, tm, tn);
+  // (wave-uniform by construction; said explicitly so that the operand
+  // pointers derived from them stay in scalar registers)
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  grp = __builtin_amdgcn_readfirstlane(grp);
+  slice = __builtin_amdgcn_readfirstlane(slice);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
