@@ -624,6 +624,112 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
       }
     }
   };
+  // Tiles wholly inside C with a store-only epilogue go through LDS: each
+  // wave writes one 32-row block of 128 output bytes per row (one fp32
+  // fragment, or two bf16 fragments) into its own region of the stage
+  // buffers, reads it back by rows and stores whole 128-byte row segments, so
+  // that every store instruction writes full cache lines (the accumulator
+  // layout alone gives 16- or 32-byte pieces of 32 rows per instruction).
+  constexpr bool kCanStage = EPI != kEpiMulAux;
+  if constexpr (kCanStage) {
+    if (m0 + BM <= M && n0 + BNO <= N && !accumulate) {
+      constexpr int kElt = (EPI == kEpiStoreF32 || EPI == kEpiAccumF32) ? 4 : 2;
+      constexpr int kFragsPerChunk = (kElt == 2 && FNO % 2 == 0) ? 2 : 1;
+      constexpr int kChunkBytes = kFragsPerChunk * 32 * kElt;  // one row of a chunk: 128 or 64 bytes
+      constexpr int kRowStride = kChunkBytes + 16;             // padded (bank spread)
+      constexpr int kRegion = 32 * kRowStride;
+      constexpr int kRegionsPerStage = STAGE / kRegion;
+      static_assert(kRegionsPerStage * NBUF >= NW, "epilogue staging regions");
+      constexpr int kLanesPerRow = kChunkBytes / 16;
+      constexpr int kRowsPerPass = 64 / kLanesPerRow;
+      constexpr int kPasses = 32 / kRowsPerPass;
+      constexpr int kNumOut = EPI == kEpiBiasGeluSave ? 2 : 1;
+      // Every wave is past its last fragment read and every DMA of the
+      // workgroup has landed before the stage buffers are reused.
+      asm volatile("s_barrier" ::: "memory");
+      const int sidx = wave / kRegionsPerStage;
+      uint32_t region = lds_offset(st0);
+      if (sidx == 1) region = lds_offset(st1);
+      if (sidx == 2) region = lds_offset(st2);
+      if (NBUF > 3 && sidx == 3) region = lds_offset(st3);
+      if (NBUF > 4 && sidx == 4) region = lds_offset(st4);
+      if (NBUF > 5 && sidx == 5) region = lds_offset(st5);
+      region += (uint32_t)((wave % kRegionsPerStage) * kRegion);
+      using lds_char = __attribute__((address_space(3))) char;
+      lds_char* R = (lds_char*)(uintptr_t)region;
+      const int rrow = lane / kLanesPerRow, rcol = (lane % kLanesPerRow) * 16;
+      void* outs[2] = {Cout, aux};
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int c = 0; c < FNO / kFragsPerChunk; ++c) {
+          // final values of the chunk's fragments: v[o][f][gq] (4 columns each)
+          f32x4_t v[kNumOut][kFragsPerChunk][4];
+#pragma unroll
+          for (int f = 0; f < kFragsPerChunk; ++f) {
+            const int j = c * kFragsPerChunk + f;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              f32x4_t a;
+              if constexpr (DUAL) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = silu_f32(acc[i][j][4 * gq + e]) * acc[i][FNO + j][4 * gq + e];
+              } else if constexpr (GSUM) {
+                a = f32x4_t{z[i][j][4 * gq], z[i][j][4 * gq + 1], z[i][j][4 * gq + 2], z[i][j][4 * gq + 3]};
+              } else {
+                a = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                            acc[i][j][4 * gq + 3]};
+              }
+              if constexpr (kBias) a += bias4[j][gq];
+              if constexpr (EPI == kEpiBiasGelu) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = gelu_f32(a[e]);
+              }
+              if constexpr (EPI == kEpiBiasGeluSave) {
+                float y[4], g[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gelu_and_grad_f32(a[e], y[e], g[e]);
+                v[0][f][gq] = f32x4_t{y[0], y[1], y[2], y[3]};
+                v[kNumOut - 1][f][gq] = f32x4_t{g[0], g[1], g[2], g[3]};
+              } else {
+                v[0][f][gq] = a;
+              }
+            }
+          }
+#pragma unroll
+          for (int o = 0; o < kNumOut; ++o) {
+            // lane (row l32, half lane / 32) holds columns 32 f + 8 gq + 4 (lane / 32) .. + 3
+#pragma unroll
+            for (int f = 0; f < kFragsPerChunk; ++f)
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                lds_char* dst = R + l32 * kRowStride + (32 * f + 8 * gq + hcol) * kElt;
+                const f32x4_t x = v[o][f][gq];
+                if constexpr (kElt == 4) {
+                  *(__attribute__((address_space(3))) f32x4_t*)dst = x;
+                } else {
+                  u32x2_t w;
+                  w[0] = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
+                  w[1] = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
+                  *(__attribute__((address_space(3))) u32x2_t*)dst = w;
+                }
+              }
+            u32x4_t rows[kPasses];
+#pragma unroll
+            for (int t = 0; t < kPasses; ++t)
+              rows[t] = *(__attribute__((address_space(3))) u32x4_t*)(R + (rrow + t * kRowsPerPass) * kRowStride + rcol);
+            char* base = static_cast<char*>(outs[o]) +
+                         ((int64_t)(m0 + wm * WTM + i * 32 + rrow) * ldc + n0 + wn * WTNO + c * kFragsPerChunk * 32) *
+                             kElt + rcol;
+#pragma unroll
+            for (int t = 0; t < kPasses; ++t)
+              *reinterpret_cast<u32x4_t*>(base + (int64_t)t * kRowsPerPass * ldc * kElt) = rows[t];
+          }
+        }
+      }
+      return;
+    }
+  }
   if (m0 + BM <= M && n0 + BNO <= N)
     epilogue(std::false_type{});
   else
