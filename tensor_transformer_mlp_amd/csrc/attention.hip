@@ -74,8 +74,9 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
   constexpr int DMA_PER_WAVE = TILE / 1024 / 4;
   constexpr int KS = D / 16;                 // MFMA k-steps over D (scores)
   constexpr int DT = D / 32;                 // output tiles of 32 along D
-  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  // Two stage buffers of [K tile | V tile] in one array, so that the second
+  // stage is a constant offset from the first.
+  __shared__ __attribute__((aligned(1024))) char stages[2 * STAGE];
 
   // Heaviest query blocks (the last ones, under the causal mask) first.
   const int per_qb = p.groups * p.B * p.heads;
@@ -137,14 +138,15 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
 
   // LDS read offsets.  K fragment (A operand of S^T) of 32-key tile u and
   // k-step j: key 32 u + l32, chunk 2 j + h2 (swz(key) does not depend on u).
-  int koff[KS];
+  const uint32_t L0 = lds_offset(stages);
+  uint32_t kaddr[KS];  // stage 0's LDS address; + 32 u ROW and + s STAGE are immediates
 #pragma unroll
-  for (int j = 0; j < KS; ++j) koff[j] = l32 * ROW + (((2 * j + h2) ^ swz<D>(l32)) << 4);
+  for (int j = 0; j < KS; ++j) kaddr[j] = L0 + l32 * ROW + (((2 * j + h2) ^ swz<D>(l32)) << 4);
   // V^T fragment (A operand of O^T += V^T P^T) of output tile t, k-step jj
   // (keys 16 jj ..): two transpose reads at keys 16 jj + 4 h2 + 8 r + (q / 4),
   // columns 32 t + 16 ((lane >> 4) & 1) + 4 (q % 4), q = lane % 16; the
   // swizzle does not depend on jj.
-  int voff[DT][2];
+  uint32_t vaddr[DT][2];  // stage 0's LDS address; + 16 jj ROW and + s STAGE are immediates
   {
     const int q = lane & 15;
 #pragma unroll
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
       for (int r = 0; r < 2; ++r) {
         const int key = 4 * h2 + 8 * r + (q >> 2);
         const int col = 32 * t + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
-        voff[t][r] = TILE + key * ROW + (((col >> 3) ^ swz<D>(key)) << 4) + ((col >> 2) & 1) * 8;
+        vaddr[t][r] = L0 + TILE + key * ROW + (((col >> 3) ^ swz<D>(key)) << 4) + ((col >> 2) & 1) * 8;
       }
   }
 
@@ -168,19 +170,42 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
   const int kend = CAUSAL ? min(q0 + kBQ, S) : S;
   const int nb = (kend + kBK - 1) / kBK;
 
-  auto block = [&](const char* Sb, int k0) {
+  using lds_frag = const __attribute__((address_space(3))) bf16x8_t;
+  using lds_half = __attribute__((address_space(3))) i16x4_t;
+  // One 64-key block from stage buffer SB (a compile-time index: every LDS
+  // address below is a per-lane register plus an immediate).  All fragment
+  // reads of a product are issued before its MFMAs, so their latencies
+  // overlap instead of adding up.
+  auto block = [&](auto sset, int k0) {
+    constexpr int SB = decltype(sset)::value * STAGE;
     // S^T for the 64 keys: two 32-key tiles.
     f32x16_t s[2];
+    bf16x8_t kf[2][KS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < KS; ++j) kf[u][j] = *(lds_frag*)(uintptr_t)(kaddr[j] + SB + u * 32 * ROW);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[u][e] = 0.f;
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Sb + u * 32 * ROW + koff[j]);
-        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j], s[u], 0, 0, 0);
-      }
+      for (int j = 0; j < KS; ++j) s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[u][j], qf[j], s[u], 0, 0, 0);
     }
+    // every K fragment read first, then the score MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);
+    // V^T fragments of the first k-step, read while the softmax runs.
+    bf16x8_t vf[2][DT];
+    auto read_v = [&](int jj, bf16x8_t* dst) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_half*)(uintptr_t)(vaddr[t][0] + SB + jj * 16 * ROW));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_half*)(uintptr_t)(vaddr[t][1] + SB + jj * 16 * ROW));
+        dst[t] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    read_v(0, vf[0]);
     // Mask, block maximum of the raw scores (lane pair l, l ^ 32 hold one
     // query); the running maximum m is kept in base-2 units, m = max s c2.
     const bool edge = k0 + kBK > S || (CAUSAL && k0 + kBK - 1 > q0 + 32 * wave);
@@ -226,28 +251,41 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
 #pragma unroll
       for (int t = 0; t < DT; ++t) acc[t] = acc[t] * alpha;
     }
-    // O^T += V^T P^T over the 64 keys (4 k-steps of 16).
+    // O^T += V^T P^T over the 64 keys (4 k-steps of 16), the next k-step's
+    // V^T fragments read while this one's MFMAs run.
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < 4; ++jj) {
+      if (jj + 1 < 4) read_v(jj + 1, vf[(jj + 1) & 1]);
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const char* v0 = Sb + voff[t][0] + jj * 16 * ROW;
-        const bf16x8_t vf = ds_read_tr_pair(v0, v0 + (voff[t][1] - voff[t][0]));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[jj], acc[t], 0, 0, 0);
-      }
+      for (int t = 0; t < DT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[jj & 1][t], pf[jj], acc[t], 0, 0, 0);
+    }
   };
 
   // Two stage buffers: block j + 1 loads while block j is computed.  At the
-  // top of iteration j the only loads in flight are block j's.
-  issue(lds_offset(st0), 0);
-  for (int j = 0; j < nb; ++j) {
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): block j has landed
-    asm volatile("s_barrier" ::: "memory");             // visible to all; block j - 1 done
-    const bool odd = j & 1;
-    if (j + 1 < nb) issue(odd ? lds_offset(st0) : lds_offset(st1), (j + 1) * kBK);
-    block(odd ? st1 : st0, j * kBK);
+  // top of iteration j the only loads in flight are block j's.  The loop is
+  // unrolled by two so that each block's stage is a compile-time index.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // vmcnt(0) lgkmcnt(0) before each barrier: this wave's loads of the next
+  // block have landed and its reads of the previous block have returned (the
+  // compiler may place the MFMAs that consume those reads after the barrier,
+  // and the barrier alone does not wait for them).
+  constexpr int kWaitAll = 7 << 4;
+  issue(L0, 0);
+  for (int j = 0; j < nb; j += 2) {
+    __builtin_amdgcn_s_waitcnt(kWaitAll);    // block j has landed
+    asm volatile("s_barrier" ::: "memory");  // visible to all; block j - 1 done
+    if (j + 1 < nb) issue(L0 + STAGE, (j + 1) * kBK);
+    block(I0{}, j * kBK);
+    if (j + 1 < nb) {
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      asm volatile("s_barrier" ::: "memory");
+      if (j + 2 < nb) issue(L0, (j + 2) * kBK);
+      block(I1{}, (j + 1) * kBK);
+    }
   }
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
 
   // O = O^T / l: lane holds query qq, columns 32 t + 8 (e / 4) + 4 h2 + e % 4.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
