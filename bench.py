@@ -197,7 +197,7 @@ def roofline(kern, w, variant, dtype, kind=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        log("bench.py measures one GPU only: this build has no multi-GPU path "
+        log("bench.py measures one GPU only: the library has no multi-GPU path "
             "(the k shards run back to back on one device); run with --gpus 1")
         sys.exit(2)
 
