@@ -28,6 +28,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
 }
 
+// Four floats to four round-to-nearest-even bf16, packed low to high.
+__device__ __forceinline__ u32x2_t pack4_bf16(f32x4_t x) {
+  return u32x2_t{f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16),
+                 f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16)};
+}
+
 // h = Phi(-|x|) = erfc(|x| / sqrt 2) / 2 and e = exp(-x^2 / 2), the two
 // pieces of GeLU(x) = x Phi(x) (the erf form of GeLU, not the tanh
 // approximation) and of GeLU'(x) = Phi(x) + x phi(x).
@@ -37,26 +43,30 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
 //   erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2) + e(z),
 //   t = 1 / (1 + p z),  |e(z)| <= 1.5e-7,
 // with p = 0.3275911, a1..a5 = 0.254829592, -0.284496736, 1.421413741,
-// -1.453152027, 1.061405429.  Here z = |x| / sqrt 2 and the factor 1/2 is
-// folded into the a_i.  The reciprocal and exp2 run on the hardware
-// transcendental unit; the whole evaluation is branch-free (about 20 VALU
-// operations), which matters because it runs once per element of Y_i.
+// -1.453152027, 1.061405429.  Here z = |x| / sqrt 2: p z = (p / sqrt 2) |x|
+// and exp(-z^2) = 2^(-x^2 log2(e) / 2), and the factor 1/2 is folded into the
+// a_i.  The reciprocal and exp2 run on the hardware transcendental unit; the
+// whole evaluation is branch-free (ten VALU operations besides the two
+// transcendentals), which matters because it runs once per element of Y_i.
 __device__ __forceinline__ void phi_parts(float x, float& h, float& e) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, fabsf(x), 1.0f));
   float q = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
   q = fmaf(t, q, 0.5f * 1.421413741f);
   q = fmaf(t, q, 0.5f * -0.284496736f);
   q = fmaf(t, q, 0.5f * 0.254829592f);
   q *= t;
-  e = __builtin_amdgcn_exp2f((z * -1.4426950408889634f) * z);  // exp(-z^2) = exp(-x^2 / 2)
+  e = __builtin_amdgcn_exp2f((x * x) * -0.72134752044448170f);  // exp(-x^2 / 2)
   h = q * e;
 }
 
+// GeLU(x) = x Phi(x) = max(x, 0) - |x| Phi(-|x|): for x >= 0 it is
+// x (1 - Phi(-x)), for x < 0 it is x Phi(x) with Phi(-|x|) = Phi(x).  Written
+// this way the sign case costs one maximum and the last step is one fused
+// multiply-add (|x| is an operand modifier).
 __device__ __forceinline__ float gelu_f32(float x) {
   float h, e;
   phi_parts(x, h, e);
-  return x * (x < 0.0f ? h : 1.0f - h);
+  return fmaf(-fabsf(x), h, fmaxf(x, 0.0f));
 }
 
 // y = GeLU(x) and g = GeLU'(x) = Phi(x) + x phi(x), phi(x) = exp(-x^2/2) / sqrt(2 pi).
@@ -64,7 +74,7 @@ __device__ __forceinline__ void gelu_and_grad_f32(float x, float& y, float& g) {
   float h, e;
   phi_parts(x, h, e);
   const float Phi = x < 0.0f ? h : 1.0f - h;
-  y = x * Phi;
+  y = fmaf(-fabsf(x), h, fmaxf(x, 0.0f));  // as gelu_f32, bit for bit
   g = fmaf(x * 0.3989422804014327f, e, Phi);
 }
 

@@ -237,8 +237,22 @@ struct OperandFrags {
 // columns), every wave reads its FN / 2 gate and FN / 2 up fragments at the
 // same offsets of the two sub-tiles, and the epilogue stores
 // SiLU(gate) * up: a BM x BN / 2 tile of the output.
+// Waves per SIMD to ask the register allocator for: as many as the
+// workgroups that the tile's LDS stages let share a CU bring (two 8-wave
+// workgroups of 72 KB: four waves per SIMD, so at most 128 VGPRs each).  A
+// group sum keeps a second accumulator set, and the training epilogue a
+// second output; both are left to the allocator (at 128 VGPRs they would
+// spill, measured slower than one workgroup per CU).
+constexpr int gemm_waves_per_eu(int EPI, int BM, int BN, int WM, int WN, int NBUF, bool GSUM) {
+  if (GSUM || EPI == kEpiBiasGeluSave) return 1;
+  const int per_cu = (160 * 1024) / (NBUF * (BM + BN) * 64);
+  const int w = per_cu * WM * WN / 4;
+  return w < 1 ? 1 : (w > 4 ? 4 : w);
+}
+
 template <int EPI, int LAYOUT, int BM, int BN, int WM, int WN, int NBUF, bool KTAIL, bool GSUM>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
+__global__ __launch_bounds__(WM* WN * 64, gemm_waves_per_eu(EPI, BM, BN, WM, WN, NBUF, GSUM))
+void gemm_bf16_kernel(GemmParams p) {
   constexpr bool AK = LAYOUT != kTN;  // A K-major
   constexpr bool BK = LAYOUT == kNT;  // B K-major
   constexpr bool DUAL = EPI == kEpiSwiGLU;
@@ -658,13 +672,37 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
       using lds_char = __attribute__((address_space(3))) char;
       lds_char* R = (lds_char*)(uintptr_t)region;
       const int rrow = lane / kLanesPerRow, rcol = (lane % kLanesPerRow) * 16;
-      void* outs[2] = {Cout, aux};
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int c = 0; c < FNO / kFragsPerChunk; ++c) {
-          // final values of the chunk's fragments: v[o][f][gq] (4 columns each)
-          f32x4_t v[kNumOut][kFragsPerChunk][4];
+          // Each group of 4 final values goes to LDS as soon as it is
+          // computed (lane (row l32, half lane / 32) holds columns
+          // 32 f + 8 gq + 4 (lane / 32) .. + 3); the second output of the
+          // training epilogue waits packed in registers until the first has
+          // been read back.
+          u32x2_t second[kNumOut - 1 ? kFragsPerChunk : 1][4];
+          auto put = [&](int f, int gq, f32x4_t x) {
+            lds_char* dst = R + l32 * kRowStride + (32 * f + 8 * gq + hcol) * kElt;
+            if constexpr (kElt == 4) {
+              *(__attribute__((address_space(3))) f32x4_t*)dst = x;
+            } else {
+              *(__attribute__((address_space(3))) u32x2_t*)dst = pack4_bf16(x);
+            }
+          };
+          // Rows back from LDS, whole 128-byte (or 64-byte) row segments to C.
+          auto drain = [&](void* out) {
+            u32x4_t rows[kPasses];
+#pragma unroll
+            for (int t = 0; t < kPasses; ++t)
+              rows[t] = *(__attribute__((address_space(3))) u32x4_t*)(R + (rrow + t * kRowsPerPass) * kRowStride + rcol);
+            char* base = static_cast<char*>(out) +
+                         ((int64_t)(m0 + wm * WTM + i * 32 + rrow) * ldc + n0 + wn * WTNO + c * kFragsPerChunk * 32) *
+                             kElt + rcol;
+#pragma unroll
+            for (int t = 0; t < kPasses; ++t)
+              *reinterpret_cast<u32x4_t*>(base + (int64_t)t * kRowsPerPass * ldc * kElt) = rows[t];
+          };
 #pragma unroll
           for (int f = 0; f < kFragsPerChunk; ++f) {
             const int j = c * kFragsPerChunk + f;
@@ -689,41 +727,22 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
                 float y[4], g[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) gelu_and_grad_f32(a[e], y[e], g[e]);
-                v[0][f][gq] = f32x4_t{y[0], y[1], y[2], y[3]};
-                v[kNumOut - 1][f][gq] = f32x4_t{g[0], g[1], g[2], g[3]};
+                put(f, gq, f32x4_t{y[0], y[1], y[2], y[3]});
+                second[f][gq] = pack4_bf16(f32x4_t{g[0], g[1], g[2], g[3]});
               } else {
-                v[0][f][gq] = a;
+                put(f, gq, a);
               }
             }
           }
-#pragma unroll
-          for (int o = 0; o < kNumOut; ++o) {
-            // lane (row l32, half lane / 32) holds columns 32 f + 8 gq + 4 (lane / 32) .. + 3
+          drain(Cout);
+          if constexpr (kNumOut == 2) {
 #pragma unroll
             for (int f = 0; f < kFragsPerChunk; ++f)
 #pragma unroll
-              for (int gq = 0; gq < 4; ++gq) {
-                lds_char* dst = R + l32 * kRowStride + (32 * f + 8 * gq + hcol) * kElt;
-                const f32x4_t x = v[o][f][gq];
-                if constexpr (kElt == 4) {
-                  *(__attribute__((address_space(3))) f32x4_t*)dst = x;
-                } else {
-                  u32x2_t w;
-                  w[0] = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
-                  w[1] = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
-                  *(__attribute__((address_space(3))) u32x2_t*)dst = w;
-                }
-              }
-            u32x4_t rows[kPasses];
-#pragma unroll
-            for (int t = 0; t < kPasses; ++t)
-              rows[t] = *(__attribute__((address_space(3))) u32x4_t*)(R + (rrow + t * kRowsPerPass) * kRowStride + rcol);
-            char* base = static_cast<char*>(outs[o]) +
-                         ((int64_t)(m0 + wm * WTM + i * 32 + rrow) * ldc + n0 + wn * WTNO + c * kFragsPerChunk * 32) *
-                             kElt + rcol;
-#pragma unroll
-            for (int t = 0; t < kPasses; ++t)
-              *reinterpret_cast<u32x4_t*>(base + (int64_t)t * kRowsPerPass * ldc * kElt) = rows[t];
+              for (int gq = 0; gq < 4; ++gq)
+                *(__attribute__((address_space(3))) u32x2_t*)(R + l32 * kRowStride + (32 * f + 8 * gq + hcol) * kElt) =
+                    second[f][gq];
+            drain(aux);
           }
         }
       }
