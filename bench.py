@@ -613,6 +613,32 @@ def bench_attention(tpm, w, X, fused, args, elt):
     if not bool(torch.isfinite(Z).all()):
         raise RuntimeError("non-finite attention output")
 
+    # The other variant of the same step, timed the same way (bit-identical Z).
+    oflags = (0 if fused else tpm.TP_FUSED_ACCUM) | tpm.TP_CAUSAL
+    ows = torch.empty(max(tpm.tp_attn_workspace_bytes(k, w.B, w.S, H, nh, tpm.TP_BF16, oflags), 1),
+                      dtype=torch.uint8, device=dev)
+    Z2 = torch.empty_like(Z)
+
+    def ostep():
+        tpm.tp_attn_shard_forward(X, Wqkv, bqkv, Wo, w.B, w.S, nh, Z=Z2, workspace=ows, fused=not fused,
+                                  causal=True)
+
+    warm(ostep, args)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ostep()
+    torch.cuda.synchronize()
+    oms = (time.perf_counter() - t0) * 1e3 / args.steps
+    if not torch.equal(Z, Z2):
+        raise RuntimeError("literal and fused attention blocks differ")
+    variants = {args.variant: {"value": round(tflops, 3), "ms_per_step": round(ms, 5)},
+                ("literal" if fused else "fused"): {"value": round(flop / (oms * 1e-3) / 1e12, 3),
+                                                    "ms_per_step": round(oms, 5)}}
+    log("  other variant (%s): %.4f ms/step, %.1f TFLOP/s" % ("literal" if fused else "fused", oms,
+                                                            flop / (oms * 1e-3) / 1e12))
+    del ows, Z2
+
     G = min(k, tpm.TP_MAX_BATCH)
     batches = [(i0, min(G, k - i0)) for i0 in range(0, k, G)]
     QKV = [torch.empty(M, 3 * Hk, dtype=torch.bfloat16, device=dev) for _ in range(G)]
@@ -641,7 +667,7 @@ def bench_attention(tpm, w, X, fused, args, elt):
     return {"metric": "TP-shard attention block forward TFLOP/s (causal; 3 projections + attention)",
             "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
             "pct_of_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2), "heads": nh, "head_dim": d,
-            "roofline": roof,
+            "variants": variants, "roofline": roof,
             "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],
                              "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()}}
 
