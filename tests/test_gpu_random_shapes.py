@@ -1,4 +1,4 @@
-"""GPU parity of the block forward at seeded random shapes (M any size, H and
+"""GPU parity of the block forward and backward at seeded random shapes (M any size, H and
 F/k any multiple of 8, 1 to 6 shards, both element types), literal and fused:
 every output element within the oracle's bound, the relative Frobenius bar,
 and the two variants bit-identical.  The shapes land on every mix of whole
@@ -68,3 +68,63 @@ def test_random_shape_forward(tpm, orc, M, H, Fk, k, dtype):
                            for i in range(k)], axis=1)
     assert_within(Zg, Zr, forward_bound(tolY, Y, V64, k), "Z")
     assert rel_fro(Zg, Zr) <= (1e-2 if dtype == "bf16" else 1e-5)
+
+
+def _bwd_cases(n=12, seed=20261203):
+    rng = np.random.RandomState(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.randint(1, 1200))
+        H = 8 * int(rng.randint(1, 49))
+        Fk = 8 * int(rng.randint(1, 49))
+        k = int(rng.randint(1, 5))
+        dtype = "f32" if rng.rand() < 0.25 else "bf16"
+        bias = bool(rng.rand() < 0.75)
+        if M * H * Fk * k > 40_000_000:
+            continue
+        out.append((M, H, Fk, k, dtype, bias))
+    return out
+
+
+@pytest.mark.parametrize("M,H,Fk,k,dtype,bias", _bwd_cases())
+def test_random_shape_backward(tpm, orc, M, H, Fk, k, dtype, bias):
+    """The block backward (dX, dW_i, db_i, dV_i) at seeded random shapes,
+    literal and fused bit-identical, within the oracle's element bounds."""
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    from test_gpu_backward import backward_bounds
+    say("random backward M=%d H=%d Fk=%d k=%d %s bias=%s" % (M, H, Fk, k, dtype, bias))
+    F = Fk * k
+    seed = M * 17 + H + Fk * 3 + k
+    X = inputs.draw(0, (M, H), 1.0, dtype, seed=seed)
+    W = inputs.draw(1, (H, F), 0.05, dtype, seed=seed)
+    b = inputs.draw(2, (F,), 0.05, dtype, seed=seed) if bias else None
+    V = inputs.draw(3, (F, H), 0.05, dtype, seed=seed)
+    dZ = inputs.draw(4, (M, H), 1.0, dtype, seed=seed)
+    Ws, bs, Vs = inputs.shard_slices(W, b if bias else np.zeros(F, W.dtype), V, k)
+    dev_args = (to_dev(X), [to_dev(w) for w in Ws], [to_dev(x) for x in bs] if bias else None,
+                [to_dev(v) for v in Vs], to_dev(dZ))
+    outs = []
+    for fused in (False, True):
+        dX = torch.empty(M, H, device="cuda")
+        dW = [torch.empty(H, Fk, device="cuda") for _ in range(k)]
+        dV = [torch.empty(Fk, H, device="cuda") for _ in range(k)]
+        db = [torch.empty(Fk, device="cuda") for _ in range(k)] if bias else None
+        tpm.tp_mlp_shard_backward(*dev_args, dX=dX, dW=dW, db=db, dV=dV, fused=fused)
+        outs.append((dX, dW, db, dV))
+    torch.cuda.synchronize()
+    (dX, dW, db, dV), (dX2, dW2, db2, dV2) = outs
+    assert torch.equal(dX, dX2), "fused and literal dX differ"
+    rX, rW, rb, rV = orc.backward(X, W, b, V, dZ, k)
+    bX, bW, bb, bV = backward_bounds(orc, X, W, b, V, dZ, k, dtype)
+    gotW = np.concatenate([f64(from_dev(t)) for t in dW], axis=1)
+    gotV = np.concatenate([f64(from_dev(t)) for t in dV], axis=0)
+    assert_within(f64(from_dev(dX)), rX, bX, "dX")
+    assert_within(gotW, rW, bW, "dW")
+    assert_within(gotV, rV, bV, "dV")
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    for got, ref in ((f64(from_dev(dX)), rX), (gotW, rW), (gotV, rV)):
+        assert rel_fro(got, ref) <= tol
+    if bias:
+        gotb = np.concatenate([f64(from_dev(t)) for t in db])
+        assert_within(gotb, rb, bb, "db")
