@@ -1,8 +1,10 @@
-"""GPU parity of the block forward and backward at seeded random shapes (M any size, H and
-F/k any multiple of 8, 1 to 6 shards, both element types), literal and fused:
-every output element within the oracle's bound, the relative Frobenius bar,
-and the two variants bit-identical.  The shapes land on every mix of whole
-and partial tiles in M, N and K that the fixed cases do not name one by one.
+"""GPU parity at seeded random shapes: the block forward and backward (M any
+size, H and F/k any multiple of 8, 1 to 6 shards, both element types; literal
+and fused bit-identical), the SwiGLU column step, and the attention kernel
+(random sequence lengths, head counts, widths 64 and 128, causal or not).
+Every output element within the oracle's bound and the relative Frobenius
+bar.  The shapes land on mixes of whole and partial tiles (in M, N, K and in
+query and key blocks) that the fixed cases do not name one by one.
 """
 import numpy as np
 import pytest
@@ -128,3 +130,71 @@ def test_random_shape_backward(tpm, orc, M, H, Fk, k, dtype, bias):
     if bias:
         gotb = np.concatenate([f64(from_dev(t)) for t in db])
         assert_within(gotb, rb, bb, "db")
+
+
+def _swiglu_cases(n=12, seed=20261204):
+    rng = np.random.RandomState(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.randint(1, 1500))
+        H = 8 * int(rng.randint(1, 81))
+        Fk = 8 * int(rng.randint(1, 81))
+        dtype = "f32" if rng.rand() < 0.25 else "bf16"
+        if M * H * Fk > 60_000_000:
+            continue
+        out.append((M, H, Fk, dtype))
+    return out
+
+
+@pytest.mark.parametrize("M,H,Fk,dtype", _swiglu_cases())
+def test_random_shape_swiglu_col(tpm, orc, M, H, Fk, dtype):
+    """The SwiGLU column step (two weights, SiLU(X Wg) * (X Wu)) at seeded
+    random shapes, within the oracle's element bounds."""
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    from _helpers import swiglu_bound
+    say("random swiglu_col M=%d H=%d Fk=%d %s" % (M, H, Fk, dtype))
+    inp = inputs.make_swiglu(M=M, H=H, F=Fk, dtype=dtype, std=0.05, seed=M * 3 + H + Fk)
+    X, Wg, Wu = inp["X"], inp["Wg"], inp["Wu"]
+    Y = tpm.tp_swiglu_col(to_dev(X), to_dev(Wg), to_dev(Wu))
+    torch.cuda.synchronize()
+    Yg = f64(from_dev(Y))
+    Yr = orc.swiglu_col(X, Wg, Wu, 1, 0)
+    X64 = f64(X)
+    G, U = X64 @ f64(Wg), X64 @ f64(Wu)
+    assert_within(Yg, Yr, swiglu_bound(X64, f64(Wg), f64(Wu), G, U, Yr, dtype), "Y")
+    assert rel_fro(Yg, Yr) <= (1e-2 if dtype == "bf16" else 1e-5)
+
+
+def _attn_cases(n=12, seed=20261205):
+    rng = np.random.RandomState(seed)
+    out = []
+    while len(out) < n:
+        B = int(rng.randint(1, 4))
+        S = int(rng.randint(1, 700))
+        heads = int(rng.randint(1, 4))
+        d = 64 if rng.rand() < 0.5 else 128
+        causal = bool(rng.rand() < 0.7)
+        std = float(rng.choice([0.5, 1.0, 2.0]))
+        out.append((B, S, heads, d, causal, std))
+    return out
+
+
+@pytest.mark.parametrize("B,S,heads,d,causal,std", _attn_cases())
+def test_random_shape_attention_core(tpm, orc, B, S, heads, d, causal, std):
+    """The attention kernel at seeded random sequence lengths, head counts and
+    widths, causal or not, within the oracle's element bounds."""
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    from _helpers import attn_core_bound
+    say("random attn_core B=%d S=%d heads=%d d=%d causal=%s std=%g" % (B, S, heads, d, causal, std))
+    Hk = heads * d
+    qkv = inputs.draw(inputs.STREAM_X, (B * S, 3 * Hk), std, "bf16", seed=B * 7919 + S * 13 + heads + d)
+    A = torch.full((B * S, Hk), float("nan"), dtype=torch.bfloat16, device="cuda")
+    tpm.tp_attn_core_shards([to_dev(qkv)], [A], B, S, heads, d, causal=causal)
+    torch.cuda.synchronize()
+    Ag = f64(from_dev(A))
+    assert np.all(np.isfinite(Ag))
+    Ar = orc.attn_core(qkv, B, S, heads, d, causal)
+    assert_within(Ag, Ar, attn_core_bound(f64(qkv), Ar, B, S, heads, d, causal), "A")
+    assert rel_fro(Ag, Ar) <= 1e-2
