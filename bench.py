@@ -21,7 +21,9 @@ under "attention".
 
 Prints ONE JSON line (metric, value in TFLOP/s, ms_per_step, roofline of the
 dominant kernel, CPU-oracle baseline, backward) on stdout; diagnostics go to
-stderr.
+stderr.  `value` and ms_per_step come from K steps timed back to back between
+two synchronisations; "step_ms" gives the median, minimum and 90th percentile
+of K further steps timed one by one with HIP events.
 """
 from __future__ import annotations
 
@@ -57,6 +59,29 @@ def warm(step, args):
         torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
+
+
+def step_distribution(step, n: int) -> dict:
+    """n more steps, each between its own pair of HIP events on the stream the
+    steps launch on: median, minimum and 90th percentile of one step (ms)."""
+    import torch
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record(s)
+        step()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return percentiles([e0.elapsed_time(e1) for e0, e1 in ev])
+
+
+def percentiles(ms) -> dict:
+    """Median, minimum and 90th percentile (nearest rank) of a list of times."""
+    t = sorted(ms)
+    n = len(t)
+    med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+    p90 = t[max(0, -(-9 * n // 10) - 1)]
+    return {"median": round(med, 5), "min": round(t[0], 5), "p90": round(p90, 5), "n": n}
 
 
 def parse():
@@ -266,6 +291,8 @@ def main():
         args.steps, ms, tflops, 100 * tflops / PEAK_TFLOPS[w.dtype], w.dtype))
     if not bool(torch.isfinite(Z).all()):
         raise RuntimeError("non-finite output")
+    dist = step_distribution(step, args.steps)
+    log("single steps: median %.4f ms, min %.4f, p90 %.4f" % (dist["median"], dist["min"], dist["p90"]))
 
     # The other variant of the same step, timed the same way (reported beside
     # the headline; bit-identical Z).
@@ -344,7 +371,7 @@ def main():
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded Philox normals, random-init weights)",
-        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2),
+        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "step_ms": dist,
         "config": dict(w.describe(), variant=args.variant, parallelism="tp%d shards on 1 GPU" % w.k),
         "roofline": roof,
         "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],

@@ -58,6 +58,7 @@ __all__ = [
     "tp_sp_reduce_scatter", "tp_mlp_sp_workspace_bytes", "tp_mlp_shard_forward_sp",
     "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward", "TP_CAUSAL",
     "tp_attn_qkv_shards", "tp_attn_core_shards", "tp_attn_workspace_bytes", "tp_attn_shard_forward",
+    "tp_gemm_tiles", "tp_mlp_step_tile", "tp_mlp_col_gelu_shards_tile", "tp_mlp_row_partial_shards_tile",
 ]
 
 TP_F32 = 0
@@ -149,6 +150,14 @@ def lib() -> ctypes.CDLL:
         L.tp_attn_workspace_bytes.restype = sz
         L.tp_attn_shard_forward.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, ci, vp, sz, vp, cu, vp]
         L.tp_attn_shard_forward.restype = ci
+        L.tp_gemm_tiles.argtypes = [ci, ctypes.POINTER(ci)]
+        L.tp_gemm_tiles.restype = ci
+        L.tp_mlp_step_tile.argtypes = [ci, ci, i64, i64, i64]
+        L.tp_mlp_step_tile.restype = ci
+        L.tp_mlp_col_gelu_shards_tile.argtypes = [ci, vp, vp, vp, vp, ci, i64, i64, i64, vp]
+        L.tp_mlp_col_gelu_shards_tile.restype = ci
+        L.tp_mlp_row_partial_shards_tile.argtypes = [ci, vp, vp, vp, ci, i64, i64, i64, cu, vp]
+        L.tp_mlp_row_partial_shards_tile.restype = ci
         for f in (L.tp_mlp_col_gelu_shards, L.tp_mlp_row_partial_shards, L.tp_mlp_grad_act_shards,
                   L.tp_mlp_grad_row_weight_shards, L.tp_mlp_grad_col_weight_shards, L.tp_mlp_grad_input_shards):
             f.restype = ci
@@ -809,4 +818,51 @@ def tp_attn_shard_forward(X, Wqkv, bqkv, Wo, B: int, S: int, n_heads: int, Z=Non
                                        _ptrs(Wo, "Wo"), k, B, S, H, n_heads, dt, _dev(workspace, "workspace"),
                                        workspace.numel(), _dev(Z, "Z"), flags, _stream(stream)),
            "tp_attn_shard_forward")
+    return Z
+
+
+# Tile table of the bf16 GEMM (measurement of the tile choice).
+
+def tp_gemm_tiles():
+    """The bf16 GEMM's tiles: a list of {"bm", "bn", "waves", "stages"}, index = tile id."""
+    L = lib()
+    count = L.tp_gemm_tiles(-1, None)
+    out = []
+    for t in range(count):
+        info = (ctypes.c_int * 4)()
+        L.tp_gemm_tiles(t, info)
+        out.append({"bm": info[0], "bn": info[1], "waves": info[2], "stages": info[3]})
+    return out
+
+
+def tp_mlp_step_tile(step: int, n: int, M: int, H: int, Fk: int) -> int:
+    """The tile the bf16 step runs with: step 0 column (bias + GeLU), 1 row
+    partials, 2 row with the shard sum; n shards of M x H x Fk."""
+    r = lib().tp_mlp_step_tile(step, n, M, H, Fk)
+    _check(min(r, 0), "tp_mlp_step_tile")
+    return r
+
+
+def tp_mlp_col_gelu_shards_tile(tile, X, W, b, Y, stream=None):
+    """tp_mlp_col_gelu_shards (bf16, no G) with tile `tile` of tp_gemm_tiles()."""
+    n = _batch_n(len(W))
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = W[0].shape[-1]
+    _check(lib().tp_mlp_col_gelu_shards_tile(tile, _dev(X, "X"), _ptrs(W, "W"), _ptrs(b, "b"), _ptrs(Y, "Y"),
+                                             n, M, H, Fk, _stream(stream)), "tp_mlp_col_gelu_shards_tile")
+    return Y
+
+
+def tp_mlp_row_partial_shards_tile(tile, Y, V, Z, sum_shards=False, accumulate=False, stream=None):
+    """tp_mlp_row_partial_shards (bf16) with tile `tile` of tp_gemm_tiles()."""
+    n = _batch_n(len(Y))
+    Fk = Y[0].shape[-1]
+    M = Y[0].numel() // Fk if Fk else 0
+    H = V[0].shape[-1]
+    Zl = list(Z) + [None] * (n - len(Z)) if sum_shards else list(Z)
+    flags = (TP_SUM_SHARDS if sum_shards else 0) | (TP_ACCUMULATE if accumulate else 0)
+    _check(lib().tp_mlp_row_partial_shards_tile(tile, _ptrs(Y, "Y"), _ptrs(V, "V"), _ptrs(Zl, "Z", allow_none=True),
+                                                n, M, Fk, H, flags, _stream(stream)),
+           "tp_mlp_row_partial_shards_tile")
     return Z

@@ -131,8 +131,18 @@ GemmBatch single_batch(const GemmArgs& g);
 // 256x256 GEMM that adds into C, 2.14 ms per shard for the 128x256 group sum).
 constexpr int64_t kSequentialSumTiles = 1024;
 
+static bool sequential_sum(const GemmBatch& b) {
+  return b.group_sum && b.groups > 1 && b.K % 32 == 0 && tiles_of(0, b.M, b.N) >= kSequentialSumTiles;
+}
+
+int gemm_bf16_batch_tile(const GemmBatch& b) {
+  if (sequential_sum(b)) return pick_bf16_tile(b.layout, b.M, b.N, b.K, 1, false);
+  if (b.epi == kEpiSwiGLU) return pick_swiglu_tile(b.M, b.N, b.K, b.groups);
+  return pick_bf16_tile(b.layout, b.M, b.N, b.K, b.groups, b.group_sum);
+}
+
 hipError_t launch_gemm_bf16_batch(const GemmBatch& b, hipStream_t s) {
-  if (b.group_sum && b.groups > 1 && b.K % 32 == 0 && tiles_of(0, b.M, b.N) >= kSequentialSumTiles) {
+  if (sequential_sum(b)) {
     for (int g = 0; g < b.groups; ++g) {
       GemmArgs a{b.A[g], b.B[g], nullptr, nullptr, b.C[0], nullptr, b.M, b.N, b.K, b.lda, b.ldb, b.ldc,
                  b.layout, g == 0 ? b.epi : kEpiAccumF32};
@@ -141,9 +151,22 @@ hipError_t launch_gemm_bf16_batch(const GemmBatch& b, hipStream_t s) {
     }
     return hipSuccess;
   }
-  if (b.epi == kEpiSwiGLU) return launch_gemm_bf16_batch_tile(pick_swiglu_tile(b.M, b.N, b.K, b.groups), b, s);
-  return launch_gemm_bf16_batch_tile(
-      pick_bf16_tile(b.layout, b.M, b.N, b.K, b.groups, b.group_sum), b, s);
+  return launch_gemm_bf16_batch_tile(gemm_bf16_batch_tile(b), b, s);
+}
+
+int gemm_bf16_tile_count() { return kNumTiles; }
+
+void gemm_bf16_tile_shape(int tile, int info[4]) {
+  const TileCfg& c = kTiles[tile];
+  info[0] = c.bm;
+  info[1] = c.bn;
+  info[2] = c.wm * c.wn;
+  info[3] = c.nbuf;
+}
+
+bool gemm_bf16_tile_can_run(int tile, const GemmBatch& b) {
+  return tile >= 0 && tile < kNumTiles && b.groups >= 1 && b.groups <= kMaxGroups &&
+         instantiated(b.layout, tile, b.K % 32 != 0, b.group_sum, b.epi);
 }
 
 GemmBatch single_batch(const GemmArgs& g) {

@@ -88,24 +88,33 @@ GemmBatch batch(int n, tpmlp::Layout layout, tpmlp::Epilogue epi, int64_t M, int
   return b;
 }
 
-int run(const GemmBatch& b, int dtype, hipStream_t s) {
+// tile >= 0 (bf16 only, checked by the caller): that tile of the GEMM's table
+// instead of the one the library picks.
+int run(const GemmBatch& b, int dtype, hipStream_t s, int tile = -1) {
+  if (tile >= 0) return hip_status(tpmlp::launch_gemm_bf16_batch_tile(tile, b, s));
   return hip_status(dtype == TP_BF16 ? tpmlp::launch_gemm_bf16_batch(b, s)
                                      : tpmlp::launch_gemm_f32_batch(b, s));
 }
 
 // The steps, after validation; arrays hold the n shards of one batch.
 // Y_i (and G_i) = act(X W_i + b_i): [M, H] x [H, Fk], both row-major.
-int col_steps(const void* X, const void* const* W, const void* const* b, void* const* Y,
-              void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype, hipStream_t s) {
+GemmBatch col_batch(const void* X, const void* const* W, const void* const* b, void* const* Y,
+                    void* const* G, int n, int64_t M, int64_t H, int64_t Fk) {
   GemmBatch g = batch(n, tpmlp::kNN, G ? tpmlp::kEpiBiasGeluSave : tpmlp::kEpiBiasGelu, M, Fk, H, H, Fk);
   for (int i = 0; i < n; ++i) {
     g.A[i] = X;
-    g.B[i] = W[i];
+    g.B[i] = W ? W[i] : nullptr;
     g.bias[i] = b ? b[i] : nullptr;
-    g.C[i] = Y[i];
+    g.C[i] = Y ? Y[i] : nullptr;
     g.aux[i] = G ? G[i] : nullptr;
   }
-  return run(g, dtype, s);
+  return g;
+}
+
+int col_steps(const void* X, const void* const* W, const void* const* b, void* const* Y,
+              void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype, hipStream_t s,
+              int tile = -1) {
+  return run(col_batch(X, W, b, Y, G, n, M, H, Fk), dtype, s, tile);
 }
 
 // SwiGLU column step: Y_i = SiLU(X Wg_i) * (X Wu_i), two [H, Fk] row-major
@@ -151,17 +160,23 @@ int check_attn(int64_t B, int64_t S, int64_t H, int n_heads, int k) {
 
 // Z_i (+)= Y_i V_i: [M, Fk] x [Fk, H], one output per shard (sum == false),
 // or Z (+)= sum_i Y_i V_i in shard order into Z[0] (sum == true).
-int row_steps(const void* const* Y, const void* const* V, float* const* Z, int n, bool sum,
-              int64_t M, int64_t Fk, int64_t H, int dtype, bool accumulate, hipStream_t s) {
+GemmBatch row_batch(const void* const* Y, const void* const* V, float* const* Z, int n, bool sum,
+                    int64_t M, int64_t Fk, int64_t H, bool accumulate) {
   GemmBatch g = batch(n, tpmlp::kNN, accumulate ? tpmlp::kEpiAccumF32 : tpmlp::kEpiStoreF32, M, H, Fk,
                       Fk, H);
   g.group_sum = sum;
   for (int i = 0; i < n; ++i) {
-    g.A[i] = Y[i];
-    g.B[i] = V[i];
-    g.C[i] = sum ? Z[0] : Z[i];
+    g.A[i] = Y ? Y[i] : nullptr;
+    g.B[i] = V ? V[i] : nullptr;
+    g.C[i] = Z ? (sum ? Z[0] : Z[i]) : nullptr;
   }
-  return run(g, dtype, s);
+  return g;
+}
+
+int row_steps(const void* const* Y, const void* const* V, float* const* Z, int n, bool sum,
+              int64_t M, int64_t Fk, int64_t H, int dtype, bool accumulate, hipStream_t s,
+              int tile = -1) {
+  return run(row_batch(Y, V, Z, n, sum, M, Fk, H, accumulate), dtype, s, tile);
 }
 
 // dA_i = (dZ V_i^T) * G_i: [M, H] x ([Fk, H] read as its transpose).
@@ -314,11 +329,15 @@ const char* tp_status_string(int status) {
   }
 }
 
-int tp_mlp_version(void) { return 130; }
+int tp_mlp_version(void) { return 131; }
 
-int tp_mlp_col_gelu_shards(const void* X, const void* const* W, const void* const* b, void* const* Y,
-                           void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype,
-                           void* stream) {
+namespace {
+
+// tp_mlp_col_gelu_shards after the tile argument's own checks (tile < 0: the
+// library's choice).
+int col_shards(const void* X, const void* const* W, const void* const* b, void* const* Y,
+               void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype, void* stream,
+               int tile) {
   int st = check_dtype(dtype);
   if (st) return st;
   if ((st = check_dims(M, H, Fk))) return st;
@@ -339,7 +358,15 @@ int tp_mlp_col_gelu_shards(const void* X, const void* const* W, const void* cons
     if (G) out.add(G[i], size_t(M) * size_t(Fk) * e);
   }
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return col_steps(X, W, b, Y, G, n, M, H, Fk, dtype, static_cast<hipStream_t>(stream));
+  return col_steps(X, W, b, Y, G, n, M, H, Fk, dtype, static_cast<hipStream_t>(stream), tile);
+}
+
+}  // namespace
+
+int tp_mlp_col_gelu_shards(const void* X, const void* const* W, const void* const* b, void* const* Y,
+                           void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype,
+                           void* stream) {
+  return col_shards(X, W, b, Y, G, n, M, H, Fk, dtype, stream, -1);
 }
 
 int tp_mlp_col_gelu(const void* X, const void* W_i, const void* b_i, void* Y_i, int64_t M,
@@ -354,9 +381,10 @@ int tp_mlp_col_gelu_save(const void* X, const void* W_i, const void* b_i, void* 
                                 stream);
 }
 
-int tp_mlp_row_partial_shards(const void* const* Y, const void* const* V, float* const* Z, int n,
-                              int64_t M, int64_t Fk, int64_t H, int dtype, unsigned flags,
-                              void* stream) {
+namespace {
+
+int row_shards(const void* const* Y, const void* const* V, float* const* Z, int n, int64_t M,
+               int64_t Fk, int64_t H, int dtype, unsigned flags, void* stream, int tile) {
   int st = check_dtype(dtype);
   if (st) return st;
   if (flags & ~(TP_ACCUMULATE | TP_SUM_SHARDS)) return TP_ERR_FLAGS;
@@ -377,7 +405,15 @@ int tp_mlp_row_partial_shards(const void* const* Y, const void* const* V, float*
   }
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
   return row_steps(Y, V, Z, n, sum, M, Fk, H, dtype, (flags & TP_ACCUMULATE) != 0,
-                   static_cast<hipStream_t>(stream));
+                   static_cast<hipStream_t>(stream), tile);
+}
+
+}  // namespace
+
+int tp_mlp_row_partial_shards(const void* const* Y, const void* const* V, float* const* Z, int n,
+                              int64_t M, int64_t Fk, int64_t H, int dtype, unsigned flags,
+                              void* stream) {
+  return row_shards(Y, V, Z, n, M, Fk, H, dtype, flags, stream, -1);
 }
 
 int tp_mlp_row_partial(const void* Y_i, const void* V_i, float* Z_i, int64_t M, int64_t Fk,
@@ -984,6 +1020,57 @@ int tp_mlp_shard_backward(const void* X, const void* const* W, const void* const
   }
   if (M > 0 && !fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, dX, M * H, s));
   return TP_OK;
+}
+
+int tp_gemm_tiles(int tile, int* info) {
+  const int count = tpmlp::gemm_bf16_tile_count();
+  if (tile >= 0 && tile < count && info) tpmlp::gemm_bf16_tile_shape(tile, info);
+  return count;
+}
+
+namespace {
+
+// The batch of a bf16 forward step for the tile queries (shapes only).
+int step_batch(int step, int n, int64_t M, int64_t H, int64_t Fk, unsigned flags, GemmBatch& g) {
+  int st = check_dims(M, H, Fk);
+  if (st) return st;
+  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
+  switch (step) {
+    case 0: g = col_batch(nullptr, nullptr, nullptr, nullptr, nullptr, n, M, H, Fk); return TP_OK;
+    case 1:
+    case 2:
+      if (flags & ~TP_ACCUMULATE) return TP_ERR_FLAGS;
+      g = row_batch(nullptr, nullptr, nullptr, n, step == 2, M, Fk, H, (flags & TP_ACCUMULATE) != 0);
+      return TP_OK;
+    default: return TP_ERR_SHAPE;
+  }
+}
+
+}  // namespace
+
+int tp_mlp_step_tile(int step, int n, int64_t M, int64_t H, int64_t Fk) {
+  GemmBatch g;
+  const int st = step_batch(step, n, M, H, Fk, 0, g);
+  return st ? st : tpmlp::gemm_bf16_batch_tile(g);
+}
+
+int tp_mlp_col_gelu_shards_tile(int tile, const void* X, const void* const* W, const void* const* b,
+                                void* const* Y, int n, int64_t M, int64_t H, int64_t Fk, void* stream) {
+  GemmBatch g;
+  const int st = step_batch(0, n, M, H, Fk, 0, g);
+  if (st) return st;
+  if (!tpmlp::gemm_bf16_tile_can_run(tile, g)) return TP_ERR_SHAPE;
+  return col_shards(X, W, b, Y, nullptr, n, M, H, Fk, TP_BF16, stream, tile);
+}
+
+int tp_mlp_row_partial_shards_tile(int tile, const void* const* Y, const void* const* V, float* const* Z,
+                                   int n, int64_t M, int64_t Fk, int64_t H, unsigned flags, void* stream) {
+  if (flags & ~(TP_ACCUMULATE | TP_SUM_SHARDS)) return TP_ERR_FLAGS;
+  GemmBatch g;
+  const int st = step_batch((flags & TP_SUM_SHARDS) ? 2 : 1, n, M, H, Fk, flags & TP_ACCUMULATE, g);
+  if (st) return st;
+  if (!tpmlp::gemm_bf16_tile_can_run(tile, g)) return TP_ERR_SHAPE;
+  return row_shards(Y, V, Z, n, M, Fk, H, TP_BF16, flags, stream, tile);
 }
 
 }  // extern "C"

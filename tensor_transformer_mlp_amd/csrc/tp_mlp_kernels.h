@@ -69,6 +69,18 @@ struct GemmBatch {
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_bf16_batch(const GemmBatch& b, hipStream_t s);
 
+// The bf16 GEMM's tile table, for measuring the tile choice: the number of
+// tiles; tile t's BM, BN, waves per workgroup and LDS stages; the tile a batch
+// runs with; whether tile t is compiled for a batch's layout, epilogue, group
+// sum and K; and the batch launched with tile t (every tile gives the same
+// results, bit for bit: each output element is accumulated over K in the
+// same order).
+int gemm_bf16_tile_count();
+void gemm_bf16_tile_shape(int tile, int info[4]);
+int gemm_bf16_batch_tile(const GemmBatch& b);
+bool gemm_bf16_tile_can_run(int tile, const GemmBatch& b);
+hipError_t launch_gemm_bf16_batch_tile(int tile, const GemmBatch& b, hipStream_t s);
+
 // float32 operands, float32 accumulate (same rules).  Batches run group by
 // group (a group sum accumulates into C[0] in group order).
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);

@@ -49,7 +49,8 @@ def test_exports_every_declared_symbol(L):
                      "tp_sp_reduce_scatter", "tp_mlp_sp_workspace_bytes", "tp_mlp_shard_forward_sp",
                      "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward",
                      "tp_attn_qkv_shards", "tp_attn_core_shards", "tp_attn_workspace_bytes",
-                     "tp_attn_shard_forward"}
+                     "tp_attn_shard_forward", "tp_gemm_tiles", "tp_mlp_step_tile",
+                     "tp_mlp_col_gelu_shards_tile", "tp_mlp_row_partial_shards_tile"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -581,3 +582,79 @@ def test_attention_errors(L):
     assert f(*a) == c["TP_ERR_ALIAS"]
     a = base(); a[6] = 0
     assert f(*a) == c["TP_OK"]
+
+
+def test_tile_table_and_choice(L):
+    import tensor_transformer_mlp_amd as tpm
+    tiles = tpm.tp_gemm_tiles()
+    assert len(tiles) == L.tp_gemm_tiles(-1, None) >= 2
+    for t in tiles:
+        assert t["bm"] in (128, 256) and t["bn"] in (128, 256)
+        assert t["waves"] in (4, 8) and 3 <= t["stages"] <= 6
+        # LDS: the stages of one workgroup fit the 160 KB of a CU
+        assert t["stages"] * (t["bm"] + t["bn"]) * 64 <= 160 * 1024
+    info = (ctypes.c_int * 4)(7, 7, 7, 7)
+    assert L.tp_gemm_tiles(len(tiles), info) == len(tiles) and list(info) == [7, 7, 7, 7]
+    big = [i for i, t in enumerate(tiles) if t["bm"] == t["bn"] == 256]
+    # the choices the tile rule documents: 4 gpt2_small shards (768 workgroups of
+    # 128 x 256) and 8 llama7b shards (256 x 256, at least two rounds of the CUs)
+    for step in (0, 1, 2):
+        t = tpm.tp_mlp_step_tile(step, 4, 8192, 768, 768)
+        assert (tiles[t]["bm"], tiles[t]["bn"]) == (128, 256), step
+    assert tpm.tp_mlp_step_tile(0, 8, 8192, 4096, 2048) in big
+    assert tpm.tp_mlp_step_tile(1, 8, 8192, 4096, 2048) in big
+    # a group sum keeps two accumulator sets: never a 256 x 256 tile of 8 waves,
+    # unless the sum runs shard by shard (32768 x 8192 outputs)
+    assert tpm.tp_mlp_step_tile(2, 8, 8192, 4096, 2048) not in big
+    assert tpm.tp_mlp_step_tile(2, 8, 32768, 8192, 4096) in big
+    # K = H not a multiple of 32: the ragged-K tile for any shape
+    assert len({tpm.tp_mlp_step_tile(0, n, M, 200, 512) for n in (1, 4) for M in (64, 8192)}) == 1
+
+
+def test_tile_hook_errors(L):
+    c = _header_constants()
+    st = L.tp_mlp_step_tile
+    assert st(3, 4, 64, 64, 64) == c["TP_ERR_SHAPE"]
+    assert st(0, 0, 64, 64, 64) == c["TP_ERR_SHAPE"]
+    assert st(0, 17, 64, 64, 64) == c["TP_ERR_SHAPE"]
+    assert st(1, 4, 64, 60, 64) == c["TP_ERR_SHAPE"]
+    count = L.tp_gemm_tiles(-1, None)
+    arr = lambda *xs: (ctypes.c_void_p * len(xs))(*xs)
+    col = L.tp_mlp_col_gelu_shards_tile
+    X = _p(0)
+    W, b, Y = arr(P * 2, P * 3), arr(P * 4, P * 5), arr(P * 6, P * 7)
+    ok = lambda: [0, X, W, b, Y, 2, 64, 256, 128, None]
+    for bad in (-1, count, 1000):
+        a = ok(); a[0] = bad
+        assert col(*a) == c["TP_ERR_SHAPE"], bad
+    a = ok(); a[7] = 200          # K = H = 200: only the ragged-K tile runs
+    ragged = L.tp_mlp_step_tile(0, 2, 64, 200, 128)
+    for t in range(count):
+        if t != ragged:
+            a[0] = t
+            assert col(*a) == c["TP_ERR_SHAPE"], t
+    a = ok(); a[1] = None
+    assert col(*a) == c["TP_ERR_NULL"]
+    a = ok(); a[4] = arr(P * 6, P * 2)    # Y[1] over W[0]
+    assert col(*a) == c["TP_ERR_ALIAS"]
+    a = ok(); a[6] = 0
+    assert col(*a) == c["TP_OK"]
+    row = L.tp_mlp_row_partial_shards_tile
+    Yr, V, Z = arr(P * 2, P * 3), arr(P * 4, P * 5), arr(P * 6, P * 7)
+    okr = lambda: [0, Yr, V, Z, 2, 64, 128, 256, 0, None]
+    a = okr(); a[8] = 8
+    assert row(*a) == c["TP_ERR_FLAGS"]
+    a = okr(); a[0] = count
+    assert row(*a) == c["TP_ERR_SHAPE"]
+    tiles = [(ctypes.c_int * 4)() for _ in range(count)]
+    for t in range(count):
+        L.tp_gemm_tiles(t, tiles[t])
+    for t in range(count):     # the shard sum needs two accumulator sets per wave
+        a = okr(); a[0] = t; a[8] = 4
+        frags = (tiles[t][0] // 32) * (tiles[t][1] // 32) // tiles[t][2]
+        if frags > 4:
+            assert row(*a) == c["TP_ERR_SHAPE"], t
+    a = okr(); a[3] = arr(None, P * 7)
+    assert row(*a) == c["TP_ERR_NULL"]
+    a = okr(); a[5] = 0
+    assert row(*a) == c["TP_OK"]

@@ -1,6 +1,6 @@
-"""Host logic of bench.py (no GPU): the one-GPU refusal, the algorithmic
-bytes and flops of each kernel kind against their closed forms at the
-gpt2_small shapes, the roofline classification (left or right of the bf16
+"""Host logic of bench.py (no GPU): the one-GPU refusal, the per-step
+percentiles, the algorithmic bytes and flops of each kernel kind against
+their closed forms at the gpt2_small shapes, the roofline classification (left or right of the bf16
 ridge, 2516.6 TFLOP/s over 8 TB/s = 315 flop/byte), and the guard that drops
 the measured HBM traffic once the kernel source differs from the one the
 counters were taken on."""
@@ -84,3 +84,14 @@ def test_traffic_is_dropped_when_the_kernel_source_changed(bench, monkeypatch):
     assert bench.measured_traffic(workload, variant, "no_such_kind") is None
     monkeypatch.setattr(prof, "kernel_source_sha256", lambda: "0" * 64)
     assert bench.measured_traffic(workload, variant, kind) is None
+
+
+def test_step_percentiles(bench):
+    # median of an even count is the mean of the middle two; p90 is the
+    # nearest-rank 90th percentile (the ceil(0.9 n)-th smallest)
+    assert bench.percentiles([5.0, 1.0, 2.0, 3.0, 4.0]) == {"median": 3.0, "min": 1.0, "p90": 5.0, "n": 5}
+    assert bench.percentiles([float(i) for i in range(10, 0, -1)]) == {"median": 5.5, "min": 1.0, "p90": 9.0,
+                                                                          "n": 10}
+    t = [0.1] * 95 + [0.5] * 5
+    assert bench.percentiles(t)["p90"] == 0.1 and bench.percentiles(t)["median"] == 0.1
+    assert bench.percentiles([0.25]) == {"median": 0.25, "min": 0.25, "p90": 0.25, "n": 1}
