@@ -63,10 +63,15 @@ def warm(step, args):
 
 def step_distribution(step, n: int) -> dict:
     """n more steps, each between its own pair of HIP events on the stream the
-    steps launch on: median, minimum and 90th percentile of one step (ms)."""
+    steps launch on, behind a spin kernel that keeps the GPU busy while the
+    host enqueues them (so the pairs time the GPU, not the host): median,
+    minimum and 90th percentile of one step (ms)."""
     import torch
     s = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    spin = getattr(torch.cuda, "_sleep", None)
+    if spin is not None:
+        spin(max(3_000_000, 200_000 * n))
     for e0, e1 in ev:
         e0.record(s)
         step()
