@@ -23,7 +23,8 @@ Prints ONE JSON line (metric, value in TFLOP/s, ms_per_step, roofline of the
 dominant kernel, CPU-oracle baseline, backward) on stdout; diagnostics go to
 stderr.  `value` and ms_per_step come from K steps timed back to back between
 two synchronisations; "step_ms" gives the median, minimum and 90th percentile
-of K further steps timed one by one with HIP events.
+of K further steps timed one by one with HIP events, and "gpu_state" the
+socket power and GFX clocks amd-smi reads while the step repeats.
 """
 from __future__ import annotations
 
@@ -80,6 +81,61 @@ def step_distribution(step, n: int) -> dict:
     return percentiles([e0.elapsed_time(e1) for e0, e1 in ev])
 
 
+def parse_amd_smi(text: str) -> dict | None:
+    """Socket power (W) and the GFX clocks (MHz; one per XCD) from the text of
+    `amd-smi metric -c -p`."""
+    import re
+    power = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)
+    clocks = [float(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", text)]
+    if not power and not clocks:
+        return None
+    out = {"socket_power_w": float(power.group(1)) if power else None}
+    if clocks:
+        out.update({"gfx_clock_mhz_mean": round(sum(clocks) / len(clocks), 1), "gfx_clock_mhz_min": min(clocks),
+                    "gfx_clock_mhz_max": max(clocks), "gfx_clock_domains": len(clocks)})
+    return out
+
+
+def gpu_state_during(step, seconds: float):
+    """The step repeats on the GPU for `seconds` while a child process reads
+    the socket power and clocks with amd-smi halfway through (None if amd-smi
+    is missing or prints nothing usable)."""
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if seconds <= 0 or not os.path.exists(exe):
+        return None
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    bus = getattr(props, "pci_bus_id", None)
+    target = "%04x:%02x:%02x.0" % (getattr(props, "pci_domain_id", 0), bus, getattr(props, "pci_device_id", 0)) \
+        if bus is not None else "0"
+    got = {}
+
+    def probe():
+        time.sleep(seconds / 2)
+        for g in ([target, "0"] if target != "0" else ["0"]):
+            try:
+                r = subprocess.run([exe, "metric", "-c", "-p", "-g", g], capture_output=True, text=True, timeout=30)
+            except (OSError, subprocess.TimeoutExpired):
+                continue
+            parsed = parse_amd_smi(r.stdout)
+            if parsed:
+                got.update(parsed, gpu=g)
+                return
+
+    th = threading.Thread(target=probe)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while th.is_alive() or time.perf_counter() < t_end:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    th.join()
+    return got or None
+
+
 def percentiles(ms) -> dict:
     """Median, minimum and 90th percentile (nearest rank) of a list of times."""
     t = sorted(ms)
@@ -94,6 +150,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--power-seconds", type=float, default=2.0,
+                    help="after the timed steps, repeat the step this long while amd-smi (a child process) reads "
+                         "the socket power and GFX clocks; 0 disables")
     ap.add_argument("--settle-seconds", type=float, default=0.5,
                     help="before each leg's warmup steps, repeat its step for this long so that the GPU's clock "
                          "has left its idle state (untimed; 0 disables)")
@@ -298,6 +357,10 @@ def main():
         raise RuntimeError("non-finite output")
     dist = step_distribution(step, args.steps)
     log("single steps: median %.4f ms, min %.4f, p90 %.4f" % (dist["median"], dist["min"], dist["p90"]))
+    gpu_state = gpu_state_during(step, args.power_seconds)
+    if gpu_state:
+        log("amd-smi during the steps: %s W, GFX clock %s MHz (mean of %s domains)" % (
+            gpu_state.get("socket_power_w"), gpu_state.get("gfx_clock_mhz_mean"), gpu_state.get("gfx_clock_domains")))
 
     # The other variant of the same step, timed the same way (reported beside
     # the headline; bit-identical Z).
@@ -376,7 +439,7 @@ def main():
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded Philox normals, random-init weights)",
-        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "step_ms": dist,
+        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "step_ms": dist, "gpu_state": gpu_state,
         "config": dict(w.describe(), variant=args.variant, parallelism="tp%d shards on 1 GPU" % w.k),
         "roofline": roof,
         "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],

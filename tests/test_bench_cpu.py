@@ -95,3 +95,26 @@ def test_step_percentiles(bench):
     t = [0.1] * 95 + [0.5] * 5
     assert bench.percentiles(t)["p90"] == 0.1 and bench.percentiles(t)["median"] == 0.1
     assert bench.percentiles([0.25]) == {"median": 0.25, "min": 0.25, "p90": 0.25, "n": 1}
+
+
+def test_amd_smi_parse(bench):
+    text = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1007 W
+        GFX_VOLTAGE: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 2023 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        GFX_1:
+            CLK: 1979 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        MEM_0:
+            CLK: 1900 MHz
+"""
+    st = bench.parse_amd_smi(text)
+    assert st == {"socket_power_w": 1007.0, "gfx_clock_mhz_mean": 2001.0, "gfx_clock_mhz_min": 2023.0 - 44,
+                  "gfx_clock_mhz_max": 2023.0, "gfx_clock_domains": 2}
+    assert bench.parse_amd_smi("ERROR: no devices") is None
