@@ -7,9 +7,12 @@
 // head h at columns h D .. h D + D - 1, its key at Hk + h D, its value at
 // 2 Hk + h D.  Output: A [B S, Hk], head h at columns h D.
 //
-// One workgroup = 4 waves = 128 queries of one (sequence, head); each wave
-// owns 32 queries and walks the keys in blocks of 64 (causal: up to its
-// diagonal), with the online softmax (running maximum m and sum l per query):
+// One workgroup = 4 waves = 128 QG queries of one (sequence, head); each wave
+// owns QG groups of 32 queries (QG = 1 or 2) and walks the keys in blocks of
+// 64 (causal: up to its last query), with the online softmax (running maximum
+// m and sum l per query).  Every K and V fragment a wave reads from LDS feeds
+// the MFMAs of all its query groups, so QG = 2 halves the LDS reads per
+// score:
 //   S^T = K Q^T    (keys x queries) on v_mfma_f32_32x32x16_bf16, K as the
 //                  instruction's row operand, so every lane holds one query's
 //                  scores and the softmax is lane-local (the two half-waves
@@ -42,10 +45,10 @@ struct AttnParams {
   AttnPtrs t;
   int groups;
   int B, S, heads;  // heads of one shard
-  int nqb;          // query blocks of 128 per sequence
+  int nqb;          // query blocks of kBQ * QG per sequence
 };
 
-constexpr int kBQ = 128, kBK = 64;
+constexpr int kBQ = 128, kBK = 64;  // queries per workgroup and query group; keys per block
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -64,7 +67,7 @@ __device__ __forceinline__ int swz(int key) {
   else return (key >> 1) & 7;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int QG>
 __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
   constexpr int ROW = 2 * D;                 // bytes per key row in LDS
   constexpr int TILE = kBK * ROW;            // one K or V block
@@ -96,19 +99,23 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
-  const int q0 = qb * kBQ;
-  const int qq = q0 + 32 * wave + l32;  // this lane's query
+  const int q0 = qb * kBQ * QG;
+  const int qw = q0 + 32 * QG * wave;  // this wave's first query
+  int qq[QG];                          // this lane's query in each group
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) qq[qg] = qw + 32 * qg + l32;
 
   // Query fragments (B operand of S^T = K Q^T): dims 16 j + 8 h2 .. + 7.
-  bf16x8_t qf[KS];
-  {
-    const bool ok = qq < S;
-    const uint16_t* qrow = seq + (int64_t)(ok ? qq : 0) * ld + head * D + 8 * h2;
+  bf16x8_t qf[QG][KS];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const bool ok = qq[qg] < S;
+    const uint16_t* qrow = seq + (int64_t)(ok ? qq[qg] : 0) * ld + head * D + 8 * h2;
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
       u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
       if (ok) v = *reinterpret_cast<const u32x4_t*>(qrow + 16 * j);
-      qf[j] = __builtin_bit_cast(bf16x8_t, v);
+      qf[qg][j] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
@@ -159,16 +166,25 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
       }
   }
 
-  f32x16_t acc[DT];
+  f32x16_t acc[QG][DT];
+  float m_run[QG], l_run[QG];
 #pragma unroll
-  for (int t = 0; t < DT; ++t)
+  for (int qg = 0; qg < QG; ++qg) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
-  float m_run = -1e30f, l_run = 0.f;
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[qg][t][e] = 0.f;
+    m_run[qg] = -1e30f;
+    l_run[qg] = 0.f;
+  }
   const float c2 = 1.4426950408889634f / __builtin_sqrtf((float)D);  // log2(e) / sqrt(D)
 
-  const int kend = CAUSAL ? min(q0 + kBQ, S) : S;
+  const int kend = CAUSAL ? min(q0 + kBQ * QG, S) : S;
   const int nb = (kend + kBK - 1) / kBK;
+  // Causal: blocks past this wave's last query are skipped (every score in
+  // them would be masked, changing nothing); the wave still joins the loads
+  // and barriers of the workgroup.
+  const int kwave = CAUSAL ? qw + 32 * QG - 1 : S;
 
   using lds_frag = const __attribute__((address_space(3))) bf16x8_t;
   using lds_half = __attribute__((address_space(3))) i16x4_t;
@@ -178,23 +194,26 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
   // overlap instead of adding up.
   auto block = [&](auto sset, int k0) {
     constexpr int SB = decltype(sset)::value * STAGE;
-    // S^T for the 64 keys: two 32-key tiles.
-    f32x16_t s[2];
+    // S^T for the 64 keys: two 32-key tiles per query group.
+    f32x16_t s[QG][2];
     bf16x8_t kf[2][KS];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < KS; ++j) kf[u][j] = *(lds_frag*)(uintptr_t)(kaddr[j] + SB + u * 32 * ROW);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[u][e] = 0.f;
+      for (int qg = 0; qg < QG; ++qg) {
 #pragma unroll
-      for (int j = 0; j < KS; ++j) s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[u][j], qf[j], s[u], 0, 0, 0);
-    }
+        for (int e = 0; e < 16; ++e) s[qg][u][e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+          s[qg][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[u][j], qf[qg][j], s[qg][u], 0, 0, 0);
+      }
     // every K fragment read first, then the score MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS * QG, 0);
     // V^T fragments of the first k-step, read while the softmax runs.
     bf16x8_t vf[2][DT];
     auto read_v = [&](int jj, bf16x8_t* dst) {
@@ -208,48 +227,51 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
     read_v(0, vf[0]);
     // Mask, block maximum of the raw scores (lane pair l, l ^ 32 hold one
     // query); the running maximum m is kept in base-2 units, m = max s c2.
-    const bool edge = k0 + kBK > S || (CAUSAL && k0 + kBK - 1 > q0 + 32 * wave);
-    if (edge) {
+    const bool edge = k0 + kBK > S || (CAUSAL && k0 + kBK - 1 > qw);
+    bf16x8_t pf[QG][4];
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      if (edge) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int kk = k0 + 32 * u + 8 * (e >> 2) + 4 * h2 + (e & 3);
+            if (kk >= S || (CAUSAL && kk > qq[qg])) s[qg][u][e] = -__builtin_inff();
+          }
+      }
+      float mx = -1e30f;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kk = k0 + 32 * u + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          if (kk >= S || (CAUSAL && kk > qq)) s[u][e] = -__builtin_inff();
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qg][u][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[qg], mx * c2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_new);
+      m_run[qg] = m_new;
+      // p = 2^(s c2 - m), one fused multiply-add per score; a masked score
+      // (-inf) gives 0.
+      float psum = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        u32x4_t pk;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int e = 8 * (jj & 1) + 2 * e2;
+          const float a0 = __builtin_amdgcn_exp2f(fmaf(s[qg][jj >> 1][e], c2, -m_new));
+          const float a1 = __builtin_amdgcn_exp2f(fmaf(s[qg][jj >> 1][e + 1], c2, -m_new));
+          psum += a0 + a1;
+          pk[e2] = pack_bf16x2(a0, a1);
         }
-    }
-    float mx = -1e30f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    // p = 2^(s c2 - m), one fused multiply-add per score; a masked score
-    // (-inf) gives 0.
-    float psum = 0.f;
-    bf16x8_t pf[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      u32x4_t pk;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int e = 8 * (jj & 1) + 2 * e2;
-        const float a0 = __builtin_amdgcn_exp2f(fmaf(s[jj >> 1][e], c2, -m_new));
-        const float a1 = __builtin_amdgcn_exp2f(fmaf(s[jj >> 1][e + 1], c2, -m_new));
-        psum += a0 + a1;
-        pk[e2] = pack_bf16x2(a0, a1);
+        pf[qg][jj] = __builtin_bit_cast(bf16x8_t, pk);
       }
-      pf[jj] = __builtin_bit_cast(bf16x8_t, pk);
-    }
-    l_run = l_run * alpha + psum;
-    // The running maximum rarely grows after the first blocks: rescale the
-    // accumulators only when it did for some lane (alpha == 1 is exact).
-    if (__any(alpha != 1.0f)) {
+      l_run[qg] = l_run[qg] * alpha + psum;
+      // The running maximum rarely grows after the first blocks: rescale the
+      // accumulators only when it did for some lane (alpha == 1 is exact).
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int t = 0; t < DT; ++t) acc[t] = acc[t] * alpha;
+        for (int t = 0; t < DT; ++t) acc[qg][t] = acc[qg][t] * alpha;
+      }
     }
     // O^T += V^T P^T over the 64 keys (4 k-steps of 16), the next k-step's
     // V^T fragments read while this one's MFMAs run.
@@ -258,7 +280,9 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
       if (jj + 1 < 4) read_v(jj + 1, vf[(jj + 1) & 1]);
 #pragma unroll
       for (int t = 0; t < DT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[jj & 1][t], pf[jj], acc[t], 0, 0, 0);
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg)
+          acc[qg][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[jj & 1][t], pf[qg][jj], acc[qg][t], 0, 0, 0);
     }
   };
 
@@ -277,34 +301,50 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
     __builtin_amdgcn_s_waitcnt(kWaitAll);    // block j has landed
     asm volatile("s_barrier" ::: "memory");  // visible to all; block j - 1 done
     if (j + 1 < nb) issue(L0 + STAGE, (j + 1) * kBK);
-    block(I0{}, j * kBK);
+    if (j * kBK <= kwave) block(I0{}, j * kBK);
     if (j + 1 < nb) {
       __builtin_amdgcn_s_waitcnt(kWaitAll);
       asm volatile("s_barrier" ::: "memory");
       if (j + 2 < nb) issue(L0, (j + 2) * kBK);
-      block(I1{}, (j + 1) * kBK);
+      if ((j + 1) * kBK <= kwave) block(I1{}, (j + 1) * kBK);
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitAll);
 
   // O = O^T / l: lane holds query qq, columns 32 t + 8 (e / 4) + 4 h2 + e % 4.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qq < S) {
-    const float inv = __builtin_amdgcn_rcpf(l_tot);
-    uint16_t* orow = p.t.out[g] + ((int64_t)b * S + qq) * Hk + head * D + 4 * h2;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+  for (int qg = 0; qg < QG; ++qg) {
+    const float l_tot = l_run[qg] + __shfl_xor(l_run[qg], 32);
+    if (qq[qg] < S) {
+      const float inv = __builtin_amdgcn_rcpf(l_tot);
+      uint16_t* orow = p.t.out[g] + ((int64_t)b * S + qq[qg]) * Hk + head * D + 4 * h2;
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        u32x2_t o;
-        o[0] = pack_bf16x2(acc[t][4 * e4] * inv, acc[t][4 * e4 + 1] * inv);
-        o[1] = pack_bf16x2(acc[t][4 * e4 + 2] * inv, acc[t][4 * e4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + 32 * t + 8 * e4) = o;
-      }
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          u32x2_t o;
+          o[0] = pack_bf16x2(acc[qg][t][4 * e4] * inv, acc[qg][t][4 * e4 + 1] * inv);
+          o[1] = pack_bf16x2(acc[qg][t][4 * e4 + 2] * inv, acc[qg][t][4 * e4 + 3] * inv);
+          *reinterpret_cast<u32x2_t*>(orow + 32 * t + 8 * e4) = o;
+        }
+    }
   }
 }
 
 }  // namespace
+
+// Query groups of 32 per wave: two when the grid of 256-query workgroups
+// still holds at least 4096 of them (16 rounds of the CUs), else one.  Two
+// groups halve the LDS reads per score, but also the workgroups, and for
+// d = 128 the second group's registers leave one wave per SIMD.  Measured
+// (bit-identical outputs): 10% faster at S = 32768 (8 shards of 8 heads of
+// 128, 8192 workgroups), 10-25% slower at S <= 2048 (gpt2_small's and
+// llama7b's shards, 384 and 1024 workgroups).
+constexpr int64_t kWideGrid = 4096;
+
+static int attention_query_groups(int64_t S, int64_t seqs) {
+  return ((S + 2 * kBQ - 1) / (2 * kBQ)) * seqs >= kWideGrid ? 2 : 1;
+}
 
 hipError_t launch_attention_bf16(const void* const* qkv, void* const* out, int groups, int64_t B,
                                  int64_t S, int heads, int d, bool causal, hipStream_t s) {
@@ -319,15 +359,24 @@ hipError_t launch_attention_bf16(const void* const* qkv, void* const* out, int g
   p.B = (int)B;
   p.S = (int)S;
   p.heads = heads;
-  p.nqb = (int)((S + kBQ - 1) / kBQ);
+  const int qg = attention_query_groups(S, (int64_t)groups * B * heads);
+  p.nqb = (int)((S + kBQ * qg - 1) / (kBQ * qg));
   const int64_t blocks = (int64_t)p.nqb * groups * B * heads;
   const dim3 grid((unsigned)blocks), block(256);
+  const auto launch = [&](auto dd, auto cc, auto gg) {
+    hipLaunchKernelGGL((attention_kernel<decltype(dd)::value, decltype(cc)::value, decltype(gg)::value>), grid,
+                       block, 0, s, p);
+  };
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
+  using G1 = std::integral_constant<int, 1>;
+  using G2 = std::integral_constant<int, 2>;
   if (d == 128) {
-    if (causal) hipLaunchKernelGGL((attention_kernel<128, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attention_kernel<128, false>), grid, block, 0, s, p);
+    if (qg == 2) causal ? launch(D128{}, std::true_type{}, G2{}) : launch(D128{}, std::false_type{}, G2{});
+    else causal ? launch(D128{}, std::true_type{}, G1{}) : launch(D128{}, std::false_type{}, G1{});
   } else {
-    if (causal) hipLaunchKernelGGL((attention_kernel<64, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attention_kernel<64, false>), grid, block, 0, s, p);
+    if (qg == 2) causal ? launch(D64{}, std::true_type{}, G2{}) : launch(D64{}, std::false_type{}, G2{});
+    else causal ? launch(D64{}, std::true_type{}, G1{}) : launch(D64{}, std::false_type{}, G1{});
   }
   return hipGetLastError();
 }

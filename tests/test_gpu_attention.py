@@ -84,6 +84,42 @@ def test_attn_core_shards_equal_single(tpm):
         assert torch.equal(Ai, A[i]), i
 
 
+# Grids of at least 4096 workgroups of 256 queries (ceil(S / 256) x shards x
+# sequences x heads) run two 32-query groups per wave; the same shards one at a
+# time run one group per wave.
+WIDE_CASES = [
+    # shards, B, S, heads, d, causal
+    (8, 16, 384, 16, 64, True), (8, 16, 300, 16, 64, False), (16, 8, 1000, 8, 128, True),
+]
+
+
+@pytest.mark.parametrize("G,B,S,heads,d,causal", WIDE_CASES)
+def test_attn_core_wide_grid(tpm, orc, G, B, S, heads, d, causal):
+    """The two-group kernel (a wide batch) equals the one-group kernel (each
+    shard alone) bit for bit, and shard 0's first sequence passes the oracle
+    bounds."""
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    assert -(-S // 256) * G * B * heads >= 4096 and -(-S // 256) * B * heads < 4096
+    say("attn_core wide grid G=%d B=%d S=%d heads=%d d=%d causal=%s" % (G, B, S, heads, d, causal))
+    Hk = heads * d
+    qkv_h = [inputs.draw(inputs.STREAM_X, (B * S, 3 * Hk), 1.0, "bf16", seed=70 + i) for i in range(G)]
+    qkvs = [to_dev(q) for q in qkv_h]
+    A = [torch.full((B * S, Hk), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(G)]
+    tpm.tp_attn_core_shards(qkvs, A, B, S, heads, d, causal=causal)
+    for i in range(G):
+        Ai = torch.full_like(A[i], float("nan"))
+        tpm.tp_attn_core_shards([qkvs[i]], [Ai], B, S, heads, d, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(Ai, A[i]), i
+    A0 = f64(from_dev(A[0][:S]))
+    q0 = qkv_h[0][:S]
+    Ar = orc.attn_core(q0, 1, S, heads, d, causal)
+    assert np.all(np.isfinite(A0))
+    assert_within(A0, Ar, attn_core_bound(f64(q0), Ar, 1, S, heads, d, causal), "A")
+    assert rel_fro(A0, Ar) <= 1e-2
+
+
 def _shard_inputs(inp, n_heads, k):
     from tensor_transformer_mlp_amd import inputs
     Wqkv, bqkv = inputs.qkv_shards(inp["Wq"], inp["Wk"], inp["Wv"], inp["bq"], inp["bk"], inp["bv"], n_heads, k)
