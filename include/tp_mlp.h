@@ -383,8 +383,10 @@ int tp_mlp_grad_input_partial(const void* dA_i, const void* W_i, float* dX_i, in
 /*
  * Bytes of device workspace tp_mlp_shard_backward needs: Y_i and G_i / dA_i
  * [M, Fk] for every shard of a batch (up to 16), the weight-gradient
- * workspace of a batch, and k - 1 float32 partials [M, H] unless
- * TP_FUSED_ACCUM is set.  Returns 0 for invalid arguments.
+ * workspace of a batch, k - 1 float32 partials [M, H] unless TP_FUSED_ACCUM
+ * is set, and for bf16 with M >= 4096 transposed copies of W_i and V_i
+ * (bf16 [Fk, H] and [H, Fk]) for every shard of a batch, through which the
+ * products by W_i^T and V_i^T run.  Returns 0 for invalid arguments.
  */
 size_t tp_mlp_backward_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dtype,
                                        unsigned flags);

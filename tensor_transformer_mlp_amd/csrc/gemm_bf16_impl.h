@@ -93,7 +93,7 @@ constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 // Epilogues each layout is instantiated with.
 constexpr bool layout_has_epi(int layout, int epi) {
   return layout == kNN ? (epi == kEpiBiasGelu || epi == kEpiBiasGeluSave || epi == kEpiStoreF32 ||
-                          epi == kEpiAccumF32 || epi == kEpiSwiGLU || epi == kEpiBias)
+                          epi == kEpiAccumF32 || epi == kEpiSwiGLU || epi == kEpiBias || epi == kEpiMulAux)
        : layout == kNT ? (epi == kEpiMulAux || epi == kEpiStoreF32 || epi == kEpiAccumF32)
                        : (epi == kEpiStoreF32 || epi == kEpiAccumF32);
 }

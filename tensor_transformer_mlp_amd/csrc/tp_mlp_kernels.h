@@ -123,6 +123,11 @@ hipError_t launch_sp_reduce_scatter(const float* const* parts, int nparts, const
                                     void* const* out, bool o_bf16, int k, int64_t block_elems,
                                     hipStream_t s);
 
+// dst[g] [C, R] = src[g]^T for row-major bf16 src[g] [R, C], g < groups;
+// R and C multiples of 8, 16-byte aligned pointers.
+hipError_t launch_transpose_bf16(const void* const* src, void* const* dst, int groups, int64_t R, int64_t C,
+                                 hipStream_t s);
+
 // Scaled dot-product attention of `heads` heads of dimension d (64 or 128)
 // for `groups` shards at once: qkv[g] [B S, 3 heads d] bf16 (query, key and
 // value of head h at columns h d, heads d + h d, 2 heads d + h d), out[g]

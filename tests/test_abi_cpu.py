@@ -321,6 +321,9 @@ def test_backward_workspace_bytes(L):
         # workspace of the batch, which covers at least the single-shard one
         assert fused >= 2 * G * act + gw(M, H, Fk, dt)
         assert (fused - 2 * G * act) % 256 == 0
+        # bf16 with M >= 4096: transposed copies of W_i and V_i for the shards of a batch
+        tw = 2 * G * (-(-H * Fk * 2 // 256) * 256) if dt == 1 and M >= 4096 else 0
+        assert fused == 2 * G * act + L.tp_mlp_grad_weight_workspace_bytes_shards(G, M, H, Fk, dt) + tw
     assert gw(8192, 768, 768, 1) >= 768 * 4
     assert f(0, 8, 64, 128, 0, 0) == 0
     assert f(2, 8, 60, 128, 0, 0) == 0

@@ -364,3 +364,35 @@ def test_backward_empty_and_single_row(tpm, orc):
     assert rel_fro(np.concatenate([from_dev(t) for t in dW1], axis=1), rW) <= 1e-5
     assert rel_fro(np.concatenate([from_dev(t) for t in db1]), rb) <= 1e-5
     assert rel_fro(np.concatenate([from_dev(t) for t in dV1], axis=0), rV) <= 1e-5
+
+
+@pytest.mark.parametrize("M,H,F,k,fused", [(4096, 256, 1024, 4, False), (4100, 136, 544, 4, True),
+                                           (8192, 768, 3072, 4, False)])
+def test_backward_transposed_weights_equal_steps(tpm, M, H, F, k, fused):
+    """From M = 4096 tokens (bf16) the whole backward multiplies by V_i^T and
+    W_i^T through transposed copies of the weights on the GEMM's NN path; the
+    step entry points read the weights as transposes (NT).  Both accumulate
+    every output element over K in the same order: equal bit for bit."""
+    import torch
+    say("backward transposed weights M=%d H=%d F=%d k=%d fused=%s" % (M, H, F, k, fused))
+    X, Ws, bs, Vs, dZ = _bwd_args(tpm, M, H, F, k, "bf16", 11)
+    dX, dW, db, dV = tpm.tp_mlp_shard_backward(X, Ws, bs, Vs, dZ, fused=fused)
+    Fk = F // k
+    Y = [torch.empty(M, Fk, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    G = [torch.empty(M, Fk, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    tpm.tp_mlp_col_gelu_shards(X, Ws, bs, Y, G)
+    dA = [torch.empty_like(g) for g in G]
+    tpm.tp_mlp_grad_act_shards(dZ, Vs, G, dA)
+    dV2 = [torch.empty(Fk, H, device="cuda") for _ in range(k)]
+    tpm.tp_mlp_grad_row_weight_shards(Y, dZ, dV2)
+    dW2 = [torch.empty(H, Fk, device="cuda") for _ in range(k)]
+    db2 = [torch.empty(Fk, device="cuda") for _ in range(k)]
+    tpm.tp_mlp_grad_col_weight_shards(X, dA, dW2, db2)
+    dXp = [torch.empty(M, H, device="cuda") for _ in range(k)]
+    tpm.tp_mlp_grad_input_shards(dA, Ws, dXp)
+    dX2 = tpm.tp_shard_reduce(dXp)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dX2)
+    for i in range(k):
+        assert torch.equal(dW[i], dW2[i]) and torch.equal(db[i], db2[i]), ("dW/db", i)
+        assert torch.equal(dV[i], dV2[i]), ("dV", i)
