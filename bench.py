@@ -24,7 +24,7 @@ dominant kernel, CPU-oracle baseline, backward) on stdout; diagnostics go to
 stderr.  `value` and ms_per_step come from K steps timed back to back between
 two synchronisations; "step_ms" gives the median, minimum and 90th percentile
 of K further steps timed one by one with HIP events, and "gpu_state" the
-socket power and GFX clocks amd-smi reads while the step repeats.
+socket power and shader clock sampled from sysfs while the step repeats.
 """
 from __future__ import annotations
 
@@ -81,59 +81,84 @@ def step_distribution(step, n: int) -> dict:
     return percentiles([e0.elapsed_time(e1) for e0, e1 in ev])
 
 
-def parse_amd_smi(text: str) -> dict | None:
-    """Socket power (W) and the GFX clocks (MHz; one per XCD) from the text of
-    `amd-smi metric -c -p`."""
+def read_hwmon(dev_dir: str) -> dict | None:
+    """Socket power and its cap (W) and the shader clock (MHz) from the amdgpu
+    hwmon files of one device (dev_dir: its /sys/bus/pci/devices/<address> directory): plain
+    file reads, no other program is run.  None if the files are not there."""
+    import glob
+    for d in sorted(glob.glob(os.path.join(dev_dir, "hwmon", "hwmon*"))):
+        out = {}
+        for fname, key, scale in (("power1_average", "socket_power_w", 1e-6), ("power1_input", "socket_power_w", 1e-6),
+                                  ("power1_cap", "power_cap_w", 1e-6), ("freq1_input", "gfx_clock_mhz", 1e-6)):
+            if key in out:
+                continue
+            try:
+                out[key] = float(open(os.path.join(d, fname)).read().strip()) * scale
+            except (OSError, ValueError):
+                pass
+        if "gfx_clock_mhz" not in out:
+            clk = current_sclk_mhz(dev_dir)
+            if clk is not None:
+                out["gfx_clock_mhz"] = clk
+        if out:
+            return out
+    return None
+
+
+def current_sclk_mhz(dev_dir: str):
+    """The shader clock level marked current ('*') in the device's pp_dpm_sclk
+    table, in MHz (None if the file is missing or marks none)."""
     import re
-    power = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)
-    clocks = [float(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", text)]
-    if not power and not clocks:
+    try:
+        lines = open(os.path.join(dev_dir, "pp_dpm_sclk")).read().splitlines()
+    except OSError:
         return None
-    out = {"socket_power_w": float(power.group(1)) if power else None}
-    if clocks:
-        out.update({"gfx_clock_mhz_mean": round(sum(clocks) / len(clocks), 1), "gfx_clock_mhz_min": min(clocks),
-                    "gfx_clock_mhz_max": max(clocks), "gfx_clock_domains": len(clocks)})
-    return out
+    for line in lines:
+        m = re.match(r"\s*\w+:\s*([0-9.]+)\s*[Mm][Hh]z\s*\*", line)
+        if m:
+            return float(m.group(1))
+    return None
 
 
 def gpu_state_during(step, seconds: float):
-    """The step repeats on the GPU for `seconds` while a child process reads
-    the socket power and clocks with amd-smi halfway through (None if amd-smi
-    is missing or prints nothing usable)."""
-    import shutil
-    import subprocess
+    """The step repeats on the GPU for `seconds` while a thread samples the
+    device's socket power and shader clock from sysfs every 0.1 s; returns
+    their means (None where the files are missing)."""
     import threading
     import torch
-    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
-    if seconds <= 0 or not os.path.exists(exe):
+    if seconds <= 0:
         return None
     props = torch.cuda.get_device_properties(torch.cuda.current_device())
-    bus = getattr(props, "pci_bus_id", None)
-    target = "%04x:%02x:%02x.0" % (getattr(props, "pci_domain_id", 0), bus, getattr(props, "pci_device_id", 0)) \
-        if bus is not None else "0"
-    got = {}
+    if getattr(props, "pci_bus_id", None) is None:
+        return None
+    bdf = "%04x:%02x:%02x.0" % (getattr(props, "pci_domain_id", 0), props.pci_bus_id, getattr(props, "pci_device_id", 0))
+    dev_dir = "/sys/bus/pci/devices/" + bdf
+    if read_hwmon(dev_dir) is None:
+        return None
+    samples = []
+    stop = threading.Event()
 
-    def probe():
-        time.sleep(seconds / 2)
-        for g in ([target, "0"] if target != "0" else ["0"]):
-            try:
-                r = subprocess.run([exe, "metric", "-c", "-p", "-g", g], capture_output=True, text=True, timeout=30)
-            except (OSError, subprocess.TimeoutExpired):
-                continue
-            parsed = parse_amd_smi(r.stdout)
-            if parsed:
-                got.update(parsed, gpu=g)
-                return
+    def sampler():
+        while not stop.wait(0.1):
+            r = read_hwmon(dev_dir)
+            if r:
+                samples.append(r)
 
-    th = threading.Thread(target=probe)
+    th = threading.Thread(target=sampler)
     th.start()
     t_end = time.perf_counter() + seconds
-    while th.is_alive() or time.perf_counter() < t_end:
+    while time.perf_counter() < t_end:
         for _ in range(10):
             step()
         torch.cuda.synchronize()
+    stop.set()
     th.join()
-    return got or None
+    out = {"device": bdf, "samples": len(samples)}
+    for key in ("socket_power_w", "power_cap_w", "gfx_clock_mhz"):
+        vals = [x[key] for x in samples if key in x]
+        if vals:
+            out[key] = round(sum(vals) / len(vals), 1)
+    return out if len(out) > 2 else None
 
 
 def percentiles(ms) -> dict:
@@ -151,8 +176,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--power-seconds", type=float, default=2.0,
-                    help="after the timed steps, repeat the step this long while amd-smi (a child process) reads "
-                         "the socket power and GFX clocks; 0 disables")
+                    help="after the timed steps, repeat the step this long while the device's socket power and "
+                         "shader clock are sampled from sysfs; 0 disables")
     ap.add_argument("--settle-seconds", type=float, default=0.5,
                     help="before each leg's warmup steps, repeat its step for this long so that the GPU's clock "
                          "has left its idle state (untimed; 0 disables)")
@@ -359,8 +384,9 @@ def main():
     log("single steps: median %.4f ms, min %.4f, p90 %.4f" % (dist["median"], dist["min"], dist["p90"]))
     gpu_state = gpu_state_during(step, args.power_seconds)
     if gpu_state:
-        log("amd-smi during the steps: %s W, GFX clock %s MHz (mean of %s domains)" % (
-            gpu_state.get("socket_power_w"), gpu_state.get("gfx_clock_mhz_mean"), gpu_state.get("gfx_clock_domains")))
+        log("during the steps (sysfs, %d samples): %s W (cap %s W), shader clock %s MHz" % (
+            gpu_state["samples"], gpu_state.get("socket_power_w"), gpu_state.get("power_cap_w"),
+            gpu_state.get("gfx_clock_mhz")))
 
     # The other variant of the same step, timed the same way (reported beside
     # the headline; bit-identical Z).

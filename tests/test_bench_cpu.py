@@ -97,24 +97,24 @@ def test_step_percentiles(bench):
     assert bench.percentiles([0.25]) == {"median": 0.25, "min": 0.25, "p90": 0.25, "n": 1}
 
 
-def test_amd_smi_parse(bench):
-    text = """GPU: 0
-    POWER:
-        SOCKET_POWER: 1007 W
-        GFX_VOLTAGE: N/A
-    CLOCK:
-        GFX_0:
-            CLK: 2023 MHz
-            MIN_CLK: 500 MHz
-            MAX_CLK: 2400 MHz
-        GFX_1:
-            CLK: 1979 MHz
-            MIN_CLK: 500 MHz
-            MAX_CLK: 2400 MHz
-        MEM_0:
-            CLK: 1900 MHz
-"""
-    st = bench.parse_amd_smi(text)
-    assert st == {"socket_power_w": 1007.0, "gfx_clock_mhz_mean": 2001.0, "gfx_clock_mhz_min": 2023.0 - 44,
-                  "gfx_clock_mhz_max": 2023.0, "gfx_clock_domains": 2}
-    assert bench.parse_amd_smi("ERROR: no devices") is None
+def test_hwmon_read(bench, tmp_path):
+    d = tmp_path / "hwmon" / "hwmon3"
+    d.mkdir(parents=True)
+    (d / "power1_average").write_text("1258000000\n")
+    (d / "freq1_input").write_text("1986000000\n")
+    assert bench.read_hwmon(str(tmp_path)) == {"socket_power_w": 1258.0, "gfx_clock_mhz": 1986.0}
+    (d / "power1_cap").write_text("1400000000\n")
+    assert bench.read_hwmon(str(tmp_path))["power_cap_w"] == 1400.0
+    (d / "power1_cap").unlink()
+    (d / "power1_average").unlink()
+    (d / "power1_input").write_text("700000000\n")
+    assert bench.read_hwmon(str(tmp_path)) == {"socket_power_w": 700.0, "gfx_clock_mhz": 1986.0}
+    assert bench.read_hwmon(str(tmp_path / "missing")) is None
+    # no freq1_input: the current level of pp_dpm_sclk
+    (d / "freq1_input").unlink()
+    (tmp_path / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 1933Mhz *\n2: 2400Mhz\n")
+    assert bench.read_hwmon(str(tmp_path)) == {"socket_power_w": 700.0, "gfx_clock_mhz": 1933.0}
+    (tmp_path / "pp_dpm_sclk").write_text("S: 1986Mhz *\n")
+    assert bench.current_sclk_mhz(str(tmp_path)) == 1986.0
+    (tmp_path / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 2400Mhz\n")
+    assert bench.current_sclk_mhz(str(tmp_path)) is None
