@@ -170,7 +170,7 @@ def percentiles(ms) -> dict:
     return {"median": round(med, 5), "min": round(t[0], 5), "p90": round(p90, 5), "n": n}
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -196,7 +196,7 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain float32 copy kernel (y = x * 1) over MIB MiB, 5 times: "
                          "the known-size reference for the HBM byte counters")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def kernel_bytes(kind, w, elt, n):
@@ -308,8 +308,8 @@ def roofline(kern, w, variant, dtype, kind=None):
     return roof
 
 
-def main():
-    args = parse()
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         log("bench.py measures one GPU only: the library has no multi-GPU path "
             "(the k shards run back to back on one device); run with --gpus 1")
