@@ -333,30 +333,6 @@ int check_sp(const float* const* parts, int nparts, const void* R, int r_dtype, 
   return TP_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* tp_status_string(int status) {
-  switch (status) {
-    case TP_OK: return "ok";
-    case TP_ERR_NULL: return "a required pointer is NULL";
-    case TP_ERR_SHAPE:
-      return "a size is out of range (H and F/k must be multiples of 8, 8 <= H, F/k <= 2^22)";
-    case TP_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case TP_ERR_DTYPE: return "unknown dtype (expected TP_F32 or TP_BF16)";
-    case TP_ERR_WORKSPACE: return "workspace is missing or too small";
-    case TP_ERR_HIP: return "a HIP launch failed";
-    case TP_ERR_FLAGS: return "unknown flag bits";
-    case TP_ERR_ALIAS: return "an output overlaps an input or another output";
-    default: return "unknown status";
-  }
-}
-
-int tp_mlp_version(void) { return 131; }
-
-namespace {
-
 // tp_mlp_col_gelu_shards after the tile argument's own checks (tile < 0: the
 // library's choice).
 int col_shards(const void* X, const void* const* W, const void* const* b, void* const* Y,
@@ -385,28 +361,8 @@ int col_shards(const void* X, const void* const* W, const void* const* b, void* 
   return col_steps(X, W, b, Y, G, n, M, H, Fk, dtype, static_cast<hipStream_t>(stream), tile);
 }
 
-}  // namespace
-
-int tp_mlp_col_gelu_shards(const void* X, const void* const* W, const void* const* b, void* const* Y,
-                           void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype,
-                           void* stream) {
-  return col_shards(X, W, b, Y, G, n, M, H, Fk, dtype, stream, -1);
-}
-
-int tp_mlp_col_gelu(const void* X, const void* W_i, const void* b_i, void* Y_i, int64_t M,
-                    int64_t H, int64_t Fk, int dtype, void* stream) {
-  return tp_mlp_col_gelu_shards(X, &W_i, b_i ? &b_i : nullptr, &Y_i, nullptr, 1, M, H, Fk, dtype,
-                                stream);
-}
-
-int tp_mlp_col_gelu_save(const void* X, const void* W_i, const void* b_i, void* Y_i, void* G_i,
-                         int64_t M, int64_t H, int64_t Fk, int dtype, void* stream) {
-  return tp_mlp_col_gelu_shards(X, &W_i, b_i ? &b_i : nullptr, &Y_i, &G_i, 1, M, H, Fk, dtype,
-                                stream);
-}
-
-namespace {
-
+// tp_mlp_row_partial_shards after the tile argument's own checks (tile < 0:
+// the library's choice).
 int row_shards(const void* const* Y, const void* const* V, float* const* Z, int n, int64_t M,
                int64_t Fk, int64_t H, int dtype, unsigned flags, void* stream, int tile) {
   int st = check_dtype(dtype);
@@ -432,7 +388,61 @@ int row_shards(const void* const* Y, const void* const* V, float* const* Z, int 
                    static_cast<hipStream_t>(stream), tile);
 }
 
+// The batch of a bf16 forward step for the tile queries (shapes only).
+int step_batch(int step, int n, int64_t M, int64_t H, int64_t Fk, unsigned flags, GemmBatch& g) {
+  int st = check_dims(M, H, Fk);
+  if (st) return st;
+  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
+  switch (step) {
+    case 0: g = col_batch(nullptr, nullptr, nullptr, nullptr, nullptr, n, M, H, Fk); return TP_OK;
+    case 1:
+    case 2:
+      if (flags & ~TP_ACCUMULATE) return TP_ERR_FLAGS;
+      g = row_batch(nullptr, nullptr, nullptr, n, step == 2, M, Fk, H, (flags & TP_ACCUMULATE) != 0);
+      return TP_OK;
+    default: return TP_ERR_SHAPE;
+  }
+}
+
 }  // namespace
+
+extern "C" {
+
+const char* tp_status_string(int status) {
+  switch (status) {
+    case TP_OK: return "ok";
+    case TP_ERR_NULL: return "a required pointer is NULL";
+    case TP_ERR_SHAPE:
+      return "a size is out of range (H and F/k must be multiples of 8, 8 <= H, F/k <= 2^22)";
+    case TP_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case TP_ERR_DTYPE: return "unknown dtype (expected TP_F32 or TP_BF16)";
+    case TP_ERR_WORKSPACE: return "workspace is missing or too small";
+    case TP_ERR_HIP: return "a HIP launch failed";
+    case TP_ERR_FLAGS: return "unknown flag bits";
+    case TP_ERR_ALIAS: return "an output overlaps an input or another output";
+    default: return "unknown status";
+  }
+}
+
+int tp_mlp_version(void) { return 131; }
+
+int tp_mlp_col_gelu_shards(const void* X, const void* const* W, const void* const* b, void* const* Y,
+                           void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype,
+                           void* stream) {
+  return col_shards(X, W, b, Y, G, n, M, H, Fk, dtype, stream, -1);
+}
+
+int tp_mlp_col_gelu(const void* X, const void* W_i, const void* b_i, void* Y_i, int64_t M,
+                    int64_t H, int64_t Fk, int dtype, void* stream) {
+  return tp_mlp_col_gelu_shards(X, &W_i, b_i ? &b_i : nullptr, &Y_i, nullptr, 1, M, H, Fk, dtype,
+                                stream);
+}
+
+int tp_mlp_col_gelu_save(const void* X, const void* W_i, const void* b_i, void* Y_i, void* G_i,
+                         int64_t M, int64_t H, int64_t Fk, int dtype, void* stream) {
+  return tp_mlp_col_gelu_shards(X, &W_i, b_i ? &b_i : nullptr, &Y_i, &G_i, 1, M, H, Fk, dtype,
+                                stream);
+}
 
 int tp_mlp_row_partial_shards(const void* const* Y, const void* const* V, float* const* Z, int n,
                               int64_t M, int64_t Fk, int64_t H, int dtype, unsigned flags,
@@ -1077,26 +1087,6 @@ int tp_gemm_tiles(int tile, int* info) {
   if (tile >= 0 && tile < count && info) tpmlp::gemm_bf16_tile_shape(tile, info);
   return count;
 }
-
-namespace {
-
-// The batch of a bf16 forward step for the tile queries (shapes only).
-int step_batch(int step, int n, int64_t M, int64_t H, int64_t Fk, unsigned flags, GemmBatch& g) {
-  int st = check_dims(M, H, Fk);
-  if (st) return st;
-  if (n < 1 || n > TP_MAX_BATCH) return TP_ERR_SHAPE;
-  switch (step) {
-    case 0: g = col_batch(nullptr, nullptr, nullptr, nullptr, nullptr, n, M, H, Fk); return TP_OK;
-    case 1:
-    case 2:
-      if (flags & ~TP_ACCUMULATE) return TP_ERR_FLAGS;
-      g = row_batch(nullptr, nullptr, nullptr, n, step == 2, M, Fk, H, (flags & TP_ACCUMULATE) != 0);
-      return TP_OK;
-    default: return TP_ERR_SHAPE;
-  }
-}
-
-}  // namespace
 
 int tp_mlp_step_tile(int step, int n, int64_t M, int64_t H, int64_t Fk) {
   GemmBatch g;
