@@ -21,10 +21,12 @@ constexpr int kTPitch = kT + 2;  // LDS row pitch (elements): spreads a column o
 // 16-byte stores along dst rows (8 consecutive src rows of one src column).
 // R and C are multiples of 8, so every 8-element chunk is wholly inside or
 // wholly outside the matrix.
+// Grid: x = tile index (column tiles fastest), y = group.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(TransposePtrs t, int64_t R, int64_t C) {
   __shared__ uint16_t tile[kT * kTPitch];
-  const int g = blockIdx.z;
-  const int64_t c0 = (int64_t)blockIdx.x * kT, r0 = (int64_t)blockIdx.y * kT;
+  const int g = blockIdx.y;
+  const int64_t ct = (C + kT - 1) / kT;
+  const int64_t c0 = ((int64_t)blockIdx.x % ct) * kT, r0 = ((int64_t)blockIdx.x / ct) * kT;
   const uint16_t* src = t.src[g];
   uint16_t* dst = t.dst[g];
 #pragma unroll
@@ -67,7 +69,11 @@ hipError_t launch_transpose_bf16(const void* const* src, void* const* dst, int g
     t.src[g] = static_cast<const uint16_t*>(src[g]);
     t.dst[g] = static_cast<uint16_t*>(dst[g]);
   }
-  const dim3 grid((unsigned)((C + kT - 1) / kT), (unsigned)((R + kT - 1) / kT), (unsigned)groups);
+  // one dimension for the tiles: a matrix of fewer than 2^40 elements has
+  // fewer than 2^28 of them (the y and z grid dimensions stop at 65535)
+  const int64_t tiles = ((C + kT - 1) / kT) * ((R + kT - 1) / kT);
+  if (tiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles, (unsigned)groups);
   hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, t, R, C);
   return hipGetLastError();
 }
