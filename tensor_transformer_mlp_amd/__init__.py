@@ -89,6 +89,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libtpmlp.so is not built (run `python -m tensor_transformer_mlp_amd.build`"
                                " or __graft_entry__.build()); there is no fallback path")
+        # PyTorch first: its HIP runtime must be the process's one, so that the
+        # library's launches and torch's allocations and streams share it
+        # (loaded the other way round, the library's libamdhip64 would be
+        # bound first and every launch would fail).
+        _torch()
         L = ctypes.CDLL(LIB_PATH)
         i64, vp, ci, cu, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
         L.tp_status_string.argtypes = [ci]

@@ -661,3 +661,19 @@ def test_tile_hook_errors(L):
     assert row(*a) == c["TP_ERR_NULL"]
     a = okr(); a[5] = 0
     assert row(*a) == c["TP_OK"]
+
+
+def test_library_binds_torchs_hip_runtime():
+    """lib() loads PyTorch before libtpmlp.so, so that the process has one HIP
+    runtime (torch's) and the library's launches share torch's memory and
+    streams; loaded first, the library would bind a second runtime and every
+    launch would fail.  Checked in a fresh interpreter (no GPU is touched)."""
+    import subprocess
+    import sys
+    code = ("import os, sys, tensor_transformer_mlp_amd as t; t.lib(); import torch; "
+            "libs = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}; "
+            "d = os.path.realpath(os.path.join(os.path.dirname(torch.__file__), 'lib')); "
+            "print(sorted(libs)); "
+            "assert libs and all(os.path.realpath(p).startswith(d) for p in libs), libs")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
