@@ -1,6 +1,7 @@
 """GPU parity at seeded random shapes: the block forward and backward (M any
 size, H and F/k any multiple of 8, 1 to 6 shards, both element types; literal
-and fused bit-identical), the SwiGLU column step, and the attention kernel
+and fused bit-identical; a few bf16 backward cases with M >= 4096, the path
+through transposed weights), the SwiGLU column step, and the attention kernel
 (random sequence lengths, head counts, widths 64 and 128, causal or not).
 Every output element within the oracle's bound and the relative Frobenius
 bar.  The shapes land on mixes of whole and partial tiles (in M, N, K and in
@@ -88,7 +89,15 @@ def _bwd_cases(n=12, seed=20261203):
     return out
 
 
-@pytest.mark.parametrize("M,H,Fk,k,dtype,bias", _bwd_cases())
+def _bwd_big_m_cases(n=4, seed=20261206):
+    """bf16 with M >= 4096: the whole backward's path through transposed
+    weight copies (narrow H and F/k keep the oracle quick)."""
+    rng = np.random.RandomState(seed)
+    return [(int(rng.randint(4096, 6500)), 8 * int(rng.randint(1, 13)), 8 * int(rng.randint(1, 13)),
+             int(rng.randint(1, 4)), "bf16", bool(rng.rand() < 0.7)) for _ in range(n)]
+
+
+@pytest.mark.parametrize("M,H,Fk,k,dtype,bias", _bwd_cases() + _bwd_big_m_cases())
 def test_random_shape_backward(tpm, orc, M, H, Fk, k, dtype, bias):
     """The block backward (dX, dW_i, db_i, dV_i) at seeded random shapes,
     literal and fused bit-identical, within the oracle's element bounds."""
