@@ -181,7 +181,14 @@ def parse(argv=None):
     ap.add_argument("--settle-seconds", type=float, default=0.5,
                     help="before each leg's warmup steps, repeat its step for this long so that the GPU's clock "
                          "has left its idle state (untimed; 0 disables)")
-    ap.add_argument("--workload", default="gpt2_small")
+    ap.add_argument("--workload", default="long_seq",
+                    help="the headline workload (default: the long-sequence layer, the largest configuration)")
+    ap.add_argument("--configs", default="gpt2_small,llama7b,gpt3_175b,long_seq",
+                    help="comma-separated workloads whose forward is also measured and reported under "
+                         "\"configs\" (empty: none)")
+    ap.add_argument("--legs-workload", default="llama7b",
+                    help="workload of the backward, sequence-parallel, SwiGLU and attention legs "
+                         "(empty: the headline workload)")
     ap.add_argument("--variant", choices=["literal", "fused"], default="literal")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables the CPU leg)")
@@ -308,40 +315,12 @@ def roofline(kern, w, variant, dtype, kind=None):
     return roof
 
 
-def main(argv=None):
-    args = parse(argv)
-    if args.gpus != 1:
-        log("bench.py measures one GPU only: the library has no multi-GPU path "
-            "(the k shards run back to back on one device); run with --gpus 1")
-        sys.exit(2)
-
+def upload_workload(w, dev):
+    """Seeded host inputs of workload w, the device tensors of its k shards:
+    (host dict, X, [W_i], [b_i], [V_i])."""
     import numpy as np
     import torch
-    import tensor_transformer_mlp_amd as tpm
     from tensor_transformer_mlp_amd import inputs
-
-    if args.calibrate_copy:
-        n = args.calibrate_copy * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
-                          "launches": 5}), flush=True)
-        return
-
-    tpm.lib()  # raises if the HIP library is not built: there is no fallback
-    w = inputs.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    fused = args.variant == "fused"
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    elt = 2 if w.dtype == "bf16" else 4
-
-    log("workload %s: M=%d H=%d F=%d k=%d dtype=%s variant=%s" % (w.name, w.M, w.H, w.F, w.k, w.dtype,
-                                                                 args.variant))
-    t = time.time()
     inp = inputs.make_inputs(w)
 
     def up(a):
@@ -356,60 +335,70 @@ def main(argv=None):
     bs = [bd[i * Fk:(i + 1) * Fk].contiguous() for i in range(w.k)]
     Vs = [Vd[i * Fk:(i + 1) * Fk, :].contiguous() for i in range(w.k)]
     del Wd, bd, Vd
+    return inp, X, Ws, bs, Vs
+
+
+def forward_leg(tpm, w, X, Ws, bs, Vs, variant, args, power_seconds, distribution=True):
+    """Time tp_mlp_shard_forward on workload w: `variant` (literal: fp32 partials
+    and the shard-reduce kernel; fused: the shard sum folded into the row GEMM)
+    back to back, the other variant the same way (both results checked against
+    each other), the step distribution and the power state, then each kernel
+    kind in the step's own launch configuration.  Returns the summary dict."""
+    import torch
+    dev = X.device
+    fused = variant == "fused"
+    dt = tpm.TP_BF16 if w.dtype == "bf16" else tpm.TP_F32
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    elt = 2 if w.dtype == "bf16" else 4
+    Fk = w.Fk
+
+    def timed(fused_, Z):
+        ws = torch.empty(max(tpm.tp_mlp_workspace_bytes(w.k, w.M, w.H, Fk, dt,
+                                                        tpm.TP_FUSED_ACCUM if fused_ else 0), 1),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            tpm.tp_mlp_shard_forward(X, Ws, bs, Vs, Z=Z, workspace=ws, fused=fused_)
+
+        warm(step, args)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, step, ws
+
     Z = torch.empty(w.M, w.H, dtype=torch.float32, device=dev)
-    flags = tpm.TP_FUSED_ACCUM if fused else 0
-    ws_bytes = tpm.tp_mlp_workspace_bytes(w.k, w.M, w.H, Fk, tpm.TP_BF16 if w.dtype == "bf16" else tpm.TP_F32,
-                                          flags)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    log("inputs ready in %.1f s (workspace %.1f MB)" % (time.time() - t, ws_bytes / 1e6))
-
-    def step():
-        tpm.tp_mlp_shard_forward(X, Ws, bs, Vs, Z=Z, workspace=ws, fused=fused)
-
-    warm(step, args)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms, step, ws = timed(fused, Z)
     tflops = w.flop / (ms * 1e-3) / 1e12
-    log("timed %d steps: %.4f ms/step, %.1f TFLOP/s (%.1f%% of %s peak)" % (
-        args.steps, ms, tflops, 100 * tflops / PEAK_TFLOPS[w.dtype], w.dtype))
+    log("%s %s: %d steps, %.4f ms/step, %.1f TFLOP/s (%.1f%% of %s peak)" % (
+        w.name, variant, args.steps, ms, tflops, 100 * tflops / PEAK_TFLOPS[w.dtype], w.dtype))
     if not bool(torch.isfinite(Z).all()):
         raise RuntimeError("non-finite output")
-    dist = step_distribution(step, args.steps)
-    log("single steps: median %.4f ms, min %.4f, p90 %.4f" % (dist["median"], dist["min"], dist["p90"]))
-    gpu_state = gpu_state_during(step, args.power_seconds)
+    dist = None
+    if distribution:
+        dist = step_distribution(step, args.steps)
+        log("  single steps: median %.4f ms, min %.4f, p90 %.4f" % (dist["median"], dist["min"], dist["p90"]))
+    gpu_state = gpu_state_during(step, power_seconds)
     if gpu_state:
-        log("during the steps (sysfs, %d samples): %s W (cap %s W), shader clock %s MHz" % (
+        log("  during the steps (sysfs, %d samples): %s W (cap %s W), shader clock %s MHz" % (
             gpu_state["samples"], gpu_state.get("socket_power_w"), gpu_state.get("power_cap_w"),
             gpu_state.get("gfx_clock_mhz")))
+    del ws
 
-    # The other variant of the same step, timed the same way (reported beside
-    # the headline; bit-identical Z).
-    other = not fused
-    oflags = tpm.TP_FUSED_ACCUM if other else 0
-    ows = torch.empty(max(tpm.tp_mlp_workspace_bytes(w.k, w.M, w.H, Fk, tpm.TP_BF16 if w.dtype == "bf16" else
-                                                     tpm.TP_F32, oflags), 1), dtype=torch.uint8, device=dev)
+    # The other variant of the same step, timed the same way.  Both compute
+    # Z = sum_i Z_i in float32 in shard order; the fused one accumulates the
+    # shards' products in one running sum, so the two agree to within the
+    # float32 rounding of that sum (checked here against an element bound).
+    other = "literal" if fused else "fused"
     Z2 = torch.empty_like(Z)
-    warm(lambda: tpm.tp_mlp_shard_forward(X, Ws, bs, Vs, Z=Z2, workspace=ows, fused=other), args)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        tpm.tp_mlp_shard_forward(X, Ws, bs, Vs, Z=Z2, workspace=ows, fused=other)
-    torch.cuda.synchronize()
-    oms = (time.perf_counter() - t0) * 1e3 / args.steps
-    if not torch.equal(Z, Z2):
-        raise RuntimeError("literal and fused forward differ")
-    variants = {args.variant: {"value": round(tflops, 3), "ms_per_step": round(ms, 5)},
-                ("fused" if other else "literal"): {"value": round(w.flop / (oms * 1e-3) / 1e12, 3),
-                                                    "ms_per_step": round(oms, 5)}}
-    log("other variant (%s): %.4f ms/step, %.1f TFLOP/s" % ("fused" if other else "literal", oms,
-                                                          w.flop / (oms * 1e-3) / 1e12))
-    del ows, Z2
+    oms, _, ows = timed(not fused, Z2)
+    del ows
+    check_variants_agree(Z, Z2, w)
+    del Z2
+    variants = {variant: {"value": round(tflops, 3), "ms_per_step": round(ms, 5)},
+                other: {"value": round(w.flop / (oms * 1e-3) / 1e12, 3), "ms_per_step": round(oms, 5)}}
+    log("  other variant (%s): %.4f ms/step, %.1f TFLOP/s" % (other, oms, w.flop / (oms * 1e-3) / 1e12))
 
     # Per-kernel pass: the launches of one step through the batched per-step
     # entry points, in the same launch configuration as the step (the shards
@@ -418,7 +407,8 @@ def main(argv=None):
     G = min(w.k, tpm.TP_MAX_BATCH)
     batches = [(i0, min(G, w.k - i0)) for i0 in range(0, w.k, G)]
     Yb = [torch.empty(w.M, Fk, dtype=tdt, device=dev) for _ in range(G)]
-    parts = [Z] + [torch.empty(w.M, w.H, dtype=torch.float32, device=dev) for _ in range(w.k - 1)]
+    parts = [Z] + ([] if fused else [torch.empty(w.M, w.H, dtype=torch.float32, device=dev)
+                                     for _ in range(w.k - 1)])
     if fused:
         kinds = ["col_gelu", "row_sum"]
     else:
@@ -439,39 +429,139 @@ def main(argv=None):
             tpm.tp_shard_reduce(parts, Z=Z)
 
     kern = time_kinds(kinds, launch, nlaunch, nshards, ks, args.warmup, w, elt)
-    roof = roofline(kern, w, args.variant, w.dtype)
-    del Yb, parts
+    roof = roofline(kern, w, variant, w.dtype)
+    del Yb, parts, Z
+    out = {"workload": w.name, "variant": variant, "value": round(tflops, 3), "unit": "TFLOP/s",
+           "ms_per_step": round(ms, 5), "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2),
+           "flop_per_step": w.flop, "variants": variants, "roofline": roof,
+           "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],
+                            "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()},
+           "gpu_state": gpu_state}
+    if dist is not None:
+        out["step_ms"] = dist
+    return out
 
-    bwd = None
-    if not args.no_backward:
-        bwd = bench_backward(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt)
-    sp = None
-    if not args.no_sp and w.M % w.k == 0:
-        sp = bench_sp(tpm, w, X, Ws, bs, Vs, fused, args, elt, tdt)
-    del Ws, bs
-    swiglu = None
-    if not args.no_swiglu:
-        swiglu = bench_swiglu(tpm, w, X, Vs, fused, args, elt, tdt)
-    del Vs
-    attn = None
-    if args.attention and w.dtype == "bf16":
-        attn = bench_attention(tpm, w, X, fused, args, elt)
+
+def check_variants_agree(Z, Z2, w):
+    """The literal and fused Z both hold the float32 sum over the shards of
+    the shards' products and differ only in where that sum is rounded: their
+    relative Frobenius difference stays at float32 rounding level (<= 1e-5).
+    A sanity check of the timed outputs; parity with the oracle is the
+    tests' job."""
+    import torch
+    den = float(torch.linalg.vector_norm(Z.double()))
+    diff = float(torch.linalg.vector_norm((Z.double() - Z2.double())))
+    if not bool(torch.isfinite(Z2).all()) or diff > 1e-5 * den:
+        raise RuntimeError("literal and fused forward differ by %.3g (relative) on %s" % (diff / den, w.name))
+
+
+def host_cpu() -> dict:
+    """Model name and logical CPU count of the host, from /proc/cpuinfo."""
+    model, n = None, 0
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("processor"):
+                n += 1
+            elif model is None and line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": n or os.cpu_count()}
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.gpus != 1:
+        log("bench.py measures one GPU only: the library has no multi-GPU path "
+            "(the k shards run back to back on one device); run with --gpus 1")
+        sys.exit(2)
+
+    import torch
+    import tensor_transformer_mlp_amd as tpm
+    from tensor_transformer_mlp_amd import inputs
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
+                          "launches": 5}), flush=True)
+        return
+
+    tpm.lib()  # raises if the HIP library is not built: there is no fallback
+    w = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log("workload %s: M=%d H=%d F=%d k=%d dtype=%s variant=%s" % (w.name, w.M, w.H, w.F, w.k, w.dtype,
+                                                                 args.variant))
+    t = time.time()
+    inp, X, Ws, bs, Vs = upload_workload(w, dev)
+    torch.cuda.synchronize()
+    log("inputs ready in %.1f s" % (time.time() - t))
+    head = forward_leg(tpm, w, X, Ws, bs, Vs, args.variant, args, args.power_seconds)
+    del X, Ws, bs, Vs
+    torch.cuda.empty_cache()
+
+    # The other bf16 workloads' forward, the same measurement (one line holds
+    # every configuration).
+    configs = {w.name: {k_: head[k_] for k_ in ("value", "ms_per_step", "pct_of_peak", "variants", "roofline",
+                                                 "kernels", "gpu_state")}}
+    for name in [c for c in args.configs.split(",") if c and c != w.name]:
+        cw = inputs.WORKLOADS[name]
+        t = time.time()
+        _, cX, cWs, cbs, cVs = upload_workload(cw, dev)
+        log("workload %s: inputs ready in %.1f s" % (name, time.time() - t))
+        r = forward_leg(tpm, cw, cX, cWs, cbs, cVs, args.variant, args, min(args.power_seconds, 1.0),
+                        distribution=False)
+        configs[name] = {k_: r[k_] for k_ in ("value", "ms_per_step", "pct_of_peak", "variants", "roofline",
+                                               "kernels", "gpu_state")}
+        configs[name]["config"] = cw.describe()
+        del cX, cWs, cbs, cVs
+        torch.cuda.empty_cache()
+
+    # Training and variant legs, on one workload (default: the 7B-shaped layer).
+    lw = inputs.WORKLOADS[args.legs_workload or w.name]
+    bwd = sp = swiglu = attn = None
+    if not (args.no_backward and args.no_sp and args.no_swiglu and not args.attention):
+        _, lX, lWs, lbs, lVs = upload_workload(lw, dev)
+        fused = args.variant == "fused"
+        elt = 2 if lw.dtype == "bf16" else 4
+        tdt = torch.bfloat16 if lw.dtype == "bf16" else torch.float32
+        if not args.no_backward:
+            bwd = bench_backward(tpm, lw, lX, lWs, lbs, lVs, fused, args, elt, tdt)
+        if not args.no_sp and lw.M % lw.k == 0:
+            sp = bench_sp(tpm, lw, lX, lWs, lbs, lVs, fused, args, elt, tdt)
+        del lWs, lbs
+        if not args.no_swiglu:
+            swiglu = bench_swiglu(tpm, lw, lX, lVs, fused, args, elt, tdt)
+        del lVs
+        if args.attention and lw.dtype == "bf16":
+            attn = bench_attention(tpm, lw, lX, fused, args, elt)
+        del lX
+        torch.cuda.empty_cache()
+        for leg in (bwd, sp, swiglu, attn):
+            if leg is not None:
+                leg["workload"] = lw.name
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
         cpu = cpu_baseline(w, inp, args.cpu_baseline_seconds)
 
     out = {
-        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": head["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded Philox normals, random-init weights)",
-        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2), "step_ms": dist, "gpu_state": gpu_state,
+        "pct_of_peak": head["pct_of_peak"], "step_ms": head["step_ms"], "gpu_state": head["gpu_state"],
         "config": dict(w.describe(), variant=args.variant, parallelism="tp%d shards on 1 GPU" % w.k),
-        "roofline": roof,
-        "kernels": {k_: {"avg_ms": round(v["avg_ms"], 5), "per_step": v["launches_per_step"],
-                         "shards_per_launch": v["shards_per_launch"]} for k_, v in kern.items()},
-        "variants": variants,
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "variants": head["variants"],
         "cpu_baseline": cpu,
+        "configs": configs,
         "backward": bwd,
         "sequence_parallel": sp,
         "swiglu": swiglu,
@@ -818,18 +908,17 @@ def cpu_baseline(w, inp, target_s):
     import numpy as np
     import oracle
 
-    oracle.build_oracle()
-    X64 = oracle.widen(inp["X"])
     W64, b64, V64 = oracle.widen(inp["W"]), oracle.widen(inp["b"]), oracle.widen(inp["V"])
     probe = min(w.M, 32)
     t = time.perf_counter()
-    oracle.forward_rows(X64, W64, b64, V64, w.k, np.arange(probe))
+    oracle.forward_rows(oracle.widen(inp["X"][:probe]), W64, b64, V64, w.k)
     tp = time.perf_counter() - t
     rows = int(min(w.M, max(probe, probe * target_s / max(tp, 1e-6))))
+    X64 = oracle.widen(inp["X"][:rows])
     passes, dt = 0, 0.0
     while passes == 0 or (rows == w.M and dt < target_s and passes < 100):
         t = time.perf_counter()
-        oracle.forward_rows(X64, W64, b64, V64, w.k, np.arange(rows))
+        oracle.forward_rows(X64, W64, b64, V64, w.k)
         dt += time.perf_counter() - t
         passes += 1
     flop = 4 * rows * w.H * w.F * passes
@@ -837,8 +926,9 @@ def cpu_baseline(w, inp, target_s):
     what = ("%d full passes over all %d rows" % (passes, w.M)) if rows == w.M else \
         ("rows 0..%d of %d" % (rows - 1, w.M))
     log("cpu oracle: %s in %.2f s with %d threads: %.4f TFLOP/s" % (what, dt, oracle.max_threads(), val))
-    return {"value": val, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": "%s (all %d shards, full W and V), fp64, %.1f s" % (what, w.k, dt)}
+    return dict({"value": val, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+                 "sample": "%s of the %s workload (all %d shards, full W and V), fp64, %.1f s" % (
+                     what, w.name, w.k, dt)}, **host_cpu())
 
 
 if __name__ == "__main__":

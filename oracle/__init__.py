@@ -65,12 +65,18 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build_oracle(force: bool = False) -> str:
-    """Compile liboracle.so with gcc and OpenMP."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+def _source_sha256() -> str:
+    import hashlib
+    return hashlib.sha256(open(_SRC, "rb").read()).hexdigest()
+
+
+def build_oracle(force: bool = True) -> str:
+    """Compile liboracle.so with gcc and OpenMP (called by the build step only,
+    before anything touches the GPU); the source's SHA-256 is compiled in."""
+    if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                               "-o", tmp, _SRC, "-lm"])
+                               '-DORACLE_SOURCE_SHA256="%s"' % _source_sha256(), "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -78,9 +84,13 @@ def build_oracle(force: bool = False) -> str:
 def _L():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-            build_oracle()
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("oracle/liboracle.so is not built: run __graft_entry__.build() first")
         lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_source_sha256.restype = ctypes.c_char_p
+        if lib.oracle_source_sha256().decode() != _source_sha256():
+            raise RuntimeError("oracle/liboracle.so was built from another version of tp_mlp_oracle.c: "
+                               "run __graft_entry__.build() again")
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.oracle_gelu.argtypes = [ctypes.c_double]
         lib.oracle_gelu.restype = ctypes.c_double
@@ -99,6 +109,7 @@ def _L():
         lib.oracle_swiglu_forward_rows.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp, i64, vp]
         lib.oracle_attn_qkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, vp]
         lib.oracle_attn_core.argtypes = [vp, i64, i64, ci, i64, ci, vp]
+        lib.oracle_attn_core_rows.argtypes = [vp, i64, ci, i64, ci, vp, i64, vp]
         lib.oracle_attn_forward_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, vp, i64,
                                                  vp]
         lib.oracle_gelu_grad.argtypes = [ctypes.c_double]
@@ -118,6 +129,7 @@ def _L():
                   lib.oracle_input_grad_partial, lib.oracle_backward_rows, lib.oracle_backward_cols,
                   lib.oracle_sp_reduce_scatter, lib.oracle_silu_array, lib.oracle_swiglu_col,
                   lib.oracle_swiglu_forward_rows, lib.oracle_attn_qkv, lib.oracle_attn_core,
+                  lib.oracle_attn_core_rows,
                   lib.oracle_attn_forward_rows):
             f.restype = None
         _lib = lib
@@ -500,6 +512,21 @@ def attn_core(QKV, B: int, S: int, hk: int, d: int, causal: bool = True) -> np.n
     A = np.empty((B * S, hk * d))
     if B * S:
         _L().oracle_attn_core(_p(Q), B, S, hk, d, 1 if causal else 0, _p(A))
+    return A
+
+
+def attn_core_rows(QKV, B: int, S: int, hk: int, d: int, rows, causal: bool = True) -> np.ndarray:
+    """Rows `rows` (indices into [B S]) of attn_core's output, float64
+    [len(rows), hk d]: each query row evaluated on its own (a row at position t
+    of its sequence needs keys 0..t, or the whole sequence without the mask)."""
+    Q = np.ascontiguousarray(widen(QKV))
+    assert Q.shape == (B * S, 3 * hk * d)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    if r.size and (r.min() < 0 or r.max() >= B * S):
+        raise IndexError("row index out of range")
+    A = np.empty((r.size, hk * d))
+    if r.size:
+        _L().oracle_attn_core_rows(_p(Q), S, hk, d, 1 if causal else 0, _p(r), r.size, _p(A))
     return A
 
 

@@ -523,6 +523,23 @@ void oracle_attn_core(const double* QKV, int64_t B, int64_t S, int hk, int64_t d
   }
 }
 
+/* Selected rows of A_i (step 15): A[r, :] for row m = rows[r] = b S + t of
+   the shard's projection QKV_i [B S, 3 Hk], every head of the shard; the
+   same per-row evaluation as oracle_attn_core. */
+void oracle_attn_core_rows(const double* QKV, int64_t S, int hk, int64_t d, int causal,
+                           const int64_t* rows, int64_t nrows, double* A) {
+  const int64_t Hk = hk * d;
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+#pragma omp for schedule(dynamic, 1) collapse(2)
+    for (int64_t r = 0; r < nrows; ++r)
+      for (int64_t h = 0; h < hk; ++h)
+        attn_head_row(QKV, S, Hk, d, rows[r] / S, rows[r] % S, h, causal, p, A + r * Hk + h * d);
+    free(p);
+  }
+}
+
 /* The whole block for selected rows (steps 14-17): Z[r, :] for row
    m = rows[r] = b S + t.  Only the rows the query attends to are projected
    (positions 0..t of sequence b when causal, the whole sequence otherwise). */
@@ -571,3 +588,11 @@ int oracle_max_threads(void) {
   return 1;
 #endif
 }
+
+/* SHA-256 of this file's text, passed on the compiler command line by the
+   build, so that the loader can refuse a library built from an older copy
+   of the source instead of running stale arithmetic. */
+#ifndef ORACLE_SOURCE_SHA256
+#define ORACLE_SOURCE_SHA256 "unknown"
+#endif
+const char* oracle_source_sha256(void) { return ORACLE_SOURCE_SHA256; }

@@ -43,6 +43,8 @@ TP_MAX_BATCH shards in one launch (what the k-shard calls do inside).
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 
 __all__ = [
@@ -209,11 +211,31 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_caller_stream(fn):
+    """Run ``fn`` with its ``stream`` argument (when one is given) made torch's
+    current stream.  Every tensor the binding allocates on the caller's behalf
+    (outputs, workspaces) then belongs to the stream its kernels run on, so
+    torch's caching allocator never hands such a block to other work while
+    those kernels may still read or write it."""
+    pos = list(inspect.signature(fn).parameters).index("stream")
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = kwargs["stream"] if "stream" in kwargs else (args[pos] if len(args) > pos else None)
+        if stream is None:
+            return fn(*args, **kwargs)
+        with _torch().cuda.stream(stream):
+            return fn(*args, **kwargs)
+
+    return wrapper
+
+
 def _check(code: int, where: str):
     if code != 0:
         raise TpMlpError(code, where)
 
 
+@_on_caller_stream
 def tp_mlp_col_gelu(X, W_i, b_i=None, Y_i=None, stream=None):
     """Y_i = GeLU(X W_i + b_i); X [..., H], W_i [H, Fk], b_i [Fk] or None."""
     torch = _torch()
@@ -235,6 +257,7 @@ def tp_mlp_col_gelu(X, W_i, b_i=None, Y_i=None, stream=None):
     return Y_i
 
 
+@_on_caller_stream
 def tp_mlp_row_partial(Y_i, V_i, Z_i=None, accumulate: bool = False, stream=None):
     """Z_i = Y_i V_i (float32), or Z_i += Y_i V_i with accumulate=True."""
     torch = _torch()
@@ -258,6 +281,7 @@ def tp_mlp_row_partial(Y_i, V_i, Z_i=None, accumulate: bool = False, stream=None
     return Z_i
 
 
+@_on_caller_stream
 def tp_shard_reduce(parts, Z=None, stream=None):
     """Z = parts[0] + parts[1] + ... (float32, left to right).  Z may be parts[0]."""
     torch = _torch()
@@ -281,6 +305,7 @@ def tp_mlp_workspace_bytes(k: int, M: int, H: int, Fk: int, dtype: int, flags: i
     return int(lib().tp_mlp_workspace_bytes(k, M, H, Fk, dtype, flags))
 
 
+@_on_caller_stream
 def tp_mlp_shard_forward(X, W, b, V, Z=None, workspace=None, fused: bool = False, stream=None):
     """Z = sum_i GeLU(X W[i] + b[i]) V[i] over the k shards in the lists W, b, V.
 
@@ -343,6 +368,7 @@ def _workspace(t, need, device):
     return t
 
 
+@_on_caller_stream
 def tp_mlp_col_gelu_save(X, W_i, b_i=None, Y_i=None, G_i=None, stream=None):
     """Y_i = GeLU(A_i), G_i = GeLU'(A_i) with A_i = X W_i + b_i.  Returns (Y_i, G_i)."""
     H = X.shape[-1]
@@ -360,6 +386,7 @@ def tp_mlp_col_gelu_save(X, W_i, b_i=None, Y_i=None, G_i=None, stream=None):
     return Y_i, G_i
 
 
+@_on_caller_stream
 def tp_mlp_grad_act(dZ, V_i, G_i, dA_i=None, stream=None):
     """dA_i = (dZ V_i^T) * G_i; dA_i may be G_i (in place)."""
     H = dZ.shape[-1]
@@ -380,6 +407,7 @@ def tp_mlp_grad_weight_workspace_bytes(M: int, H: int, Fk: int, dtype: int) -> i
     return int(lib().tp_mlp_grad_weight_workspace_bytes(M, H, Fk, dtype))
 
 
+@_on_caller_stream
 def tp_mlp_grad_row_weight(Y_i, dZ, dV_i=None, workspace=None, accumulate: bool = False, stream=None):
     """dV_i = Y_i^T dZ (float32), or dV_i += ... with accumulate=True."""
     torch = _torch()
@@ -402,6 +430,7 @@ def tp_mlp_grad_row_weight(Y_i, dZ, dV_i=None, workspace=None, accumulate: bool 
     return dV_i
 
 
+@_on_caller_stream
 def tp_mlp_grad_col_weight(X, dA_i, dW_i=None, db_i=None, want_db: bool = True, workspace=None,
                            accumulate: bool = False, stream=None):
     """dW_i = X^T dA_i and db_i = sum over rows of dA_i (float32).  Returns (dW_i, db_i)."""
@@ -428,6 +457,7 @@ def tp_mlp_grad_col_weight(X, dA_i, dW_i=None, db_i=None, want_db: bool = True, 
     return dW_i, (db_i if want_db else None)
 
 
+@_on_caller_stream
 def tp_mlp_grad_input_partial(dA_i, W_i, dX_i=None, accumulate: bool = False, stream=None):
     """dX_i = dA_i W_i^T (float32), or dX_i += ... with accumulate=True."""
     torch = _torch()
@@ -451,6 +481,7 @@ def tp_mlp_backward_workspace_bytes(k: int, M: int, H: int, Fk: int, dtype: int,
     return int(lib().tp_mlp_backward_workspace_bytes(k, M, H, Fk, dtype, flags))
 
 
+@_on_caller_stream
 def tp_mlp_shard_backward(X, W, b, V, dZ, dX=None, dW=None, db=None, dV=None, want_db: bool = True,
                           workspace=None, fused: bool = False, accumulate: bool = False, stream=None):
     """Gradients of Z = sum_i GeLU(X W[i] + b[i]) V[i] for dZ = dL/dZ.
@@ -518,6 +549,7 @@ def _batch_n(n):
     return n
 
 
+@_on_caller_stream
 def tp_mlp_col_gelu_shards(X, W, b, Y, G=None, stream=None):
     """Y[i] = GeLU(X W[i] + b[i]) (and G[i] = GeLU'(.) when G is given) for
     every shard i of the lists, in one launch; b may be None."""
@@ -531,6 +563,7 @@ def tp_mlp_col_gelu_shards(X, W, b, Y, G=None, stream=None):
     return Y, G
 
 
+@_on_caller_stream
 def tp_mlp_row_partial_shards(Y, V, Z, sum_shards=False, accumulate=False, stream=None):
     """Z[i] (+)= Y[i] V[i] for every shard, or Z[0] (+)= sum_i Y[i] V[i] in shard
     order with sum_shards=True (Z may then hold just Z[0])."""
@@ -546,6 +579,7 @@ def tp_mlp_row_partial_shards(Y, V, Z, sum_shards=False, accumulate=False, strea
     return Z
 
 
+@_on_caller_stream
 def tp_mlp_grad_act_shards(dZ, V, G, dA, stream=None):
     """dA[i] = (dZ V[i]^T) * G[i] for every shard (dA[i] may be G[i])."""
     n = _batch_n(len(V))
@@ -561,6 +595,7 @@ def tp_mlp_grad_weight_workspace_bytes_shards(n: int, M: int, H: int, Fk: int, d
     return int(lib().tp_mlp_grad_weight_workspace_bytes_shards(n, M, H, Fk, dtype))
 
 
+@_on_caller_stream
 def tp_mlp_grad_row_weight_shards(Y, dZ, dV, workspace=None, accumulate=False, stream=None):
     """dV[i] (+)= Y[i]^T dZ for every shard."""
     n = _batch_n(len(Y))
@@ -576,6 +611,7 @@ def tp_mlp_grad_row_weight_shards(Y, dZ, dV, workspace=None, accumulate=False, s
     return dV
 
 
+@_on_caller_stream
 def tp_mlp_grad_col_weight_shards(X, dA, dW, db=None, workspace=None, accumulate=False, stream=None):
     """dW[i] (+)= X^T dA[i] and db[i] (+)= colsum(dA[i]) for every shard."""
     n = _batch_n(len(dA))
@@ -591,6 +627,7 @@ def tp_mlp_grad_col_weight_shards(X, dA, dW, db=None, workspace=None, accumulate
     return dW, db
 
 
+@_on_caller_stream
 def tp_mlp_grad_input_shards(dA, W, dX, sum_shards=False, accumulate=False, stream=None):
     """dX[i] (+)= dA[i] W[i]^T for every shard, or the shard-order sum into dX[0]."""
     n = _batch_n(len(dA))
@@ -627,6 +664,7 @@ def _sp_blocks(O, k, Mb, H, dtype, device):
     return O, blocks
 
 
+@_on_caller_stream
 def tp_sp_reduce_scatter(parts, k: int, R=None, O=None, out_dtype=None, stream=None):
     """Blocks O_r = R[rows of r] + sum_i parts[i][rows of r] for the k ranks.
 
@@ -660,6 +698,7 @@ def tp_mlp_sp_workspace_bytes(k: int, M: int, H: int, Fk: int, dtype: int, flags
     return int(lib().tp_mlp_sp_workspace_bytes(k, M, H, Fk, dtype, flags))
 
 
+@_on_caller_stream
 def tp_mlp_shard_forward_sp(X, W, b, V, O=None, out_dtype=None, workspace=None, fused: bool = False,
                             stream=None):
     """Sequence-parallel block forward: O_r = X[rows of r] + Z[rows of r] with
@@ -698,6 +737,7 @@ def tp_mlp_shard_forward_sp(X, W, b, V, O=None, out_dtype=None, workspace=None, 
 # ---------------------------------------------------------------------------
 # SwiGLU block.
 
+@_on_caller_stream
 def tp_swiglu_col(X, Wg_i, Wu_i, Y_i=None, stream=None):
     """Y_i = SiLU(X Wg_i) * (X Wu_i); X [..., H], Wg_i and Wu_i [H, Fk]."""
     H = X.shape[-1]
@@ -714,6 +754,7 @@ def tp_swiglu_col(X, Wg_i, Wu_i, Y_i=None, stream=None):
     return Y_i
 
 
+@_on_caller_stream
 def tp_swiglu_col_shards(X, Wg, Wu, Y, stream=None):
     """tp_swiglu_col for the n shards of the lists Wg, Wu, Y in one launch."""
     n = len(Wg)
@@ -733,6 +774,7 @@ def tp_swiglu_col_shards(X, Wg, Wu, Y, stream=None):
     return Y
 
 
+@_on_caller_stream
 def tp_swiglu_shard_forward(X, Wg, Wu, V, Z=None, workspace=None, fused: bool = False, stream=None):
     """Z = sum_i (SiLU(X Wg[i]) * (X Wu[i])) V[i] over the k shards."""
     torch = _torch()
@@ -761,6 +803,7 @@ def tp_swiglu_shard_forward(X, Wg, Wu, V, Z=None, workspace=None, fused: bool = 
 # ---------------------------------------------------------------------------
 # Tensor-parallel attention.
 
+@_on_caller_stream
 def tp_attn_qkv_shards(X, Wqkv, bqkv, QKV, stream=None):
     """QKV[i] = X Wqkv[i] + bqkv[i] for the n shards (bqkv may be None)."""
     n = len(Wqkv)
@@ -782,6 +825,7 @@ def tp_attn_qkv_shards(X, Wqkv, bqkv, QKV, stream=None):
     return QKV
 
 
+@_on_caller_stream
 def tp_attn_core_shards(QKV, A, B: int, S: int, heads: int, head_dim: int, causal: bool = True, stream=None):
     """A[i] = the attention of shard i's heads from its projection QKV[i]."""
     n = len(QKV)
@@ -802,6 +846,7 @@ def tp_attn_workspace_bytes(k: int, B: int, S: int, H: int, n_heads: int, dtype:
     return int(lib().tp_attn_workspace_bytes(k, B, S, H, n_heads, dtype, flags))
 
 
+@_on_caller_stream
 def tp_attn_shard_forward(X, Wqkv, bqkv, Wo, B: int, S: int, n_heads: int, Z=None, workspace=None,
                           fused: bool = False, causal: bool = True, stream=None):
     """Z = sum_i A_i Wo[i] over the k shards of the attention block; X [B S, H]."""
@@ -848,6 +893,7 @@ def tp_mlp_step_tile(step: int, n: int, M: int, H: int, Fk: int) -> int:
     return r
 
 
+@_on_caller_stream
 def tp_mlp_col_gelu_shards_tile(tile, X, W, b, Y, stream=None):
     """tp_mlp_col_gelu_shards (bf16, no G) with tile `tile` of tp_gemm_tiles()."""
     n = _batch_n(len(W))
@@ -859,6 +905,7 @@ def tp_mlp_col_gelu_shards_tile(tile, X, W, b, Y, stream=None):
     return Y
 
 
+@_on_caller_stream
 def tp_mlp_row_partial_shards_tile(tile, Y, V, Z, sum_shards=False, accumulate=False, stream=None):
     """tp_mlp_row_partial_shards (bf16) with tile `tile` of tp_gemm_tiles()."""
     n = _batch_n(len(Y))

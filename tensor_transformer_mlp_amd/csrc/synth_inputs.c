@@ -136,3 +136,11 @@ void synth_round_bf16(const float* in, int64_t n, uint16_t* out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(in[i]);
 }
+
+/* SHA-256 of this file's text, passed on the compiler command line by the
+   build, so that the loader can refuse a library built from an older copy
+   of the source. */
+#ifndef SYNTH_SOURCE_SHA256
+#define SYNTH_SOURCE_SHA256 "unknown"
+#endif
+const char* synth_source_sha256(void) { return SYNTH_SOURCE_SHA256; }

@@ -2,6 +2,7 @@
 // shard loops and the workspace layouts.  Every check runs on the host before
 // the first HIP call, so a rejected call launches nothing.
 #include "tp_mlp.h"
+#include "tp_mlp_dev.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -97,12 +97,18 @@ WORKLOADS = {
 }
 
 
-def build_synth(force: bool = False) -> str:
-    """Compile libtpsynth.so with gcc (host code only)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+def _source_sha256() -> str:
+    import hashlib
+    return hashlib.sha256(open(_SRC, "rb").read()).hexdigest()
+
+
+def build_synth(force: bool = True) -> str:
+    """Compile libtpsynth.so with gcc (host code only; called by the build step,
+    before anything touches the GPU); the source's SHA-256 is compiled in."""
+    if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                               "-o", tmp, _SRC, "-lm"])
+                               '-DSYNTH_SOURCE_SHA256="%s"' % _source_sha256(), "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -114,8 +120,12 @@ def _synth():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
-            build_synth()
+            raise RuntimeError("libtpsynth.so is not built: run __graft_entry__.build() first")
         lib = ctypes.CDLL(_LIB_PATH)
+        lib.synth_source_sha256.restype = ctypes.c_char_p
+        if lib.synth_source_sha256().decode() != _source_sha256():
+            raise RuntimeError("libtpsynth.so was built from another version of synth_inputs.c: "
+                               "run __graft_entry__.build() again")
         i64, u64, dbl, vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_double, ctypes.c_void_p
         lib.synth_philox4x64.argtypes = [vp, vp, ctypes.c_int, vp]
         lib.synth_normal_f64.argtypes = [u64, u64, i64, i64, vp]

@@ -11,8 +11,11 @@ Error model (u = unit roundoff: 2^-24 for float32, 2^-8 for bfloat16):
   error of the kernel's erfc approximation (absolute error <= 1.5e-7 in erfc,
   i.e. <= 0.75e-7 in Phi, times |a|, plus its float32 evaluation).
 * row step from the GPU's own Y_i:  |Z_gpu - Z| <= 2 (K + 2) u32 (|Y_i| |V_i|).
-* whole forward:  |Z_gpu - Z| <= tolY |V| + 2 (Fk + k + 4) u32 (|Y| |V|), with
-  tolY the column-step bound of every shard, side by side.
+* whole forward:  |Z_gpu - Z| <= tolY |V| + 2 (T + 4) u32 (|Y| |V|), with
+  tolY the column-step bound of every shard, side by side, and T the number
+  of float32 additions per output: Fk + k for the literal variant (each
+  shard's Fk products, then the k partials), F for the fused one (one running
+  sum through every shard's products).
 
 Backward (dY = dZ V_i^T, dA = dY * G, G = GeLU'(A)):
 
@@ -37,7 +40,11 @@ Backward (dY = dZ V_i^T, dA = dY * G, G = GeLU'(A)):
     |A_gpu - A| <= 1.5 u16 W_t + 1.01 u16 |A| + 2^-16 W_t
   (the probabilities are rounded to bf16 for the products with V while the
   normaliser sums them unrounded, the output is rounded to bf16, and the
-  float32 scores, exp2 and sums add far less).  From the block's inputs the
+  float32 scores, exp2 and sums add far less).  On long sequences the
+  float32 sums over n keys add up to 4 (n + 2) u32 W_t (the weighted sum and
+  the normaliser, n terms each) and the float32 scores move each weight by
+  up to 2 e_s with e_s = 2 (d + 2) u32 max_j (|q| . |k_j|) / sqrt d; the
+  rows-only bound (attn_rows_bound) adds both terms.  From the block's inputs the
   scores also carry the projection's error: |ds_tj| <= e_s = 2 u16 (|q| . |k|)
   / sqrt(d) + the GEMMs' accumulation bound, which moves each output by at
   most 2 max_j e_s W_t; the value's rounding adds u16 W_t.
@@ -57,6 +64,28 @@ GELU_LIP = 1.13
 
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def gpu_initialised() -> bool:
+    """True once this process has initialised the GPU: from then on it must not
+    start another program (a child interpreter or a compiler)."""
+    if "torch" not in sys.modules:
+        return False
+    import torch
+    return bool(torch.cuda.is_initialized())
+
+
+def tile_rows(M, tile=256, per_tile=2):
+    """Rows that cover every `tile`-row block of the output: per block,
+    `per_tile` rows at offsets that move through the block from one block to
+    the next, plus the first and the last row."""
+    rows = {0, M - 1}
+    for t in range((M + tile - 1) // tile):
+        for j in range(per_tile):
+            r = t * tile + (t * 37 + j * (tile // per_tile) + 11) % tile
+            if r < M:
+                rows.add(r)
+    return np.array(sorted(rows))
 
 
 def to_dev(a: np.ndarray, device="cuda"):
@@ -107,10 +136,14 @@ def row_bound(Y64, Vi64):
     return 2 * (K + 2) * U32 * (np.abs(Y64) @ np.abs(Vi64)) + 1e-30
 
 
-def forward_bound(tolY, Y64, V64, k: int):
-    """tolY, Y64: [rows, F] (all shards side by side); V64: [F, H]."""
-    Fk = Y64.shape[1] // k
-    return (tolY + 2 * (Fk + k + 4) * U32 * np.abs(Y64)) @ np.abs(V64) + 1e-30
+def forward_bound(tolY, Y64, V64, k: int, fused: bool = False, absV=None):
+    """tolY, Y64: [rows, F] (all shards side by side); V64: [F, H].  The
+    literal variant sums each shard's Fk products and then the k partials;
+    the fused one carries one float32 sum through all F products."""
+    F = Y64.shape[1]
+    terms = F if fused else F // k + k
+    aV = np.abs(V64) if absV is None else absV
+    return (tolY + 2 * (terms + 4) * U32 * np.abs(Y64)) @ aV + 1e-30
 
 
 def assert_within(got, ref, bound, what: str, max_report: int = 5):
@@ -221,6 +254,31 @@ def attn_core_bound(qkv64, A, B: int, S: int, hk: int, d: int, causal: bool, e_s
         es = np.repeat(e_s.transpose(0, 2, 1).reshape(B * S, hk), d, axis=1)
         bound = bound + 2 * es * W + U16 * W
     return bound + 1e-30
+
+
+def attn_rows_bound(qkv64, rows, S: int, hk: int, d: int, A, causal: bool = True):
+    """Element-wise bound for rows `rows` (indices into [B S]) of the GPU
+    attention A from exact q, k, v (see the module docstring): the per-row
+    softmax weights are evaluated here in float64 for the bound only."""
+    Hk = hk * d
+    out = np.empty_like(A)
+    for r, m in enumerate(np.asarray(rows)):
+        b, t = divmod(int(m), S)
+        n = t + 1 if causal else S
+        base = b * S
+        for h in range(hk):
+            q = qkv64[m, h * d:(h + 1) * d]
+            K = qkv64[base:base + n, Hk + h * d:Hk + (h + 1) * d]
+            aV = np.abs(qkv64[base:base + n, 2 * Hk + h * d:2 * Hk + (h + 1) * d])
+            s = K @ q / np.sqrt(d)
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            W = p @ aV
+            e_s = 2 * (d + 2) * U32 * float((np.abs(K) @ np.abs(q)).max()) / np.sqrt(d)
+            a = np.abs(A[r, h * d:(h + 1) * d])
+            out[r, h * d:(h + 1) * d] = ((1.5 * U16 + 2.0 ** -16 + 4 * (n + 2) * U32 + 2 * e_s) * W
+                                         + 1.01 * U16 * a)
+    return out + 1e-30
 
 
 def attn_score_err(qkv64, B: int, S: int, hk: int, d: int, H: int, X64=None, Wq=None, Wk=None):

@@ -1,6 +1,7 @@
 """Host-side checks of the C ABI that need no GPU.
 
-The library must load and export every function include/tp_mlp.h declares, and
+The library must load and export every function include/tp_mlp.h (the product
+interface) and include/tp_mlp_dev.h (the tile-measurement hooks) declare, and
 every argument error must be reported before any HIP call (so these calls are
 safe without a device: fake, aligned, non-NULL pointers are never touched).
 """
@@ -12,18 +13,19 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tp_mlp.h")
+DEV_HEADER = os.path.join(ROOT, "include", "tp_mlp_dev.h")
 
 
 @pytest.fixture(scope="module")
 def L():
     import tensor_transformer_mlp_amd as tpm
-    from tensor_transformer_mlp_amd import build
-    build.build_lib(force=False)
-    return tpm.lib()
+    return tpm.lib()   # built by __graft_entry__.build(); raises if it is not
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(path=None):
+    if path is None:
+        return _declared(HEADER) | _declared(DEV_HEADER)
+    text = open(path).read()
     return set(re.findall(r"^(?:int|size_t|const char\s*\*)\s*(tp_\w+)\s*\(", text, re.M))
 
 
@@ -53,6 +55,10 @@ def test_exports_every_declared_symbol(L):
                      "tp_mlp_col_gelu_shards_tile", "tp_mlp_row_partial_shards_tile"}
     for n in names:
         assert hasattr(L, n), n
+    # the measurement hooks live in the dev header only
+    assert _declared(DEV_HEADER) == {"tp_gemm_tiles", "tp_mlp_step_tile", "tp_mlp_col_gelu_shards_tile",
+                                     "tp_mlp_row_partial_shards_tile"}
+    assert not _declared(HEADER) & _declared(DEV_HEADER)
 
 
 def test_python_constants_match_header():
@@ -670,6 +676,9 @@ def test_library_binds_torchs_hip_runtime():
     launch would fail.  Checked in a fresh interpreter (no GPU is touched)."""
     import subprocess
     import sys
+    from _helpers import gpu_initialised
+    if gpu_initialised():
+        pytest.skip("this process has initialised the GPU: it must not start a child interpreter")
     code = ("import os, sys, tensor_transformer_mlp_amd as t; t.lib(); import torch; "
             "libs = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}; "
             "d = os.path.realpath(os.path.join(os.path.dirname(torch.__file__), 'lib')); "

@@ -6,7 +6,6 @@ the measured HBM traffic once the kernel source differs from the one the
 counters were taken on."""
 import json
 import os
-import subprocess
 import sys
 
 import pytest
@@ -27,11 +26,13 @@ def gpt2():
     return inputs.WORKLOADS["gpt2_small"]
 
 
-def test_more_than_one_gpu_is_refused():
-    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
-                       text=True, timeout=120)
-    assert r.returncode == 2
-    assert "one GPU" in r.stderr and r.stdout == ""
+def test_more_than_one_gpu_is_refused(bench, capsys):
+    """Run in this process: the refusal comes before anything touches the GPU."""
+    with pytest.raises(SystemExit) as e:
+        bench.main(["--gpus", "2"])
+    assert e.value.code == 2
+    out = capsys.readouterr()
+    assert "one GPU" in out.err and out.out == ""
 
 
 def test_kernel_bytes_and_flops_closed_forms(bench, gpt2):

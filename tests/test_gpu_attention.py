@@ -12,8 +12,8 @@ float64 computation; expected values come from the oracle).
 import numpy as np
 import pytest
 
-from _helpers import (U32, assert_within, attn_core_bound, attn_score_err, f64, from_dev, gemm_bound,
-                      rel_fro, say, to_dev)
+from _helpers import (U32, assert_within, attn_core_bound, attn_rows_bound, attn_score_err, f64, from_dev,
+                      gemm_bound, rel_fro, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -236,3 +236,52 @@ def test_attn_workload_sampled_rows(tpm, orc, name):
     assert rel_fro(Zg, Zr) <= 1e-2
     for j in range(len(rows)):
         assert rel_fro(Zg[j], Zr[j]) <= 2e-2, rows[j]
+
+
+def _late_positions(S):
+    """Query positions that reach deep into a sequence: the first key blocks,
+    both halves of the first 256-query blocks (the wide-grid kernel's two
+    query groups per wave), the middle, and the last positions before and
+    after 32-, 64- and 128-row block boundaries."""
+    pos = {0, 1, 31, 32, 63, 64, 127, 128, 160, 191, 192, 224, 255, 256,
+           S // 2 - 1, S // 2, S // 2 + 100, S - 257, S - 256, S - 129, S - 128, S - 100, S - 65, S - 64,
+           S - 33, S - 32, S - 2, S - 1}
+    return sorted(p for p in pos if 0 <= p < S)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["gpt2_small", "llama7b", "gpt3_175b", "long_seq"])
+def test_attn_core_late_queries(tpm, orc, name):
+    """The attention kernel at the workloads' full sequence lengths (S = 1024,
+    2048, 2048 and 32768), every shard of the workload in one launch (the
+    benchmark's launch configuration: the long-sequence one runs the wide-grid
+    kernel with two query groups per wave), from given bf16 projections drawn
+    on the host; query rows deep into the sequences, every head of every
+    shard, against the oracle's rows-only attention, element by element."""
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    w = inputs.WORKLOADS[name]
+    nh, k = w.heads, w.k
+    hk, d = nh // k, w.H // nh
+    Hk, M, S = hk * d, w.M, w.S
+    n = min(k, tpm.TP_MAX_BATCH)
+    say("attn_core late queries %s: B=%d S=%d heads/shard=%d d=%d shards=%d" % (name, w.B, S, hk, d, n))
+    qkv_h = [inputs.draw(inputs.STREAM_X, (M, 3 * Hk), 1.0, "bf16", seed=2000 + i) for i in range(n)]
+    QKV = [to_dev(x) for x in qkv_h]
+    A = [torch.empty(M, Hk, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    tpm.tp_attn_core_shards(QKV, A, w.B, S, hk, d, causal=True)
+    torch.cuda.synchronize()
+    pos = _late_positions(S)
+    seqs = sorted({0, w.B - 1})
+    rows = np.array([b * S + t for b in seqs for t in pos])
+    rows_t = torch.from_numpy(rows).cuda()
+    for i in range(n):
+        q64 = f64(qkv_h[i])
+        ref = orc.attn_core_rows(q64, w.B, S, hk, d, rows, True)
+        got = f64(from_dev(A[i].index_select(0, rows_t)))
+        assert np.all(np.isfinite(got))
+        assert_within(got, ref, attn_rows_bound(q64, rows, S, hk, d, ref, True), "%s shard %d A" % (name, i))
+        err = rel_fro(got, ref)
+        say("  %s shard %d: rel_fro on %d late rows = %.3e" % (name, i, rows.size, err))
+        assert err <= 1e-2
+        del q64

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from _helpers import (U32, assert_within, f64, forward_bound, from_dev, rel_fro, say, swiglu_bound,
-                      to_dev)
+                      tile_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -155,24 +155,39 @@ def test_swiglu_fused_equals_literal_and_empty(tpm):
     assert Z0.numel() == 0 and Y0.numel() == 0
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["tiny", "gpt2_small", "llama7b", "gpt3_175b", "long_seq"])
-def test_swiglu_workload_sampled_rows(tpm, orc, name):
-    """Full-size SwiGLU forward in the benchmark's launch configuration;
-    sampled rows against the oracle."""
+def test_swiglu_workload_tile_rows(tpm, orc, name):
+    """Full-size SwiGLU forward in the benchmark's launch configuration, both
+    variants; rows covering every 256-row tile of the output (all rows of the
+    tiny workload) against the oracle, element by element with the SwiGLU
+    bound through V."""
     import torch
     from tensor_transformer_mlp_amd import inputs
     w = inputs.WORKLOADS[name]
     say("workload swiglu %s M=%d H=%d F=%d k=%d" % (name, w.M, w.H, w.F, w.k))
     inp = inputs.make_swiglu(w)
     X, Wg, Wu, V = inp["X"], inp["Wg"], inp["Wu"], inp["V"]
-    Fk = w.Fk
-    Z = tpm.tp_swiglu_shard_forward(to_dev(X), [to_dev(x) for x in inputs.col_slices(Wg, w.k)],
-                                    [to_dev(x) for x in inputs.col_slices(Wu, w.k)],
-                                    [to_dev(np.ascontiguousarray(V[i * Fk:(i + 1) * Fk])) for i in range(w.k)])
+    Fk, k = w.Fk, w.k
+    args = (to_dev(X), [to_dev(x) for x in inputs.col_slices(Wg, k)], [to_dev(x) for x in inputs.col_slices(Wu, k)],
+            [to_dev(np.ascontiguousarray(V[i * Fk:(i + 1) * Fk])) for i in range(k)])
+    Zl = tpm.tp_swiglu_shard_forward(*args, fused=False)
+    Zf = tpm.tp_swiglu_shard_forward(*args, fused=True)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(7)
-    rows = np.sort(rng.choice(w.M, min(12, w.M), replace=False))
-    Zg = f64(from_dev(Z[torch.from_numpy(rows).cuda()]))
-    Zr = orc.swiglu_forward_rows(X, Wg, Wu, V, w.k, rows)
-    assert rel_fro(Zg, Zr) <= (1e-2 if w.dtype == "bf16" else 1e-5)
-    assert np.all(np.isfinite(Zg))
+    del args
+    rows = np.arange(w.M) if w.M <= 64 else tile_rows(w.M)
+    rows_t = torch.from_numpy(rows).cuda()
+    Zr = orc.swiglu_forward_rows(X, Wg, Wu, V, k, rows)
+    X64 = f64(X[rows])
+    Wg64, Wu64, V64 = f64(Wg), f64(Wu), f64(V)
+    G, U = X64 @ Wg64, X64 @ Wu64
+    Y = np.concatenate([orc.swiglu_col(X[rows], Wg, Wu, k, i) for i in range(k)], axis=1)
+    tolY = swiglu_bound(X64, Wg64, Wu64, G, U, Y, w.dtype)
+    tol = 1e-2 if w.dtype == "bf16" else 1e-5
+    for label, fused, Zd in (("literal", False, Zl), ("fused", True, Zf)):
+        Zg = f64(from_dev(Zd.index_select(0, rows_t)))
+        assert np.all(np.isfinite(Zg))
+        assert_within(Zg, Zr, forward_bound(tolY, Y, V64, k, fused=fused), "%s Z (%s)" % (name, label))
+        err = rel_fro(Zg, Zr)
+        say("  %s: rel_fro on %d rows covering every row tile = %.3e (%s)" % (name, rows.size, err, label))
+        assert err <= tol

@@ -186,3 +186,33 @@ def test_attention_splits_and_numpy(oracle_mod, causal):
     rows = [0, 6, 7, 13, 3]
     np.testing.assert_allclose(oracle_mod.attn_forward_rows(X, Wq, Wk, Wv, bq, bk, bv, Wo, nh, S, 4, rows, causal),
                                Zs[4][rows], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_core_rows(oracle_mod, causal):
+    """The rows-only evaluation of the attention core equals the whole-output
+    one on the same rows bit for bit (the same per-row evaluation, pinned
+    above), and an independent numpy softmax attention of those rows to
+    1e-12; rows from both sequences, first, middle and last positions."""
+    rng = np.random.default_rng(11 + causal)
+    B, S, hk, d = 2, 37, 3, 8
+    Hk = hk * d
+    qkv = rng.standard_normal((B * S, 3 * Hk)) * 1.5
+    rows = np.array([0, 1, 17, 36, 37, 38, 55, 73])
+    full = oracle_mod.attn_core(qkv, B, S, hk, d, causal)
+    got = oracle_mod.attn_core_rows(qkv, B, S, hk, d, rows, causal)
+    np.testing.assert_array_equal(got, full[rows])
+    for r, m in enumerate(rows):
+        b, t = divmod(int(m), S)
+        n = t + 1 if causal else S
+        for h in range(hk):
+            q = qkv[m, h * d:(h + 1) * d]
+            K = qkv[b * S:b * S + n, Hk + h * d:Hk + (h + 1) * d]
+            V = qkv[b * S:b * S + n, 2 * Hk + h * d:2 * Hk + (h + 1) * d]
+            s = K @ q / np.sqrt(d)
+            p = np.exp(s - s.max())
+            ref = (p / p.sum()) @ V
+            np.testing.assert_allclose(got[r, h * d:(h + 1) * d], ref, rtol=0, atol=1e-12)
+    assert oracle_mod.attn_core_rows(qkv, B, S, hk, d, np.array([], dtype=np.int64), causal).shape == (0, Hk)
+    with pytest.raises(IndexError):
+        oracle_mod.attn_core_rows(qkv, B, S, hk, d, [B * S], causal)
