@@ -164,10 +164,12 @@ size_t tp_mlp_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dtype
  * flags = 0: every P_i is materialised (P_0 in Z, the rest in the workspace)
  * and tp_shard_reduce sums them; this is the literal one-GPU stand-in for the
  * all-reduce.  flags = TP_FUSED_ACCUM: the row GEMMs of a batch of shards run
- * as one kernel in which every output tile forms each shard's product in its
- * own float32 accumulator and adds them into Z in shard order, so no partial
- * goes through memory.  Both perform the same float32 additions in the same
- * order and give bit-identical Z.
+ * as one kernel in which every output tile carries one float32 accumulator
+ * through the products of every shard in shard order, so no partial goes
+ * through memory: the row-parallel identity sum_i Y_i V_i = [Y_0 ... Y_{k-1}] V
+ * ("千亿参数模型如何拆分到多张GPU上训练", 方案二) evaluated as the unsplit GEMM.
+ * The two variants give the same sum up to float32 rounding; each is
+ * deterministic (the same bits on every run).
  */
 int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const* b,
                          const void* const* V, int k, int64_t M, int64_t H, int64_t Fk,
@@ -221,9 +223,9 @@ size_t tp_mlp_sp_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, int dt
  * tp_mlp_shard_forward, with O a HOST array of k device pointers to [M/k, H]
  * blocks of `out_dtype`, which k must divide M, and `workspace` of
  * tp_mlp_sp_workspace_bytes(...) bytes.  flags = TP_FUSED_ACCUM sums the
- * shards inside the row GEMMs (one partial in memory instead of k); both
- * give bit-identical blocks, and the float32 blocks equal X + Z of
- * tp_mlp_shard_forward bit for bit.
+ * shards inside the row GEMMs (one partial in memory instead of k), as for
+ * tp_mlp_shard_forward; the float32 blocks equal X + Z of
+ * tp_mlp_shard_forward with the same flags, bit for bit.
  */
 int tp_mlp_shard_forward_sp(const void* X, const void* const* W, const void* const* b,
                             const void* const* V, int k, int64_t M, int64_t H, int64_t Fk,
@@ -406,8 +408,9 @@ size_t tp_mlp_backward_workspace_bytes(int k, int64_t M, int64_t H, int64_t Fk, 
  *
  * W, b, V, dW, db and dV are HOST arrays of k device pointers (b == NULL: no
  * bias; db == NULL: no bias gradient; otherwise every entry is non-NULL).
- * flags: TP_FUSED_ACCUM folds the sum of the P_i into the dX GEMMs (same
- * additions in the same order as the literal sum, bit-identical dX);
+ * flags: TP_FUSED_ACCUM folds the sum of the P_i into the dX GEMMs (one
+ * float32 accumulator through every shard's products, as in the forward; the
+ * same dX up to float32 rounding);
  * TP_GRAD_ACCUMULATE adds into dW, db and dV.  M == 0 leaves dX empty and
  * gives zero (or unchanged) parameter gradients; X, dZ and dX may then be
  * NULL.
@@ -436,9 +439,11 @@ int tp_mlp_col_gelu_shards(const void* X, const void* const* W, const void* cons
 
 /* tp_mlp_row_partial for shards 0..n-1: Z[i] (+)= Y[i] V[i].  With
  * TP_SUM_SHARDS, Z[0] = Y[0] V[0] + ... + Y[n-1] V[n-1] (or Z[0] + ... with
- * TP_ACCUMULATE), each product in its own float32 accumulator and the sum
- * formed in shard order: the same values as n partials followed by
- * tp_shard_reduce (only Z[0] is used). */
+ * TP_ACCUMULATE) as one GEMM [Y[0] ... Y[n-1]] [V[0]; ...; V[n-1]]: one float32
+ * accumulator per output element runs through the shards in order (starting
+ * at Z[0] with TP_ACCUMULATE, so a batch split over several calls gives the
+ * same bits as one call); equal to n partials followed by tp_shard_reduce up
+ * to float32 rounding (only Z[0] is used). */
 int tp_mlp_row_partial_shards(const void* const* Y, const void* const* V, float* const* Z, int n,
                               int64_t M, int64_t Fk, int64_t H, int dtype, unsigned flags,
                               void* stream);

@@ -67,17 +67,12 @@ GemmParams base_params(const GemmBatch& b, int tile) {
 //   * otherwise 128x128 (two workgroups per CU);
 //   * K % 32 != 0 (K ends inside a 32-deep stage): the ragged-K variant of the
 //     128x128 tile.
-// A group sum keeps two accumulator sets, so it uses tiles of at most
-// 4 fragments per wave: 128x256 (4 stages from 512 workgroups up, 3 stages
-// below) when it gives at least 192 workgroups, else the 4-wave 128x128 tile
-// (two workgroups per CU).
+// A group sum is one GEMM of the output's size (its K runs through every
+// group): the same rule with one group.
 int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K, int groups, bool group_sum) {
   (void)layout;
   if (K % 32) return kTailTile;
-  if (group_sum) {
-    const int64_t t = tiles_of(6, M, N);
-    return t >= 512 ? 5 : t >= 192 ? 6 : 7;
-  }
+  if (group_sum) groups = 1;
   const int64_t t256 = tiles_of(0, M, N) * groups;
   if (t256 >= 512 || (t256 >= 192 && t256 < 256)) return 0;
   if (N > 128) return 6;
@@ -123,34 +118,12 @@ hipError_t launch_gemm_bf16_batch_tile(int tile, const GemmBatch& b, hipStream_t
 
 GemmBatch single_batch(const GemmArgs& g);
 
-// A group sum whose per-group GEMM alone fills the chip four times over with
-// 256x256 tiles runs group by group instead: group 0 applies the epilogue to
-// C[0] and each later group adds its product into C[0] (the same float32
-// additions in the same order), keeping the larger tile (measured on the
-// row step of the 32768 x 8192 x 4096 shards: 2.09 ms per shard for the
-// 256x256 GEMM that adds into C, 2.14 ms per shard for the 128x256 group sum).
-constexpr int64_t kSequentialSumTiles = 1024;
-
-static bool sequential_sum(const GemmBatch& b) {
-  return b.group_sum && b.groups > 1 && b.K % 32 == 0 && tiles_of(0, b.M, b.N) >= kSequentialSumTiles;
-}
-
 int gemm_bf16_batch_tile(const GemmBatch& b) {
-  if (sequential_sum(b)) return pick_bf16_tile(b.layout, b.M, b.N, b.K, 1, false);
   if (b.epi == kEpiSwiGLU) return pick_swiglu_tile(b.M, b.N, b.K, b.groups);
   return pick_bf16_tile(b.layout, b.M, b.N, b.K, b.groups, b.group_sum);
 }
 
 hipError_t launch_gemm_bf16_batch(const GemmBatch& b, hipStream_t s) {
-  if (sequential_sum(b)) {
-    for (int g = 0; g < b.groups; ++g) {
-      GemmArgs a{b.A[g], b.B[g], nullptr, nullptr, b.C[0], nullptr, b.M, b.N, b.K, b.lda, b.ldb, b.ldc,
-                 b.layout, g == 0 ? b.epi : kEpiAccumF32};
-      const hipError_t e = launch_gemm_bf16(a, s);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-  }
   return launch_gemm_bf16_batch_tile(gemm_bf16_batch_tile(b), b, s);
 }
 

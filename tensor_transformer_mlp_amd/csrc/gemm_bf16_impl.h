@@ -225,11 +225,13 @@ struct OperandFrags {
 };
 
 // GSUM: the groups are summed instead of launched side by side: each output
-// tile runs its K loop through every group in turn, with a fresh float32
-// accumulator per group that is added, in group order, into a running sum z
-// (z starts as group 0's product, or as C itself with kEpiAccumF32), and z is
-// stored once.  Each group's product is bit-identical to that group's own
-// GEMM, so this equals storing every product and summing them left to right.
+// tile runs its K loop through every group in turn with one float32
+// accumulator (which starts at zero, or at C itself with kEpiAccumF32), and
+// stores once.  This is the GEMM of the groups' A operands side by side with
+// their B operands stacked, [A_0 ... A_{n-1}] [B_0; ...; B_{n-1}], accumulated
+// in group order; it equals the sum of the groups' products up to float32
+// rounding, and a batch run in several launches (accumulating into C) gives
+// the same bits as one launch.
 //
 // DUAL (kEpiSwiGLU): two B operands, the gate B and the up projection B2, of
 // the same shape.  The stage holds A and two B sub-tiles of BN / 2 columns
@@ -239,12 +241,12 @@ struct OperandFrags {
 // SiLU(gate) * up: a BM x BN / 2 tile of the output.
 // Waves per SIMD to ask the register allocator for: as many as the
 // workgroups that the tile's LDS stages let share a CU bring (two 8-wave
-// workgroups of 72 KB: four waves per SIMD, so at most 128 VGPRs each).  A
-// group sum keeps a second accumulator set, and the training epilogue a
-// second output; both are left to the allocator (at 128 VGPRs they would
-// spill, measured slower than one workgroup per CU).
+// workgroups of 72 KB: four waves per SIMD, so at most 128 VGPRs each).  The
+// training epilogue keeps a second output and is left to the allocator (at
+// 128 VGPRs it would spill, measured slower than one workgroup per CU).
 constexpr int gemm_waves_per_eu(int EPI, int BM, int BN, int WM, int WN, int NBUF, bool GSUM) {
-  if (GSUM || EPI == kEpiBiasGeluSave) return 1;
+  (void)GSUM;
+  if (EPI == kEpiBiasGeluSave) return 1;
   const int per_cu = (160 * 1024) / (NBUF * (BM + BN) * 64);
   const int w = per_cu * WM * WN / 4;
   return w < 1 ? 1 : (w > 4 ? 4 : w);
@@ -388,54 +390,25 @@ void gemm_bf16_kernel(GemmParams p) {
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  // Group sum: z, the running sum over groups (same fragment layout as acc).
-  f32x16_t z[GSUM ? FM : 1][GSUM ? FN : 1];
-  const bool z_from_c = GSUM && EPI == kEpiAccumF32;
-  if constexpr (GSUM) {
-    if (z_from_c) {
-      const int l32 = lane & 31, hcol = 4 * (lane >> 5);
+  // Group sum accumulating into C: the accumulator starts at C's values.
+  if constexpr (GSUM && EPI == kEpiAccumF32) {
+    const int l32 = lane & 31, hcol = 4 * (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WTM + i * 32 + l32;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
-            f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (m < p.M && n < p.N)
-              v = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.t.C[0]) +
-                                                    (int64_t)m * p.ldc + n);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[i][j][4 * gq + e] = v[e];
-          }
-      }
-    }
-  }
-  int cmp_g = 0, cmp_kt = 0;
-  // After the last stage of a group: z (+)= acc, acc = 0.
-  auto fold = [&]() {
-    if (++cmp_kt < nk) return;
-    cmp_kt = 0;
-    if (cmp_g == 0 && !z_from_c) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) z[i][j] = acc[i][j];
-    } else {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) z[i][j] = z[i][j] + acc[i][j];
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm * WTM + i * 32 + l32;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    ++cmp_g;
-  };
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
+          f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (m < p.M && n < p.N)
+            v = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.t.C[0]) + (int64_t)m * p.ldc + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * gq + e] = v[e];
+        }
+    }
+  }
 
   bf16x8_t fa[2][FM], fb[2][FN];
   auto read_frags = [&](auto fset, auto bset, int ks) {
@@ -450,7 +423,7 @@ void gemm_bf16_kernel(GemmParams p) {
   // feeding the matrix pipe ahead of the other wave's loads and LDS reads
   // (0 to 1.3% faster on the 256x256 tile across the four bf16 workloads'
   // column and row steps, measured; no gain with two workgroups per CU).
-  constexpr bool kPrio = !GSUM && !DUAL && WM * WN == 8 && gemm_waves_per_eu(EPI, BM, BN, WM, WN, NBUF, GSUM) == 2;
+  constexpr bool kPrio = !DUAL && WM * WN == 8 && gemm_waves_per_eu(EPI, BM, BN, WM, WN, NBUF, GSUM) == 2;
   auto mfmas = [&](auto fset) {
     constexpr int f = decltype(fset)::value;
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
@@ -507,7 +480,6 @@ void gemm_bf16_kernel(GemmParams p) {
       if (m < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (GSUM) fold();
   };
   // The loop body walks the NBUF buffers in order; an early exit handles a
   // stage count that is not a multiple of NBUF (uniform across the workgroup).
@@ -533,7 +505,7 @@ void gemm_bf16_kernel(GemmParams p) {
   void* Cout = p.t.C[grp];
   void* aux = p.t.aux[grp];
   const uint16_t* bias = p.t.bias[grp];
-  bool accumulate = EPI == kEpiAccumF32 && !GSUM;  // (the group sum already holds C)
+  bool accumulate = EPI == kEpiAccumF32 && !GSUM;  // (a group sum's accumulator started at C)
   if (slice > 0) {  // a K-split partial: plain float32 store
     Cout = p.part + ((int64_t)grp * (p.slices - 1) + slice - 1) * p.part_stride;
     ldc = N;
@@ -600,11 +572,7 @@ void gemm_bf16_kernel(GemmParams p) {
             *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = o;
             continue;
           }
-          if constexpr (GSUM)
-            v = f32x4_t{z[i][j][4 * gq], z[i][j][4 * gq + 1], z[i][j][4 * gq + 2], z[i][j][4 * gq + 3]};
-          else
-            v = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
-                        acc[i][j][4 * gq + 3]};
+          v = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]};
           if constexpr (kBias) {
             v += bias4[j][gq];
             if constexpr (EPI == kEpiBias) {
@@ -640,7 +608,7 @@ void gemm_bf16_kernel(GemmParams p) {
           } else if constexpr (EPI == kEpiStoreF32) {
             *reinterpret_cast<f32x4_t*>(static_cast<float*>(Cout) + idx) = v;
           } else {
-            *reinterpret_cast<f32x4_t*>(static_cast<float*>(Cout) + idx) = old4[j][gq] + v;
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(Cout) + idx) = accumulate ? old4[j][gq] + v : v;
           }
         }
       }
@@ -720,8 +688,6 @@ void gemm_bf16_kernel(GemmParams p) {
               if constexpr (DUAL) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a[e] = silu_f32(acc[i][j][4 * gq + e]) * acc[i][FNO + j][4 * gq + e];
-              } else if constexpr (GSUM) {
-                a = f32x4_t{z[i][j][4 * gq], z[i][j][4 * gq + 1], z[i][j][4 * gq + 2], z[i][j][4 * gq + 3]};
               } else {
                 a = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
                             acc[i][j][4 * gq + 3]};
@@ -763,11 +729,9 @@ void gemm_bf16_kernel(GemmParams p) {
     epilogue(std::true_type{});
 }
 
-// A group sum holds two accumulator sets per wave: tiles with at most 4
-// fragments per wave.
-constexpr bool tile_allows_group_sum(int t) {
-  return (kTiles[t].bm / kTiles[t].wm / 32) * (kTiles[t].bn / kTiles[t].wn / 32) <= 4;
-}
+// A group sum keeps one accumulator set, like any other GEMM: every tile but
+// the 4-wave 256x256 one (whose epilogue spills) is compiled for it.
+constexpr bool tile_allows_group_sum(int t) { return !(kTiles[t].bm == 256 && kTiles[t].bn == 256 && kTiles[t].wm * kTiles[t].wn == 4); }
 
 // SwiGLU splits a tile's BN columns into a gate and an up sub-tile of BN / 2
 // columns each (MN-major sub-tiles need 128, 256 or 512 columns) and every

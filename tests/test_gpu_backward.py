@@ -2,7 +2,7 @@
 by element, at small and ragged sizes (several tiles, partial tiles in M, N
 and K, K-split weight gradients with a ragged last slice), plus the edge
 cases: M = 0, M = 1, k = 1, no bias, gradient accumulation, in-place dA,
-guard bands around every output, literal == fused, run-to-run determinism.
+guard bands around every output, run-to-run determinism of both variants.
 
 Inputs are seeded draws (X, W, b, V, dZ and, for the per-step entry points,
 G, Y and dA themselves); expected values come from the oracle only, and the
@@ -220,8 +220,10 @@ def test_grad_input_partial_parity(tpm, orc, M, Fk, H, dtype, accumulate):
     assert rel_fro(got, ref) <= 1e-5
 
 
-def backward_bounds(orc, X, W, b, V, dZ, k, dtype):
-    """Element-wise bounds of the whole backward (small shapes, all entries)."""
+def backward_bounds(orc, X, W, b, V, dZ, k, dtype, fused=False):
+    """Element-wise bounds of the whole backward (small shapes, all entries).
+    dX: each shard's Fk products then the k partials (literal), or one float32
+    sum through all F products (fused)."""
     M, H = X.shape
     F = W.shape[1]
     Fk = F // k
@@ -234,7 +236,7 @@ def backward_bounds(orc, X, W, b, V, dZ, k, dtype):
         bV[sl] = gemm_bound(t["Y"].T, f64(dZ), M, ea=t["tolY"].T)
         bW[:, sl] = gemm_bound(f64(X).T, t["dA"], M, eb=t["errdA"])
         bb[sl] = t["errdA"].sum(axis=0) + 2 * (M + 2) * U32 * (np.abs(t["dA"]) + t["errdA"]).sum(axis=0)
-        part = gemm_bound(t["dA"], f64(W[:, sl]).T, Fk, ea=t["errdA"])
+        part = gemm_bound(t["dA"], f64(W[:, sl]).T, F if fused else Fk, ea=t["errdA"])
         bX += part + (k + 2) * U32 * ((np.abs(t["dA"]) + t["errdA"]) @ np.abs(f64(W[:, sl])).T)
     del absX
     return bX + 1e-30, bW + 1e-30, bb + 1e-30, bV + 1e-30
@@ -275,7 +277,7 @@ def test_shard_backward_parity(tpm, orc, M, H, F, k, dtype, bias, fused):
     for buf, _ in [(bx, None)] + gW + gV + (gb if bias else []):
         assert _guards_ok(torch, buf, pad)
     rX, rW, rb, rV = orc.backward(X, W, b, V, dZ, k)
-    bX, bW, bb, bV = backward_bounds(orc, X, W, b, V, dZ, k, dtype)
+    bX, bW, bb, bV = backward_bounds(orc, X, W, b, V, dZ, k, dtype, fused=fused)
     tol = 1e-2 if dtype == "bf16" else 1e-5
     gotX = f64(from_dev(dX))
     gotW = np.concatenate([f64(from_dev(t)) for _, t in gW], axis=1)
@@ -303,20 +305,27 @@ def _bwd_args(tpm, M, H, F, k, dtype, seed):
             to_dev(dZ))
 
 
-def test_backward_fused_equals_literal_and_deterministic(tpm):
+def test_backward_fused_and_literal_deterministic(tpm):
+    """Each variant gives the same bits on every run; the parameter gradients
+    do not involve the dX sum and are equal across the variants bit for bit;
+    the two dX (the same sum, rounded in different places) agree to float32
+    rounding."""
     import torch
     args = _bwd_args(tpm, 2100, 136, 1088, 8, "bf16", 5)
     say("backward fused vs literal")
     r1 = tpm.tp_mlp_shard_backward(*args, fused=False)
     r2 = tpm.tp_mlp_shard_backward(*args, fused=True)
     r3 = tpm.tp_mlp_shard_backward(*args, fused=False)
+    r4 = tpm.tp_mlp_shard_backward(*args, fused=True)
     torch.cuda.synchronize()
-    for a, b_, c in zip(r1, r2, r3):
+    for a, b_, c, d in zip(r1, r2, r3, r4):
         if isinstance(a, list):
-            for x, y, z in zip(a, b_, c):
-                assert torch.equal(x, y) and torch.equal(x, z)
+            for x, y, z, u in zip(a, b_, c, d):
+                assert torch.equal(x, y) and torch.equal(x, z) and torch.equal(y, u)
         else:
-            assert torch.equal(a, b_) and torch.equal(a, c)
+            assert torch.equal(a, c) and torch.equal(b_, d)
+            assert float(torch.linalg.vector_norm((a - b_).double())) <= 1e-5 * float(
+                torch.linalg.vector_norm(a.double()))
 
 
 def test_backward_gradient_accumulation(tpm):

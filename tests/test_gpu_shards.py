@@ -1,15 +1,20 @@
 """GPU checks of the batched (*_shards) entry points: a batch of n shards in one
-launch gives bit-identical results to n single-shard calls, and the
-shard-order sum (TP_SUM_SHARDS) is bit-identical to the materialised partials
-followed by tp_shard_reduce.  Covers grouped tiles, ragged shapes, the
-ragged-K variant, both dtypes and the sequential path taken by very large
-sums; the single-shard calls themselves are checked against the oracle in
-test_gpu_parity_small.py and test_gpu_backward.py.
+launch gives bit-identical results to n single-shard calls; the shard sum
+(TP_SUM_SHARDS) is the unsplit GEMM of the shards side by side, [Y_0 ...
+Y_{n-1}] [V_0; ...; V_{n-1}] (the row-parallel identity of "千亿参数模型如何拆分到多张
+GPU上训练", 方案二): in bf16 with Fk a multiple of 32 it equals the single GEMM over
+the concatenated operands bit for bit, it agrees with the materialised
+partials followed by tp_shard_reduce within the float32 accumulation bound,
+and a batch split over several calls (TP_ACCUMULATE) gives the same bits as
+one call.  In float32 the sum runs shard by shard and equals partials +
+reduce bit for bit.  Covers grouped tiles, ragged shapes, the ragged-K
+variant and both dtypes; the single-shard calls themselves are checked
+against the oracle in test_gpu_parity_small.py and test_gpu_backward.py.
 """
 import numpy as np
 import pytest
 
-from _helpers import say, to_dev
+from _helpers import U32, assert_within, f64, from_dev, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +65,7 @@ def test_forward_shards_bitwise(tpm, M, H, Fk, n, dtype):
         assert torch.equal(P1, Pb[i]), i
     Zr = tpm.tp_shard_reduce(Pb)
     torch.cuda.synchronize()
-    assert torch.equal(Zr, Zs), "shard-order sum differs from partials + reduce"
+    _check_sum(tpm, torch, Zs, Zr, Yb, V, dtype, Fk, transposed=False)
 
 
 @pytest.mark.parametrize("M,H,Fk,n,dtype", CASES)
@@ -97,11 +102,35 @@ def test_backward_shards_bitwise(tpm, M, H, Fk, n, dtype):
         assert torch.equal(v1, dV[i]), ("dV", i)
     dXr = tpm.tp_shard_reduce(dXp)
     torch.cuda.synchronize()
-    assert torch.equal(dXr, dXs)
+    _check_sum(tpm, torch, dXs, dXr, dA, W, dtype, Fk, transposed=True)
+
+
+def _check_sum(tpm, torch, Zs, Zr, A, B, dtype, Fk, transposed):
+    """Zs: the shard sum of A_i B_i (B_i^T when transposed); Zr: partials +
+    tp_shard_reduce.  float32: equal bit for bit.  bf16: within the float32
+    accumulation bound of both orders, and, when Fk is a multiple of 32, equal
+    bit for bit to one GEMM over the concatenated operands."""
+    if dtype == "f32":
+        assert torch.equal(Zs, Zr), "float32 shard sum differs from partials + reduce"
+        return
+    n = len(A)
+    Acat = torch.cat(A, dim=1).contiguous()
+    Bcat = torch.cat(B, dim=1 if transposed else 0).contiguous()
+    a64 = np.abs(f64(from_dev(Acat)))
+    b64 = np.abs(f64(from_dev(Bcat)))
+    mag = a64 @ (b64.T if transposed else b64)
+    bound = 2 * (n * Fk + n + 4) * U32 * 2 * mag + 1e-30
+    assert_within(f64(from_dev(Zs)), f64(from_dev(Zr)), bound, "shard sum vs partials + reduce")
+    if Fk % 32 == 0:
+        Zu = (tpm.tp_mlp_grad_input_partial(Acat, Bcat) if transposed else tpm.tp_mlp_row_partial(Acat, Bcat))
+        torch.cuda.synchronize()
+        assert torch.equal(Zs, Zu), "shard sum differs from the GEMM over the concatenated shards"
 
 
 def test_sum_shards_accumulate_continues_the_order(tpm):
-    """Two batches, the second with TP_ACCUMULATE, equal one left-to-right sum."""
+    """Two batches, the second with TP_ACCUMULATE, give the bits of one batch
+    (the accumulator of the second starts at the first's float32 result),
+    and agree with partials + reduce within the accumulation bound."""
     import torch
     M, H, Fk, n = 300, 136, 264, 6
     say("sum across two batches")
@@ -110,20 +139,24 @@ def test_sum_shards_accumulate_continues_the_order(tpm):
     Z = torch.empty(M, H, device="cuda")
     tpm.tp_mlp_row_partial_shards(Y[:4], V[:4], [Z], sum_shards=True)
     tpm.tp_mlp_row_partial_shards(Y[4:], V[4:], [Z], sum_shards=True, accumulate=True)
+    Z1 = torch.empty(M, H, device="cuda")
+    tpm.tp_mlp_row_partial_shards(Y, V, [Z1], sum_shards=True)
     P = [torch.empty(M, H, device="cuda") for _ in range(n)]
     tpm.tp_mlp_row_partial_shards(Y, V, P)
     Zr = tpm.tp_shard_reduce(P)
     torch.cuda.synchronize()
-    assert torch.equal(Z, Zr)
+    assert torch.equal(Z, Z1)
+    _check_sum(tpm, torch, Z, Zr, Y, V, "bf16", Fk, transposed=False)
 
 
 @pytest.mark.timeout(300)
-def test_large_sum_sequential_path(tpm):
-    """A sum whose per-shard GEMM fills the chip many times over runs shard by
-    shard with the 256x256 tile; still bit-identical to partials + reduce."""
+def test_large_sum(tpm):
+    """A sum whose output fills the chip many times over (256 x 256 tiles, K
+    through both shards) equals the GEMM over the concatenated shards bit for
+    bit, and partials + reduce within the accumulation bound."""
     import torch
     M, H, Fk, n = 16384, 4096, 512, 2
-    say("large sequential sum M=%d H=%d" % (M, H))
+    say("large sum M=%d H=%d" % (M, H))
     Y = [_draw(0, (M, Fk), 0.5, "bf16", 100 + i) for i in range(n)]
     V = [_draw(3, (Fk, H), 0.05, "bf16", 110 + i) for i in range(n)]
     Z = torch.empty(M, H, device="cuda")
@@ -132,4 +165,4 @@ def test_large_sum_sequential_path(tpm):
     tpm.tp_mlp_row_partial_shards(Y, V, P)
     Zr = tpm.tp_shard_reduce(P)
     torch.cuda.synchronize()
-    assert torch.equal(Z, Zr)
+    _check_sum(tpm, torch, Z, Zr, Y, V, "bf16", Fk, transposed=False)
