@@ -381,7 +381,9 @@ def test_backward_transposed_weights_equal_steps(tpm, M, H, F, k, fused):
     """From M = 4096 tokens (bf16) the whole backward multiplies by V_i^T and
     W_i^T through transposed copies of the weights on the GEMM's NN path; the
     step entry points read the weights as transposes (NT).  Both accumulate
-    every output element over K in the same order: equal bit for bit."""
+    every output element over K in the same order: equal bit for bit (the
+    fused dX against the steps' shard sum, the literal one against partials
+    + reduce)."""
     import torch
     say("backward transposed weights M=%d H=%d F=%d k=%d fused=%s" % (M, H, F, k, fused))
     X, Ws, bs, Vs, dZ = _bwd_args(tpm, M, H, F, k, "bf16", 11)
@@ -397,9 +399,13 @@ def test_backward_transposed_weights_equal_steps(tpm, M, H, F, k, fused):
     dW2 = [torch.empty(H, Fk, device="cuda") for _ in range(k)]
     db2 = [torch.empty(Fk, device="cuda") for _ in range(k)]
     tpm.tp_mlp_grad_col_weight_shards(X, dA, dW2, db2)
-    dXp = [torch.empty(M, H, device="cuda") for _ in range(k)]
-    tpm.tp_mlp_grad_input_shards(dA, Ws, dXp)
-    dX2 = tpm.tp_shard_reduce(dXp)
+    if fused:
+        dX2 = torch.empty(M, H, device="cuda")
+        tpm.tp_mlp_grad_input_shards(dA, Ws, [dX2], sum_shards=True)
+    else:
+        dXp = [torch.empty(M, H, device="cuda") for _ in range(k)]
+        tpm.tp_mlp_grad_input_shards(dA, Ws, dXp)
+        dX2 = tpm.tp_shard_reduce(dXp)
     torch.cuda.synchronize()
     assert torch.equal(dX, dX2)
     for i in range(k):

@@ -226,11 +226,13 @@ def test_workload_backward_parity(name):
     assert same, "run-to-run results differ"
     del r2
     rf = tpm.tp_mlp_shard_backward(Xd, Ws, bs, Vs, dZd, fused=True)
+    rf2 = tpm.tp_mlp_shard_backward(Xd, Ws, bs, Vs, dZd, fused=True)
     torch.cuda.synchronize()
-    same = torch.equal(r1[0], rf[0]) and all(torch.equal(a, c) for g1, g2 in zip(r1[1:], rf[1:])
-                                            for a, c in zip(g1, g2))
-    assert same, "literal and fused variants differ"
-    del rf, r1
+    assert torch.equal(rf[0], rf2[0]), "run-to-run results differ (fused dX)"
+    same = all(torch.equal(a, c) for g1, g2 in zip(r1[1:], rf[1:]) for a, c in zip(g1, g2))
+    assert same, "parameter gradients of the literal and fused variants differ"
+    dXfr = from_dev(rf[0].index_select(0, rows_t)).astype(np.float64)
+    del rf, rf2, r1
     torch.cuda.empty_cache()
 
     # dX on sampled rows: every shard's dA_i on those rows.
@@ -238,16 +240,20 @@ def test_workload_backward_parity(name):
     Xr, dZr = X[rows], dZ[rows]
     ref = oracle.backward_rows(Xr, W, b, V, dZr, k)
     bound = np.zeros_like(ref)
+    boundf = np.zeros_like(ref)     # fused: one float32 sum through all F products
     for i in range(k):
         sl = slice(i * Fk, (i + 1) * Fk)
         t = backward_terms(oracle, Xr, W[:, sl], b[sl], V[sl], dZr, w.dtype)
         Wi64 = f64(W[:, sl])
         bound += gemm_bound(t["dA"], Wi64.T, Fk, ea=t["errdA"])
         bound += (k + 2) * U32 * ((np.abs(t["dA"]) + t["errdA"]) @ np.abs(Wi64).T)
+        boundf += gemm_bound(t["dA"], Wi64.T, w.F, ea=t["errdA"])
     assert_within(dXr, ref, bound, "%s dX" % name)
-    err = rel_fro(dXr, ref)
-    say("  %s: dX rel_fro on sampled rows = %.3e (bar %.0e)" % (name, err, tol))
-    assert err <= tol
+    assert_within(dXfr, ref, boundf, "%s dX (fused)" % name)
+    for label, got in (("literal", dXr), ("fused", dXfr)):
+        err = rel_fro(got, ref)
+        say("  %s: dX rel_fro on sampled rows = %.3e (bar %.0e), %s" % (name, err, tol, label))
+        assert err <= tol
 
     # Parameter gradients on sampled columns, over all M rows.
     say("  %s: oracle dW, db, dV on %d columns" % (name, cols.size))
