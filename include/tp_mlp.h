@@ -103,6 +103,9 @@ extern "C" {
 #define TP_SUM_SHARDS 4u      /* row / input-gradient batches: one output, the shard-order sum */
 #define TP_CAUSAL 8u          /* attention: each query attends to keys at or before it only */
 
+/* Size of the device scratch array of tp_mlp_shard_forward_noalloc (per GPU). */
+#define TP_NOALLOC_SCRATCH_BYTES (128u << 20)
+
 /*
  * Column-parallel linear + bias + GeLU of one shard (ColumnParallelLinear
  * forward, "AI大模型分布式训练：张量并行与流水线并行深度实践" §2.1, followed by the
@@ -175,6 +178,28 @@ int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const*
                          const void* const* V, int k, int64_t M, int64_t H, int64_t Fk,
                          int dtype, void* workspace, size_t workspace_bytes, float* Z,
                          unsigned flags, void* stream);
+
+/*
+ * tp_mlp_shard_forward without a workspace argument and without any memory
+ * allocation, for callers that cannot allocate device memory during the call:
+ * code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments, results and errors are those of
+ * tp_mlp_shard_forward (the same Z, bit for bit, for the same flags); the
+ * intermediate Y_i and, for the literal variant, the k - 1 float32 partials
+ * live in a static device array of TP_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends.  The shards run in
+ * batches small enough for the array; when even one shard's Y_i [M, Fk]
+ * (plus, literal, the k - 1 partials [M, H] of 4 bytes) does not fit, the
+ * call returns TP_ERR_WORKSPACE before any launch.  It calls no hipMalloc or
+ * hipFree; the first call on a GPU places the array there (the HIP runtime
+ * loads the library code that holds it), so make one call before capturing
+ * a graph.  All calls on one GPU share its array: calls that overlap in time
+ * on one GPU (on different streams, or from different threads) race on it
+ * and must be ordered by the caller.  The device is that of `stream`.
+ */
+int tp_mlp_shard_forward_noalloc(const void* X, const void* const* W, const void* const* b,
+                                 const void* const* V, int k, int64_t M, int64_t H, int64_t Fk,
+                                 int dtype, float* Z, unsigned flags, void* stream);
 
 /*
  * Sequence parallelism.  Megatron's sequence parallelism also splits the

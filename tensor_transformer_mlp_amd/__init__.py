@@ -61,6 +61,7 @@ __all__ = [
     "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward", "TP_CAUSAL",
     "tp_attn_qkv_shards", "tp_attn_core_shards", "tp_attn_workspace_bytes", "tp_attn_shard_forward",
     "tp_gemm_tiles", "tp_mlp_step_tile", "tp_mlp_col_gelu_shards_tile", "tp_mlp_row_partial_shards_tile",
+    "tp_mlp_shard_forward_noalloc", "TP_NOALLOC_SCRATCH_BYTES",
 ]
 
 TP_F32 = 0
@@ -72,6 +73,7 @@ TP_SUM_SHARDS = 4
 TP_CAUSAL = 8
 TP_MAX_SHARDS = 64
 TP_MAX_BATCH = 16
+TP_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtpmlp.so")
@@ -112,6 +114,8 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_workspace_bytes.restype = sz
         L.tp_mlp_shard_forward.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, sz, vp, cu, vp]
         L.tp_mlp_shard_forward.restype = ci
+        L.tp_mlp_shard_forward_noalloc.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, vp, cu, vp]
+        L.tp_mlp_shard_forward_noalloc.restype = ci
         L.tp_mlp_col_gelu_save.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
         L.tp_mlp_col_gelu_save.restype = ci
         L.tp_mlp_grad_act.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
@@ -342,6 +346,34 @@ def tp_mlp_shard_forward(X, W, b, V, Z=None, workspace=None, fused: bool = False
                                       flags, _stream(stream)), "tp_mlp_shard_forward")
     return Z
 
+
+
+@_on_caller_stream
+def tp_mlp_shard_forward_noalloc(X, W, b, V, Z=None, fused: bool = False, stream=None):
+    """tp_mlp_shard_forward without a workspace: the library keeps the
+    intermediates in its static device scratch array (TP_NOALLOC_SCRATCH_BYTES
+    per GPU) and the call allocates no device memory (only Z, when it is not
+    given, is allocated here before the call).  Calls that overlap in time on
+    one GPU share that array and must be ordered by the caller."""
+    torch = _torch()
+    k = len(W)
+    if k < 1 or len(V) != k or (b is not None and len(b) != k):
+        raise ValueError("W, V (and b) must hold the same number k >= 1 of shards")
+    H = X.shape[-1]
+    M = X.numel() // H if H else 0
+    Fk = W[0].shape[-1]
+    dt = _dtype_code(X)
+    if Z is None:
+        Z = torch.empty(*X.shape[:-1], H, dtype=torch.float32, device=X.device)
+    elif Z.dtype != torch.float32 or Z.numel() != M * H:
+        raise ValueError("Z must be float32 with %d elements" % (M * H))
+    Wp = (ctypes.c_void_p * k)(*[_dev(w, "W[%d]" % i) for i, w in enumerate(W)])
+    Vp = (ctypes.c_void_p * k)(*[_dev(v, "V[%d]" % i) for i, v in enumerate(V)])
+    bp = None if b is None else (ctypes.c_void_p * k)(*[_dev(x, "b[%d]" % i) for i, x in enumerate(b)])
+    _check(lib().tp_mlp_shard_forward_noalloc(_dev(X, "X"), Wp, bp, Vp, k, M, H, Fk, dt, _dev(Z, "Z"),
+                                              TP_FUSED_ACCUM if fused else 0, _stream(stream)),
+           "tp_mlp_shard_forward_noalloc")
+    return Z
 
 def _same_dtype(where, ref, *ts):
     for t in ts:

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, f) for f in (
     "gemm_bf16_nn.hip", "gemm_bf16_nt.hip", "gemm_bf16_tn.hip", "gemm_bf16.hip", "gemm_f32.hip",
-    "reduce.hip", "transpose.hip", "attention.hip", "tp_mlp_abi.cpp")]
+    "reduce.hip", "transpose.hip", "attention.hip", "noalloc.hip", "tp_mlp_abi.cpp")]
 HEADERS = [os.path.join(CSRC, f) for f in ("device_common.h", "gemm_bf16_impl.h", "tp_mlp_kernels.h")]
 DEPS = SOURCES + HEADERS + [os.path.join(INCLUDE, "tp_mlp.h"), os.path.join(INCLUDE, "tp_mlp_dev.h")]
 OBJDIR = os.path.join(HERE, "_build")

@@ -279,15 +279,15 @@ int input_grad_steps(const void* const* dA, const void* const* W, float* const* 
   return run(g, dtype, s);
 }
 
-// The column and row steps of k shards, in batches of up to kMaxGroups
+// The column and row steps of k shards, in batches of up to G (<= kMaxGroups)
 // shards per launch.  col(i0, n) runs the column step of shards i0 ..
 // i0 + n - 1 into Y[0 .. n-1].  Literal (fused == false): partial i goes to
 // part(i) and its pointer to parts[i].  Fused: the row step of every batch
 // adds its shards, in shard order, into part(0) (the first batch stores).
+// The batch size changes no result bit.
 template <class Col, class Part>
 int shard_steps(Col col, const void* const* V, int k, int64_t M, int64_t H, int64_t Fk, int dtype,
-                void* const* Y, bool fused, Part part, const float** parts, hipStream_t s) {
-  const int G = batch_size(k);
+                void* const* Y, bool fused, Part part, const float** parts, hipStream_t s, int G) {
   float* P[kMaxGroups];
   int st;
   for (int i0 = 0; i0 < k; i0 += G) {
@@ -389,6 +389,61 @@ int row_shards(const void* const* Y, const void* const* V, float* const* Z, int 
                    static_cast<hipStream_t>(stream), tile);
 }
 
+// Argument rules of the whole forward (everything but the workspace).
+int check_forward(const void* X, const void* const* W, const void* const* b, const void* const* V, int k,
+                  int64_t M, int64_t H, int64_t Fk, int dtype, const float* Z, unsigned flags) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (flags & ~TP_FUSED_ACCUM) return TP_ERR_FLAGS;
+  if (k < 1 || k > TP_MAX_SHARDS) return TP_ERR_SHAPE;
+  if ((st = check_dims(M, H, Fk))) return st;
+  if (M == 0) return TP_OK;
+  if (!X || !W || !V || !Z) return TP_ERR_NULL;
+  for (int i = 0; i < k; ++i) {
+    if (!W[i] || !V[i] || (b && !b[i])) return TP_ERR_NULL;
+    if (!aligned16(W[i]) || !aligned16(V[i]) || (b && !aligned16(b[i]))) return TP_ERR_ALIGN;
+  }
+  if (!aligned16(X) || !aligned16(Z)) return TP_ERR_ALIGN;
+  return TP_OK;
+}
+
+// The forward's inputs, for the overlap check.
+void forward_regions(const void* X, const void* const* W, const void* const* b, const void* const* V, int k,
+                     int64_t M, int64_t H, int64_t Fk, int dtype, Regions& in) {
+  const size_t e = elt_size(dtype);
+  in.add(X, size_t(M) * size_t(H) * e);
+  for (int i = 0; i < k; ++i) {
+    in.add(W[i], size_t(H) * size_t(Fk) * e);
+    in.add(V[i], size_t(Fk) * size_t(H) * e);
+    if (b) in.add(b[i], size_t(Fk) * e);
+  }
+}
+
+// The whole forward on a buffer `ws` that holds G shards' Y_i [M, Fk] and,
+// for the literal variant, the k - 1 float32 partials after them.
+int run_forward(const void* X, const void* const* W, const void* const* b, const void* const* V, int k,
+                int64_t M, int64_t H, int64_t Fk, int dtype, float* Z, unsigned flags, char* ws, int G,
+                hipStream_t s) {
+  const bool fused = (flags & TP_FUSED_ACCUM) != 0;
+  const size_t y_bytes = round_up(size_t(M) * size_t(Fk) * elt_size(dtype), kWsAlign);
+  const size_t part_bytes = round_up(size_t(M) * size_t(H) * 4, kWsAlign);
+  void* Y[kMaxGroups];
+  for (int j = 0; j < G; ++j) Y[j] = ws + size_t(j) * y_bytes;
+  char* part_base = ws + size_t(G) * y_bytes;
+  const float* parts[TP_MAX_SHARDS];
+  // P_0 (or the fused sum) in Z, P_1 .. P_{k-1} after the Y_i.
+  auto part = [&](int i) {
+    return i == 0 ? Z : reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
+  };
+  auto col = [&](int i0, int n) {
+    return col_steps(X, W + i0, b ? b + i0 : nullptr, Y, nullptr, n, M, H, Fk, dtype, s);
+  };
+  int st = shard_steps(col, V, k, M, H, Fk, dtype, Y, fused, part, parts, s, G);
+  if (st) return st;
+  if (!fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
+  return TP_OK;
+}
+
 // The batch of a bf16 forward step for the tile queries (shapes only).
 int step_batch(int step, int n, int64_t M, int64_t H, int64_t Fk, unsigned flags, GemmBatch& g) {
   int st = check_dims(M, H, Fk);
@@ -488,54 +543,43 @@ int tp_mlp_shard_forward(const void* X, const void* const* W, const void* const*
                          const void* const* V, int k, int64_t M, int64_t H, int64_t Fk,
                          int dtype, void* workspace, size_t workspace_bytes, float* Z,
                          unsigned flags, void* stream) {
-  int st = check_dtype(dtype);
-  if (st) return st;
-  if (flags & ~TP_FUSED_ACCUM) return TP_ERR_FLAGS;
-  if (k < 1 || k > TP_MAX_SHARDS) return TP_ERR_SHAPE;
-  if ((st = check_dims(M, H, Fk))) return st;
-  if (M == 0) return TP_OK;
-  if (!X || !W || !V || !Z) return TP_ERR_NULL;
-  for (int i = 0; i < k; ++i) {
-    if (!W[i] || !V[i] || (b && !b[i])) return TP_ERR_NULL;
-    if (!aligned16(W[i]) || !aligned16(V[i]) || (b && !aligned16(b[i]))) return TP_ERR_ALIGN;
-  }
-  if (!aligned16(X) || !aligned16(Z)) return TP_ERR_ALIGN;
+  int st = check_forward(X, W, b, V, k, M, H, Fk, dtype, Z, flags);
+  if (st || M == 0) return st;
   const size_t need = tp_mlp_workspace_bytes(k, M, H, Fk, dtype, flags);
   if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TP_ERR_ALIGN;
-  const size_t e = elt_size(dtype);
-  const size_t nz = size_t(M) * size_t(H) * 4;
   Regions in, out;
-  in.add(X, size_t(M) * size_t(H) * e);
-  for (int i = 0; i < k; ++i) {
-    in.add(W[i], size_t(H) * size_t(Fk) * e);
-    in.add(V[i], size_t(Fk) * size_t(H) * e);
-    if (b) in.add(b[i], size_t(Fk) * e);
-  }
-  out.add(Z, nz);
+  forward_regions(X, W, b, V, k, M, H, Fk, dtype, in);
+  out.add(Z, size_t(M) * size_t(H) * 4);
   out.add(workspace, need);
   if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return run_forward(X, W, b, V, k, M, H, Fk, dtype, Z, flags, static_cast<char*>(workspace), batch_size(k),
+                     static_cast<hipStream_t>(stream));
+}
 
+int tp_mlp_shard_forward_noalloc(const void* X, const void* const* W, const void* const* b,
+                                 const void* const* V, int k, int64_t M, int64_t H, int64_t Fk,
+                                 int dtype, float* Z, unsigned flags, void* stream) {
+  int st = check_forward(X, W, b, V, k, M, H, Fk, dtype, Z, flags);
+  if (st || M == 0) return st;
+  // The scratch array holds a batch of G shards' Y_i and, literal, the k - 1
+  // partials: the largest G <= TP_MAX_BATCH that fits (none: TP_ERR_WORKSPACE).
+  const size_t y_bytes = round_up(size_t(M) * size_t(Fk) * elt_size(dtype), kWsAlign);
+  const size_t p_bytes = (flags & TP_FUSED_ACCUM) ? 0 : size_t(k - 1) * round_up(size_t(M) * size_t(H) * 4, kWsAlign);
+  const size_t cap = TP_NOALLOC_SCRATCH_BYTES;
+  if (p_bytes >= cap || (cap - p_bytes) / y_bytes < 1) return TP_ERR_WORKSPACE;
+  const size_t fit = (cap - p_bytes) / y_bytes;
+  const int G = fit < size_t(batch_size(k)) ? int(fit) : batch_size(k);
+  Regions in;
+  forward_regions(X, W, b, V, k, M, H, Fk, dtype, in);
+  Regions out;
+  out.add(Z, size_t(M) * size_t(H) * 4);
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fused = (flags & TP_FUSED_ACCUM) != 0;
-  char* ws = static_cast<char*>(workspace);
-  const int G = batch_size(k);
-  const size_t y_bytes = round_up(size_t(M) * size_t(Fk) * e, kWsAlign);
-  const size_t part_bytes = round_up(nz, kWsAlign);
-  void* Y[kMaxGroups];
-  for (int j = 0; j < G; ++j) Y[j] = ws + size_t(j) * y_bytes;
-  char* part_base = ws + size_t(G) * y_bytes;
-  const float* parts[TP_MAX_SHARDS];
-  // P_0 (or the fused sum) in Z, P_1 .. P_{k-1} in the workspace.
-  auto part = [&](int i) {
-    return i == 0 ? Z : reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
-  };
-  auto col = [&](int i0, int n) {
-    return col_steps(X, W + i0, b ? b + i0 : nullptr, Y, nullptr, n, M, H, Fk, dtype, s);
-  };
-  if ((st = shard_steps(col, V, k, M, H, Fk, dtype, Y, fused, part, parts, s))) return st;
-  if (!fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
-  return TP_OK;
+  void* scratch = nullptr;
+  if (tpmlp::noalloc_scratch(s, &scratch) != hipSuccess) return TP_ERR_HIP;
+  // Y_i batches first, the partials after them (run_forward's layout).
+  return run_forward(X, W, b, V, k, M, H, Fk, dtype, Z, flags, static_cast<char*>(scratch), G, s);
 }
 
 int tp_sp_reduce_scatter(const float* const* Z_parts, int nparts, const void* R, int r_dtype,
@@ -605,7 +649,7 @@ int tp_mlp_shard_forward_sp(const void* X, const void* const* W, const void* con
   auto col = [&](int i0, int n) {
     return col_steps(X, W + i0, b ? b + i0 : nullptr, Y, nullptr, n, M, H, Fk, dtype, s);
   };
-  if ((st = shard_steps(col, V, k, M, H, Fk, dtype, Y, fused, part, parts, s))) return st;
+  if ((st = shard_steps(col, V, k, M, H, Fk, dtype, Y, fused, part, parts, s, G))) return st;
   if (fused) parts[0] = part(0);
   // The reduce-scatter over the k sequence blocks, with X as the residual.
   return hip_status(tpmlp::launch_sp_reduce_scatter(parts, fused ? 1 : k, X, dtype == TP_BF16, O,
@@ -686,7 +730,7 @@ int tp_swiglu_shard_forward(const void* X, const void* const* Wg, const void* co
     return i == 0 ? Z : reinterpret_cast<float*>(part_base + size_t(i - 1) * part_bytes);
   };
   auto col = [&](int i0, int n) { return swiglu_col_steps(X, Wg + i0, Wu + i0, Y, n, M, H, Fk, dtype, s); };
-  if ((st = shard_steps(col, V, k, M, H, Fk, dtype, Y, fused, part, parts, s))) return st;
+  if ((st = shard_steps(col, V, k, M, H, Fk, dtype, Y, fused, part, parts, s, G))) return st;
   if (!fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
   return TP_OK;
 }
@@ -810,7 +854,7 @@ int tp_attn_shard_forward(const void* X, const void* const* Wqkv, const void* co
     if (r) return r;
     return hip_status(tpmlp::launch_attention_bf16(QKV, A, n, B, S, (int)hk, (int)d, causal, s));
   };
-  if ((st = shard_steps(col, Wo, k, M, H, Hk, dtype, A, fused, part, parts, s))) return st;
+  if ((st = shard_steps(col, Wo, k, M, H, Hk, dtype, A, fused, part, parts, s, G))) return st;
   if (!fused && k > 1) return hip_status(tpmlp::launch_shard_reduce(parts, k, Z, M * H, s));
   return TP_OK;
 }

@@ -136,4 +136,8 @@ hipError_t launch_transpose_bf16(const void* const* src, void* const* dst, int g
 hipError_t launch_attention_bf16(const void* const* qkv, void* const* out, int groups, int64_t B,
                                  int64_t S, int heads, int d, bool causal, hipStream_t s);
 
+// This device's copy of the static scratch array of the entry point that
+// allocates nothing (TP_NOALLOC_SCRATCH_BYTES; the device of `stream`).
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
+
 }  // namespace tpmlp

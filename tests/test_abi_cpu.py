@@ -52,7 +52,8 @@ def test_exports_every_declared_symbol(L):
                      "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward",
                      "tp_attn_qkv_shards", "tp_attn_core_shards", "tp_attn_workspace_bytes",
                      "tp_attn_shard_forward", "tp_gemm_tiles", "tp_mlp_step_tile",
-                     "tp_mlp_col_gelu_shards_tile", "tp_mlp_row_partial_shards_tile"}
+                     "tp_mlp_col_gelu_shards_tile", "tp_mlp_row_partial_shards_tile",
+                     "tp_mlp_shard_forward_noalloc"}
     for n in names:
         assert hasattr(L, n), n
     # the measurement hooks live in the dev header only
@@ -67,6 +68,9 @@ def test_python_constants_match_header():
     for n in ("TP_F32", "TP_BF16", "TP_ACCUMULATE", "TP_FUSED_ACCUM", "TP_GRAD_ACCUMULATE",
               "TP_SUM_SHARDS", "TP_MAX_SHARDS", "TP_MAX_BATCH", "TP_CAUSAL"):
         assert getattr(tpm, n) == c[n], n
+    text = open(HEADER).read()
+    assert re.search(r"#define TP_NOALLOC_SCRATCH_BYTES \(128u << 20\)", text)
+    assert tpm.TP_NOALLOC_SCRATCH_BYTES == 128 << 20
 
 
 def test_status_strings(L):
@@ -685,3 +689,39 @@ def test_library_binds_torchs_hip_runtime():
             "assert libs and all(os.path.realpath(p).startswith(d) for p in libs), libs")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_noalloc_forward_errors(L):
+    """tp_mlp_shard_forward_noalloc rejects bad arguments, and shapes whose
+    intermediates exceed the static scratch array, before any HIP call."""
+    c = _header_constants()
+    f = L.tp_mlp_shard_forward_noalloc
+    arr = lambda *xs: (ctypes.c_void_p * len(xs))(*xs)
+    W, V, b = arr(P * 2, P * 3), arr(P * 4, P * 5), arr(P * 6, P * 7)
+    # X, W, b, V, k, M, H, Fk, dtype, Z, flags, stream
+    ok = lambda: [P, W, b, V, 2, 64, 128, 256, c["TP_BF16"], P * 8, 0, None]
+    a = ok(); a[8] = 7
+    assert f(*a) == c["TP_ERR_DTYPE"]
+    a = ok(); a[10] = 2
+    assert f(*a) == c["TP_ERR_FLAGS"]
+    a = ok(); a[4] = 0
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = ok(); a[6] = 60
+    assert f(*a) == c["TP_ERR_SHAPE"]
+    a = ok(); a[9] = None
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = ok(); a[1] = arr(P * 2, None)
+    assert f(*a) == c["TP_ERR_NULL"]
+    a = ok(); a[0] = P + 8
+    assert f(*a) == c["TP_ERR_ALIGN"]
+    a = ok(); a[5] = 0                      # M == 0: nothing to do
+    assert f(*a) == c["TP_OK"]
+    a = ok(); a[9] = P                      # Z over X
+    assert f(*a) == c["TP_ERR_ALIAS"]
+    # one shard's Y_i [32768, 4096] bf16 (268 MB) exceeds the 128 MiB array
+    a = ok(); a[5], a[6], a[7] = 32768, 64, 4096
+    assert f(*a) == c["TP_ERR_WORKSPACE"]
+    # literal: 7 float32 partials [8192, 1024] (235 MB) do not fit; fused fits
+    big = [P, arr(*[P * (10 + i) for i in range(8)]), None, arr(*[P * (30 + i) for i in range(8)]), 8,
+           8192, 1024, 1024, c["TP_BF16"], P * 60, 0, None]
+    assert f(*big) == c["TP_ERR_WORKSPACE"]
