@@ -6,9 +6,9 @@ column GEMM + bias + GeLU and the row GEMM, then the on-device shard sum, over
 one batch of seeded synthetic inputs already resident in HBM.  The headline
 workload is the long-sequence layer (M = 32768, H = 8192, F = 32768, k = 8),
 the largest configuration; `value` is its forward throughput in the chosen
-variant (literal by default: fp32 partials and the shard-reduce kernel;
-fused: the shard sum carried through the row GEMM's accumulator), and
-"variants" gives both.  "configs" holds the same measurement for the other
+variant (fused by default: the shard sum carried through the row GEMM's
+accumulator, the unsplit GEMM of the row-split identity; literal: fp32
+partials and the shard-reduce kernel), and "variants" gives both.  "configs" holds the same measurement for the other
 bf16 workloads (GPT-2-small, 7B and 175B shaped layers).  The backward of the
 block (tp_mlp_shard_backward: per shard the training-mode column step, dA, dV,
 dW + db and the partial dX, then the dX shard sum), the sequence-parallel
@@ -193,7 +193,11 @@ def parse(argv=None):
     ap.add_argument("--legs-workload", default="llama7b",
                     help="workload of the backward, sequence-parallel, SwiGLU and attention legs "
                          "(empty: the headline workload)")
-    ap.add_argument("--variant", choices=["literal", "fused"], default="literal")
+    ap.add_argument("--variant", choices=["literal", "fused"], default="fused",
+                    help="the variant `value` reports (both are timed and reported under \"variants\"): fused "
+                         "carries the shard sum through the row GEMM's accumulator (the unsplit GEMM "
+                         "[Y_0 .. Y_k-1] V of the row-split identity), literal materialises the k partials and "
+                         "sums them with the shard-reduce kernel")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables the CPU leg)")
     ap.add_argument("--kernel-steps", type=int, default=None,

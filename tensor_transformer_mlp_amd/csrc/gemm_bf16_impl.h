@@ -171,15 +171,18 @@ struct OperandTile {
   // Loads of the next stage (k0 .. k0 + 31) into the LDS block at lds_addr;
   // kleft = K - k0.  A stage past the end (kleft <= 0) gets an empty
   // descriptor: every lane writes zeros and no memory is read.
+  __device__ __forceinline__ i32x4_t desc(int kleft) const {
+    return buffer_desc(reinterpret_cast<const void*>(cur), kleft > 0 ? 0x7FFFFFF0u : 0u);
+  }
+  __device__ __forceinline__ void issue_one(const i32x4_t& d, uint32_t lds_addr, int wave, int i, int kleft) const {
+    uint32_t off = src[i];
+    if constexpr (KTAIL) off = kidx[i] < kleft ? off : kOob;
+    lds_dma16(d, lds_addr + (uint32_t)((wave * kPerWave + i) * 1024), off);
+  }
   __device__ __forceinline__ void issue(uint32_t lds_addr, int wave, int kleft) {
-    const i32x4_t desc =
-        buffer_desc(reinterpret_cast<const void*>(cur), kleft > 0 ? 0x7FFFFFF0u : 0u);
+    const i32x4_t d = desc(kleft);
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      uint32_t off = src[i];
-      if constexpr (KTAIL) off = kidx[i] < kleft ? off : kOob;
-      lds_dma16(desc, lds_addr + (uint32_t)((wave * kPerWave + i) * 1024), off);
-    }
+    for (int i = 0; i < kPerWave; ++i) issue_one(d, lds_addr, wave, i, kleft);
     cur += step;
   }
 };
@@ -205,6 +208,16 @@ struct OperandFrags {
         const int col = wbase + 32 * f + 16 * (g & 1) + 4 * (t & 3);
         off[f] = krow * kRow + (((col >> 3) ^ swzMN(krow)) * 16) + ((col >> 2) & 1) * 8;
       }
+    }
+  }
+
+  // Fragment f alone (the explicit issue order of the K loop).
+  __device__ __forceinline__ void read_one(const char* S, int ks, int f, bf16x8_t* dst) const {
+    if constexpr (KMAJ) {
+      dst[f] = *reinterpret_cast<const bf16x8_t*>(S + off[ks] + f * 2048);
+    } else {
+      const char* p = S + off[f] + ks * 16 * kRow;
+      dst[f] = ds_read_tr_pair(p, p + 4 * kRow);
     }
   }
 
@@ -418,26 +431,9 @@ void gemm_bf16_kernel(GemmParams p) {
     rb.read(S + A_BYTES, ks, fb[f]);
     if constexpr (DUAL) rb.read(S + A_BYTES + TB::kBytes, ks, fb[f] + FNO);
   };
-  // With one 8-wave workgroup per CU (two waves per SIMD), the wave issuing
-  // its block of MFMAs runs at a raised priority so that the SIMD keeps
-  // feeding the matrix pipe ahead of the other wave's loads and LDS reads
-  // (0 to 1.3% faster on the 256x256 tile across the four bf16 workloads'
-  // column and row steps, measured; no gain with two workgroups per CU).
-  constexpr bool kPrio = !DUAL && WM * WN == 8 && gemm_waves_per_eu(EPI, BM, BN, WM, WN, NBUF, GSUM) == 2;
-  auto mfmas = [&](auto fset) {
-    constexpr int f = decltype(fset)::value;
-    if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
-    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
-  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   constexpr int kMfma = FM * FN;
-  constexpr int kReads = RA::kReads + NB * RB::kReads;
   // vmcnt((D - 1) L), expcnt(7), lgkmcnt(0): this wave's loads of the next
   // stage (all but the D - 1 younger stages) and all its LDS reads are done.
   constexpr int kWaitN = (D - 1) * L;
@@ -451,35 +447,89 @@ void gemm_bf16_kernel(GemmParams p) {
   read_frags(I0{}, I0{}, 0);
 
   // One K step of 32 on stage buffer c (static, so that every LDS access
-  // names its buffer at compile time).
+  // names its buffer at compile time), written out in issue order: each half
+  // step is MFMA m, then the fragment reads and DMA loads assigned to it, then
+  // a scheduling fence.  The fences keep the compiler from hoisting the loads:
+  // they are inline assembly, which scheduling-group hints cannot place, and
+  // left alone every DMA and fragment read of a half step issues ahead of its
+  // first MFMA.  A stage's DMA is prepared once (descriptors, then the
+  // pointers advance) and its loads are spread over the MFMAs of the first
+  // half step; the fragment reads of the other half are front-loaded.
+  struct StageIssue {
+    uint32_t S;
+    int kleft;
+    i32x4_t da, db, db2;
+  };
+  auto stage_begin = [&](auto bset) {
+    StageIssue r;
+    r.S = stage_lds(bset);
+    r.kleft = iss_g < ngroups ? K - iss_kt * 32 : 0;
+    r.da = ta.desc(r.kleft);
+    r.db = tb.desc(r.kleft);
+    if constexpr (DUAL) r.db2 = tb2.desc(r.kleft);
+    ta.cur += ta.step;
+    tb.cur += tb.step;
+    if constexpr (DUAL) tb2.cur += tb2.step;
+    if (++iss_kt == nk) {
+      iss_kt = 0;
+      if (GSUM && ++iss_g < ngroups) {
+        ta.rebase(a_ptr(iss_g));
+        tb.rebase(b_ptr(iss_g));
+      } else if (!GSUM) {
+        iss_g = 1;
+      }
+    }
+    return r;
+  };
+  constexpr int kFragOps = FM + NB * FNO;  // fragment reads per half step (a B fragment of MN-major: 2 reads)
+  auto dma_one = [&](const StageIssue& r, auto lset) {
+    constexpr int l = decltype(lset)::value;
+    if constexpr (l < TA::kPerWave) ta.issue_one(r.da, r.S, wave, l, r.kleft);
+    else if constexpr (l < TA::kPerWave + TB::kPerWave)
+      tb.issue_one(r.db, r.S + A_BYTES, wave, l - TA::kPerWave, r.kleft);
+    else tb2.issue_one(r.db2, r.S + A_BYTES + TB::kBytes, wave, l - TA::kPerWave - TB::kPerWave, r.kleft);
+  };
+  auto frag_one = [&](auto fset, auto bset, int ks, auto rset) {
+    constexpr int f = decltype(fset)::value, r = decltype(rset)::value;
+    const char* S = stage(bset);
+    if constexpr (r < FM) ra.read_one(S, ks, r, fa[f]);
+    else if constexpr (r < FM + FNO) rb.read_one(S + A_BYTES, ks, r - FM, fb[f]);
+    else rb.read_one(S + A_BYTES + TB::kBytes, ks, r - FM - FNO, fb[f] + FNO);
+  };
+  // MFMAs on fragment set U; fragment op r after MFMA r (front-loaded), DMA
+  // load l after MFMA l kMfma / L (spread), then a fence.
+  auto half_ilv = [&](auto uset, auto lset, auto bset, int ks, const StageIssue* dma) {
+    constexpr int U = decltype(uset)::value;
+    auto one = [&](auto mset) {
+      constexpr int m = decltype(mset)::value;
+      constexpr int i = m / FN, j = m % FN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[U][j], fa[U][i], acc[i][j], 0, 0, 0);
+      if constexpr (m < kFragOps) frag_one(lset, bset, ks, std::integral_constant<int, m>{});
+      if constexpr (m == kMfma - 1 && kFragOps > kMfma) {
+        [&]<int... r>(std::integer_sequence<int, r...>) {
+          (frag_one(lset, bset, ks, std::integral_constant<int, kMfma + r>{}), ...);
+        }(std::make_integer_sequence<int, (kFragOps > kMfma ? kFragOps - kMfma : 0)>{});
+      }
+      if (dma) {
+        [&]<int... l>(std::integer_sequence<int, l...>) {
+          ((l * kMfma / L == m ? (dma_one(*dma, std::integral_constant<int, l>{}), 0) : 0), ...);
+        }(std::make_integer_sequence<int, L>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    [&]<int... m>(std::integer_sequence<int, m...>) {
+      (one(std::integral_constant<int, m>{}), ...);
+    }(std::make_integer_sequence<int, kMfma>{});
+  };
   auto kstep = [&](auto cset) {
     constexpr int c = decltype(cset)::value;
     using Refill = std::integral_constant<int, (c + D) % NBUF>;
     using Next = std::integral_constant<int, (c + 1) % NBUF>;
-    // k16 step 0: refill the buffer freed by the previous stage with the
-    // stage D ahead, read step 1's fragments, MFMAs of step 0.
-    issue_stage(Refill{});
-    read_frags(I1{}, cset, 1);
-    mfmas(I0{});
-#pragma unroll
-    for (int m = 0; m < kMfma; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (m < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (m < L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // k16 step 1: once the next stage has landed for every wave, read its
-    // step 0 fragments while the MFMAs of step 1 run.
+    const StageIssue st = stage_begin(Refill{});
+    half_ilv(I0{}, I1{}, cset, 1, &st);
     __builtin_amdgcn_s_waitcnt(kWaitNext);
     asm volatile("s_barrier" ::: "memory");
-    read_frags(I0{}, Next{}, 0);
-    mfmas(I1{});
-#pragma unroll
-    for (int m = 0; m < kMfma; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (m < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    half_ilv(I1{}, I0{}, Next{}, 0, nullptr);
   };
   // The loop body walks the NBUF buffers in order; an early exit handles a
   // stage count that is not a multiple of NBUF (uniform across the workgroup).
@@ -731,7 +781,9 @@ void gemm_bf16_kernel(GemmParams p) {
 
 // A group sum keeps one accumulator set, like any other GEMM: every tile but
 // the 4-wave 256x256 one (whose epilogue spills) is compiled for it.
-constexpr bool tile_allows_group_sum(int t) { return !(kTiles[t].bm == 256 && kTiles[t].bn == 256 && kTiles[t].wm * kTiles[t].wn == 4); }
+constexpr bool tile_allows_group_sum(int t) {
+  return !(kTiles[t].bm == 256 && kTiles[t].bn == 256 && kTiles[t].wm * kTiles[t].wn == 4);
+}
 
 // SwiGLU splits a tile's BN columns into a gate and an up sub-tile of BN / 2
 // columns each (MN-major sub-tiles need 128, 256 or 512 columns) and every

@@ -480,7 +480,7 @@ const char* tp_status_string(int status) {
   }
 }
 
-int tp_mlp_version(void) { return 131; }
+int tp_mlp_version(void) { return 200; }
 
 int tp_mlp_col_gelu_shards(const void* X, const void* const* W, const void* const* b, void* const* Y,
                            void* const* G, int n, int64_t M, int64_t H, int64_t Fk, int dtype,

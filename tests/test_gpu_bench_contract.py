@@ -35,7 +35,7 @@ def test_bench_output_line(capsys):
     assert d["value"] > 0 and d["ms_per_step"] > 0
     M, H, F = 32768, 8192, 32768
     assert abs(d["value"] - 4 * M * H * F / (d["ms_per_step"] * 1e-3) / 1e12) <= 1e-3 * d["value"] + 1e-3
-    assert d["config"]["workload"] == "long_seq" and d["config"]["variant"] == "literal"
+    assert d["config"]["workload"] == "long_seq" and d["config"]["variant"] == "fused"
     assert (d["config"]["M"], d["config"]["H"], d["config"]["F"], d["config"]["k"]) == (M, H, F, 8)
     assert set(d["variants"]) == {"literal", "fused"}
     sm = d["step_ms"]
@@ -48,7 +48,7 @@ def test_bench_output_line(capsys):
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["unit"] == "TFLOP/s" and c["sample"]
     assert c["logical_cpus"] >= 1 and "cpu_model" in c
-    assert set(d["kernels"]) == {"col_gelu", "row_partial", "shard_reduce"}
+    assert set(d["kernels"]) == {"col_gelu", "row_sum"}
     assert set(d["configs"]) == {"long_seq", "gpt2_small"}
     for name, cf in d["configs"].items():
         assert cf["value"] > 0 and set(cf["variants"]) == {"literal", "fused"}, name
