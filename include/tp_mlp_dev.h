@@ -46,8 +46,8 @@ int tp_mlp_step_tile(int step, int n, int64_t M, int64_t H, int64_t Fk);
 int tp_mlp_col_gelu_shards_tile(int tile, const void* X, const void* const* W, const void* const* b,
                                 void* const* Y, int n, int64_t M, int64_t H, int64_t Fk, void* stream);
 
-/* tp_mlp_row_partial_shards (bf16) with tile `tile`, as above; with
- * TP_SUM_SHARDS every tile but the 4-wave 256 x 256 one can run. */
+/* tp_mlp_row_partial_shards (bf16) with tile `tile`, as above (with
+ * TP_SUM_SHARDS too). */
 int tp_mlp_row_partial_shards_tile(int tile, const void* const* Y, const void* const* V, float* const* Z,
                                    int n, int64_t M, int64_t Fk, int64_t H, unsigned flags, void* stream);
 

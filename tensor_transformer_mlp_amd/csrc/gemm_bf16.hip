@@ -63,7 +63,9 @@ GemmParams base_params(const GemmBatch& b, int tile) {
 // MI355X (random bf16 data), counting the workgroups of the whole batch:
 //   * 256x256 (8 waves, 4 stages) when it fills at least two rounds of the 256
 //     CUs, or 192..255 tiles (a 0.75 round still beats the smaller tiles);
-//   * otherwise 128x256 with 3 stages (two workgroups per CU) when N > 128;
+//   * otherwise 128x256 when N > 128: with 4 stages when its tiles fit one
+//     round of the CUs (one workgroup per CU, the deeper prefetch pays), else
+//     with 3 stages (two workgroups per CU);
 //   * otherwise 128x128 (two workgroups per CU);
 //   * K % 32 != 0 (K ends inside a 32-deep stage): the ragged-K variant of the
 //     128x128 tile.
@@ -75,7 +77,7 @@ int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K, int groups, b
   if (group_sum) groups = 1;
   const int64_t t256 = tiles_of(0, M, N) * groups;
   if (t256 >= 512 || (t256 >= 192 && t256 < 256)) return 0;
-  if (N > 128) return 6;
+  if (N > 128) return tiles_of(5, M, N) * groups <= 256 ? 5 : 6;
   return 8;
 }
 
@@ -90,7 +92,6 @@ int pick_swiglu_tile(int64_t M, int64_t N, int64_t K, int groups) {
 
 hipError_t launch_gemm_bf16_batch_tile(int tile, const GemmBatch& b, hipStream_t s) {
   if (tile < 0 || tile >= kNumTiles || b.groups < 1 || b.groups > kMaxGroups) return hipErrorInvalidValue;
-  if (b.group_sum && !tile_allows_group_sum(tile)) return hipErrorInvalidValue;
   if (b.epi == kEpiSwiGLU && (b.group_sum || b.layout != kNN || !tile_allows_swiglu(tile)))
     return hipErrorInvalidValue;
   if (b.M <= 0 || b.N <= 0) return hipSuccess;

@@ -1,10 +1,10 @@
 // bf16 GEMM for gfx950: C[M,N] = epilogue(A B), bf16 operands on the
-// v_mfma_f32_32x32x16_bf16 matrix cores, float32 accumulate, for the three
+// v_mfma_f32_16x16x32_bf16 matrix cores, float32 accumulate, for the three
 // operand layouts the MLP shard's forward and backward use (kNN, kNT, kTN).
 //
 // Workgroup tile BM x BN, WM x WN waves, each wave a (BM/WM) x (BN/WN) block
-// of 32x32 MFMA tiles.  K advances 32 per stage through NBUF LDS stages with a
-// prefetch distance of NBUF - 1.  Global data goes straight into LDS with
+// of 16x16 MFMA tiles.  K advances 32 per stage (one MFMA deep) through NBUF
+// LDS stages with a prefetch distance of NBUF - 1.  Global data goes straight into LDS with
 // `buffer_load_dwordx4 ... lds` (lane l of a wave instruction fills bytes
 // 16 l .. 16 l + 15 of a 1 KB LDS block, so the LDS swizzle is applied by
 // choosing which global 16-byte chunk each lane fetches): no staging
@@ -13,7 +13,8 @@
 // Each operand tile is stored in LDS in its global orientation:
 //   K-major operand (A in kNN/kNT, B in kNT): [R rows][32 k], 64-byte rows;
 //     chunk c (8 k-values) of row r at position c ^ swzK(r).  An MFMA
-//     fragment (8 consecutive k of one row) is one 16-byte LDS read.
+//     fragment (16 rows by 32 k; each lane 8 consecutive k of one row) is one
+//     16-byte LDS read per lane.
 //   MN-major operand (B in kNN/kTN, A in kTN): [32 k][R], 2R-byte rows;
 //     chunk c (8 row/column indices) of k-row k at position c ^ swzMN(k).  A
 //     fragment is two ds_read_b64_tr_b16 transpose reads.
@@ -31,9 +32,12 @@
 // and each lane ends up owning runs of 4 consecutive output columns of one
 // row (16-byte fp32 / 8-byte bf16 stores).
 //
-// One barrier per stage, placed before the MFMAs of the stage's second k16
-// step, so the next stage's first fragment reads overlap those MFMAs.  The
-// barrier is a bare s_barrier after an explicit wait for this wave's loads
+// One barrier per stage, placed before the MFMAs of the second half of the
+// wave's rows, so the next stage's first fragment reads overlap those MFMAs.
+// (The 16x16x32 instruction gives the same float32 results as two
+// 32x32x16 steps over the same 32 k, bit for bit, measured on every output of
+// the MLP's GEMM shapes; it runs at a ~10% higher clock under the power cap.)
+// The barrier is a bare s_barrier after an explicit wait for this wave's loads
 // of the next stage only (a full workgroup fence would also wait for the
 // loads of the stages still in flight).
 #pragma once
@@ -80,7 +84,7 @@ struct TileCfg {
 constexpr TileCfg kTiles[] = {
     {256, 256, 2, 4, 4},  // 0
     {256, 256, 2, 4, 5},  // 1
-    {256, 256, 2, 2, 4},  // 2
+    {256, 256, 2, 4, 3},  // 2
     {256, 128, 4, 2, 4},  // 3
     {256, 128, 4, 2, 3},  // 4
     {128, 256, 2, 4, 4},  // 5
@@ -99,16 +103,20 @@ constexpr bool layout_has_epi(int layout, int epi) {
 }
 
 // LDS chunk swizzles (see the file comment).  K-major rows are 64 bytes
-// (four chunks) and a fragment read takes one chunk of each of 32
-// consecutive rows (lanes 0-31 and 32-63 take neighbouring chunks).  Among
-// the swizzles that XOR the chunk index with two parity bits of the row,
-// timing every one of them for this read on MI355X (the 16-byte reads are
-// spread over 64 four-byte banks) splits them into a conflict-free class
-// and a class 1.5x slower; swzK, bits 2..3 of the row, is in the fast one.
+// (four chunks) and a fragment read takes the four chunks of 16 consecutive
+// rows (lanes 16 c .. 16 c + 15 take chunk c).  Timing every swizzle that
+// XORs the chunk index with two parity bits of row bits 0..3 for this read on
+// MI355X (core cycles per read; 16-byte reads spread over 64 four-byte banks)
+// splits them into a conflict-free class and classes 1.7x and 3.3x slower.
+// swzK, with q = row bits 2..3, XORs with (-q) mod 4 (bit 0: row bit 2; bit
+// 1: row bits 2 ^ 3) and is in the conflict-free class; XOR with q itself is
+// in the 1.7x one.
 // MN-major rows hold >= 16 chunks; swzMN rotates by 4 chunks per k-row so
-// that the four k-rows of a transpose read fall in distinct bank groups.
-__device__ __forceinline__ int swzK(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int swzMN(int k) { return 4 * (k & 3); }
+// that the four k-rows of a transpose read fall in distinct bank groups, and
+// by 2 more chunks for k-rows 8..15 of every 16 (a fragment's lanes 16-31
+// read the same columns 8 k-rows below lanes 0-15).
+__device__ __forceinline__ int swzK(int r) { return (-(r >> 2)) & 3; }
+__device__ __forceinline__ int swzMN(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
 
 // One operand's tile: R rows of the operand (rows of A, or columns of B) by
 // 32 k per stage, loaded by NW waves.  KTAIL: K may end inside a stage, so the
@@ -188,51 +196,39 @@ struct OperandTile {
 };
 
 // Fragment reads of one operand for a wave whose F fragments start at tile
-// row `wbase` (K-major: F row blocks of 32; MN-major: F column blocks of 32).
+// row `wbase` (K-major: F blocks of 16 rows; MN-major: F blocks of 16
+// columns).  A fragment covers 16 rows (or columns) by the stage's 32 k; lane
+// l holds k 8 (l / 16) .. + 7 of row l % 16.
 template <int R, bool KMAJ, int F>
 struct OperandFrags {
   static constexpr int kRow = KMAJ ? 64 : 2 * R;
-  static constexpr int kReads = KMAJ ? F : 2 * F;  // LDS read instructions per k16 step
-  int off[KMAJ ? 2 : F];
+  int off[KMAJ ? 1 : F];
 
   __device__ __forceinline__ void init(int wbase, int lane) {
     if constexpr (KMAJ) {
-      const int row = wbase + (lane & 31);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) off[ks] = row * 64 + ((2 * ks + (lane >> 5)) ^ swzK(row)) * 16;
+      const int row = wbase + (lane & 15);
+      off[0] = row * 64 + ((lane >> 4) ^ swzK(row)) * 16;  // fragment f: + 16 rows of 64 bytes
     } else {
+      // ds_read_b64_tr_b16: 16 lanes read 4 k-rows x 16 columns (lane t: k-row
+      // t / 4, columns 4 (t % 4) .. + 3) and each gets one column's 4 k; the
+      // second read takes the 4 k-rows below.
       const int g = lane >> 4, t = lane & 15;
-      const int krow = 8 * (g >> 1) + (t >> 2);  // + 16 ks, + 4 for the second read
+      const int krow = 8 * g + (t >> 2);
 #pragma unroll
       for (int f = 0; f < F; ++f) {
-        const int col = wbase + 32 * f + 16 * (g & 1) + 4 * (t & 3);
+        const int col = wbase + 16 * f + 4 * (t & 3);
         off[f] = krow * kRow + (((col >> 3) ^ swzMN(krow)) * 16) + ((col >> 2) & 1) * 8;
       }
     }
   }
 
-  // Fragment f alone (the explicit issue order of the K loop).
-  __device__ __forceinline__ void read_one(const char* S, int ks, int f, bf16x8_t* dst) const {
+  // Fragment f.  swzK(r + 16 f) == swzK(r) and swzMN(k + 4) == swzMN(k).
+  __device__ __forceinline__ bf16x8_t get(const char* S, int f) const {
     if constexpr (KMAJ) {
-      dst[f] = *reinterpret_cast<const bf16x8_t*>(S + off[ks] + f * 2048);
+      return *reinterpret_cast<const bf16x8_t*>(S + off[0] + f * 1024);
     } else {
-      const char* p = S + off[f] + ks * 16 * kRow;
-      dst[f] = ds_read_tr_pair(p, p + 4 * kRow);
-    }
-  }
-
-  // swzK(r + 32 f) == swzK(r) and swzMN(k + 4) == swzMN(k + 16) == swzMN(k).
-  // dst: F fragments.
-  __device__ __forceinline__ void read(const char* S, int ks, bf16x8_t* dst) const {
-    if constexpr (KMAJ) {
-#pragma unroll
-      for (int f = 0; f < F; ++f) dst[f] = *reinterpret_cast<const bf16x8_t*>(S + off[ks] + f * 2048);
-    } else {
-#pragma unroll
-      for (int f = 0; f < F; ++f) {
-        const char* p = S + off[f] + ks * 16 * kRow;
-        dst[f] = ds_read_tr_pair(p, p + 4 * kRow);
-      }
+      const char* p = S + off[f];
+      return ds_read_tr_pair(p, p + 4 * kRow);
     }
   }
 };
@@ -274,7 +270,7 @@ void gemm_bf16_kernel(GemmParams p) {
   constexpr int D = NBUF - 1;         // prefetch distance in K steps of 32
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int NB = DUAL ? 2 : 1;              // B sub-tiles per stage
   constexpr int BNO = BN / NB, WTNO = WTN / NB;  // output columns per workgroup / wave
   constexpr int FNO = FN / NB;                  // output fragments per wave row
@@ -285,7 +281,7 @@ void gemm_bf16_kernel(GemmParams p) {
   constexpr int A_BYTES = TA::kBytes, STAGE = TA::kBytes + NB * TB::kBytes;
   constexpr int L = TA::kPerWave + NB * TB::kPerWave;  // DMA instructions per wave per stage
   static_assert(!DUAL || (LAYOUT == kNN && FN % 2 == 0 && !GSUM), "SwiGLU: kNN, two fragment sets");
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(WTM % 32 == 0 && WTN % 16 == 0, "wave tile: two halves of 16-row fragments by 16-column ones");
   static_assert(NBUF >= 3 && NBUF <= 6, "stage count");
   static_assert((D - 1) * L <= 63, "vmcnt immediate");
   static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
@@ -396,44 +392,31 @@ void gemm_bf16_kernel(GemmParams p) {
   ra.init(wm * WTM, lane);
   rb.init(wn * WTNO, lane);
 
-  f32x16_t acc[FM][FN];
+  // Output layout of an MFMA tile (the B fragment goes in the instruction's A
+  // slot): lane l holds row l % 16 of the tile, columns 4 (l / 16) .. + 3.
+  const int lrow = lane & 15;
+  const int hcol = 4 * (lane >> 4);
+  f32x4_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // Group sum accumulating into C: the accumulator starts at C's values.
   if constexpr (GSUM && EPI == kEpiAccumF32) {
-    const int l32 = lane & 31, hcol = 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int m = m0 + wm * WTM + i * 32 + l32;
+      const int m = m0 + wm * WTM + i * 16 + lrow;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * WTN + j * 32 + 8 * gq + hcol;
-          f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if (m < p.M && n < p.N)
-            v = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.t.C[0]) + (int64_t)m * p.ldc + n);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * gq + e] = v[e];
-        }
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * WTN + j * 16 + hcol;
+        if (m < p.M && n < p.N)
+          acc[i][j] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.t.C[0]) + (int64_t)m * p.ldc + n);
+      }
     }
   }
 
-  bf16x8_t fa[2][FM], fb[2][FN];
-  auto read_frags = [&](auto fset, auto bset, int ks) {
-    constexpr int f = decltype(fset)::value;
-    const char* S = stage(bset);
-    ra.read(S, ks, fa[f]);
-    rb.read(S + A_BYTES, ks, fb[f]);
-    if constexpr (DUAL) rb.read(S + A_BYTES + TB::kBytes, ks, fb[f] + FNO);
-  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  constexpr int kMfma = FM * FN;
   // vmcnt((D - 1) L), expcnt(7), lgkmcnt(0): this wave's loads of the next
   // stage (all but the D - 1 younger stages) and all its LDS reads are done.
   constexpr int kWaitN = (D - 1) * L;
@@ -444,17 +427,15 @@ void gemm_bf16_kernel(GemmParams p) {
   }(std::make_integer_sequence<int, D>{});
   __builtin_amdgcn_s_waitcnt(kWaitNext);
   asm volatile("s_barrier" ::: "memory");
-  read_frags(I0{}, I0{}, 0);
 
-  // One K step of 32 on stage buffer c (static, so that every LDS access
-  // names its buffer at compile time), written out in issue order: each half
-  // step is MFMA m, then the fragment reads and DMA loads assigned to it, then
-  // a scheduling fence.  The fences keep the compiler from hoisting the loads:
-  // they are inline assembly, which scheduling-group hints cannot place, and
-  // left alone every DMA and fragment read of a half step issues ahead of its
-  // first MFMA.  A stage's DMA is prepared once (descriptors, then the
+  // The K loop is written out in issue order: each part of a step is MFMA
+  // m, then the fragment reads and DMA loads assigned to it, then a
+  // scheduling fence.  The fences keep the compiler from hoisting
+  // the loads: they are inline assembly, which scheduling-group hints cannot
+  // place, and left alone every DMA and fragment read of a part issues ahead
+  // of its first MFMA.  A stage's DMA is prepared once (descriptors, then the
   // pointers advance) and its loads are spread over the MFMAs of the first
-  // half step; the fragment reads of the other half are front-loaded.
+  // part; the fragment reads are front-loaded.
   struct StageIssue {
     uint32_t S;
     int kleft;
@@ -481,7 +462,6 @@ void gemm_bf16_kernel(GemmParams p) {
     }
     return r;
   };
-  constexpr int kFragOps = FM + NB * FNO;  // fragment reads per half step (a B fragment of MN-major: 2 reads)
   auto dma_one = [&](const StageIssue& r, auto lset) {
     constexpr int l = decltype(lset)::value;
     if constexpr (l < TA::kPerWave) ta.issue_one(r.da, r.S, wave, l, r.kleft);
@@ -489,67 +469,97 @@ void gemm_bf16_kernel(GemmParams p) {
       tb.issue_one(r.db, r.S + A_BYTES, wave, l - TA::kPerWave, r.kleft);
     else tb2.issue_one(r.db2, r.S + A_BYTES + TB::kBytes, wave, l - TA::kPerWave - TB::kPerWave, r.kleft);
   };
-  auto frag_one = [&](auto fset, auto bset, int ks, auto rset) {
-    constexpr int f = decltype(fset)::value, r = decltype(rset)::value;
-    const char* S = stage(bset);
-    if constexpr (r < FM) ra.read_one(S, ks, r, fa[f]);
-    else if constexpr (r < FM + FNO) rb.read_one(S + A_BYTES, ks, r - FM, fb[f]);
-    else rb.read_one(S + A_BYTES + TB::kBytes, ks, r - FM - FNO, fb[f] + FNO);
+  // A step of 32 k on stage buffer c runs the wave's FM x FN MFMAs in two
+  // parts.  A's fragments are read in two halves (the wave's fragment rows
+  // [0, FH) and [FH, FM)), B's into one of two sets by step parity.  Part 0:
+  // the MFMAs of A's first half (read in the previous step) while the second
+  // half is read and the refill DMA issues; then the barrier; part 1: the
+  // MFMAs of the second half while the next stage's first half of A and its
+  // B are read, in the order the next step's first MFMAs use them (A fragment
+  // 0, every B fragment, the other A fragments).
+  constexpr int FH = FM / 2;
+  constexpr int kM = FH * FN;  // MFMAs per part
+  bf16x8_t fa0[FH], fa1[FH], fb[2][FN];
+  auto read_b = [&](const char* S, int f) {
+    return f < FNO ? rb.get(S + A_BYTES, f) : rb.get(S + A_BYTES + TB::kBytes, f - FNO);
   };
-  // MFMAs on fragment set U; fragment op r after MFMA r (front-loaded), DMA
-  // load l after MFMA l kMfma / L (spread), then a fence.
-  auto half_ilv = [&](auto uset, auto lset, auto bset, int ks, const StageIssue* dma) {
-    constexpr int U = decltype(uset)::value;
+  {
+    const char* S = stage(I0{});
+#pragma unroll
+    for (int f = 0; f < FH; ++f) fa0[f] = ra.get(S, f);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) fb[0][f] = read_b(S, f);
+  }
+  // Part P of a step with B set BP, fragment reads from stage buffer sset:
+  // MFMA m, then fragment read m (reads past the last MFMA follow it), then
+  // the DMA loads l with l kM / L == m, then a fence.
+  auto part = [&](auto pset, auto bpset, auto sset, const StageIssue* dma) {
+    constexpr int P = decltype(pset)::value, BP = decltype(bpset)::value;
+    constexpr int kOps = P == 0 ? FH : FH + FN;
+    const char* S = stage(sset);
+    auto op = [&](auto rset) {
+      constexpr int r = decltype(rset)::value;
+      if constexpr (P == 0) fa1[r] = ra.get(S, FH + r);
+      else if constexpr (r == 0) fa0[0] = ra.get(S, 0);
+      else if constexpr (r <= FN) fb[1 - BP][r - 1] = read_b(S, r - 1);
+      else fa0[r - FN] = ra.get(S, r - FN);
+    };
     auto one = [&](auto mset) {
-      constexpr int m = decltype(mset)::value;
-      constexpr int i = m / FN, j = m % FN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[U][j], fa[U][i], acc[i][j], 0, 0, 0);
-      if constexpr (m < kFragOps) frag_one(lset, bset, ks, std::integral_constant<int, m>{});
-      if constexpr (m == kMfma - 1 && kFragOps > kMfma) {
+      constexpr int m = decltype(mset)::value, i = m / FN, j = m % FN;
+      if constexpr (P == 0)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[BP][j], fa0[i], acc[i][j], 0, 0, 0);
+      else
+        acc[FH + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[BP][j], fa1[i], acc[FH + i][j], 0, 0, 0);
+      if constexpr (m < kOps) op(std::integral_constant<int, m>{});
+      if constexpr (m == kM - 1 && kOps > kM) {
         [&]<int... r>(std::integer_sequence<int, r...>) {
-          (frag_one(lset, bset, ks, std::integral_constant<int, kMfma + r>{}), ...);
-        }(std::make_integer_sequence<int, (kFragOps > kMfma ? kFragOps - kMfma : 0)>{});
+          (op(std::integral_constant<int, kM + r>{}), ...);
+        }(std::make_integer_sequence<int, (kOps > kM ? kOps - kM : 0)>{});
       }
       if (dma) {
         [&]<int... l>(std::integer_sequence<int, l...>) {
-          ((l * kMfma / L == m ? (dma_one(*dma, std::integral_constant<int, l>{}), 0) : 0), ...);
+          ((l * kM / L == m ? (dma_one(*dma, std::integral_constant<int, l>{}), 0) : 0), ...);
         }(std::make_integer_sequence<int, L>{});
       }
       __builtin_amdgcn_sched_barrier(0);
     };
     [&]<int... m>(std::integer_sequence<int, m...>) {
       (one(std::integral_constant<int, m>{}), ...);
-    }(std::make_integer_sequence<int, kMfma>{});
+    }(std::make_integer_sequence<int, kM>{});
   };
-  auto kstep = [&](auto cset) {
-    constexpr int c = decltype(cset)::value;
+  // Step b (static: buffer b % NBUF, B set b % 2, so every LDS access names
+  // its buffer at compile time).
+  auto kstep = [&](auto bset) {
+    constexpr int b = decltype(bset)::value, c = b % NBUF;
+    using Cur = std::integral_constant<int, c>;
+    using BP = std::integral_constant<int, b % 2>;
     using Refill = std::integral_constant<int, (c + D) % NBUF>;
     using Next = std::integral_constant<int, (c + 1) % NBUF>;
     const StageIssue st = stage_begin(Refill{});
-    half_ilv(I0{}, I1{}, cset, 1, &st);
+    part(I0{}, BP{}, Cur{}, &st);
     __builtin_amdgcn_s_waitcnt(kWaitNext);
     asm volatile("s_barrier" ::: "memory");
-    half_ilv(I1{}, I0{}, Next{}, 0, nullptr);
+    part(I1{}, BP{}, Next{}, nullptr);
   };
-  // The loop body walks the NBUF buffers in order; an early exit handles a
-  // stage count that is not a multiple of NBUF (uniform across the workgroup).
-  for (int st = 0; st < nstages; st += NBUF) {
+  // The loop body walks U consecutive steps (a multiple of NBUF and of 2);
+  // an early exit handles a stage count that is not a multiple of U (uniform
+  // across the workgroup).
+  constexpr int U = NBUF % 2 == 0 ? NBUF : 2 * NBUF;
+  for (int st = 0; st < nstages; st += U) {
     bool more = true;
     [&]<int... b>(std::integer_sequence<int, b...>) {
       ((more = more && (st + b < nstages), more ? (kstep(std::integral_constant<int, b>{}), 0) : 0), ...);
-    }(std::make_integer_sequence<int, NBUF>{});
+    }(std::make_integer_sequence<int, U>{});
   }
   // The last stages' loads (out of range, writing zeros) must have landed
   // before this workgroup's LDS can be handed to another.
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
 
-  // Epilogue.  Per 32-row block i, every global load the epilogue needs (the
+  // Epilogue.  Per 16-row block i, every global load the epilogue needs (the
   // multiplier or the old value of C) is issued before any store, so the
   // loads overlap; each element is read and written by the same lane only,
   // so this order is also correct when C is aux.  The bias is loaded once.
   // Tiles wholly inside C take a path without per-store bounds checks.
-  const int l32 = lane & 31;
-  const int hcol = 4 * (lane >> 5);
   const int M = p.M, N = p.N;
   int64_t ldc = p.ldc;
   void* Cout = p.t.C[grp];
@@ -562,127 +572,108 @@ void gemm_bf16_kernel(GemmParams p) {
     accumulate = false;
   }
   constexpr bool kBias = EPI == kEpiBiasGelu || EPI == kEpiBiasGeluSave || EPI == kEpiBias;
-  f32x4_t bias4[FN][4];
+  // Output column of lane `lane`'s 4 values in output fragment j.
+  auto col = [&](int j) { return n0 + wn * WTNO + j * 16 + hcol; };
+  f32x4_t bias4[FN];
   if constexpr (kBias) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int n = n0 + wn * WTNO + j * 32 + 8 * gq + hcol;
-        u32x2_t bb = u32x2_t{0u, 0u};
-        if (bias && n < N) bb = *reinterpret_cast<const u32x2_t*>(bias + n);
-        bias4[j][gq] = f32x4_t{bf16_bits_to_f32(bb[0] & 0xFFFFu), bf16_bits_to_f32(bb[0] >> 16),
-                               bf16_bits_to_f32(bb[1] & 0xFFFFu), bf16_bits_to_f32(bb[1] >> 16)};
-      }
+    for (int j = 0; j < FN; ++j) {
+      const int n = col(j);
+      u32x2_t bb = u32x2_t{0u, 0u};
+      if (bias && n < N) bb = *reinterpret_cast<const u32x2_t*>(bias + n);
+      bias4[j] = f32x4_t{bf16_bits_to_f32(bb[0] & 0xFFFFu), bf16_bits_to_f32(bb[0] >> 16),
+                         bf16_bits_to_f32(bb[1] & 0xFFFFu), bf16_bits_to_f32(bb[1] >> 16)};
+    }
   }
+  // The final value of output fragment (i, j) before rounding: SiLU(gate)
+  // times up for SwiGLU, else the accumulator plus the bias.
+  auto value = [&](int i, int j) {
+    f32x4_t v;
+    if constexpr (DUAL) {
+      // gate fragment j and up fragment FNO + j hold the same columns
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = silu_f32(acc[i][j][e]) * acc[i][FNO + j][e];
+    } else {
+      v = acc[i][j];
+      if constexpr (kBias) v += bias4[j];
+    }
+    return v;
+  };
   auto epilogue = [&](auto guard) {
     constexpr bool G = decltype(guard)::value;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int m = m0 + wm * WTM + i * 32 + l32;
+      const int m = m0 + wm * WTM + i * 16 + lrow;
       const bool mrow = !G || m < M;
       const int64_t row = (int64_t)m * ldc;
-      u32x2_t aux2[FN][4];
-      f32x4_t old4[FN][4];
+      u32x2_t aux2[FN];
+      f32x4_t old4[FN];
       if constexpr (EPI == kEpiMulAux || EPI == kEpiAccumF32) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int n = n0 + wn * WTNO + j * 32 + 8 * gq + hcol;
-            const bool ok = !G || (mrow && n < N);
-            if constexpr (EPI == kEpiMulAux) {
-              aux2[j][gq] = u32x2_t{0u, 0u};
-              if (ok)
-                aux2[j][gq] =
-                    *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(aux) + row + n);
-            } else {
-              old4[j][gq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-              if (ok && accumulate)
-                old4[j][gq] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(Cout) + row + n);
-            }
+        for (int j = 0; j < FN; ++j) {
+          const int n = col(j);
+          const bool ok = !G || (mrow && n < N);
+          if constexpr (EPI == kEpiMulAux) {
+            aux2[j] = u32x2_t{0u, 0u};
+            if (ok) aux2[j] = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(aux) + row + n);
+          } else {
+            old4[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (ok && accumulate)
+              old4[j] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(Cout) + row + n);
           }
+        }
       }
 #pragma unroll
       for (int j = 0; j < FNO; ++j) {
+        const int n = col(j);
+        if (G && (!mrow || n >= N)) continue;
+        const int64_t idx = row + n;
+        const f32x4_t v = value(i, j);
+        if constexpr (DUAL || EPI == kEpiBias) {
+          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = pack4_bf16(v);
+        } else if constexpr (EPI == kEpiBiasGelu) {
+          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) =
+              pack4_bf16(f32x4_t{gelu_f32(v[0]), gelu_f32(v[1]), gelu_f32(v[2]), gelu_f32(v[3])});
+        } else if constexpr (EPI == kEpiBiasGeluSave) {
+          float y[4], g[4];
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * WTNO + j * 32 + 8 * gq + hcol;
-          if (G && (!mrow || n >= N)) continue;
-          const int64_t idx = row + n;
-          f32x4_t v;
-          if constexpr (DUAL) {
-            // gate fragment j and up fragment FNO + j hold the same columns
-            u32x2_t o;
-            float y[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = silu_f32(acc[i][j][4 * gq + e]) * acc[i][FNO + j][4 * gq + e];
-            o[0] = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
-            o[1] = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
-            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = o;
-            continue;
-          }
-          v = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]};
-          if constexpr (kBias) {
-            v += bias4[j][gq];
-            if constexpr (EPI == kEpiBias) {
-              u32x2_t o;
-              o[0] = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-              o[1] = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = o;
-            } else if constexpr (EPI == kEpiBiasGelu) {
-              u32x2_t o;
-              o[0] = f32_to_bf16_bits(gelu_f32(v[0])) | (f32_to_bf16_bits(gelu_f32(v[1])) << 16);
-              o[1] = f32_to_bf16_bits(gelu_f32(v[2])) | (f32_to_bf16_bits(gelu_f32(v[3])) << 16);
-              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = o;
-            } else {
-              float y[4], g[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) gelu_and_grad_f32(v[e], y[e], g[e]);
-              u32x2_t oy, og;
-              oy[0] = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
-              oy[1] = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
-              og[0] = f32_to_bf16_bits(g[0]) | (f32_to_bf16_bits(g[1]) << 16);
-              og[1] = f32_to_bf16_bits(g[2]) | (f32_to_bf16_bits(g[3]) << 16);
-              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = oy;
-              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(aux) + idx) = og;
-            }
-          } else if constexpr (EPI == kEpiMulAux) {
-            const u32x2_t gg = aux2[j][gq];
-            u32x2_t o;
-            o[0] = f32_to_bf16_bits(v[0] * bf16_bits_to_f32(gg[0] & 0xFFFFu)) |
-                   (f32_to_bf16_bits(v[1] * bf16_bits_to_f32(gg[0] >> 16)) << 16);
-            o[1] = f32_to_bf16_bits(v[2] * bf16_bits_to_f32(gg[1] & 0xFFFFu)) |
-                   (f32_to_bf16_bits(v[3] * bf16_bits_to_f32(gg[1] >> 16)) << 16);
-            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = o;
-          } else if constexpr (EPI == kEpiStoreF32) {
-            *reinterpret_cast<f32x4_t*>(static_cast<float*>(Cout) + idx) = v;
-          } else {
-            *reinterpret_cast<f32x4_t*>(static_cast<float*>(Cout) + idx) = accumulate ? old4[j][gq] + v : v;
-          }
+          for (int e = 0; e < 4; ++e) gelu_and_grad_f32(v[e], y[e], g[e]);
+          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) = pack4_bf16(f32x4_t{y[0], y[1], y[2], y[3]});
+          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(aux) + idx) = pack4_bf16(f32x4_t{g[0], g[1], g[2], g[3]});
+        } else if constexpr (EPI == kEpiMulAux) {
+          const u32x2_t gg = aux2[j];
+          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(Cout) + idx) =
+              pack4_bf16(f32x4_t{v[0] * bf16_bits_to_f32(gg[0] & 0xFFFFu), v[1] * bf16_bits_to_f32(gg[0] >> 16),
+                                 v[2] * bf16_bits_to_f32(gg[1] & 0xFFFFu), v[3] * bf16_bits_to_f32(gg[1] >> 16)});
+        } else if constexpr (EPI == kEpiStoreF32) {
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(Cout) + idx) = v;
+        } else {
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(Cout) + idx) = accumulate ? old4[j] + v : v;
         }
       }
     }
   };
   // Tiles wholly inside C with a store-only epilogue go through LDS: each
-  // wave writes one 32-row block of 128 output bytes per row (one fp32
-  // fragment, or two bf16 fragments) into its own region of the stage
-  // buffers, reads it back by rows and stores whole 128-byte row segments, so
-  // that every store instruction writes full cache lines (the accumulator
-  // layout alone gives 16- or 32-byte pieces of 32 rows per instruction).
+  // wave writes one 16-row block of 128 output bytes per row (two fp32 or
+  // four bf16 output fragments) into its own region of the stage buffers,
+  // reads it back by rows and stores whole 128-byte row segments, so that
+  // every store instruction writes full cache lines (the accumulator layout
+  // alone gives 16- or 8-byte pieces of 16 rows per instruction).
   constexpr bool kCanStage = EPI != kEpiMulAux;
   if constexpr (kCanStage) {
     if (m0 + BM <= M && n0 + BNO <= N && !accumulate) {
       constexpr int kElt = (EPI == kEpiStoreF32 || EPI == kEpiAccumF32) ? 4 : 2;
-      constexpr int kFragsPerChunk = (kElt == 2 && FNO % 2 == 0) ? 2 : 1;
-      constexpr int kChunkBytes = kFragsPerChunk * 32 * kElt;  // one row of a chunk: 128 or 64 bytes
+      constexpr int kWant = 128 / (16 * kElt);  // fragments per 128-byte row segment
+      constexpr int kFragsPerChunk = FNO % kWant == 0 ? kWant : (FNO % 2 == 0 ? 2 : 1);
+      constexpr int kChunkBytes = kFragsPerChunk * 16 * kElt;  // one row of a chunk: 128 bytes or less
       constexpr int kRowStride = kChunkBytes + 16;             // padded (bank spread)
-      constexpr int kRegion = 32 * kRowStride;
+      constexpr int kRegion = 16 * kRowStride;
       constexpr int kRegionsPerStage = STAGE / kRegion;
       static_assert(kRegionsPerStage * NBUF >= NW, "epilogue staging regions");
       constexpr int kLanesPerRow = kChunkBytes / 16;
       constexpr int kRowsPerPass = 64 / kLanesPerRow;
-      constexpr int kPasses = 32 / kRowsPerPass;
+      static_assert(kRowsPerPass <= 16 && 16 % kRowsPerPass == 0, "row passes");
+      constexpr int kPasses = 16 / kRowsPerPass;
       constexpr int kNumOut = EPI == kEpiBiasGeluSave ? 2 : 1;
       // Every wave is past its last fragment read and every DMA of the
       // workgroup has landed before the stage buffers are reused.
@@ -702,20 +693,12 @@ void gemm_bf16_kernel(GemmParams p) {
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int c = 0; c < FNO / kFragsPerChunk; ++c) {
-          // Each group of 4 final values goes to LDS as soon as it is
-          // computed (lane (row l32, half lane / 32) holds columns
-          // 32 f + 8 gq + 4 (lane / 32) .. + 3); the second output of the
-          // training epilogue waits packed in registers until the first has
-          // been read back.
-          u32x2_t second[kNumOut - 1 ? kFragsPerChunk : 1][4];
-          auto put = [&](int f, int gq, f32x4_t x) {
-            lds_char* dst = R + l32 * kRowStride + (32 * f + 8 * gq + hcol) * kElt;
-            if constexpr (kElt == 4) {
-              *(__attribute__((address_space(3))) f32x4_t*)dst = x;
-            } else {
-              *(__attribute__((address_space(3))) u32x2_t*)dst = pack4_bf16(x);
-            }
-          };
+          // Each fragment's 4 final values go to LDS as soon as they are
+          // computed (lane l: row l % 16, columns 16 f + 4 (l / 16) .. + 3);
+          // the second output of the training epilogue waits packed in
+          // registers until the first has been read back.
+          u32x2_t second[kNumOut - 1 ? kFragsPerChunk : 1];
+          auto slot = [&](int f) { return R + lrow * kRowStride + (16 * f + hcol) * kElt; };
           // Rows back from LDS, whole 128-byte (or 64-byte) row segments to C.
           auto drain = [&](void* out) {
             u32x4_t rows[kPasses];
@@ -723,7 +706,7 @@ void gemm_bf16_kernel(GemmParams p) {
             for (int t = 0; t < kPasses; ++t)
               rows[t] = *(__attribute__((address_space(3))) u32x4_t*)(R + (rrow + t * kRowsPerPass) * kRowStride + rcol);
             char* base = static_cast<char*>(out) +
-                         ((int64_t)(m0 + wm * WTM + i * 32 + rrow) * ldc + n0 + wn * WTNO + c * kFragsPerChunk * 32) *
+                         ((int64_t)(m0 + wm * WTM + i * 16 + rrow) * ldc + n0 + wn * WTNO + c * kFragsPerChunk * 16) *
                              kElt + rcol;
 #pragma unroll
             for (int t = 0; t < kPasses; ++t)
@@ -731,41 +714,25 @@ void gemm_bf16_kernel(GemmParams p) {
           };
 #pragma unroll
           for (int f = 0; f < kFragsPerChunk; ++f) {
-            const int j = c * kFragsPerChunk + f;
+            f32x4_t a = value(i, c * kFragsPerChunk + f);
+            if constexpr (EPI == kEpiBiasGelu) {
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              f32x4_t a;
-              if constexpr (DUAL) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = silu_f32(acc[i][j][4 * gq + e]) * acc[i][FNO + j][4 * gq + e];
-              } else {
-                a = f32x4_t{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
-                            acc[i][j][4 * gq + 3]};
-              }
-              if constexpr (kBias) a += bias4[j][gq];
-              if constexpr (EPI == kEpiBiasGelu) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = gelu_f32(a[e]);
-              }
-              if constexpr (EPI == kEpiBiasGeluSave) {
-                float y[4], g[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) gelu_and_grad_f32(a[e], y[e], g[e]);
-                put(f, gq, f32x4_t{y[0], y[1], y[2], y[3]});
-                second[f][gq] = pack4_bf16(f32x4_t{g[0], g[1], g[2], g[3]});
-              } else {
-                put(f, gq, a);
-              }
+              for (int e = 0; e < 4; ++e) a[e] = gelu_f32(a[e]);
             }
+            if constexpr (EPI == kEpiBiasGeluSave) {
+              float y[4], g[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) gelu_and_grad_f32(a[e], y[e], g[e]);
+              a = f32x4_t{y[0], y[1], y[2], y[3]};
+              second[f] = pack4_bf16(f32x4_t{g[0], g[1], g[2], g[3]});
+            }
+            if constexpr (kElt == 4) *(__attribute__((address_space(3))) f32x4_t*)slot(f) = a;
+            else *(__attribute__((address_space(3))) u32x2_t*)slot(f) = pack4_bf16(a);
           }
           drain(Cout);
           if constexpr (kNumOut == 2) {
 #pragma unroll
-            for (int f = 0; f < kFragsPerChunk; ++f)
-#pragma unroll
-              for (int gq = 0; gq < 4; ++gq)
-                *(__attribute__((address_space(3))) u32x2_t*)(R + l32 * kRowStride + (32 * f + 8 * gq + hcol) * kElt) =
-                    second[f][gq];
+            for (int f = 0; f < kFragsPerChunk; ++f) *(__attribute__((address_space(3))) u32x2_t*)slot(f) = second[f];
             drain(aux);
           }
         }
@@ -779,17 +746,11 @@ void gemm_bf16_kernel(GemmParams p) {
     epilogue(std::true_type{});
 }
 
-// A group sum keeps one accumulator set, like any other GEMM: every tile but
-// the 4-wave 256x256 one (whose epilogue spills) is compiled for it.
-constexpr bool tile_allows_group_sum(int t) {
-  return !(kTiles[t].bm == 256 && kTiles[t].bn == 256 && kTiles[t].wm * kTiles[t].wn == 4);
-}
-
 // SwiGLU splits a tile's BN columns into a gate and an up sub-tile of BN / 2
 // columns each (MN-major sub-tiles need 128, 256 or 512 columns) and every
 // wave's fragments into two equal sets.
 constexpr bool tile_allows_swiglu(int t) {
-  return (kTiles[t].bn / 2 == 128 || kTiles[t].bn / 2 == 256) && (kTiles[t].bn / kTiles[t].wn / 32) % 2 == 0;
+  return (kTiles[t].bn / 2 == 128 || kTiles[t].bn / 2 == 256) && (kTiles[t].bn / kTiles[t].wn / 16) % 2 == 0;
 }
 
 // Output columns of one workgroup tile.
@@ -804,8 +765,7 @@ constexpr int kTailTileSwiGLU = 6;
 // compiled for.
 constexpr bool instantiated(int layout, int t, bool ktail, bool gsum, int epi) {
   if (!layout_has_epi(layout, epi)) return false;
-  if (gsum && (layout == kTN || (epi != kEpiStoreF32 && epi != kEpiAccumF32) || !tile_allows_group_sum(t)))
-    return false;
+  if (gsum && (layout == kTN || (epi != kEpiStoreF32 && epi != kEpiAccumF32))) return false;
   if (epi == kEpiSwiGLU) return !gsum && tile_allows_swiglu(t) && (!ktail || t == kTailTileSwiGLU);
   return !ktail || t == kTailTile;
 }
