@@ -63,6 +63,10 @@ GemmParams base_params(const GemmBatch& b, int tile) {
 // MI355X (random bf16 data), counting the workgroups of the whole batch:
 //   * 256x256 (8 waves, 4 stages) when it fills at least two rounds of the 256
 //     CUs, or 192..255 tiles (a 0.75 round still beats the smaller tiles);
+//   * between one and two rounds of 256x256 tiles, with N a multiple of 384
+//     and a long K loop (K >= 4096): 128x384 (4 stages, one workgroup per
+//     CU), whose grid is half as many tiles again (gpt3_175b's shard sum:
+//     384 tiles of 256x256, 1.5 rounds; 512 of 128x384, two whole rounds);
 //   * otherwise 128x256 when N > 128: with 4 stages when its tiles fit one
 //     round of the CUs (one workgroup per CU, the deeper prefetch pays), else
 //     with 3 stages (two workgroups per CU);
@@ -74,9 +78,11 @@ GemmParams base_params(const GemmBatch& b, int tile) {
 int pick_bf16_tile(Layout layout, int64_t M, int64_t N, int64_t K, int groups, bool group_sum) {
   (void)layout;
   if (K % 32) return kTailTile;
+  const int64_t kloop = group_sum ? K * groups : K;  // the K loop of one tile
   if (group_sum) groups = 1;
   const int64_t t256 = tiles_of(0, M, N) * groups;
   if (t256 >= 512 || (t256 >= 192 && t256 < 256)) return 0;
+  if (t256 > 256 && N % 384 == 0 && kloop >= 4096) return 9;
   if (N > 128) return tiles_of(5, M, N) * groups <= 256 ? 5 : 6;
   return 8;
 }

@@ -91,6 +91,7 @@ constexpr TileCfg kTiles[] = {
     {128, 256, 2, 4, 3},  // 6
     {128, 128, 2, 2, 4},  // 7
     {128, 128, 2, 4, 4},  // 8
+    {128, 384, 2, 4, 4},  // 9
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -126,7 +127,6 @@ struct OperandTile {
   static constexpr int kBytes = R * 64;  // R x 32 x 2 bytes
   static constexpr int kPerWave = kBytes / 1024 / NW;
   static constexpr int kRow = KMAJ ? 64 : 2 * R;  // LDS row bytes
-  static constexpr int kRowsPerBlock = 1024 / kRow;
   static constexpr int kLanesPerRow = kRow / 16;
   static_assert(kBytes % (1024 * NW) == 0, "DMA split");
   static_assert(KMAJ || (R % 128 == 0 && R <= 512), "MN-major tiles need 16-chunk row groups");
@@ -162,8 +162,11 @@ struct OperandTile {
       step = (uint64_t)ld * 64u;  // 32 k-rows
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) {
-        const int row = (wave * kPerWave + i) * kRowsPerBlock + lane / kLanesPerRow;
-        const int c = (lane % kLanesPerRow) ^ swzMN(row);
+        // chunk o of the tile (LDS bytes 16 o ..): k-row o / kLanesPerRow,
+        // position o % kLanesPerRow (a 1 KB block may end inside a k-row)
+        const int o = (wave * kPerWave + i) * 64 + lane;
+        const int row = o / kLanesPerRow;
+        const int c = (o % kLanesPerRow) ^ swzMN(row);
         src[i] = r0 + c * 8 < rtot ? (uint32_t)row * (uint32_t)ld * 2u + (uint32_t)c * 16u : kOob;
         kidx[i] = row;
       }

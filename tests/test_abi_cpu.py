@@ -602,7 +602,7 @@ def test_tile_table_and_choice(L):
     tiles = tpm.tp_gemm_tiles()
     assert len(tiles) == L.tp_gemm_tiles(-1, None) >= 2
     for t in tiles:
-        assert t["bm"] in (128, 256) and t["bn"] in (128, 256)
+        assert t["bm"] in (128, 256) and t["bn"] in (128, 256, 384)
         assert t["waves"] in (4, 8) and 3 <= t["stages"] <= 6
         # LDS: the stages of one workgroup fit the 160 KB of a CU
         assert t["stages"] * (t["bm"] + t["bn"]) * 64 <= 160 * 1024
@@ -626,6 +626,12 @@ def test_tile_table_and_choice(L):
     # llama7b's 8192 x 4096 output is two rounds of 256 x 256 tiles, and so on
     assert tpm.tp_mlp_step_tile(2, 8, 8192, 4096, 2048) in big
     assert tpm.tp_mlp_step_tile(2, 8, 32768, 8192, 4096) in big
+    # gpt3_175b's shard sum: 1.5 rounds of 256 x 256 tiles, two whole rounds
+    # of 128 x 384 ones; its per-shard steps fill 6 and 12 rounds of 256 x 256
+    t = tpm.tp_mlp_step_tile(2, 8, 2048, 12288, 6144)
+    assert (tiles[t]["bm"], tiles[t]["bn"]) == (128, 384)
+    assert tpm.tp_mlp_step_tile(0, 8, 2048, 12288, 6144) in big
+    assert tpm.tp_mlp_step_tile(1, 8, 2048, 12288, 6144) in big
     # K = H not a multiple of 32: the ragged-K tile for any shape
     assert len({tpm.tp_mlp_step_tile(0, n, M, 200, 512) for n in (1, 4) for M in (64, 8192)}) == 1
 
