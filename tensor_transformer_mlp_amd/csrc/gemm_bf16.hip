@@ -54,6 +54,8 @@ GemmParams base_params(const GemmBatch& b, int tile) {
   p.k_slice = p.K;
   p.part = nullptr;
   p.part_stride = 0;
+  p.shared_a = 1;
+  for (int g = 1; g < b.groups; ++g) p.shared_a &= b.A[g] == b.A[0];
   return p;
 }
 

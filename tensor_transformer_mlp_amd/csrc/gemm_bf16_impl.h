@@ -75,6 +75,9 @@ struct GemmParams {
   int slices, k_slice;
   float* part;
   int64_t part_stride;
+  // Every group reads the same A (a column step's X): groups that divide
+  // the XCDs are pinned to XCD subsets (see the tile mapping).
+  int shared_a;
 };
 
 // Workgroup tile configurations (index = tile id used by the picker).
@@ -330,6 +333,22 @@ void gemm_bf16_kernel(GemmParams p) {
     grp = sg % p.groups;
     slice = sg / p.groups;
     strip_coords<8>(sg_tile - sg * tiles, p.tiles_m, p.tiles_n, tm, tn);
+  } else if (!GSUM && p.shared_a && p.groups > 1 && kNumXcd % p.groups == 0 &&
+             tiles % (kNumXcd / p.groups) == 0) {
+    // A batch that shares A, with groups dividing the XCDs: group g runs on
+    // XCDs [g per, (g + 1) per) only (workgroup b runs on XCD b % 8), each of
+    // them a contiguous range of the group's tiles walked in strips.  At any
+    // time the XCDs of different groups then stream the same rows of A (the
+    // last-level cache serves all but one of them) and each group's B stays
+    // in `per` L2s.  Measured against the group-major order: long_seq's
+    // column step 5% faster, llama7b's 2%, gpt3_175b's and gpt2_small's
+    // within 1%; on row steps, whose groups share nothing, it was 3-5%
+    // slower on the large shapes, so they keep the group-major order.
+    const int per = kNumXcd / p.groups;
+    const int x = bid % kNumXcd;
+    grp = x / per;
+    const int local = (bid / kNumXcd) * per + x % per;  // 0 .. tiles - 1 within the group
+    strip_coords<8>((local % per) * (tiles / per) + local / per, p.tiles_m, p.tiles_n, tm, tn);
   } else {
     if (!GSUM && p.groups > 1) {
       grp = bid / tiles;

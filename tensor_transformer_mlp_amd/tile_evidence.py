@@ -232,8 +232,8 @@ def _match(records, disp):
     for i, r in enumerate(records):
         key = (STEP_EPI[r["step"]], r["bm"], r["bn"], r["waves"], r["stages"], int(r["step"] == "sum"),
                r["workgroups"] * r["waves"] * 64)
-        # the library's own call shares its kernel with a forced-tile row (or,
-        # for a shard-by-shard sum, launches several): counters only on the latter
+        # the library's own call shares its kernel with the picked tile's row:
+        # counters only on the latter
         out[i] = by_key.get(key, []) if r["tile"] >= 0 else []
     return out
 
@@ -256,8 +256,8 @@ def summary(run_json, mfma_dir, fetch_dir, write_dir, out_md, commands):
              "Commands (run from the repository root on one MI355X):", "", "```", commands.strip(), "```", "",
              "Each row is one forward step of a workload's shards, all shards in one launch, with one tile of "
              "the table (BM x BN outputs per workgroup, waves, LDS stages); `*` marks the tile the library "
-             "picks, `library` the library's own call (the same kernel, or for a shard sum whose shards "
-             "each fill the chip several times, one accumulating launch per shard).  Time: median of %d "
+             "picks, `library` the library's own call (the picked tile's kernel, timed through the "
+             "library's entry point).  Time: median of %d "
              "event-timed groups of %d launches.  MFMA busy: rocprofv3 MfmaUtil "
              "(MFMA busy cycles over active cycles x %d SIMDs).  MFMA flop / algorithmic: "
              "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 over 2 M N K n.  Clock: active cycles over the "
@@ -287,9 +287,7 @@ def summary(run_json, mfma_dir, fetch_dir, write_dir, out_md, commands):
         fmt = lambda v, f: ("%" + f) % v if v is not None else "-"
         regs = "%d" % m[0]["scratch"] if m else "-"
         if r["tile"] < 0:
-            label = "library" + (" (shard by shard)" if r["step"] == "sum" and r["workgroups"] and not any(
-                q["tile"] >= 0 and q["workload"] == r["workload"] and q["step"] == "sum" and q["picked"]
-                for q in records) else "")
+            label = "library"
         else:
             label = "%d%s" % (r["tile"], " *" if r["picked"] else "")
         lines.append("| %s | %s | %s | %dx%d, %d, %d | %s | %d | %.1f | %.0f | %.1f | %s | %s | %s | %s | %s "
