@@ -254,13 +254,13 @@ struct OperandFrags {
 // columns), every wave reads its FN / 2 gate and FN / 2 up fragments at the
 // same offsets of the two sub-tiles, and the epilogue stores
 // SiLU(gate) * up: a BM x BN / 2 tile of the output.
+
 // Waves per SIMD to ask the register allocator for: as many as the
 // workgroups that the tile's LDS stages let share a CU bring (two 8-wave
 // workgroups of 72 KB: four waves per SIMD, so at most 128 VGPRs each).  The
 // training epilogue keeps a second output and is left to the allocator (at
 // 128 VGPRs it would spill, measured slower than one workgroup per CU).
-constexpr int gemm_waves_per_eu(int EPI, int BM, int BN, int WM, int WN, int NBUF, bool GSUM) {
-  (void)GSUM;
+constexpr int gemm_waves_per_eu(int EPI, int BM, int BN, int WM, int WN, int NBUF) {
   if (EPI == kEpiBiasGeluSave) return 1;
   const int per_cu = (160 * 1024) / (NBUF * (BM + BN) * 64);
   const int w = per_cu * WM * WN / 4;
@@ -268,7 +268,7 @@ constexpr int gemm_waves_per_eu(int EPI, int BM, int BN, int WM, int WN, int NBU
 }
 
 template <int EPI, int LAYOUT, int BM, int BN, int WM, int WN, int NBUF, bool KTAIL, bool GSUM>
-__global__ __launch_bounds__(WM* WN * 64, gemm_waves_per_eu(EPI, BM, BN, WM, WN, NBUF, GSUM))
+__global__ __launch_bounds__(WM* WN * 64, gemm_waves_per_eu(EPI, BM, BN, WM, WN, NBUF))
 void gemm_bf16_kernel(GemmParams p) {
   constexpr bool AK = LAYOUT != kTN;  // A K-major
   constexpr bool BK = LAYOUT == kNT;  // B K-major
@@ -354,7 +354,14 @@ void gemm_bf16_kernel(GemmParams p) {
       grp = bid / tiles;
       bid -= grp * tiles;
     }
-    tile_coords<8>(bid, tiles, p.tiles_m, p.tiles_n, tm, tn);
+    // A group sum's K loop runs through every shard, so each A row panel is
+    // long (long_seq: 256 rows x 32768 k) and cannot stay in the last-level
+    // cache from one column round to the next: strips of 4 tile rows (x 8
+    // columns per XCD round) read each A panel half as many times as strips
+    // of 8 (x 4), for twice the B panels, which every XCD shares.  Measured
+    // with 256 x 256 tiles: long_seq's shard sum 2% faster, llama7b's the same.
+    constexpr int kStrip = (GSUM && BM == 256 && BN == 256) ? 4 : 8;
+    tile_coords<kStrip>(bid, tiles, p.tiles_m, p.tiles_n, tm, tn);
   }
   // (wave-uniform by construction; said explicitly so that the operand
   // pointers derived from them stay in scalar registers)
