@@ -330,37 +330,44 @@ void oracle_backward_cols(const double* X, const double* W, const double* b, con
   {
     double* y = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
     double* da = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+    double* w = (double*)malloc(sizeof(double) * (size_t)(H > 0 ? H : 1));
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < ncols; ++r) {
       const int64_t c = cols[r];
       const double* v = V + c * H;
+      for (int64_t h = 0; h < H; ++h) w[h] = W[h * F + c];              /* column c of W */
       for (int64_t m = 0; m < M; ++m) {
+        const double* x = X + m * H;
+        const double* dz = dZ + m * H;
         double a = 0.0;                                                  /* step 2 */
-        for (int64_t h = 0; h < H; ++h) a += X[m * H + h] * W[h * F + c];
+        for (int64_t h = 0; h < H; ++h) a += x[h] * w[h];
         if (b) a += b[c];
         double s = 0.0;                                                  /* step 7 */
-        for (int64_t n = 0; n < H; ++n) s += dZ[m * H + n] * v[n];
+        for (int64_t n = 0; n < H; ++n) s += dz[n] * v[n];
         y[m] = oracle_gelu(a);                                           /* step 3 */
         da[m] = s * oracle_gelu_grad(a);                                 /* step 8 */
       }
-      double* dw = dWc + r * H;                                          /* step 9 */
-      for (int64_t h = 0; h < H; ++h) {
-        double s = 0.0;
-        for (int64_t m = 0; m < M; ++m) s += X[m * H + h] * da[m];
-        dw[h] = s;
-      }
+      /* dW[:, c] = X^T da, db[c] = sum da (step 9) and dV[c, :] = y^T dZ
+         (step 7): every sum runs over m = 0 .. M-1 in order, one row of X
+         and of dZ at a time. */
+      double* dw = dWc + r * H;
+      double* dv = dVc + r * H;
+      for (int64_t h = 0; h < H; ++h) dw[h] = 0.0;
+      for (int64_t n = 0; n < H; ++n) dv[n] = 0.0;
       double sb = 0.0;
-      for (int64_t m = 0; m < M; ++m) sb += da[m];
-      dbc[r] = sb;
-      double* dv = dVc + r * H;                                          /* step 7 */
-      for (int64_t n = 0; n < H; ++n) {
-        double s = 0.0;
-        for (int64_t m = 0; m < M; ++m) s += y[m] * dZ[m * H + n];
-        dv[n] = s;
+      for (int64_t m = 0; m < M; ++m) {
+        const double* x = X + m * H;
+        const double* dz = dZ + m * H;
+        const double d = da[m], ym = y[m];
+        for (int64_t h = 0; h < H; ++h) dw[h] += x[h] * d;
+        for (int64_t n = 0; n < H; ++n) dv[n] += ym * dz[n];
+        sb += d;
       }
+      dbc[r] = sb;
     }
     free(y);
     free(da);
+    free(w);
   }
 }
 
