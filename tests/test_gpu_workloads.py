@@ -16,7 +16,7 @@ run to run, bit for bit.
 import numpy as np
 import pytest
 
-from _helpers import (assert_within, col_bound, f64, forward_bound, from_dev, rel_fro,
+from _helpers import (assert_within, check_forward_rows, col_bound, f64, from_dev, rel_fro,
                       row_bound, say, tile_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -33,39 +33,6 @@ def _rows(M, n_random=10, seed=7):
     rng = np.random.default_rng(seed)
     base.update(int(x) for x in rng.integers(0, M, size=n_random))
     return np.array(sorted(base))
-
-
-def check_forward_rows(name, w, X, W, b, V, variants, rows, block=512):
-    """Compare the GPU's Z on `rows` with the oracle's forward, element by
-    element against forward_bound, in blocks of rows.  `variants` maps a label
-    to (fused, Zg_of) with Zg_of(row_indices) -> float32 numpy rows.  Returns
-    each variant's relative Frobenius error over all the rows compared."""
-    import oracle
-    W64, b64, V64 = f64(W), f64(b), f64(V)
-    aW, aV = np.abs(W64), np.abs(V64)
-    k = w.k
-    num = {lb: 0.0 for lb in variants}
-    den = 0.0
-    for r0 in range(0, rows.size, block):
-        rr = rows[r0:r0 + block]
-        X64r = f64(X[rr])
-        Zr = oracle.forward_rows(X64r, W64, b64, V64, k)     # expected values: the oracle
-        # bound (magnitudes only): the column step's bound per shard, through V
-        A = X64r @ W64 + b64[None, :]
-        Y = oracle.gelu(A)
-        S = np.abs(X64r) @ aW + np.abs(b64)[None, :]
-        u_out = 2.0 ** -8 if w.dtype == "bf16" else 0.0
-        tolY = ((1 + u_out) * (1.13 * 2 * (w.H + 2) * 2.0 ** -24 * S + 8 * 2.0 ** -24 * (2 + A * A) * np.abs(Y)
-                               + 2e-7 * np.abs(A)) + u_out * np.abs(Y) + 1e-30)
-        del A, S
-        den += float(np.sum(Zr ** 2))
-        for lb, (fused, Zg_of) in variants.items():
-            Zg = Zg_of(rr).astype(np.float64)
-            bound = forward_bound(tolY, Y, V64, k, fused=fused, absV=aV)
-            assert_within(Zg, Zr, bound, "%s Z rows %d..%d (%s)" % (name, rr[0], rr[-1], lb))
-            num[lb] += float(np.sum((Zg - Zr) ** 2))
-        del tolY, Y
-    return {lb: (num[lb] / den) ** 0.5 if den else num[lb] ** 0.5 for lb in variants}
 
 
 @pytest.mark.timeout(900)
