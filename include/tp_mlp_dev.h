@@ -51,6 +51,18 @@ int tp_mlp_col_gelu_shards_tile(int tile, const void* X, const void* const* W, c
 int tp_mlp_row_partial_shards_tile(int tile, const void* const* Y, const void* const* V, float* const* Z,
                                    int n, int64_t M, int64_t Fk, int64_t H, unsigned flags, void* stream);
 
+/*
+ * tp_attn_core_shards with a chosen attention kernel, for measuring the
+ * library's choice between them (all give the same results, bit for bit;
+ * the head-split attention of "AI大模型分布式训练：张量并行与流水线并行深度实践"
+ * §2.3): variant 0 = one group of 32 queries per wave (4 waves, 128 queries
+ * per workgroup), 1 = two groups per wave (256 queries per workgroup).  Other
+ * arguments and rules as tp_attn_core_shards; TP_ERR_SHAPE for another
+ * variant.
+ */
+int tp_attn_core_shards_variant(int variant, const void* const* QKV, void* const* A, int n, int64_t B, int64_t S,
+                                int heads, int head_dim, int dtype, unsigned flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,7 +61,7 @@ __all__ = [
     "tp_swiglu_col", "tp_swiglu_col_shards", "tp_swiglu_shard_forward", "TP_CAUSAL",
     "tp_attn_qkv_shards", "tp_attn_core_shards", "tp_attn_workspace_bytes", "tp_attn_shard_forward",
     "tp_gemm_tiles", "tp_mlp_step_tile", "tp_mlp_col_gelu_shards_tile", "tp_mlp_row_partial_shards_tile",
-    "tp_mlp_shard_forward_noalloc", "TP_NOALLOC_SCRATCH_BYTES",
+    "tp_attn_core_shards_variant", "tp_mlp_shard_forward_noalloc", "TP_NOALLOC_SCRATCH_BYTES",
 ]
 
 TP_F32 = 0
@@ -157,6 +157,8 @@ def lib() -> ctypes.CDLL:
         L.tp_attn_qkv_shards.restype = ci
         L.tp_attn_core_shards.argtypes = [vp, vp, ci, i64, i64, ci, ci, ci, cu, vp]
         L.tp_attn_core_shards.restype = ci
+        L.tp_attn_core_shards_variant.argtypes = [ci, vp, vp, ci, i64, i64, ci, ci, ci, cu, vp]
+        L.tp_attn_core_shards_variant.restype = ci
         L.tp_attn_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ci, cu]
         L.tp_attn_workspace_bytes.restype = sz
         L.tp_attn_shard_forward.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, ci, ci, vp, sz, vp, cu, vp]
@@ -860,6 +862,18 @@ def tp_attn_qkv_shards(X, Wqkv, bqkv, QKV, stream=None):
 @_on_caller_stream
 def tp_attn_core_shards(QKV, A, B: int, S: int, heads: int, head_dim: int, causal: bool = True, stream=None):
     """A[i] = the attention of shard i's heads from its projection QKV[i]."""
+    return _attn_core(-1, QKV, A, B, S, heads, head_dim, causal, stream)
+
+
+@_on_caller_stream
+def tp_attn_core_shards_variant(variant: int, QKV, A, B: int, S: int, heads: int, head_dim: int,
+                                causal: bool = True, stream=None):
+    """tp_attn_core_shards with attention kernel `variant` (0: one query group per wave, 1: two; a
+    measurement hook)."""
+    return _attn_core(variant, QKV, A, B, S, heads, head_dim, causal, stream)
+
+
+def _attn_core(variant, QKV, A, B, S, heads, head_dim, causal, stream):
     n = len(QKV)
     if n < 1 or len(A) != n:
         raise ValueError("QKV and A must hold the same number n >= 1 of shards")
@@ -868,9 +882,14 @@ def tp_attn_core_shards(QKV, A, B: int, S: int, heads: int, head_dim: int, causa
         if QKV[i].numel() != B * S * 3 * Hk or A[i].numel() != B * S * Hk:
             raise ValueError("shard %d has the wrong size" % i)
     _same_dtype("tp_attn_core_shards", QKV[0], *QKV, *A)
-    _check(lib().tp_attn_core_shards(_ptrs(QKV, "QKV"), _ptrs(A, "A"), n, B, S, heads, head_dim,
-                                     _dtype_code(QKV[0]), TP_CAUSAL if causal else 0, _stream(stream)),
-           "tp_attn_core_shards")
+    flags = TP_CAUSAL if causal else 0
+    if variant < 0:
+        st = lib().tp_attn_core_shards(_ptrs(QKV, "QKV"), _ptrs(A, "A"), n, B, S, heads, head_dim,
+                                       _dtype_code(QKV[0]), flags, _stream(stream))
+    else:
+        st = lib().tp_attn_core_shards_variant(variant, _ptrs(QKV, "QKV"), _ptrs(A, "A"), n, B, S, heads,
+                                               head_dim, _dtype_code(QKV[0]), flags, _stream(stream))
+    _check(st, "tp_attn_core_shards" if variant < 0 else "tp_attn_core_shards_variant")
     return A
 
 

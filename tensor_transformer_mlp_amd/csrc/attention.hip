@@ -331,6 +331,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
   }
 }
 
+
 }  // namespace
 
 // Query groups of 32 per wave: two when the grid of 256-query workgroups
@@ -346,9 +347,10 @@ static int attention_query_groups(int64_t S, int64_t seqs) {
   return ((S + 2 * kBQ - 1) / (2 * kBQ)) * seqs >= kWideGrid ? 2 : 1;
 }
 
-hipError_t launch_attention_bf16(const void* const* qkv, void* const* out, int groups, int64_t B,
-                                 int64_t S, int heads, int d, bool causal, hipStream_t s) {
+hipError_t launch_attention_bf16_variant(int variant, const void* const* qkv, void* const* out, int groups,
+                                         int64_t B, int64_t S, int heads, int d, bool causal, hipStream_t s) {
   if (groups < 1 || groups > kMaxGroups || (d != 64 && d != 128)) return hipErrorInvalidValue;
+  if (variant < -1 || variant > 1) return hipErrorInvalidValue;
   if (B <= 0 || S <= 0) return hipSuccess;
   AttnParams p{};
   for (int gi = 0; gi < groups; ++gi) {
@@ -359,16 +361,18 @@ hipError_t launch_attention_bf16(const void* const* qkv, void* const* out, int g
   p.B = (int)B;
   p.S = (int)S;
   p.heads = heads;
-  const int qg = attention_query_groups(S, (int64_t)groups * B * heads);
+  const int64_t seqs = (int64_t)groups * B * heads;
+  if (variant < 0) variant = attention_query_groups(S, seqs) - 1;
+  const int qg = variant + 1;
   p.nqb = (int)((S + kBQ * qg - 1) / (kBQ * qg));
-  const int64_t blocks = (int64_t)p.nqb * groups * B * heads;
+  const int64_t blocks = (int64_t)p.nqb * seqs;
   const dim3 grid((unsigned)blocks), block(256);
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
   const auto launch = [&](auto dd, auto cc, auto gg) {
     hipLaunchKernelGGL((attention_kernel<decltype(dd)::value, decltype(cc)::value, decltype(gg)::value>), grid,
                        block, 0, s, p);
   };
-  using D64 = std::integral_constant<int, 64>;
-  using D128 = std::integral_constant<int, 128>;
   using G1 = std::integral_constant<int, 1>;
   using G2 = std::integral_constant<int, 2>;
   if (d == 128) {
@@ -379,6 +383,11 @@ hipError_t launch_attention_bf16(const void* const* qkv, void* const* out, int g
     else causal ? launch(D64{}, std::true_type{}, G1{}) : launch(D64{}, std::false_type{}, G1{});
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attention_bf16(const void* const* qkv, void* const* out, int groups, int64_t B,
+                                 int64_t S, int heads, int d, bool causal, hipStream_t s) {
+  return launch_attention_bf16_variant(-1, qkv, out, groups, B, S, heads, d, causal, s);
 }
 
 }  // namespace tpmlp

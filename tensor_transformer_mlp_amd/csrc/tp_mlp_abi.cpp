@@ -460,6 +460,31 @@ int step_batch(int step, int n, int64_t M, int64_t H, int64_t Fk, unsigned flags
   }
 }
 
+// tp_attn_core_shards with a chosen attention kernel (-1: the library's).
+int attn_core_variant(int variant, const void* const* QKV, void* const* A, int n, int64_t B, int64_t S,
+                      int heads, int head_dim, int dtype, unsigned flags, void* stream) {
+  if (check_dtype(dtype)) return TP_ERR_DTYPE;
+  if (dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (flags & ~TP_CAUSAL) return TP_ERR_FLAGS;
+  if (n < 1 || n > TP_MAX_BATCH || heads < 1) return TP_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return TP_ERR_SHAPE;
+  int st = check_attn(B, S, int64_t(heads) * head_dim, heads, 1);
+  if (st) return st;
+  if (B == 0 || S == 0) return TP_OK;
+  if (!QKV || !A) return TP_ERR_NULL;
+  const size_t M = size_t(B) * size_t(S), Hk = size_t(heads) * size_t(head_dim);
+  Regions in, out;
+  for (int i = 0; i < n; ++i) {
+    if (!QKV[i] || !A[i]) return TP_ERR_NULL;
+    if (!aligned16(QKV[i]) || !aligned16(A[i])) return TP_ERR_ALIGN;
+    in.add(QKV[i], M * 3 * Hk * 2);
+    out.add(A[i], M * Hk * 2);
+  }
+  if (any_overlap(out, in)) return TP_ERR_ALIAS;
+  return hip_status(tpmlp::launch_attention_bf16_variant(variant, QKV, A, n, B, S, heads, head_dim,
+                                                         (flags & TP_CAUSAL) != 0, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -761,26 +786,7 @@ int tp_attn_qkv_shards(const void* X, const void* const* Wqkv, const void* const
 
 int tp_attn_core_shards(const void* const* QKV, void* const* A, int n, int64_t B, int64_t S, int heads,
                         int head_dim, int dtype, unsigned flags, void* stream) {
-  if (check_dtype(dtype)) return TP_ERR_DTYPE;
-  if (dtype != TP_BF16) return TP_ERR_DTYPE;
-  if (flags & ~TP_CAUSAL) return TP_ERR_FLAGS;
-  if (n < 1 || n > TP_MAX_BATCH || heads < 1) return TP_ERR_SHAPE;
-  if (head_dim != 64 && head_dim != 128) return TP_ERR_SHAPE;
-  int st = check_attn(B, S, int64_t(heads) * head_dim, heads, 1);
-  if (st) return st;
-  if (B == 0 || S == 0) return TP_OK;
-  if (!QKV || !A) return TP_ERR_NULL;
-  const size_t M = size_t(B) * size_t(S), Hk = size_t(heads) * size_t(head_dim);
-  Regions in, out;
-  for (int i = 0; i < n; ++i) {
-    if (!QKV[i] || !A[i]) return TP_ERR_NULL;
-    if (!aligned16(QKV[i]) || !aligned16(A[i])) return TP_ERR_ALIGN;
-    in.add(QKV[i], M * 3 * Hk * 2);
-    out.add(A[i], M * Hk * 2);
-  }
-  if (any_overlap(out, in)) return TP_ERR_ALIAS;
-  return hip_status(tpmlp::launch_attention_bf16(QKV, A, n, B, S, heads, head_dim, (flags & TP_CAUSAL) != 0,
-                                                 static_cast<hipStream_t>(stream)));
+  return attn_core_variant(-1, QKV, A, n, B, S, heads, head_dim, dtype, flags, stream);
 }
 
 size_t tp_attn_workspace_bytes(int k, int64_t B, int64_t S, int64_t H, int n_heads, int dtype, unsigned flags) {
@@ -1156,6 +1162,12 @@ int tp_mlp_row_partial_shards_tile(int tile, const void* const* Y, const void* c
   if (st) return st;
   if (!tpmlp::gemm_bf16_tile_can_run(tile, g)) return TP_ERR_SHAPE;
   return row_shards(Y, V, Z, n, M, Fk, H, TP_BF16, flags, stream, tile);
+}
+
+int tp_attn_core_shards_variant(int variant, const void* const* QKV, void* const* A, int n, int64_t B, int64_t S,
+                                int heads, int head_dim, int dtype, unsigned flags, void* stream) {
+  if (variant < 0 || variant > 1) return TP_ERR_SHAPE;
+  return attn_core_variant(variant, QKV, A, n, B, S, heads, head_dim, dtype, flags, stream);
 }
 
 }  // extern "C"

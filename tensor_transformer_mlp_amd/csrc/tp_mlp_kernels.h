@@ -135,6 +135,11 @@ hipError_t launch_transpose_bf16(const void* const* src, void* const* dst, int g
 // heads d) keeps a sequence's rows within 32-bit offsets.
 hipError_t launch_attention_bf16(const void* const* qkv, void* const* out, int groups, int64_t B,
                                  int64_t S, int heads, int d, bool causal, hipStream_t s);
+// The same with a chosen kernel: 0 one query group of 32 per wave (128
+// queries per workgroup), 1 two groups per wave (256 queries); -1 the
+// library's choice.
+hipError_t launch_attention_bf16_variant(int variant, const void* const* qkv, void* const* out, int groups,
+                                         int64_t B, int64_t S, int heads, int d, bool causal, hipStream_t s);
 
 // This device's copy of the static scratch array of the entry point that
 // allocates nothing (TP_NOALLOC_SCRATCH_BYTES; the device of `stream`).

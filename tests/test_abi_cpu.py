@@ -53,12 +53,12 @@ def test_exports_every_declared_symbol(L):
                      "tp_attn_qkv_shards", "tp_attn_core_shards", "tp_attn_workspace_bytes",
                      "tp_attn_shard_forward", "tp_gemm_tiles", "tp_mlp_step_tile",
                      "tp_mlp_col_gelu_shards_tile", "tp_mlp_row_partial_shards_tile",
-                     "tp_mlp_shard_forward_noalloc"}
+                     "tp_attn_core_shards_variant", "tp_mlp_shard_forward_noalloc"}
     for n in names:
         assert hasattr(L, n), n
     # the measurement hooks live in the dev header only
     assert _declared(DEV_HEADER) == {"tp_gemm_tiles", "tp_mlp_step_tile", "tp_mlp_col_gelu_shards_tile",
-                                     "tp_mlp_row_partial_shards_tile"}
+                                     "tp_mlp_row_partial_shards_tile", "tp_attn_core_shards_variant"}
     assert not _declared(HEADER) & _declared(DEV_HEADER)
 
 
@@ -675,6 +675,23 @@ def test_tile_hook_errors(L):
     assert row(*a) == c["TP_ERR_NULL"]
     a = okr(); a[5] = 0
     assert row(*a) == c["TP_OK"]
+    att = L.tp_attn_core_shards_variant
+    Q, A = arr(P * 2, P * 3), arr(P * 4, P * 5)
+    oka = lambda: [0, Q, A, 2, 1, 64, 2, 64, c["TP_BF16"], c["TP_CAUSAL"], None]
+    for bad in (-1, 2, 100):
+        a = oka(); a[0] = bad
+        assert att(*a) == c["TP_ERR_SHAPE"], bad
+    a = oka(); a[7] = 96
+    assert att(*a) == c["TP_ERR_SHAPE"]
+    a = oka(); a[9] = 4
+    assert att(*a) == c["TP_ERR_FLAGS"]
+    a = oka(); a[2] = arr(P * 4, None)
+    assert att(*a) == c["TP_ERR_NULL"]
+    a = oka(); a[2] = arr(P * 4, P * 2)   # A[1] over QKV[0]
+    assert att(*a) == c["TP_ERR_ALIAS"]
+    for v in (0, 1):
+        a = oka(); a[0] = v; a[5] = 0
+        assert att(*a) == c["TP_OK"]
 
 
 def test_library_binds_torchs_hip_runtime():

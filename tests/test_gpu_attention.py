@@ -120,6 +120,47 @@ def test_attn_core_wide_grid(tpm, orc, G, B, S, heads, d, causal):
     assert rel_fro(A0, Ar) <= 1e-2
 
 
+VARIANT_CASES = CORE_CASES + [
+    # B, S, heads, d, causal, score std: several 256-query blocks, ragged tails
+    (1, 511, 2, 128, True, 1.0), (2, 777, 1, 128, False, 1.0), (1, 1300, 2, 64, True, 2.0),
+    (3, 257, 3, 64, False, 1.0), (1, 2048, 1, 128, True, 1.0), (2, 33, 2, 128, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("B,S,heads,d,causal,std", VARIANT_CASES)
+def test_attn_core_variants_identical(tpm, orc, B, S, heads, d, causal, std):
+    """Both attention kernels (one and two query groups per wave), chosen
+    through the measurement hook at shapes where the library would pick
+    either, give the same bits, write nothing outside A, and the two-group
+    kernel passes the oracle bounds element by element."""
+    import torch
+    from tensor_transformer_mlp_amd import inputs
+    say("attn_core variants B=%d S=%d heads=%d d=%d causal=%s" % (B, S, heads, d, causal))
+    Hk = heads * d
+    M = B * S
+    n = 2
+    qkv_h = [inputs.draw(inputs.STREAM_X, (M, 3 * Hk), std, "bf16", seed=B * 777 + S + heads + d + i)
+             for i in range(n)]
+    qkvs = [to_dev(q) for q in qkv_h]
+    pad = 64
+    outs = {}
+    for v in (0, 1):
+        bufs, As = zip(*[_guarded(torch, (M, Hk), torch.bfloat16, pad) for _ in range(n)])
+        tpm.tp_attn_core_shards_variant(v, qkvs, list(As), B, S, heads, d, causal=causal)
+        torch.cuda.synchronize()
+        for buf in bufs:
+            assert bool(torch.all(torch.isnan(buf[:pad]))) and bool(torch.all(torch.isnan(buf[-pad:]))), v
+        outs[v] = As
+    for v in (1,):
+        for i in range(n):
+            assert torch.equal(outs[v][i], outs[0][i]), (v, i)
+    Ag = f64(from_dev(outs[1][1]))
+    assert np.all(np.isfinite(Ag))
+    Ar = orc.attn_core(qkv_h[1], B, S, heads, d, causal)
+    assert_within(Ag, Ar, attn_core_bound(f64(qkv_h[1]), Ar, B, S, heads, d, causal), "A")
+    assert rel_fro(Ag, Ar) <= 1e-2
+
+
 def _shard_inputs(inp, n_heads, k):
     from tensor_transformer_mlp_amd import inputs
     Wqkv, bqkv = inputs.qkv_shards(inp["Wq"], inp["Wk"], inp["Wv"], inp["bq"], inp["bk"], inp["bv"], n_heads, k)
