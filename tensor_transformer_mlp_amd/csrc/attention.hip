@@ -58,13 +58,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-// Chunk swizzle of a [keys][D] tile: D = 128 rows are one 256-byte bank row,
-// so the 16 chunks of consecutive keys are rotated by key & 15; D = 64 rows
-// pair up in a bank row, rotated by (key >> 1) & 7.
+// Chunk swizzle of a [keys][D] tile: the 16-byte chunk c of key row k sits
+// at position c ^ swz(k).  The LDS (64 banks of 4 bytes) serves a 16-byte
+// read of a wave in four passes of 16 lanes, lanes {0-7, 16-23}, {8-15,
+// 24-31}, {32-39, 48-55}, {40-47, 56-63} (the grouping that separates the
+// conflict-free swizzle of the GEMM's K-major fragments, measured, from the
+// ones measured 1.7x slower), and an 8-byte transpose read in two passes of
+// 32 lanes.  A K fragment read (lane l: key l % 32, chunk 2 j + l / 32) is
+// then conflict-free when swz takes 16 distinct values on keys {0-7, 16-23}
+// and on {8-15, 24-31}; a V^T transpose read (lanes 0-31: keys 4 m .. 4 m +
+// 3, four consecutive chunks each) when the four keys of every aligned
+// quad put their chunk quads apart.  D = 128 (256-byte rows, 16 chunks):
+// bits 2-3 of swz = key bits 0-1, bit 0 = key bit 2, bit 1 = key bit 4.  D =
+// 64 (128-byte rows, two keys per bank row, 8 chunks): bit 2 = key bit 1,
+// bit 0 = key bit 2, bit 1 = key bit 4.  Key bit 5 is not used, so keys k and
+// k + 32 share a swizzle (the two 32-key halves of a block are one address
+// immediate apart); key bit 4 is, so the V^T reads of keys 16 .. 31 of each
+// half have their own lane addresses.  (The previous swizzles, key & 15 and
+// (key >> 1) & 7, gave 2-way conflicts on the K reads and 2- to 4-way on the
+// V^T reads under this model; rocprofv3's SQ_LDS_BANK_CONFLICT for the
+// kernel went from 2.6e7 to 0 with these.)
 template <int D>
 __device__ __forceinline__ int swz(int key) {
-  if constexpr (D == 128) return key & 15;
-  else return (key >> 1) & 7;
+  if constexpr (D == 128) return ((key & 3) << 2) | ((key >> 2) & 1) | (((key >> 4) & 1) << 1);
+  else return ((key >> 2) & 1) | (((key >> 4) & 1) << 1) | (((key >> 1) & 1) << 2);
 }
 
 template <int D, bool CAUSAL, int QG>
@@ -152,18 +169,20 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
   // V^T fragment (A operand of O^T += V^T P^T) of output tile t, k-step jj
   // (keys 16 jj ..): two transpose reads at keys 16 jj + 4 h2 + 8 r + (q / 4),
   // columns 32 t + 16 ((lane >> 4) & 1) + 4 (q % 4), q = lane % 16; the
-  // swizzle does not depend on jj.
-  uint32_t vaddr[DT][2];  // stage 0's LDS address; + 16 jj ROW and + s STAGE are immediates
+  // swizzle depends on jj % 2 only.
+  uint32_t vaddr[2][DT][2];  // [jj % 2]: stage 0's LDS address; + 32 (jj / 2) ROW and + s STAGE are immediates
   {
     const int q = lane & 15;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int par = 0; par < 2; ++par)
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int key = 4 * h2 + 8 * r + (q >> 2);
-        const int col = 32 * t + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
-        vaddr[t][r] = L0 + TILE + key * ROW + (((col >> 3) ^ swz<D>(key)) << 4) + ((col >> 2) & 1) * 8;
-      }
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int key = 16 * par + 4 * h2 + 8 * r + (q >> 2);
+          const int col = 32 * t + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+          vaddr[par][t][r] = L0 + TILE + key * ROW + (((col >> 3) ^ swz<D>(key)) << 4) + ((col >> 2) & 1) * 8;
+        }
   }
 
   f32x16_t acc[QG][DT];
@@ -219,8 +238,10 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
     auto read_v = [&](int jj, bf16x8_t* dst) {
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_half*)(uintptr_t)(vaddr[t][0] + SB + jj * 16 * ROW));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_half*)(uintptr_t)(vaddr[t][1] + SB + jj * 16 * ROW));
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_half*)(uintptr_t)(vaddr[jj & 1][t][0] + SB + (jj >> 1) * 32 * ROW));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_half*)(uintptr_t)(vaddr[jj & 1][t][1] + SB + (jj >> 1) * 32 * ROW));
         dst[t] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
