@@ -710,19 +710,7 @@ void gemm_bf16_kernel(GemmParams p) {
       constexpr int kWant = 128 / (16 * kElt);  // fragments per 128-byte row segment
       constexpr int kFragsPerChunk = FNO % kWant == 0 ? kWant : (FNO % 2 == 0 ? 2 : 1);
       constexpr int kChunkBytes = kFragsPerChunk * 16 * kElt;  // one row of a chunk: 128 bytes or less
-      // Full 128-byte rows are stored unpadded and swizzled: row r in row
-      // slot r ^ ((r >> 1) & 1), its 16-byte unit u at position u ^ sx(r).
-      // The LDS serves a 16-byte access of a wave in four passes of 16 lanes
-      // (lanes {0-7, 16-23}, {8-15, 24-31}, {32-39, 48-55}, {40-47, 56-63})
-      // and an 8-byte one in two of 32: the row slots put the two rows of a
-      // read-back pass (r, r + 2) in different halves of the 64 banks, and
-      // sx spreads the rows of a write pass (8 rows by two units, or 16 rows
-      // by one) over distinct bank groups, so neither the writes (16- or
-      // 8-byte) nor the read-back conflicts.  (A 16-byte pad per row, the
-      // layout of shorter chunks, leaves 2-way conflicts on the read-back and
-      // on 16-byte writes.)
-      constexpr bool kSwz = kChunkBytes == 128;
-      constexpr int kRowStride = kSwz ? 128 : kChunkBytes + 16;
+      constexpr int kRowStride = kChunkBytes + 16;             // padded (bank spread)
       constexpr int kRegion = 16 * kRowStride;
       constexpr int kRegionsPerStage = STAGE / kRegion;
       static_assert(kRegionsPerStage * NBUF >= NW, "epilogue staging regions");
@@ -754,21 +742,13 @@ void gemm_bf16_kernel(GemmParams p) {
           // the second output of the training epilogue waits packed in
           // registers until the first has been read back.
           u32x2_t second[kNumOut - 1 ? kFragsPerChunk : 1];
-          auto srow = [](int r) { return kSwz ? (r ^ ((r >> 1) & 1)) : r; };
-          auto sx = [](int r) { return kSwz ? 2 * ((r >> 1) & 3) + ((r >> 3) & 1) : 0; };
-          auto slot = [&](int f) {
-            const int b = (16 * f + hcol) * kElt;  // byte in the row (within one 16-byte unit)
-            return R + srow(lrow) * kRowStride + ((((b >> 4) ^ sx(lrow)) << 4) | (b & 15));
-          };
+          auto slot = [&](int f) { return R + lrow * kRowStride + (16 * f + hcol) * kElt; };
           // Rows back from LDS, whole 128-byte (or 64-byte) row segments to C.
           auto drain = [&](void* out) {
             u32x4_t rows[kPasses];
 #pragma unroll
-            for (int t = 0; t < kPasses; ++t) {
-              const int r = rrow + t * kRowsPerPass;
-              rows[t] = *(__attribute__((address_space(3))) u32x4_t*)(R + srow(r) * kRowStride +
-                                                                      (((rcol >> 4) ^ sx(r)) << 4));
-            }
+            for (int t = 0; t < kPasses; ++t)
+              rows[t] = *(__attribute__((address_space(3))) u32x4_t*)(R + (rrow + t * kRowsPerPass) * kRowStride + rcol);
             char* base = static_cast<char*>(out) +
                          ((int64_t)(m0 + wm * WTM + i * 16 + rrow) * ldc + n0 + wn * WTNO + c * kFragsPerChunk * 16) *
                              kElt + rcol;
