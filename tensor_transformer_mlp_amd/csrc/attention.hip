@@ -78,6 +78,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // (key >> 1) & 7, gave 2-way conflicts on the K reads and 2- to 4-way on the
 // V^T reads under this model; rocprofv3's SQ_LDS_BANK_CONFLICT for the
 // kernel went from 2.6e7 to 0 with these.)
+// The value of lane l ^ 32 (the other half-wave), by v_permlane32_swap: a
+// swap of the upper half of one register with the lower half of another,
+// here both x, leaves x of lanes 0-31 in every lane of one result and x of
+// lanes 32-63 in every lane of the other.
+__device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  // (the elements are copied out first: a bit cast of an element of the
+  // returned vector reads element 0 with this compiler)
+  const uint32_t r0 = r[0], r1 = r[1];
+  lo = __builtin_bit_cast(float, r0);
+  hi = __builtin_bit_cast(float, r1);
+}
+
 template <int D>
 __device__ __forceinline__ int swz(int key) {
   if constexpr (D == 128) return ((key & 3) << 2) | ((key >> 2) & 1) | (((key >> 4) & 1) << 1);
@@ -197,6 +211,8 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
     l_run[qg] = 0.f;
   }
   const float c2 = 1.4426950408889634f / __builtin_sqrtf((float)D);  // log2(e) / sqrt(D)
+  constexpr float kSlack = 8.f;  // the weights stay below 2^8
+  const bf16x2_t kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
   const int kend = CAUSAL ? min(q0 + kBQ * QG, S) : S;
   const int nb = (kend + kBK - 1) / kBK;
@@ -247,52 +263,71 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
     };
     read_v(0, vf[0]);
     // Mask, block maximum of the raw scores (lane pair l, l ^ 32 hold one
-    // query); the running maximum m is kept in base-2 units, m = max s c2.
+    // query); the maximum m is kept in base-2 units (scores times c2).
     const bool edge = k0 + kBK > S || (CAUSAL && k0 + kBK - 1 > qw);
     bf16x8_t pf[QG][4];
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
       if (edge) {
+        // score e of tile u is key k0 + 4 h2 + (32 u + 8 (e / 4) + e % 4),
+        // masked past the last key this query sees
+        const int last = (CAUSAL ? min(S - 1, qq[qg]) : S - 1) - k0 - 4 * h2;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int kk = k0 + 32 * u + 8 * (e >> 2) + 4 * h2 + (e & 3);
-            if (kk >= S || (CAUSAL && kk > qq[qg])) s[qg][u][e] = -__builtin_inff();
-          }
+          for (int e = 0; e < 16; ++e)
+            if (32 * u + 8 * (e >> 2) + (e & 3) > last) s[qg][u][e] = -__builtin_inff();
       }
-      float mx = -1e30f;
+      // four independent chains, then the two half-waves' maxima
+      float m4[4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int c = 0; c < 4; ++c) {
+        m4[c] = c == 0 ? -1e30f : s[qg][c >> 1][8 * (c & 1)];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qg][u][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qg], mx * c2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_new);
-      m_run[qg] = m_new;
-      // p = 2^(s c2 - m), one fused multiply-add per score; a masked score
-      // (-inf) gives 0.
-      float psum = 0.f;
+        for (int e = c == 0 ? 0 : 1; e < 8; ++e) m4[c] = fmaxf(m4[c], s[qg][c >> 1][8 * (c & 1) + e]);
+      }
+      float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])), mlo, mhi;
+      half_pair(mx, mlo, mhi);
+      mx = fmaxf(mlo, mhi);
+      // The reference maximum m is raised only when some lane's block
+      // maximum exceeds it by more than kSlack: the weights p = 2^(s c2 - m)
+      // then stay below 2^kSlack, and the accumulators and the sum l are
+      // rescaled (by 2^(m_old - m_new), exact 1 for the lanes whose maximum
+      // did not grow) only on those blocks.  Raising m at every new maximum
+      // would rescale on nearly every block: some lane of 32 queries usually
+      // finds a new maximum among the next 64 keys.  The quotient O / l does
+      // not depend on m; the weights are rounded to bf16 relative to their
+      // size either way.
+      const float m_blk = mx * c2;
+      if (__any(m_blk > m_run[qg] + kSlack)) {
+        const float m_new = fmaxf(m_run[qg], m_blk);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_new);
+        m_run[qg] = m_new;
+        l_run[qg] *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[qg][t] = acc[qg][t] * alpha;
+      }
+      const float m = m_run[qg];
+      // p = 2^(s c2 - m), one fused multiply-add per score (a masked score,
+      // -inf, gives 0), rounded to bf16 in pairs; l sums the rounded pairs
+      // (the weights the value products use), two chains of dot products
+      // with (1, 1).
+      float ps[2] = {0.f, 0.f};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         u32x4_t pk;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int e = 8 * (jj & 1) + 2 * e2;
-          const float a0 = __builtin_amdgcn_exp2f(fmaf(s[qg][jj >> 1][e], c2, -m_new));
-          const float a1 = __builtin_amdgcn_exp2f(fmaf(s[qg][jj >> 1][e + 1], c2, -m_new));
-          psum += a0 + a1;
-          pk[e2] = pack_bf16x2(a0, a1);
+          const float a0 = __builtin_amdgcn_exp2f(fmaf(s[qg][jj >> 1][e], c2, -m));
+          const float a1 = __builtin_amdgcn_exp2f(fmaf(s[qg][jj >> 1][e + 1], c2, -m));
+          const uint32_t w = pack_bf16x2(a0, a1);  // (a bit cast of pk[e2] would read pk[0])
+          pk[e2] = w;
+          ps[e2 & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), kOnes, ps[e2 & 1], false);
         }
         pf[qg][jj] = __builtin_bit_cast(bf16x8_t, pk);
       }
-      l_run[qg] = l_run[qg] * alpha + psum;
-      // The running maximum rarely grows after the first blocks: rescale the
-      // accumulators only when it did for some lane (alpha == 1 is exact).
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int t = 0; t < DT; ++t) acc[qg][t] = acc[qg][t] * alpha;
-      }
+      l_run[qg] += ps[0] + ps[1];
     }
     // O^T += V^T P^T over the 64 keys (4 k-steps of 16), the next k-step's
     // V^T fragments read while this one's MFMAs run.
@@ -335,7 +370,9 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
   // O = O^T / l: lane holds query qq, columns 32 t + 8 (e / 4) + 4 h2 + e % 4.
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
-    const float l_tot = l_run[qg] + __shfl_xor(l_run[qg], 32);
+    float llo, lhi;
+    half_pair(l_run[qg], llo, lhi);
+    const float l_tot = llo + lhi;
     if (qq[qg] < S) {
       const float inv = __builtin_amdgcn_rcpf(l_tot);
       uint16_t* orow = p.t.out[g] + ((int64_t)b * S + qq[qg]) * Hk + head * D + 4 * h2;
@@ -351,7 +388,6 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
     }
   }
 }
-
 
 }  // namespace
 

@@ -38,9 +38,13 @@ Backward (dY = dZ V_i^T, dA = dY * G, G = GeLU'(A)):
 * attention of one head from given bf16 q, k, v (exact inputs): with
   p_tj the exact softmax weights and W_t = sum_j p_tj |v_j|,
     |A_gpu - A| <= 1.5 u16 W_t + 1.01 u16 |A| + 2^-16 W_t
-  (the probabilities are rounded to bf16 for the products with V while the
-  normaliser sums them unrounded, the output is rounded to bf16, and the
-  float32 scores, exp2 and sums add far less).  On long sequences the
+  (the probabilities are rounded to bf16 for the products with V, and the
+  normaliser sums the same rounded values, so the output is a weighted mean
+  whose weights each moved by at most one bf16 rounding; the output is
+  rounded to bf16, and the float32 scores, exp2 and sums add far less; the
+  weights are taken against a reference maximum that may trail the running
+  one, so a weight can reach 2^8, which changes none of these relative
+  terms).  On long sequences the
   float32 sums over n keys add up to 4 (n + 2) u32 W_t (the weighted sum and
   the normaliser, n terms each) and the float32 scores move each weight by
   up to 2 e_s with e_s = 2 (d + 2) u32 max_j (|q| . |k_j|) / sqrt d; the
