@@ -3,7 +3,8 @@ tp_attn_core_shards, tp_attn_shard_forward) against the CPU fp64 oracle,
 element by element: the attention kernel from given bf16 projections at
 small and ragged sizes (sequences shorter than a key block, not a multiple
 of the 128-query block, head widths 64 and 128, causal or not, several heads
-and shards per launch), the projection GEMM with its bias epilogue, and the
+and shards per launch; scores rising along the keys, so that the kernel's
+reference maximum is raised late), the projection GEMM with its bias epilogue, and the
 whole block at small sizes and at the workload sizes on sampled rows; plus
 batched == single-shard bit-identity, both variants of the shard sum and M = 0.
 Bounds: tests/_helpers.py (the softmax weights for them are an independent
@@ -168,6 +169,60 @@ def _shard_inputs(inp, n_heads, k):
     Hk = H // k
     Wo = [np.ascontiguousarray(inp["Wo"][i * Hk:(i + 1) * Hk]) for i in range(k)]
     return Wqkv, bqkv, Wo
+
+
+GROW_CASES = [
+    # B, S, heads, d, causal, score growth per 64 keys (base 2) for the queries with c = 1
+    (1, 512, 2, 128, True, 10.0), (2, 300, 1, 64, False, 16.0), (1, 640, 3, 128, False, 6.0),
+]
+
+
+def _growing_qkv(B, S, heads, d, ramp, seed):
+    """bf16 projections whose scores rise along the keys at a rate that
+    differs per query: k_j[0] = a j (j the key's position in its sequence)
+    and q_t[0] = c_t in [-1, 1), spread over every 32 queries, so that in
+    base 2 the score of query t grows by about c_t ramp per 64 keys; the
+    other entries are N(0, 1)."""
+    from tensor_transformer_mlp_amd import inputs
+    Hk = heads * d
+    x = f64(inputs.draw(inputs.STREAM_X, (B * S, 3 * Hk), 1.0, "bf16", seed=seed)).astype(np.float32)
+    pos = np.tile(np.arange(S), B).astype(np.float32)
+    c = ((np.arange(B * S) * 37) % 64).astype(np.float32) / 32.0 - 1.0
+    a = ramp * np.sqrt(d) / (64.0 * np.log2(np.e))
+    for h in range(heads):
+        x[:, Hk + h * d] = a * pos
+        x[:, h * d] = c
+    return inputs.round_bf16(x)
+
+
+@pytest.mark.parametrize("B,S,heads,d,causal,ramp", GROW_CASES)
+def test_attn_core_growing_scores(tpm, orc, B, S, heads, d, causal, ramp):
+    """Scores that keep rising along the keys for some queries of a wave and
+    fall for others: the kernel's reference maximum has to be raised on late
+    key blocks for some lanes and not for others (partial rescales of
+    accumulators that already hold many blocks), and between raises the
+    weights grow up to 2^8.  Every row, both kernel variants, against the
+    oracle; the rows bound includes the float32 score error, which grows
+    with the scores here."""
+    import torch
+    say("attn_core growing scores B=%d S=%d heads=%d d=%d causal=%s ramp=%g" % (B, S, heads, d, causal, ramp))
+    qkv = _growing_qkv(B, S, heads, d, ramp, seed=3000 + S + d)
+    q64 = f64(qkv)
+    Hk, M = heads * d, B * S
+    ref = orc.attn_core(qkv, B, S, heads, d, causal)
+    rows = np.arange(M)
+    bound = attn_rows_bound(q64, rows, S, heads, d, ref, causal)
+    outs = []
+    for v in (0, 1):
+        A = torch.empty(M, Hk, dtype=torch.bfloat16, device="cuda")
+        tpm.tp_attn_core_shards_variant(v, [to_dev(qkv)], [A], B, S, heads, d, causal=causal)
+        torch.cuda.synchronize()
+        got = f64(from_dev(A))
+        assert np.all(np.isfinite(got))
+        assert_within(got, ref, bound, "A (variant %d)" % v)
+        say("  variant %d: rel_fro %.3e" % (v, rel_fro(got, ref)))
+        outs.append(got)
+    assert np.array_equal(outs[0], outs[1])
 
 
 def test_attn_qkv_parity(tpm, orc):
