@@ -9,8 +9,9 @@
 //
 // One workgroup = 4 waves = 128 QG queries of one (sequence, head); each wave
 // owns QG groups of 32 queries (QG = 1 or 2) and walks the keys in blocks of
-// 64 (causal: up to its last query), with the online softmax (running maximum
-// m and sum l per query).  Every K and V fragment a wave reads from LDS feeds
+// 64 (causal: up to its last query), with the online softmax (a reference
+// maximum m, raised when a block's scores exceed it by more than 2^8, and the
+// sum l per query).  Every K and V fragment a wave reads from LDS feeds
 // the MFMAs of all its query groups, so QG = 2 halves the LDS reads per
 // score:
 //   S^T = K Q^T    (keys x queries) on v_mfma_f32_32x32x16_bf16, K as the
